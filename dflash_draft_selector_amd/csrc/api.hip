@@ -1,0 +1,216 @@
+// C-ABI entry points of libdflash2: argument checks (before any HIP call), workspace
+// sizing, and dispatch to the kernel launchers.
+#include <math.h>
+
+#include "dflash2.h"
+#include "dflash2_internal.h"
+#include "topk_dev.h"
+
+using namespace df2;
+
+namespace {
+
+constexpr int64_t kMaxVocab = (int64_t)kMaxChunks * kChunkVec * 8;   // 2^19
+constexpr int64_t kMaxGridRows = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+dflash2_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : DFLASH2_ERR_HIP; }
+
+dflash2_status check_logits(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t ld) {
+  if (!logits) return DFLASH2_ERR_NULL;
+  if (rows < 1 || vocab < DFLASH2_NCAND || vocab > kMaxVocab || ld < vocab) return DFLASH2_ERR_SHAPE;
+  if (rows * topk_num_chunks(vocab) > kMaxGridRows) return DFLASH2_ERR_SHAPE;
+  if (!aligned16(logits) || (ld % 8) != 0) return DFLASH2_ERR_ALIGN;
+  return DFLASH2_OK;
+}
+
+dflash2_status check_emb(const void* a, const void* b, dflash2_dtype dt, int64_t vocab, int64_t dim) {
+  if (!a || !b) return DFLASH2_ERR_NULL;
+  if (dt != DFLASH2_F32 && dt != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
+  if (vocab < DFLASH2_NCAND || vocab > kMaxVocab) return DFLASH2_ERR_SHAPE;
+  if (!(dim == 64 || dim == 128 || dim == 256 || dim == 512)) return DFLASH2_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(b)) return DFLASH2_ERR_ALIGN;
+  return DFLASH2_OK;
+}
+
+dflash2_status check_bk(int64_t batch, int64_t K) {
+  if (batch < 1 || batch >= ((int64_t)1 << 31) || K < 1 || K > DFLASH2_MAX_K) return DFLASH2_ERR_SHAPE;
+  if (batch * K > kMaxGridRows) return DFLASH2_ERR_SHAPE;
+  return DFLASH2_OK;
+}
+
+dflash2_status check_temp(float t) { return (t >= 0.f && !isnan(t) && !isinf(t)) ? DFLASH2_OK : DFLASH2_ERR_VALUE; }
+
+template <typename WsT, typename F>
+dflash2_status carve_checked(void* ws, size_t bytes, F&& carve, WsT* out) {
+  Carver sizing(nullptr);
+  carve(sizing);
+  if (!ws) return DFLASH2_ERR_WORKSPACE;
+  if (bytes < sizing.off) return DFLASH2_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DFLASH2_ERR_ALIGN;
+  Carver c(ws);
+  *out = carve(c);
+  return DFLASH2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash2_abi_version(void) { return DFLASH2_ABI_VERSION; }
+
+const char* dflash2_status_str(int status) {
+  switch (status) {
+    case DFLASH2_OK: return "DFLASH2_OK";
+    case DFLASH2_ERR_NULL: return "DFLASH2_ERR_NULL";
+    case DFLASH2_ERR_SHAPE: return "DFLASH2_ERR_SHAPE";
+    case DFLASH2_ERR_ALIGN: return "DFLASH2_ERR_ALIGN";
+    case DFLASH2_ERR_DTYPE: return "DFLASH2_ERR_DTYPE";
+    case DFLASH2_ERR_WORKSPACE: return "DFLASH2_ERR_WORKSPACE";
+    case DFLASH2_ERR_VALUE: return "DFLASH2_ERR_VALUE";
+    case DFLASH2_ERR_HIP: return "DFLASH2_ERR_HIP";
+    default: return "DFLASH2_UNKNOWN_STATUS";
+  }
+}
+
+size_t dflash2_topk16_workspace(int64_t rows, int64_t vocab) {
+  if (rows < 1 || vocab < 1) return 0;
+  Carver c(nullptr);
+  carve_topk(c, rows, vocab);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_topk16(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t ld, int32_t* cand_idx,
+                              float* cand_val, int32_t* row_status, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  dflash2_status st = check_logits(logits, rows, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  if (!cand_idx || !cand_val) return DFLASH2_ERR_NULL;
+  TopkWs ws;
+  st = carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_topk(c, rows, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_topk16(logits, (int)rows, (int)vocab, ld, cand_idx, cand_val, row_status, ws, stream));
+}
+
+size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim) {
+  if (rows < 1 || hidden < 1 || dim < 1) return 0;
+  Carver c(nullptr);
+  carve_gate(c, rows, hidden, dim);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dtype w_dtype, const float* bias,
+                                    int64_t rows, int64_t hidden, int64_t dim, dflash2_gate_act act, float* H,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!h || !w_h || !H) return DFLASH2_ERR_NULL;
+  if (w_dtype != DFLASH2_F32 && w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
+  if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
+  if (rows < 1 || rows > kMaxGridRows || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24) ||
+      !pow2_in(dim, 16, 1024))
+    return DFLASH2_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_h)) return DFLASH2_ERR_ALIGN;
+  GateWs ws;
+  dflash2_status st =
+      carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_gate(c, rows, hidden, dim); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_gate(h, w_h, w_dtype == DFLASH2_BF16, bias, (int)rows, (int)hidden, (int)dim, (int)act, H,
+                                ws, stream));
+}
+
+dflash2_status dflash2_pair_score(const int32_t* cand_idx, const float* cand_val, const int32_t* verified,
+                                  const void* emb_a, const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab,
+                                  int64_t dim, const float* H, int64_t batch, int64_t K, float* S, int32_t* row_status,
+                                  hipStream_t stream) {
+  if (!cand_idx || !cand_val || !verified || !H || !S) return DFLASH2_ERR_NULL;
+  dflash2_status st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
+  if (st != DFLASH2_OK) return st;
+  st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  if (!aligned16(H)) return DFLASH2_ERR_ALIGN;
+  return hip_status(launch_pair_score(cand_idx, cand_val, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab,
+                                      (int)dim, H, (int)batch, (int)K, S, row_status, stream));
+}
+
+dflash2_status dflash2_walk(const float* S, const int32_t* cand_idx, int64_t batch, int64_t K, float temperature,
+                            uint64_t seed, int32_t* tokens, int32_t* slots, float* q, hipStream_t stream) {
+  if (!S || !cand_idx || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  st = check_temp(temperature);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_walk(S, cand_idx, (int)batch, (int)K, temperature, seed, tokens, slots, q, stream));
+}
+
+size_t dflash2_select_workspace(int64_t batch, int64_t K, int64_t vocab) {
+  if (batch < 1 || K < 1 || vocab < 1) return 0;
+  Carver c(nullptr);
+  carve_select(c, batch, K, vocab);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                              const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab, int64_t dim, const float* H,
+                              int64_t batch, int64_t K, float temperature, uint64_t seed, int32_t* cand_idx,
+                              float* cand_val, float* S, int32_t* tokens, int32_t* slots, float* q,
+                              int32_t* row_status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  st = check_logits(logits, batch * K, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
+  if (st != DFLASH2_OK) return st;
+  if (!verified || !H || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
+  if (!aligned16(H)) return DFLASH2_ERR_ALIGN;
+  st = check_temp(temperature);
+  if (st != DFLASH2_OK) return st;
+  SelectWs ws;
+  st = carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_select(c, batch, K, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_select(logits, ld, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab, (int)dim,
+                                  H, (int)batch, (int)K, temperature, seed, cand_idx, cand_val, S, tokens, slots, q,
+                                  row_status, ws, stream));
+}
+
+dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float* taps, int64_t sites, int64_t batch,
+                                int64_t K, int64_t hidden, int64_t group, float* y, hipStream_t stream) {
+  if (!x || !x_prev || !taps || !y) return DFLASH2_ERR_NULL;
+  if (sites < 1 || batch < 1 || K < 1 || K > DFLASH2_MAX_K || hidden < 1 || group < 1 || hidden % group != 0)
+    return DFLASH2_ERR_SHAPE;
+  if (sites * batch * hidden > ((int64_t)1 << 40)) return DFLASH2_ERR_SHAPE;
+  return hip_status(launch_conv2tap(x, x_prev, taps, sites, batch, (int)K, hidden, group, y, stream));
+}
+
+size_t dflash2_spec_accept_workspace(int64_t batch, int64_t K, int64_t vocab) {
+  if (batch < 1 || K < 1 || vocab < 1) return 0;
+  Carver c(nullptr);
+  carve_accept(c, batch * (K + 1), vocab);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, int64_t batch_stride,
+                                   const int32_t* tokens, const int32_t* cand_idx, const float* q, int64_t batch,
+                                   int64_t K, int64_t vocab, float temperature, uint64_t seed, int32_t* out_tokens,
+                                   int32_t* n_accepted, int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  const int64_t nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
+  st = check_logits(target_logits, nrows, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  if (batch_stride < 0 || (batch_stride > 0 && batch_stride < (K + 1) * ld)) return DFLASH2_ERR_SHAPE;
+  if (batch_stride % 8 != 0) return DFLASH2_ERR_ALIGN;
+  if (!tokens || !cand_idx || !out_tokens || !n_accepted) return DFLASH2_ERR_NULL;
+  st = check_temp(temperature);
+  if (st != DFLASH2_OK) return st;
+  if (temperature > 0.f && !q) return DFLASH2_ERR_NULL;
+  AcceptWs ws;
+  st = carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_accept(c, nrows, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_spec_accept(target_logits, ld, batch_stride, tokens, cand_idx, q, (int)batch, (int)K,
+                                       (int)vocab, temperature, seed, out_tokens, n_accepted, row_status, ws, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace df2 {
+
+// Carves aligned sub-buffers out of a caller workspace (or only sizes them when the
+// base is null).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+struct TopkWs {
+  unsigned long long* partials;   // [rows][nchunks * 4 waves][16] sorted candidate lists
+};
+TopkWs carve_topk(Carver& c, int64_t rows, int64_t vocab);
+
+struct SelectWs {
+  TopkWs topk;
+  int* next;                      // [rows][16] successor slot per predecessor slot
+  float* qtab;                    // [rows][16][16] distribution of each predecessor's row
+};
+SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab);
+
+struct GateWs {
+  float* partial;                 // [nsplit][mtiles*16][dim]
+  unsigned int* ticket;           // [mtiles]
+};
+int gate_splits(int64_t rows, int64_t hidden);
+GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim);
+
+struct AcceptWs {
+  float* chunk_max;               // [nrows][nchunks]
+  float* chunk_sum;               // [nrows][nchunks]
+  unsigned long long* chunk_arg;  // [nrows][nchunks] (greedy)
+  float* row_max;                 // [nrows]
+  float* row_sum;                 // [nrows]
+  unsigned long long* row_arg;    // [nrows]
+  unsigned int* row_ticket;       // [nrows]
+};
+AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab);
+
+hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld, int32_t* cand_idx,
+                         float* cand_val, int32_t* row_status, TopkWs ws, hipStream_t s);
+
+hipError_t launch_pair_score(const int32_t* cand_idx, const float* cand_val, const int32_t* verified,
+                             const void* emb_a, const void* emb_b, bool bf16, int vocab, int dim, const float* H,
+                             int batch, int K, float* S, int32_t* row_status, hipStream_t s);
+
+hipError_t launch_walk(const float* S, const int32_t* cand_idx, int batch, int K, float temperature,
+                       uint64_t seed, int32_t* tokens, int32_t* slots, float* q, hipStream_t s);
+
+hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                         const void* emb_b, bool bf16, int vocab, int dim, const float* H, int batch, int K,
+                         float temperature, uint64_t seed, int32_t* cand_idx, float* cand_val, float* S,
+                         int32_t* tokens, int32_t* slots, float* q, int32_t* row_status, SelectWs ws,
+                         hipStream_t s);
+
+hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden,
+                       int dim, int act, float* H, GateWs ws, hipStream_t s);
+
+hipError_t launch_conv2tap(const float* x, const float* x_prev, const float* taps, int64_t sites, int64_t batch,
+                           int K, int64_t hidden, int64_t group, float* y, hipStream_t s);
+
+hipError_t launch_spec_accept(const uint16_t* target, int64_t ld, int64_t batch_stride, const int32_t* tokens,
+                              const int32_t* cand_idx, const float* q, int batch, int K, int vocab,
+                              float temperature, uint64_t seed, int32_t* out_tokens, int32_t* n_accepted,
+                              int32_t* row_status, AcceptWs ws, hipStream_t s);
+
+}  // namespace df2

@@ -1,0 +1,479 @@
+// Lossless verify (FreeToken PR "Adds DFlash 2", section "Details", sampled verify:
+// accept with min(1, p/q), on a reject resample from max(0, p - q); all-greedy keeps
+// the prefix match.  pegainfer issue "DFlash 2 proposer", "Proposal", phase 3).
+//
+// Pass 1 (k_accept_stats): split-vocabulary statistics of every target row -- max and
+// sum of exp((l - max)/T) per chunk and per row, or the row argmax when T == 0.
+// Pass 2 (k_accept_decide): one block per request runs the accept tests, then draws
+// the committed token by inverse CDF: the chunk is found from the pass-1 chunk masses
+// (minus the draft's mass at its candidates), and only that chunk is rescanned.
+#include "device_common.h"
+#include "dflash2_internal.h"
+#include "topk_dev.h"
+
+namespace df2 {
+
+constexpr int kAccThreads = 256;
+constexpr int kAccVecPerThread = 8;                          // 8 x 16 B loads in flight per lane
+constexpr int kAccChunkVec = kAccThreads * kAccVecPerThread;  // 2048 vectors = 16384 logits
+constexpr int kAccMaxChunks = 32;                            // vocab <= 2^19
+
+__host__ __device__ __forceinline__ int acc_num_chunks(long long vocab) {
+  const long long nvec = (vocab + 7) / 8;
+  return (int)((nvec + kAccChunkVec - 1) / kAccChunkVec);
+}
+
+AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab) {
+  AcceptWs w;
+  const size_t n = (size_t)nrows * acc_num_chunks(vocab);
+  w.chunk_max = c.take<float>(n);
+  w.chunk_sum = c.take<float>(n);
+  w.chunk_arg = c.take<unsigned long long>(n);
+  w.row_max = c.take<float>((size_t)nrows);
+  w.row_sum = c.take<float>((size_t)nrows);
+  w.row_arg = c.take<unsigned long long>((size_t)nrows);
+  w.row_ticket = c.take<unsigned int>((size_t)nrows);
+  return w;
+}
+
+__device__ __forceinline__ float order_to_float(int s) { return bf16_to_f32(order_to_bits(s)); }
+
+template <typename T>
+__device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
+  // fixed-order block reduction over 4 waves (deterministic)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const T other = __shfl_xor(v, o);
+    v = is_max ? (other > v ? other : v) : v + other;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  T r = red[0];
+  for (int w = 1; w < kAccThreads / 64; ++w) r = is_max ? (red[w] > r ? red[w] : r) : r + red[w];
+  return r;
+}
+
+__global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __restrict__ target, int64_t ld,
+                                                              int64_t batch_stride, int K, int V, int nchunks,
+                                                              float inv_t, AcceptWs ws) {
+  __shared__ float s_redf[4];
+  __shared__ int s_redi[4];
+  __shared__ unsigned long long s_redu[4];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x / nchunks;
+  const int c = blockIdx.x - r * nchunks;
+  const int b = batch_stride == 0 ? 0 : r / (K + 1);
+  const int t = batch_stride == 0 ? r : r - b * (K + 1);
+  const uint16_t* rowp = target + (size_t)b * batch_stride + (size_t)t * ld;
+  const u32x4* rowv = reinterpret_cast<const u32x4*>(rowp);
+  const int v0 = chunk_begin(V, nchunks, c), v1 = chunk_begin(V, nchunks, c + 1);
+  const int nfull = V >> 3;
+
+  u32x4 d[kAccVecPerThread];
+#pragma unroll
+  for (int k = 0; k < kAccVecPerThread; ++k) {
+    const int v = v0 + tid + k * kAccThreads;
+    if (v < v1 && v < nfull) {
+      d[k] = __builtin_nontemporal_load(rowv + v);
+    } else {
+      uint32_t wds[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};   // -inf padding
+      if (v < v1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (8 * v + e < V) {
+            const uint32_t bb = rowp[8 * v + e];
+            wds[e >> 1] = (e & 1) ? ((wds[e >> 1] & 0xffffu) | (bb << 16)) : ((wds[e >> 1] & 0xffff0000u) | bb);
+          }
+        }
+      }
+      d[k] = (u32x4){wds[0], wds[1], wds[2], wds[3]};
+    }
+  }
+
+  const size_t ci = (size_t)r * nchunks + c;
+  if (inv_t == 0.f) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int k = 0; k < kAccVecPerThread; ++k) {
+      const int v = v0 + tid + k * kAccThreads;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int id = 8 * v + e;
+        if (v < v1 && id < V) {
+          const uint32_t bits = elem_bits(d[k], e);
+          const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)id, bits);
+          best = comp > best ? comp : best;
+        }
+      }
+    }
+    best = block_reduce<unsigned long long>(best, s_redu, true);
+    if (tid == 0) st_agent(ws.chunk_arg + ci, best);
+    if (!arrive_last(ws.row_ticket + r, (unsigned)nchunks, &s_flag)) return;
+    if (tid == 0) {
+      unsigned long long m = 0ull;
+      for (int j = 0; j < nchunks; ++j) {
+        const unsigned long long a = ld_agent(ws.chunk_arg + (size_t)r * nchunks + j);
+        m = a > m ? a : m;
+      }
+      ws.row_arg[r] = m;
+    }
+    return;
+  }
+
+  // signed-order max / min (to find +inf and NaN) and the chunk maximum
+  int smax = -32768, smin = 32767;
+#pragma unroll
+  for (int k = 0; k < kAccVecPerThread; ++k) {
+    const s16x2 a = signed_order2(d[k].x), bq = signed_order2(d[k].y);
+    const s16x2 cq = signed_order2(d[k].z), dq = signed_order2(d[k].w);
+    const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, bq), __builtin_elementwise_max(cq, dq));
+    const s16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(a, bq), __builtin_elementwise_min(cq, dq));
+    smax = max_halves(mx) > smax ? max_halves(mx) : smax;
+    const int lo = mn.x < mn.y ? (int)mn.x : (int)mn.y;
+    smin = lo < smin ? lo : smin;
+  }
+  smax = block_reduce<int>(smax, s_redi, true);
+  smin = -block_reduce<int>(-smin, s_redi, true);
+  const bool nonfinite = smax >= 32640 || smin < -32641;       // +inf / +NaN, or -NaN
+  const float m_c = order_to_float(smax > 32640 ? 32640 : smax);
+  float sum = 0.f;
+  if (!nonfinite && m_c != -__builtin_inff()) {
+#pragma unroll
+    for (int k = 0; k < kAccVecPerThread; ++k) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sum += expf((bf16_lo(d[k][w]) - m_c) * inv_t);
+        sum += expf((bf16_hi(d[k][w]) - m_c) * inv_t);
+      }
+    }
+  }
+  sum = block_reduce<float>(sum, s_redf, false);
+  if (tid == 0) {
+    st_agent(ws.chunk_max + ci, nonfinite ? __builtin_nanf("") : m_c);
+    st_agent(ws.chunk_sum + ci, sum);
+  }
+  if (!arrive_last(ws.row_ticket + r, (unsigned)nchunks, &s_flag)) return;
+  if (tid == 0) {
+    float m = -__builtin_inff();
+    bool bad = false;
+    for (int j = 0; j < nchunks; ++j) {
+      const float mj = ld_agent(ws.chunk_max + (size_t)r * nchunks + j);
+      if (__builtin_isnan(mj)) bad = true;
+      else m = fmaxf(m, mj);
+    }
+    float Z = 0.f;
+    for (int j = 0; j < nchunks; ++j) {
+      const float mj = ld_agent(ws.chunk_max + (size_t)r * nchunks + j);
+      if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ld_agent(ws.chunk_sum + (size_t)r * nchunks + j) * expf((mj - m) * inv_t);
+    }
+    ws.row_max[r] = m;
+    ws.row_sum[r] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
+  }
+}
+
+struct DecideShared {
+  int status;
+  int tstar;
+  int ids_bad;
+  int q_bad;
+  int pick;
+  int chunk;
+  float rem;
+  int ncl;
+  int cl_id[kNC];
+  float cl_qf[kNC];
+  float R[kAccMaxChunks];
+  float red[4];
+  float tsum[kAccThreads];
+};
+
+// Inverse-CDF draw from row `r` (stats index) of the target: weights p (residual ==
+// false) or max(0, p - q) with q supported on the request's candidates of that
+// position.  Block-wide; returns the token id (valid in every thread).
+__device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, int V, int nchunks, float inv_t, float u,
+                             bool residual, const int32_t* __restrict__ cand, const float* __restrict__ qrow,
+                             const AcceptWs& ws, DecideShared& sm) {
+  const int tid = threadIdx.x;
+  const float m = ws.row_max[r];
+  const float invZ = 1.f / ws.row_sum[r];
+  if (tid == 0) {
+    int n = 0;
+    if (residual) {
+      // distinct candidate ids with their total draft mass, sorted by id
+      for (int j = 0; j < kNC; ++j) {
+        const int id = cand[j];
+        bool seen = false;
+        for (int i = 0; i < j; ++i) seen |= cand[i] == id;
+        if (seen) continue;
+        float qf = 0.f;
+        for (int i = 0; i < kNC; ++i) qf += cand[i] == id ? qrow[i] : 0.f;
+        int pos = n++;
+        while (pos > 0 && sm.cl_id[pos - 1] > id) {
+          sm.cl_id[pos] = sm.cl_id[pos - 1];
+          sm.cl_qf[pos] = sm.cl_qf[pos - 1];
+          --pos;
+        }
+        sm.cl_id[pos] = id;
+        sm.cl_qf[pos] = qf;
+      }
+    }
+    sm.ncl = n;
+  }
+  __syncthreads();
+  // coarse: mass of every chunk
+  for (int c = tid; c < nchunks; c += kAccThreads) {
+    const float mc = ws.chunk_max[(size_t)r * nchunks + c];
+    float P = mc == -__builtin_inff() ? 0.f : ws.chunk_sum[(size_t)r * nchunks + c] * expf((mc - m) * inv_t) * invZ;
+    const int e0 = 8 * chunk_begin(V, nchunks, c);
+    const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
+    for (int i = 0; i < sm.ncl; ++i) {
+      const int id = sm.cl_id[i];
+      if (id >= e0 && id < e1) {
+        const float p = expf((bf16_to_f32(rowp[id]) - m) * inv_t) * invZ;
+        P -= fminf(p, sm.cl_qf[i]);
+      }
+    }
+    sm.R[c] = fmaxf(P, 0.f);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Zr = 0.f;
+    for (int c = 0; c < nchunks; ++c) Zr += sm.R[c];
+    const float target = u * Zr;
+    float run = 0.f;
+    int pick = -1, lastpos = 0;
+    float before = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+      if (pick < 0 && target < run + sm.R[c]) {
+        pick = c;
+        before = run;
+      }
+      run += sm.R[c];
+      if (sm.R[c] > 0.f) lastpos = c;
+    }
+    if (pick < 0) {
+      pick = lastpos;
+      before = run - sm.R[lastpos];
+    }
+    sm.chunk = (residual && !(Zr > 0.f)) ? -1 : pick;   // a residual without mass
+    sm.rem = target - before;
+    sm.pick = -1;
+  }
+  __syncthreads();
+  if (sm.chunk < 0) return -1;
+  // fine: rescan the chosen chunk; thread i owns a contiguous run of L logits
+  const int c = sm.chunk;
+  const int e0 = 8 * chunk_begin(V, nchunks, c);
+  const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
+  const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;   // <= 64
+  const int a0 = e0 + tid * L;
+  float rv[64];
+  int ci = 0;
+  while (ci < sm.ncl && sm.cl_id[ci] < a0) ++ci;
+  float tsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    u32x4 vec = {0u, 0u, 0u, 0u};
+    const int base = a0 + 8 * k;
+    if (8 * k < L && base + 8 <= e1) vec = *reinterpret_cast<const u32x4*>(rowp + base);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int id = base + e;
+      float rr = 0.f;
+      if (8 * k < L && id < e1) {
+        const uint32_t bits = (base + 8 <= e1) ? elem_bits(vec, e) : (uint32_t)rowp[id];
+        const float p = expf((bf16_to_f32(bits) - m) * inv_t) * invZ;
+        rr = p;
+        if (ci < sm.ncl && sm.cl_id[ci] == id) {
+          rr = fmaxf(p - sm.cl_qf[ci], 0.f);
+          ++ci;
+        }
+      }
+      rv[8 * k + e] = rr;
+      tsum += rr;
+    }
+  }
+  sm.tsum[tid] = tsum;
+  __syncthreads();
+  if (tid == 0) {
+    // exclusive scan in thread order; first thread whose run crosses the remainder
+    float run = 0.f;
+    int who = -1, lastpos = -1;
+    float before = 0.f;
+    for (int i = 0; i < kAccThreads; ++i) {
+      if (who < 0 && sm.rem < run + sm.tsum[i]) {
+        who = i;
+        before = run;
+      }
+      run += sm.tsum[i];
+      if (sm.tsum[i] > 0.f) lastpos = i;
+    }
+    sm.status = who;               // borrowed as scratch: crossing thread
+    sm.red[0] = before;
+    sm.red[1] = (float)lastpos;
+  }
+  __syncthreads();
+  const int who = sm.status;
+  const int lastpos = (int)sm.red[1];
+  if (tid == who || (who < 0 && tid == lastpos)) {
+    float run = sm.red[0];
+    int pick = -1, lastp = -1;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+      if (e < L && a0 + e < e1) {
+        run += rv[e];
+        if (pick < 0 && who >= 0 && sm.rem < run) pick = a0 + e;
+        if (rv[e] > 0.f) lastp = a0 + e;
+      }
+    }
+    sm.pick = pick >= 0 ? pick : lastp;
+  }
+  __syncthreads();
+  return sm.pick;
+}
+
+__global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* __restrict__ target, int64_t ld,
+                                                               int64_t batch_stride, const int32_t* __restrict__ tokens,
+                                                               const int32_t* __restrict__ cand_idx,
+                                                               const float* __restrict__ q, int K, int V, int nchunks,
+                                                               float inv_t, uint64_t seed, int32_t* __restrict__ out_tokens,
+                                                               int32_t* __restrict__ n_accepted,
+                                                               int32_t* __restrict__ row_status, AcceptWs ws) {
+  __shared__ DecideShared sm;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int32_t* tok_b = tokens + (size_t)b * K;
+  const int32_t* cand_b = cand_idx + (size_t)b * K * kNC;
+  const uint16_t* tb = target + (size_t)b * batch_stride;
+  const int rbase = batch_stride == 0 ? 0 : b * (K + 1);
+  int32_t* out_b = out_tokens + (size_t)b * (K + 1);
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+
+  if (tid == 0) {
+    sm.ids_bad = 0;
+    sm.q_bad = 0;
+    sm.tstar = K;
+  }
+  __syncthreads();
+  for (int e = tid; e < K * (kNC + 1); e += kAccThreads) {
+    const int id = e < K ? tok_b[e] : cand_b[e - K];
+    if (id < 0 || id >= V) atomicOr(&sm.ids_bad, 1);
+  }
+  __syncthreads();
+  const bool ids_bad = sm.ids_bad != 0;
+  for (int e = tid; e <= K; e += kAccThreads) out_b[e] = -1;
+
+  if (inv_t == 0.f) {
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      while (t < K) {
+        const int g = rc_id(ws.row_arg[rbase + t]);
+        if (tok_b[t] != g) break;
+        out_b[t] = g;
+        ++t;
+      }
+      out_b[t] = rc_id(ws.row_arg[rbase + t]);
+      n_accepted[b] = t;
+      if (row_status) row_status[b] = ids_bad ? 2 : 0;
+    }
+    return;
+  }
+
+  // non-finite target rows: commit nothing
+  int nonfinite = 0;
+  for (int t = 0; t <= K; ++t) nonfinite |= !__builtin_isfinite(ws.row_sum[rbase + t]);
+  if (nonfinite) {
+    if (tid == 0) {
+      n_accepted[b] = 0;
+      if (row_status) row_status[b] = 1;
+    }
+    return;
+  }
+
+  // validity of the draft distributions
+  if (tid < K) {
+    const float* qr = q + ((size_t)b * K + tid) * kNC;
+    float s = 0.f, qx = 0.f;
+    bool ok = true;
+    for (int j = 0; j < kNC; ++j) {
+      const float v = qr[j];
+      ok &= __builtin_isfinite(v) && v >= 0.f;
+      s += v;
+      qx += cand_b[tid * kNC + j] == tok_b[tid] ? v : 0.f;
+    }
+    ok &= fabsf(s - 1.f) <= 1e-3f;
+    if (!ids_bad) ok &= qx > 0.f;
+    if (!ok) atomicOr(&sm.q_bad, 1);
+  }
+  __syncthreads();
+  const bool q_bad = sm.q_bad != 0;
+  int status = (ids_bad ? 2 : 0) | (q_bad ? 4 : 0);
+
+  if (ids_bad || q_bad) {
+    const float u_res = word_to_uniform(philox4x32_10(0u, (uint32_t)b, 1u, 0u, k0, k1).x1);
+    const int v = draw_from_row(tb, rbase, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+    if (tid == 0) {
+      out_b[0] = v;
+      n_accepted[b] = 0;
+      if (row_status) row_status[b] = status;
+    }
+    return;
+  }
+
+  // accept tests (all positions at once; the first reject decides)
+  if (tid < K) {
+    const int t = tid;
+    const int x = tok_b[t];
+    float qx = 0.f;
+    const float* qr = q + ((size_t)b * K + t) * kNC;
+    for (int j = 0; j < kNC; ++j) qx += cand_b[t * kNC + j] == x ? qr[j] : 0.f;
+    const float px = expf((bf16_to_f32(tb[(size_t)t * ld + x]) - ws.row_max[rbase + t]) * inv_t) / ws.row_sum[rbase + t];
+    const float u_acc = word_to_uniform(philox4x32_10((uint32_t)t, (uint32_t)b, 1u, 0u, k0, k1).x0);
+    if (!(u_acc * qx < px)) atomicMin(&sm.tstar, t);
+  }
+  __syncthreads();
+  const int tstar = sm.tstar;
+  for (int t = tid; t < tstar; t += kAccThreads) out_b[t] = tok_b[t];
+  const float u_res = word_to_uniform(philox4x32_10((uint32_t)tstar, (uint32_t)b, 1u, 0u, k0, k1).x1);
+  int v;
+  if (tstar < K) {
+    const uint16_t* rowp = tb + (size_t)tstar * ld;
+    const int32_t* cand_t = cand_b + tstar * kNC;
+    const float* q_t = q + ((size_t)b * K + tstar) * kNC;
+    // residual mass: 1 - sum over candidates of min(p, q) is positive after any reject
+    v = draw_from_row(rowp, rbase + tstar, V, nchunks, inv_t, u_res, true, cand_t, q_t, ws, sm);
+    if (v < 0) {
+      status |= 8;
+      v = draw_from_row(rowp, rbase + tstar, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+    }
+  } else {
+    v = draw_from_row(tb + (size_t)K * ld, rbase + K, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+  }
+  if (tid == 0) {
+    out_b[tstar] = v;
+    n_accepted[b] = tstar;
+    if (row_status) row_status[b] = status;
+  }
+}
+
+hipError_t launch_spec_accept(const uint16_t* target, int64_t ld, int64_t batch_stride, const int32_t* tokens,
+                              const int32_t* cand_idx, const float* q, int batch, int K, int vocab, float temperature,
+                              uint64_t seed, int32_t* out_tokens, int32_t* n_accepted, int32_t* row_status, AcceptWs ws,
+                              hipStream_t s) {
+  const int nchunks = acc_num_chunks(vocab);
+  const int nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
+  const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
+  hipLaunchKernelGGL(k_accept_stats, dim3((unsigned)(nrows * nchunks)), dim3(kAccThreads), 0, s, target, ld,
+                     batch_stride, K, vocab, nchunks, inv_t, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_accept_decide, dim3((unsigned)batch), dim3(kAccThreads), 0, s, target, ld, batch_stride, tokens,
+                     cand_idx, q, K, vocab, nchunks, inv_t, seed, out_tokens, n_accepted, row_status, ws);
+  return hipGetLastError();
+}
+
+}  // namespace df2

@@ -1,0 +1,306 @@
+// Top-16, pair-score and walk kernels, and the proposer step built from them.
+//
+// The proposer step (dflash2_select) runs as three back-to-back kernels on one stream:
+//   1. k_chunk_lists  streams the logits; every wave publishes a candidate list holding
+//                     the best 16 of the logits its lanes loaded (no block-level or
+//                     cross-block sync);
+//   2. k_positions    one block per draft position: merges the lists of rows t-1 and t,
+//                     writes row t's candidates, computes the 16 x 16 scores of t and
+//                     the successor table (slot taken from each predecessor slot);
+//   3. k_walk_tables  one block per request: chases the tables from the verified row
+//                     and writes tokens, slots and q.
+// Kernel boundaries replace every cross-work-group handoff, so no work-group ever
+// waits for another and no workspace counter exists.
+#include "dflash2_internal.h"
+#include "pair_dev.h"
+#include "topk_dev.h"
+
+namespace df2 {
+
+constexpr int kListsPerChunk = kTopkWaves;        // one candidate list per wave
+
+__host__ __device__ __forceinline__ int lists_per_row(long long vocab) { return topk_num_chunks(vocab) * kListsPerChunk; }
+
+TopkWs carve_topk(Carver& c, int64_t rows, int64_t vocab) {
+  TopkWs w;
+  w.partials = c.take<unsigned long long>((size_t)rows * lists_per_row(vocab) * kListLen);
+  return w;
+}
+
+SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab) {
+  SelectWs w;
+  w.topk = carve_topk(c, batch * K, vocab);
+  w.next = c.take<int>((size_t)(batch * K * kNC));
+  w.qtab = c.take<float>((size_t)(batch * K * kNC * kNC));
+  return w;
+}
+
+// Row merge state of up to two rows; their list entries sit in dynamic LDS.
+struct MergeShared {
+  unsigned long long cbuf[2][kMergeCandCap + 8];
+  unsigned long long top[2][kNC];
+  int bits;
+};
+
+// 16-byte aligned: the lists are copied in with 16-byte LDS stores.
+extern __shared__ __attribute__((aligned(16))) unsigned long long dyn_lists[];
+
+// ---- stage 1: per-wave candidate lists -------------------------------------------------
+
+__global__ void __launch_bounds__(kTopkThreads) k_chunk_lists(const uint16_t* __restrict__ logits, int64_t ld, int V,
+                                                              int nchunks, unsigned long long* __restrict__ partials) {
+  __shared__ ChunkShared sm;
+  const int row = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x - row * nchunks;
+  const int wave = threadIdx.x >> 6;
+  wave_list(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1),
+            sm.w[wave], partials + (((size_t)row * nchunks + chunk) * kListsPerChunk + wave) * kListLen);
+}
+
+// ---- top-16: merge each row's lists (one wave per row) ---------------------------------
+
+__global__ void __launch_bounds__(kWave) k_merge_lists(const unsigned long long* __restrict__ partials, int nlists,
+                                                       int32_t* __restrict__ cand_idx, float* __restrict__ cand_val,
+                                                       int32_t* __restrict__ row_status) {
+  __shared__ MergeShared ms;
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const int n = nlists * kListLen;
+  wave_stage_lists(partials + (size_t)row * n, n, dyn_lists);
+  wave_merge_lists(dyn_lists, n, ms.cbuf[0], ms.top[0]);
+  const unsigned long long rc = ms.top[0][lane & 15];
+  const float v = bf16_to_f32(rc_bits(rc));
+  if (lane < kNC) {
+    cand_idx[(size_t)row * kNC + lane] = rc ? rc_id(rc) : 0;
+    cand_val[(size_t)row * kNC + lane] = v;
+  }
+  const unsigned long long bad = __ballot(lane < kNC && !__builtin_isfinite(v));
+  if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
+}
+
+// ---- pair scores ------------------------------------------------------------------------
+
+template <int DIM, bool BF16>
+__global__ void __launch_bounds__(kPairThreads) k_pair_score(const int32_t* __restrict__ cand_idx,
+                                                             const float* __restrict__ cand_val,
+                                                             const int32_t* __restrict__ verified,
+                                                             const void* __restrict__ emb_a,
+                                                             const void* __restrict__ emb_b, int V,
+                                                             const float* __restrict__ H, int K, float* __restrict__ S,
+                                                             int32_t* __restrict__ row_status) {
+  __shared__ PairShared sm;
+  const int pos = blockIdx.x;
+  const int b = pos / K, p = pos - b * K;
+  const int tid = threadIdx.x;
+  if (tid < kNC) {
+    sm.prev[tid] = p == 0 ? verified[b] : cand_idx[((size_t)pos - 1) * kNC + tid];
+    sm.cur[tid] = cand_idx[(size_t)pos * kNC + tid];
+    sm.U[tid] = cand_val[(size_t)pos * kNC + tid];
+  }
+  __syncthreads();
+  const int bits = pair_tile<DIM, BF16>(emb_a, emb_b, V, H + (size_t)pos * DIM, S + (size_t)pos * kNC * kNC, sm);
+  if (row_status && tid == 0) row_status[pos] = bits;
+}
+
+// ---- walk ------------------------------------------------------------------------------
+
+// From scores alone: position by position, build the successor table, follow it from
+// the slot taken at the previous position, and emit that row's distribution.
+__global__ void __launch_bounds__(256) k_walk(const float* __restrict__ S, const int32_t* __restrict__ cand_idx, int K,
+                                              float inv_t, uint64_t seed, int32_t* __restrict__ tokens,
+                                              int32_t* __restrict__ slots, float* __restrict__ q) {
+  __shared__ int s_next[kNC];
+  const int b = blockIdx.x;
+  const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const float* S_b = S + (size_t)b * K * kNC * kNC;
+  int from = 0;                                       // slot taken at the previous position
+  for (int t = 0; t < K; ++t) {
+    const float u = inv_t == 0.f ? 0.f : walk_uniform(seed, (uint32_t)b, (uint32_t)t);
+    float qj;
+    const int pick = row16_pick(S_b[((size_t)t * kNC + i) * kNC + j], inv_t, u, &qj);
+    if (j == 0) s_next[i] = pick;
+    if (i == from) q[((size_t)b * K + t) * kNC + j] = qj;
+    __syncthreads();
+    const int to = s_next[from];
+    if (threadIdx.x == 0) {
+      slots[(size_t)b * K + t] = to;
+      tokens[(size_t)b * K + t] = cand_idx[((size_t)b * K + t) * kNC + to];
+    }
+    __syncthreads();
+    from = to;
+  }
+}
+
+// From the successor tables stage 2 built: next[t][i] (slot taken at t after slot i at
+// t - 1) and, when sampling, qtab[t][i][.] (that row's distribution).
+__global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ next, const float* __restrict__ qtab,
+                                                     const int32_t* __restrict__ cand_idx, int K, bool sampled,
+                                                     int32_t* __restrict__ tokens, int32_t* __restrict__ slots,
+                                                     float* __restrict__ q) {
+  __shared__ WalkShared sm;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t base = (size_t)b * K * kNC;
+  for (int e = tid; e < K * kNC; e += blockDim.x) {
+    sm.next[e] = next[base + e];
+    sm.tok[e] = cand_idx[base + e];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int i = 0;
+    for (int t = 0; t < K; ++t) {
+      const int j = sm.next[t * kNC + i];
+      sm.path[t] = j;
+      i = j;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < K * kNC; e += blockDim.x) {
+    const int t = e >> 4, j = e & 15;
+    const int from = t == 0 ? 0 : sm.path[t - 1];
+    q[base + e] = sampled ? qtab[(base + (size_t)t * kNC + from) * kNC + j] : (j == sm.path[t] ? 1.f : 0.f);
+    if (j == 0) {
+      slots[(size_t)b * K + t] = sm.path[t];
+      tokens[(size_t)b * K + t] = sm.tok[t * kNC + sm.path[t]];
+    }
+  }
+}
+
+// ---- stage 2 of the proposer step -------------------------------------------------------
+
+template <int DIM, bool BF16>
+__global__ void __launch_bounds__(kPairThreads) k_positions(const unsigned long long* __restrict__ partials, int nlists,
+                                                            int K, const int32_t* __restrict__ verified,
+                                                            const void* __restrict__ emb_a,
+                                                            const void* __restrict__ emb_b, int V,
+                                                            const float* __restrict__ H, float inv_t, uint64_t seed,
+                                                            int32_t* __restrict__ cand_idx,
+                                                            float* __restrict__ cand_val, float* __restrict__ S,
+                                                            int* __restrict__ next, float* __restrict__ qtab,
+                                                            int32_t* __restrict__ row_status) {
+  __shared__ MergeShared ms;
+  __shared__ PairShared ps;
+  const int pos = blockIdx.x;
+  const int b = pos / K, p = pos - b * K;
+  const int tid = threadIdx.x;
+  // wave 0 merges row pos, wave 1 row pos - 1 (the predecessors)
+  const int wave = tid >> 6;
+  const int n = nlists * kListLen;
+  if (wave < (p > 0 ? 2 : 1)) {
+    wave_stage_lists(partials + (size_t)(pos - wave) * n, n, dyn_lists + wave * n);
+    wave_merge_lists(dyn_lists + wave * n, n, ms.cbuf[wave], ms.top[wave]);
+  }
+  if (tid == 0) ms.bits = 0;
+  __syncthreads();
+  if (tid < kNC) {
+    const unsigned long long rc = ms.top[0][tid];
+    const int id = rc ? rc_id(rc) : 0;
+    const float v = bf16_to_f32(rc_bits(rc));
+    cand_idx[(size_t)pos * kNC + tid] = id;
+    cand_val[(size_t)pos * kNC + tid] = v;
+    ps.cur[tid] = id;
+    ps.U[tid] = v;
+    const unsigned long long rp = ms.top[1][tid];
+    ps.prev[tid] = p == 0 ? verified[b] : (rp ? rc_id(rp) : 0);
+    if (!__builtin_isfinite(v)) atomicOr(&ms.bits, 1);
+  }
+  __syncthreads();
+  const int pbits = pair_tile<DIM, BF16>(emb_a, emb_b, V, H + (size_t)pos * DIM, S + (size_t)pos * kNC * kNC, ps);
+  const float u = inv_t == 0.f ? 0.f : walk_uniform(seed, (uint32_t)b, (uint32_t)p);
+  tile_successors(ps, inv_t, u, next + (size_t)pos * kNC, inv_t == 0.f ? nullptr : qtab + (size_t)pos * kNC * kNC);
+  if (row_status && tid == 0) row_status[pos] = ms.bits | pbits;
+}
+
+// ---- launchers -----------------------------------------------------------------------
+
+hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld, int32_t* cand_idx, float* cand_val,
+                         int32_t* row_status, TopkWs ws, hipStream_t s) {
+  const int nchunks = topk_num_chunks(vocab);
+  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(rows * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
+                     nchunks, ws.partials);
+  const int nlists = nchunks * kListsPerChunk;
+  hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)rows), dim3(kWave), (size_t)nlists * kListLen * 8, s, ws.partials,
+                     nlists, cand_idx, cand_val, row_status);
+  return hipGetLastError();
+}
+
+template <int DIM, bool BF16>
+static void pair_launch(dim3 grid, hipStream_t s, const int32_t* cand_idx, const float* cand_val,
+                        const int32_t* verified, const void* a, const void* b, int V, const float* H, int K, float* S,
+                        int32_t* st) {
+  hipLaunchKernelGGL((k_pair_score<DIM, BF16>), grid, dim3(kPairThreads), 0, s, cand_idx, cand_val, verified, a, b, V,
+                     H, K, S, st);
+}
+
+hipError_t launch_pair_score(const int32_t* cand_idx, const float* cand_val, const int32_t* verified, const void* emb_a,
+                             const void* emb_b, bool bf16, int vocab, int dim, const float* H, int batch, int K,
+                             float* S, int32_t* row_status, hipStream_t s) {
+  const dim3 grid((unsigned)(batch * K));
+#define DF2_PAIR(D)                                                                                           \
+  case D:                                                                                                     \
+    if (bf16)                                                                                                 \
+      pair_launch<D, true>(grid, s, cand_idx, cand_val, verified, emb_a, emb_b, vocab, H, K, S, row_status);  \
+    else                                                                                                      \
+      pair_launch<D, false>(grid, s, cand_idx, cand_val, verified, emb_a, emb_b, vocab, H, K, S, row_status); \
+    break;
+  switch (dim) {
+    DF2_PAIR(64)
+    DF2_PAIR(128)
+    DF2_PAIR(256)
+    DF2_PAIR(512)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DF2_PAIR
+  return hipGetLastError();
+}
+
+hipError_t launch_walk(const float* S, const int32_t* cand_idx, int batch, int K, float temperature, uint64_t seed,
+                       int32_t* tokens, int32_t* slots, float* q, hipStream_t s) {
+  const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
+  hipLaunchKernelGGL(k_walk, dim3((unsigned)batch), dim3(256), 0, s, S, cand_idx, K, inv_t, seed, tokens, slots, q);
+  return hipGetLastError();
+}
+
+template <int DIM, bool BF16>
+static void positions_launch(dim3 grid, hipStream_t s, const unsigned long long* partials, int nlists, int K,
+                             const int32_t* verified, const void* a, const void* b, int V, const float* H, float inv_t,
+                             uint64_t seed, int32_t* ci, float* cv, float* S, int* next, float* qtab, int32_t* st) {
+  hipLaunchKernelGGL((k_positions<DIM, BF16>), grid, dim3(kPairThreads), (size_t)2 * nlists * kListLen * 8, s, partials,
+                     nlists, K, verified, a, b, V, H, inv_t, seed, ci, cv, S, next, qtab, st);
+}
+
+hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                         const void* emb_b, bool bf16, int vocab, int dim, const float* H, int batch, int K,
+                         float temperature, uint64_t seed, int32_t* cand_idx, float* cand_val, float* S,
+                         int32_t* tokens, int32_t* slots, float* q, int32_t* row_status, SelectWs ws, hipStream_t s) {
+  const int nchunks = topk_num_chunks(vocab);
+  const int nlists = nchunks * kListsPerChunk;
+  const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
+  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(batch * K * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
+                     nchunks, ws.topk.partials);
+  const dim3 grid((unsigned)(batch * K));
+#define DF2_POS(D)                                                                                                   \
+  case D:                                                                                                            \
+    if (bf16)                                                                                                        \
+      positions_launch<D, true>(grid, s, ws.topk.partials, nlists, K, verified, emb_a, emb_b, vocab, H, inv_t, seed, \
+                                cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                                         \
+    else                                                                                                             \
+      positions_launch<D, false>(grid, s, ws.topk.partials, nlists, K, verified, emb_a, emb_b, vocab, H, inv_t,      \
+                                 seed, cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                                  \
+    break;
+  switch (dim) {
+    DF2_POS(64)
+    DF2_POS(128)
+    DF2_POS(256)
+    DF2_POS(512)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef DF2_POS
+  hipLaunchKernelGGL(k_walk_tables, dim3((unsigned)batch), dim3(256), 0, s, ws.next, ws.qtab, cand_idx, K,
+                     inv_t != 0.f, tokens, slots, q);
+  return hipGetLastError();
+}
+
+}  // namespace df2

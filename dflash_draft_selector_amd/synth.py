@@ -125,6 +125,13 @@ def make_inputs(w: Workload) -> dict:
     return out
 
 
+def make_target(w: Workload, seed: int) -> np.ndarray:
+    """Target logits bf16 bits [B, K+1, V] ~ N(0, 3^2) from their own generator (the
+    c4 recipe at any workload's shape)."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(_normal(rng, (w.B, w.K + 1, w.V), 3.0))
+
+
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     """Reinterpret bf16 bit patterns as the float32 values they denote (exact widening)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)

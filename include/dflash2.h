@@ -1,0 +1,230 @@
+/*
+ * libdflash2 -- the DFlash 2 proposer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the pegainfer issue "qwen3/dflash: DFlash 2 proposer -- top-16 path
+ * selector + two-tap dynamic convolution" (cited as [PEGA]) and the FreeToken pull
+ * request "Adds DFlash 2 as a second speculative decoding method" (cited as [FT]).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers unless stated otherwise; tensors are row-major and
+ *    contiguous, except that logits rows may be strided (`ld`, in elements).
+ *  - bf16 data is passed as its uint16_t bit pattern.
+ *  - The caller owns every buffer.  The library allocates no device memory and keeps
+ *    no state between calls.  Scratch memory comes only from a caller-provided
+ *    workspace sized by the matching *_workspace() query.  A workspace must be
+ *    zero-filled once when first allocated; every call returns its counters to zero,
+ *    so it stays valid for later calls of the SAME entry point with the SAME sizes.
+ *    A call with other sizes lays the workspace out differently and needs its own
+ *    (or a freshly zero-filled) buffer.  Calls that overlap in time must not share
+ *    a workspace.
+ *  - Every call validates its arguments on the host, enqueues its kernels on `stream`
+ *    and returns without synchronising.  Host-detectable errors are returned before
+ *    anything is enqueued; nothing aborts, prints or reads the environment.
+ *  - Results are deterministic: bit-identical across runs for the same inputs.
+ *  - Outputs must not alias inputs.
+ *  - Per-row data faults are reported in optional int32 `row_status` arrays (pass
+ *    NULL to drop them):
+ *      bit 0  non-finite value (a selected logit, a score, or a target row)
+ *      bit 1  a token id outside [0, vocab) (clamped for reading, never dereferenced
+ *             out of bounds)
+ *      bit 2  an invalid draft distribution q (speculative accept)
+ *      bit 3  a residual distribution without mass (speculative accept)
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH2_ABI_VERSION 1
+#define DFLASH2_NCAND 16       /* candidates per draft position */
+#define DFLASH2_MAX_K 64       /* draft positions per request */
+
+typedef enum dflash2_status {
+  DFLASH2_OK = 0,
+  DFLASH2_ERR_NULL = 1,       /* a required pointer is NULL */
+  DFLASH2_ERR_SHAPE = 2,      /* a size is out of range or inconsistent */
+  DFLASH2_ERR_ALIGN = 3,      /* a pointer or row stride breaks the 16-byte alignment rule */
+  DFLASH2_ERR_DTYPE = 4,      /* an unknown dtype or activation enum */
+  DFLASH2_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the query returned */
+  DFLASH2_ERR_VALUE = 6,      /* temperature negative or NaN */
+  DFLASH2_ERR_HIP = 7         /* a HIP launch failed */
+} dflash2_status;
+
+typedef enum dflash2_dtype { DFLASH2_F32 = 0, DFLASH2_BF16 = 1 } dflash2_dtype;
+
+typedef enum dflash2_gate_act { DFLASH2_GATE_SIGMOID = 0, DFLASH2_GATE_IDENTITY = 1 } dflash2_gate_act;
+
+/* ABI version of the loaded library (DFLASH2_ABI_VERSION it was built with). */
+int dflash2_abi_version(void);
+
+/* Static, NUL-terminated name of a status code (host memory owned by the library). */
+const char* dflash2_status_str(int status);
+
+/* ---------------------------------------------------------------------------------
+ * Top-16 candidates per draft position.
+ * [PEGA] "What upstream shipped", item 1: keep the top-16 candidates per position;
+ * [FT] "Details", runtime: the target LM head gives 16 candidates per slot.
+ *
+ * logits     bf16 bits [rows, ld]; element (r, v) at logits[r*ld + v], v < vocab.
+ *            The base pointer and ld*2 bytes must be 16-byte aligned (ld % 8 == 0).
+ * cand_idx   int32 [rows, 16]: token ids sorted by (logit desc, id asc).
+ *            -0 equals +0; NaN ranks below -inf.
+ * cand_val   float [rows, 16]: the selected logits widened exactly to fp32.
+ * row_status int32 [rows] or NULL: bit 0 if a selected value is not finite.
+ * Errors: NULL pointers, rows < 1, vocab < 16 or > 2^19, ld < vocab, alignment,
+ *         workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_topk16_workspace(int64_t rows, int64_t vocab);
+dflash2_status dflash2_topk16(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t ld,
+                              int32_t* cand_idx, float* cand_val, int32_t* row_status,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Context gate H = act(W_H h + b), one `dim`-wide gate per draft position.
+ * [PEGA] "What upstream shipped", item 1 (256-dim token embeddings + context gate).
+ * The gate is read as a logistic sigmoid of an affine map (DFLASH2_GATE_SIGMOID);
+ * DFLASH2_GATE_IDENTITY returns the affine map.
+ *
+ * h        float [rows, hidden].
+ * w_h      [dim, hidden] in w_dtype.  With DFLASH2_BF16 each h value is first rounded
+ *          to bf16 (nearest, ties to even) and the product runs on bf16 MFMA with
+ *          fp32 accumulation; with DFLASH2_F32 it runs in fp32.
+ * bias     float [dim] or NULL (= 0).
+ * H        float [rows, dim].
+ * Errors: NULL pointers, rows < 1, hidden < 8 or hidden % 8 != 0, dim not a power of
+ *         two in [16, 1024], bad dtype or act, alignment of h / w_h, workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim);
+dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dtype w_dtype,
+                                    const float* bias, int64_t rows, int64_t hidden, int64_t dim,
+                                    dflash2_gate_act act, float* H, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Pair scores S_t(a, b) = U_t(b) + <A(a) (.) H(h_t), B(b)> for every adjacent pair.
+ * [PEGA] "What upstream shipped", item 1, and "Proposal", phase 1
+ * (block_size x 16 predecessors x 16 candidates x 256 dims).
+ *
+ * S[b,t,i,j] = cand_val[b,t,j] + sum_d A[prev_i, d] * H[b,t,d] * B[cand_idx[b,t,j], d]
+ * with prev_i = verified[b] at t = 0 (all 16 rows) and cand_idx[b,t-1,i] at t >= 1.
+ *
+ * cand_idx int32 [batch, K, 16], cand_val float [batch, K, 16], verified int32 [batch],
+ * emb_a, emb_b [vocab, dim] in emb_dtype (16-byte aligned), H float [batch, K, dim],
+ * S float [batch, K, 16, 16] (fp32 products and accumulation),
+ * row_status int32 [batch, K] or NULL: bit 0 non-finite score, bit 1 id out of range.
+ * Errors: NULL pointers, batch < 1, K not in [1, 64], vocab < 16, dim not in
+ *         {64, 128, 256, 512}, dtype, alignment.
+ * ------------------------------------------------------------------------------- */
+dflash2_status dflash2_pair_score(const int32_t* cand_idx, const float* cand_val,
+                                  const int32_t* verified, const void* emb_a, const void* emb_b,
+                                  dflash2_dtype emb_dtype, int64_t vocab, int64_t dim,
+                                  const float* H, int64_t batch, int64_t K, float* S,
+                                  int32_t* row_status, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Walk over the precomputed scores: the proposed path.
+ * [PEGA] "What upstream shipped", item 1 (a single greedy/sampled walk over the
+ * precomputed scores) and "Proposal", phase 1 (<= block_size argmax steps);
+ * [FT] "Details", runtime (sampled from q, or argmax when greedy) and shared changes
+ * (the proposer returns tokens, candidates and q).
+ *
+ * Step t reads row i_{t-1} of S[b,t] (i_{-1} = 0, the verified token's row).
+ * temperature == 0: greedy, slot = lowest j of the row maximum, q one-hot.
+ * temperature  > 0: q = softmax(row / T) over the 16 slots; slot = the first j whose
+ *                   prefix weight exceeds u * total, u from Philox4x32-10 with key
+ *                   (lo32(seed), hi32(seed)) and counter (t, b, 0, 0), word 0,
+ *                   u = (word >> 8) * 2^-24.
+ * Non-finite scores never win (weight 0); an all-non-finite row picks slot 0.
+ *
+ * S float [batch, K, 16, 16]; cand_idx int32 [batch, K, 16];
+ * tokens, slots int32 [batch, K]; q float [batch, K, 16].
+ * Errors: NULL pointers, batch < 1, batch >= 2^31, K not in [1, 64], temperature.
+ * ------------------------------------------------------------------------------- */
+dflash2_status dflash2_walk(const float* S, const int32_t* cand_idx, int64_t batch, int64_t K,
+                            float temperature, uint64_t seed, int32_t* tokens, int32_t* slots,
+                            float* q, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Fused proposer step: topk16 -> pair_score -> walk in ONE kernel launch.
+ * Same passages as the three calls above; the outputs are bit-identical to calling
+ * dflash2_topk16 on every position's logits row, then dflash2_pair_score, then
+ * dflash2_walk.  logits rows are addressed as logits[(b*K + t)*ld + v].
+ *
+ * row_status int32 [batch, K] or NULL (the union of the top-16 and pair-score bits).
+ * Errors: the union of the three calls' checks, plus workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_select_workspace(int64_t batch, int64_t K, int64_t vocab);
+dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t* verified,
+                              const void* emb_a, const void* emb_b, dflash2_dtype emb_dtype,
+                              int64_t vocab, int64_t dim, const float* H, int64_t batch, int64_t K,
+                              float temperature, uint64_t seed, int32_t* cand_idx, float* cand_val,
+                              float* S, int32_t* tokens, int32_t* slots, float* q,
+                              int32_t* row_status, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Two-tap dynamic depthwise convolution, at `sites` independent sublayer sites.
+ * [PEGA] "What upstream shipped", item 2:
+ *   Conv(x)_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},  x_{-1} = the last verified
+ *   token's hidden.
+ * [FT] "Tests added or changed" / "Details": taps are shared by `group` adjacent
+ * channels (conv_group_size must divide hidden); channel d uses tap d / group.
+ *
+ * x float [sites, batch, K, hidden]; x_prev float [sites, batch, hidden];
+ * taps float [sites, batch, K, 2, hidden/group]; y float [sites, batch, K, hidden].
+ * Errors: NULL pointers, sizes < 1, K > 64, hidden % group != 0.
+ * ------------------------------------------------------------------------------- */
+dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float* taps,
+                                int64_t sites, int64_t batch, int64_t K, int64_t hidden,
+                                int64_t group, float* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Lossless verify of K drafted tokens against the target.
+ * [FT] "Details", sampled verify: accept with min(1, p/q); on a reject resample from
+ * max(0, p - q), so the output follows the target distribution; all-greedy keeps the
+ * prefix match.  [PEGA] "Proposal", phase 3.
+ *
+ * target_logits bf16 bits; row (b, t) for t in [0, K] at
+ *   target_logits[b*batch_stride + t*ld], ld % 8 == 0, 16-byte aligned base.
+ *   batch_stride may be 0 (every request verifies against the same K+1 rows).
+ * tokens int32 [batch, K]; cand_idx int32 [batch, K, 16]; q float [batch, K, 16]
+ *   (q may be NULL when temperature == 0).
+ * temperature > 0, per request b, with p_t = softmax(target row t / T):
+ *   step t accepts x_t iff u_acc * q_t(x_t) < p_t(x_t), q_t(v) = sum of q[b,t,j] over
+ *   slots j with cand_idx[b,t,j] == v; at the first reject it commits
+ *   v ~ max(0, p_t - q_t) (inverse CDF in token-id order with u_res) and stops; if all
+ *   K are accepted it commits a bonus token from p_K.  (u_acc, u_res) are words 0 and
+ *   1 of Philox4x32-10 at counter (t, b, 1, 0) under key (lo32(seed), hi32(seed)).
+ * temperature == 0: g_t = argmax of target row t (lowest id); accept while
+ *   tokens[b,t] == g_t; commit g at the first mismatch, or the bonus g_K.
+ * Outputs: out_tokens int32 [batch, K+1] (committed ids, then -1), n_accepted int32
+ *   [batch], row_status int32 [batch] or NULL:
+ *   bit 0 (T > 0) a target row holds NaN or +inf: nothing is committed;
+ *   bit 1 a token or candidate id outside [0, vocab): (T > 0) commit one token from p_0;
+ *   bit 2 (T > 0) a q row has NaN / negative entries, a sum off 1 by > 1e-3, or
+ *         q_t(x_t) <= 0: commit one token drawn from p_0;
+ *   bit 3 (T > 0) the residual has no mass: draw from p_t instead.
+ * Errors: NULL pointers, batch < 1, K not in [1, 64], vocab < 16 or > 2^19,
+ *         ld < vocab, alignment, temperature, workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_spec_accept_workspace(int64_t batch, int64_t K, int64_t vocab);
+dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, int64_t batch_stride,
+                                   const int32_t* tokens, const int32_t* cand_idx, const float* q,
+                                   int64_t batch, int64_t K, int64_t vocab, float temperature,
+                                   uint64_t seed, int32_t* out_tokens, int32_t* n_accepted,
+                                   int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH2_H */

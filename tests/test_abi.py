@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash2.h")
+
+
+def _lib():
+    from dflash_draft_selector_amd import dflash2
+    if not os.path.exists(dflash2.LIB_PATH):
+        from dflash_draft_selector_amd.build import build_library
+        build_library()
+    return dflash2, dflash2.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_calls_and_the_fused_step():
+    names = _declared()
+    for n in ("dflash2_topk16", "dflash2_context_gate", "dflash2_pair_score", "dflash2_walk", "dflash2_conv2tap",
+              "dflash2_spec_accept", "dflash2_select"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    d2, lib = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", d2.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dflash2_\w+)", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    assert set(d2.EXPORTED) == set(_declared())
+    assert lib.dflash2_abi_version() == 1
+
+
+def test_header_compiles_as_c():
+    res = subprocess.run(["gcc", "-fsyntax-only", "-x", "c", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                          HEADER], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings():
+    d2, lib = _lib()
+    assert d2.status_str(0) == "DFLASH2_OK"
+    assert d2.status_str(5) == "DFLASH2_ERR_WORKSPACE"
+    assert d2.status_str(99) == "DFLASH2_UNKNOWN_STATUS"
+
+
+FAKE = ctypes.c_void_p(0x100000)          # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x100002)
+NULL = None
+
+
+def test_host_validation_before_any_launch():
+    d2, lib = _lib()
+    ws = ctypes.c_void_p(0x200000)
+    big = 1 << 30
+    # topk16
+    assert lib.dflash2_topk16(NULL, 4, 4096, 4096, FAKE, FAKE, NULL, ws, big, NULL) == 1
+    assert lib.dflash2_topk16(FAKE, 4, 15, 16, FAKE, FAKE, NULL, ws, big, NULL) == 2
+    assert lib.dflash2_topk16(FAKE, 4, 4096, 4000, FAKE, FAKE, NULL, ws, big, NULL) == 2
+    assert lib.dflash2_topk16(FAKE, 4, (1 << 20) + 8, (1 << 20) + 8, FAKE, FAKE, NULL, ws, big, NULL) == 2
+    assert lib.dflash2_topk16(FAKE, 4, 4100, 4100, FAKE, FAKE, NULL, ws, big, NULL) == 3
+    assert lib.dflash2_topk16(MIS, 4, 4096, 4096, FAKE, FAKE, NULL, ws, big, NULL) == 3
+    need = lib.dflash2_topk16_workspace(4, 4096)
+    assert need > 0
+    assert lib.dflash2_topk16(FAKE, 4, 4096, 4096, FAKE, FAKE, NULL, ws, need - 257, NULL) == 5
+    assert lib.dflash2_topk16(FAKE, 4, 4096, 4096, FAKE, FAKE, NULL, NULL, big, NULL) == 5
+    # context gate
+    assert lib.dflash2_context_gate(FAKE, FAKE, 7, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 4
+    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 512, 256, 9, FAKE, ws, big, NULL) == 4
+    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 500, 256, 0, FAKE, ws, big, NULL) == 2
+    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 512, 250, 0, FAKE, ws, big, NULL) == 2
+    assert lib.dflash2_context_gate(FAKE, MIS, 1, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 3
+    # pair score
+    assert lib.dflash2_pair_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 96, FAKE, 1, 7, FAKE, NULL, NULL) == 2
+    assert lib.dflash2_pair_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 65, FAKE, NULL, NULL) == 2
+    assert lib.dflash2_pair_score(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4096, 256, FAKE, 1, 7, FAKE, NULL, NULL) == 4
+    assert lib.dflash2_pair_score(FAKE, FAKE, NULL, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 7, FAKE, NULL, NULL) == 1
+    # walk
+    assert lib.dflash2_walk(FAKE, FAKE, 1, 7, -1.0, 0, FAKE, FAKE, FAKE, NULL) == 6
+    assert lib.dflash2_walk(FAKE, FAKE, 1, 7, float("nan"), 0, FAKE, FAKE, FAKE, NULL) == 6
+    assert lib.dflash2_walk(FAKE, FAKE, 0, 7, 0.0, 0, FAKE, FAKE, FAKE, NULL) == 2
+    # select
+    assert lib.dflash2_select(FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 7, 0.0, 0, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, NULL, ws, 16, NULL) == 5
+    assert lib.dflash2_select(FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 0, 0.0, 0, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, NULL, ws, big, NULL) == 2
+    # conv
+    assert lib.dflash2_conv2tap(FAKE, FAKE, FAKE, 1, 1, 7, 512, 3, FAKE, NULL) == 2
+    assert lib.dflash2_conv2tap(FAKE, NULL, FAKE, 1, 1, 7, 512, 1, FAKE, NULL) == 1
+    # spec accept
+    assert lib.dflash2_spec_accept(FAKE, 4096, 8 * 4096, FAKE, FAKE, NULL, 1, 7, 4096, 1.0, 0, FAKE, FAKE, NULL, ws,
+                                   big, NULL) == 1
+    assert lib.dflash2_spec_accept(FAKE, 4096, 100, FAKE, FAKE, FAKE, 2, 7, 4096, 1.0, 0, FAKE, FAKE, NULL, ws, big,
+                                   NULL) == 2
+    assert lib.dflash2_spec_accept(FAKE, 4096, 8 * 4096 + 4, FAKE, FAKE, FAKE, 2, 7, 4096, 1.0, 0, FAKE, FAKE, NULL, ws,
+                                   big, NULL) == 3
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from dflash_draft_selector_amd import dflash2
+    with pytest.raises(dflash2.Dflash2Error):
+        dflash2.load_library.__wrapped__(str(tmp_path / "missing.so")) if hasattr(dflash2.load_library, "__wrapped__") \
+            else _load_missing(dflash2, tmp_path)
+
+
+def _load_missing(dflash2, tmp_path):
+    saved = dflash2._lib
+    dflash2._lib = None
+    try:
+        dflash2.load_library(str(tmp_path / "missing.so"))
+    finally:
+        dflash2._lib = saved

@@ -1,0 +1,369 @@
+"""Parity of libdflash2 (HIP, gfx950) with the CPU oracle, through the C ABI.
+
+Sizes: the tiny workload c0 and the full single-GPU workloads c1, c2, c4 in full, c3
+on sampled rows; ragged vocabularies and degenerate rows for the edge cases.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from dflash_draft_selector_amd import synth
+from parity_util import (REL, assert_close_scaled, check_accept, check_walk, cpu, to_gpu, to_gpu_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def d2():
+    import torch
+    from dflash_draft_selector_amd import dflash2
+    dflash2.load_library()
+    torch.cuda.init()
+    return dflash2
+
+
+_INPUTS = {}
+
+
+def inputs(i, **over):
+    key = (i, tuple(sorted(over.items())))
+    if key not in _INPUTS:
+        _INPUTS[key] = synth.make_inputs(synth.workload(i, **over))
+    return _INPUTS[key]
+
+
+def tables(inp):
+    if "emb_a_bits" in inp:
+        return (oracle.bf16_to_f64(inp["emb_a_bits"]), oracle.bf16_to_f64(inp["emb_b_bits"]),
+                to_gpu_bits(inp["emb_a_bits"]), to_gpu_bits(inp["emb_b_bits"]))
+    return inp["emb_a"], inp["emb_b"], to_gpu(inp["emb_a"]), to_gpu(inp["emb_b"])
+
+
+def gate_w(inp):
+    if "w_h_bits" in inp:
+        return oracle.bf16_to_f64(inp["w_h_bits"]), to_gpu_bits(inp["w_h_bits"]), True
+    return inp["w_h"], to_gpu(inp["w_h"]), False
+
+
+# ------------------------------------------------------------------ top-16 ----------
+
+
+@pytest.mark.parametrize("wl", [0, 1, 2])
+def test_topk16_exact(d2, wl):
+    inp = inputs(wl)
+    print(f"topk16 workload c{wl}", flush=True)
+    idx, val, st = d2.topk16(to_gpu_bits(inp["logits_bits"]), row_status=True)
+    ridx, rval = oracle.topk16(inp["logits_bits"])
+    np.testing.assert_array_equal(cpu(idx), ridx)
+    np.testing.assert_array_equal(cpu(val).astype(np.float64), rval)
+    assert np.all(cpu(st) == 0)
+
+
+def _bits_of(vals):
+    return (np.asarray(vals, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def test_topk16_edge_rows(d2):
+    import torch
+    rng = np.random.default_rng(31)
+    for V in (16, 17, 23, 4096, 16384, 16392, 40003, 151936):
+        rows = []
+        rows.append(np.full(V, 0x4000, np.uint16))                                     # constant
+        rows.append(_bits_of(np.arange(V, dtype=np.float32)))                           # increasing
+        rows.append(_bits_of(-np.arange(V, dtype=np.float32)))                          # decreasing
+        r = _bits_of(rng.choice([-1.0, -0.0, 0.0, 0.5], size=V).astype(np.float32))    # zeros and ties
+        rows.append(r)
+        r = synth.f32_to_bf16_bits(rng.standard_normal(V).astype(np.float32) * 3)
+        r[rng.integers(0, V, max(1, V // 50))] = 0x7FC0                                 # NaNs
+        rows.append(r)
+        r = np.full(V, 0x7FC0, np.uint16)
+        r[rng.integers(0, V, 5)] = synth.f32_to_bf16_bits(rng.standard_normal(5).astype(np.float32))
+        rows.append(r)                                                                  # mostly NaN
+        r = synth.f32_to_bf16_bits(-np.abs(rng.standard_normal(V).astype(np.float32)) - 1)
+        rows.append(r)                                                                  # all negative
+        r = synth.f32_to_bf16_bits(rng.standard_normal(V).astype(np.float32))
+        r[rng.integers(0, V, 3)] = 0x7F80
+        r[rng.integers(0, V, 3)] = 0xFF80
+        rows.append(r)                                                                  # +-inf
+        bits = np.stack(rows)
+        ld = (V + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+        buf = np.zeros((bits.shape[0], ld), np.uint16)
+        buf[:, :V] = bits
+        g = to_gpu_bits(buf)[:, :V]
+        print(f"topk16 edge rows V={V} ld={ld}", flush=True)
+        idx, val, st = d2.topk16(g, row_status=True)
+        ridx, rval = oracle.topk16(bits)
+        np.testing.assert_array_equal(cpu(idx), ridx, err_msg=f"V={V}")
+        np.testing.assert_array_equal(cpu(val).view(np.uint32) >> 16, _bits_of(rval.astype(np.float32)).astype(np.uint32))
+        want_st = (~np.isfinite(rval)).any(axis=1).astype(np.int32)
+        np.testing.assert_array_equal(cpu(st), want_st)
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ gate ------------
+
+
+@pytest.mark.parametrize("wl", [0, 2, 3])
+def test_context_gate(d2, wl):
+    inp = inputs(wl)
+    w = synth.workload(wl)
+    W64, Wg, is_bf16 = gate_w(inp)
+    h = inp["h"].reshape(-1, w.D)
+    if wl == 3:
+        h = h[:300]
+    print(f"gate c{wl} rows={h.shape[0]}", flush=True)
+    for act in ("sigmoid", "identity"):
+        H = cpu(d2.context_gate(to_gpu(h), Wg, to_gpu(inp["bias"]), act=act))
+        Href, pre, pre_abs = oracle.context_gate(h, W64, inp["bias"], is_bf16, act=act)
+        scale = pre_abs * (0.25 if act == "sigmoid" else 1.0)
+        assert_close_scaled(H, Href, scale, what=f"gate {act}")
+
+
+def test_context_gate_ragged(d2):
+    rng = np.random.default_rng(4)
+    for rows, hidden, dim in ((1, 8, 16), (17, 520, 64), (33, 1000, 128), (5, 4096, 1024)):
+        h = rng.standard_normal((rows, hidden)).astype(np.float32)
+        w = (rng.standard_normal((dim, hidden)) / np.sqrt(hidden)).astype(np.float32)
+        wb = synth.f32_to_bf16_bits(w)
+        b = rng.standard_normal(dim).astype(np.float32)
+        print(f"gate ragged {rows}x{hidden}x{dim}", flush=True)
+        H = cpu(d2.context_gate(to_gpu(h), to_gpu_bits(wb), to_gpu(b)))
+        Href, _, pre_abs = oracle.context_gate(h, oracle.bf16_to_f64(wb), b, True)
+        assert_close_scaled(H, Href, 0.25 * pre_abs, what="gate bf16 ragged")
+        H = cpu(d2.context_gate(to_gpu(h), to_gpu(w), to_gpu(b)))
+        Href, _, pre_abs = oracle.context_gate(h, w, b, False)
+        assert_close_scaled(H, Href, 0.25 * pre_abs, what="gate f32 ragged")
+
+
+# ------------------------------------------------------------------ pair score ------
+
+
+def _oracle_cands_and_H(inp, w):
+    ridx, rval = oracle.topk16(inp["logits_bits"])
+    W64, _, is_bf16 = gate_w(inp)
+    H, _, _ = oracle.context_gate(inp["h"].reshape(-1, w.D), W64, inp["bias"], is_bf16)
+    return ridx, rval, H.reshape(w.B, w.K, -1)
+
+
+@pytest.mark.parametrize("wl", [0, 2])
+def test_pair_score(d2, wl):
+    inp = inputs(wl)
+    w = synth.workload(wl)
+    ridx, rval, H = _oracle_cands_and_H(inp, w)
+    H32 = H.astype(np.float32)
+    A64, B64, Ag, Bg = tables(inp)
+    print(f"pair_score c{wl}", flush=True)
+    S, st = d2.pair_score(to_gpu(ridx, None).int(), to_gpu(rval.astype(np.float32)), to_gpu(inp["verified"]), Ag, Bg,
+                          to_gpu(H32))
+    Sref, Sabs, rst = oracle.pair_score(ridx, rval, inp["verified"], A64, B64, H32)
+    assert_close_scaled(cpu(S), Sref, Sabs, what="pair score")
+    np.testing.assert_array_equal(cpu(st), rst)
+
+
+def test_pair_score_bad_ids_are_clamped_and_flagged(d2):
+    inp = inputs(0)
+    w = synth.workload(0)
+    ridx, rval, H = _oracle_cands_and_H(inp, w)
+    ridx = ridx.copy()
+    ridx[0, 2, 5] = w.V + 7
+    ver = inp["verified"].copy()
+    ver[0] = -3
+    A64, B64, Ag, Bg = tables(inp)
+    S, st = d2.pair_score(to_gpu(ridx, None).int(), to_gpu(rval.astype(np.float32)), to_gpu(ver), Ag, Bg,
+                          to_gpu(H.astype(np.float32)))
+    Sref, Sabs, rst = oracle.pair_score(ridx, rval, ver, A64, B64, H.astype(np.float32))
+    np.testing.assert_array_equal(cpu(st), rst)
+    assert rst[0, 0] == 2 and rst[0, 2] == 2 and rst[0, 3] == 2
+    assert_close_scaled(cpu(S), Sref, Sabs, what="pair score clamped")
+
+
+# ------------------------------------------------------------------ walk ------------
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0, 0.35])
+def test_walk_on_oracle_scores(d2, temperature):
+    rng = np.random.default_rng(9)
+    B, K = 300, 7
+    S = (rng.standard_normal((B, K, 16, 16)) * 2).astype(np.float32)
+    S[:5] = np.round(S[:5])                       # exact ties in fp32
+    S[5, 3, :, 4] = np.nan
+    S[6, 2] = np.inf
+    cand = rng.integers(0, 151936, (B, K, 16)).astype(np.int32)
+    print(f"walk T={temperature}", flush=True)
+    tok, slots, q = d2.walk(to_gpu(S), to_gpu(cand), temperature, seed=77)
+    stats = check_walk(S.astype(np.float64), cand, cpu(tok), cpu(slots), cpu(q), temperature, 77)
+    print("walk stats", stats)
+    if temperature == 0.0:
+        assert stats["band"] == 0                  # same fp32 scores -> same argmax
+
+
+# ------------------------------------------------------------------ fused select ----
+
+
+def _run_select(d2, inp, w, temperature, seed):
+    Wg = gate_w(inp)[1]
+    A64, B64, Ag, Bg = tables(inp)
+    Hg = d2.context_gate(to_gpu(inp["h"].reshape(w.B, w.K, w.D)), Wg, to_gpu(inp["bias"]))
+    out = d2.select(to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"]), Ag, Bg, Hg, temperature, seed)
+    return Hg, out
+
+
+@pytest.mark.parametrize("wl", [0, 1, 2, 4])
+def test_select_equals_three_calls(d2, wl):
+    inp = inputs(wl)
+    w = synth.workload(wl)
+    T = w.temperature
+    print(f"select vs three calls c{wl}", flush=True)
+    Hg, out = _run_select(d2, inp, w, T, w.walk_seed)
+    A64, B64, Ag, Bg = tables(inp)
+    idx, val = d2.topk16(to_gpu_bits(inp["logits_bits"]))
+    S, st = d2.pair_score(idx, val, to_gpu(inp["verified"]), Ag, Bg, Hg)
+    tok, slots, q = d2.walk(S, idx, T, w.walk_seed)
+    for name, ref in (("cand_idx", idx), ("cand_val", val), ("S", S), ("tokens", tok), ("slots", slots), ("q", q),
+                      ("row_status", st)):
+        np.testing.assert_array_equal(cpu(out[name]).view(np.uint32) if cpu(out[name]).dtype == np.float32 else cpu(out[name]),
+                                      cpu(ref).view(np.uint32) if cpu(ref).dtype == np.float32 else cpu(ref), err_msg=name)
+
+
+@pytest.mark.parametrize("wl", [0, 1, 2, 4])
+def test_select_vs_oracle(d2, wl):
+    inp = inputs(wl)
+    w = synth.workload(wl)
+    print(f"select vs oracle c{wl}", flush=True)
+    Hg, out = _run_select(d2, inp, w, w.temperature, w.walk_seed)
+    ridx, rval, H = _oracle_cands_and_H(inp, w)
+    np.testing.assert_array_equal(cpu(out["cand_idx"]), ridx)
+    np.testing.assert_array_equal(cpu(out["cand_val"]).astype(np.float64), rval)
+    A64, B64, _, _ = tables(inp)
+    Sref, Sabs, rst = oracle.pair_score(ridx, rval, inp["verified"], A64, B64, H)
+    assert_close_scaled(cpu(out["S"]), Sref, Sabs, what="select S")
+    np.testing.assert_array_equal(cpu(out["row_status"]), rst)
+    stats = check_walk(Sref, ridx, cpu(out["tokens"]), cpu(out["slots"]), cpu(out["q"]), w.temperature, w.walk_seed)
+    print(f"c{wl} walk stats", stats, flush=True)
+
+
+def test_select_c3_sampled_rows(d2):
+    w = synth.workload(3)
+    inp = inputs(3)
+    print("select c3 (sampled requests)", flush=True)
+    Hg, out = _run_select(d2, inp, w, 0.0, 0)
+    reqs = [0, 17, 63]
+    sub = inp["logits_bits"][reqs]
+    ridx, rval = oracle.topk16(sub)
+    np.testing.assert_array_equal(cpu(out["cand_idx"])[reqs], ridx)
+    W64, _, _ = gate_w(inp)
+    H, _, _ = oracle.context_gate(inp["h"][reqs].reshape(-1, w.D), W64, inp["bias"], True)
+    A64, B64, _, _ = tables(inp)
+    Sref, Sabs, _ = oracle.pair_score(ridx, rval, inp["verified"][reqs], A64, B64, H.reshape(len(reqs), w.K, -1))
+    assert_close_scaled(cpu(out["S"])[reqs], Sref, Sabs, what="c3 S")
+    check_walk(Sref, ridx, cpu(out["tokens"])[reqs], cpu(out["slots"])[reqs], cpu(out["q"])[reqs], 0.0, 0)
+    # every request: the walk is consistent with the library's own candidates
+    tok, cand, slots = cpu(out["tokens"]), cpu(out["cand_idx"]), cpu(out["slots"])
+    np.testing.assert_array_equal(tok, np.take_along_axis(cand, slots[..., None], axis=2)[..., 0])
+
+
+def test_select_deterministic(d2):
+    inp = inputs(2)
+    w = synth.workload(2)
+    _, a = _run_select(d2, inp, w, 1.0, 5)
+    _, b = _run_select(d2, inp, w, 1.0, 5)
+    for k in a:
+        np.testing.assert_array_equal(cpu(a[k]), cpu(b[k]), err_msg=k)
+
+
+# ------------------------------------------------------------------ conv ------------
+
+
+@pytest.mark.parametrize("wl", [0, 2, 3])
+def test_conv2tap(d2, wl):
+    inp = inputs(wl)
+    print(f"conv c{wl}", flush=True)
+    y = cpu(d2.conv2tap(to_gpu(inp["conv_x"]), to_gpu(inp["conv_prev"]), to_gpu(inp["conv_taps"])))
+    yref, yabs = oracle.conv2tap(inp["conv_x"], inp["conv_prev"], inp["conv_taps"])
+    assert_close_scaled(y, yref, yabs, what="conv")
+
+
+def test_conv2tap_groups_and_odd_shapes(d2):
+    rng = np.random.default_rng(3)
+    for S_, B, K, D, g in ((1, 1, 1, 4, 1), (2, 3, 5, 12, 3), (1, 2, 9, 10, 1), (3, 1, 64, 64, 16), (1, 4, 7, 5120, 2)):
+        x = rng.standard_normal((S_, B, K, D)).astype(np.float32)
+        p = rng.standard_normal((S_, B, D)).astype(np.float32)
+        k = rng.uniform(-1, 1, (S_, B, K, 2, D // g)).astype(np.float32)
+        print(f"conv shape {(S_, B, K, D, g)}", flush=True)
+        y = cpu(d2.conv2tap(to_gpu(x), to_gpu(p), to_gpu(k), group=g))
+        yref, yabs = oracle.conv2tap(x, p, k, g)
+        assert_close_scaled(y, yref, yabs, what=f"conv {(S_, B, K, D, g)}")
+
+
+# ------------------------------------------------------------------ verify ----------
+
+
+def _c4_draft(d2):
+    inp = inputs(4)
+    w = synth.workload(4)
+    _, out = _run_select(d2, inp, w, w.temperature, w.walk_seed)
+    return inp, w, out
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.0, 0.6])
+def test_spec_accept_c4(d2, temperature):
+    inp, w, out = _c4_draft(d2)
+    tb = inp["target_bits"]
+    tokens, cand, q = cpu(out["tokens"]), cpu(out["cand_idx"]), cpu(out["q"])
+    if temperature == 0.0:
+        # make some drafts match the target argmax so prefixes of several lengths occur
+        g = np.argmax(oracle.bf16_to_f64(tb), axis=-1)
+        for b in range(w.B):
+            n = b % (w.K + 1)
+            tokens[b, :n] = g[b, :n]
+    print(f"spec_accept c4 T={temperature}", flush=True)
+    o, n, st = d2.spec_accept(to_gpu_bits(tb), to_gpu(tokens), to_gpu(cand), to_gpu(q), temperature, seed=11)
+    stats = check_accept(tb, tokens, cand, q, temperature, 11, cpu(o), cpu(n), cpu(st))
+    print("verify stats", stats)
+
+
+def test_spec_accept_correlated_target(d2):
+    # target = draft logits + N(0, 1): drafts are often accepted, so every branch
+    # (accept, residual resample, bonus) is exercised against the oracle
+    inp, w, out = _c4_draft(d2)
+    rng = np.random.default_rng(8)
+    draft = synth.bf16_bits_as_f32(inp["logits_bits"])
+    # a target sharper than the draft: its mass sits on the draft's best candidates
+    tgt = 4.0 * np.concatenate([draft, draft[:, -1:]], axis=1) + rng.standard_normal((w.B, w.K + 1, w.V)).astype(np.float32) * 0.3
+    tb = synth.f32_to_bf16_bits(tgt)
+    tokens, cand, q = cpu(out["tokens"]), cpu(out["cand_idx"]), cpu(out["q"])
+    o, n, st = d2.spec_accept(to_gpu_bits(tb), to_gpu(tokens), to_gpu(cand), to_gpu(q), 1.0, seed=12)
+    stats = check_accept(tb, tokens, cand, q, 1.0, 12, cpu(o), cpu(n), cpu(st))
+    print("correlated verify stats", stats, "accepted", cpu(n).tolist())
+    assert cpu(n).max() > 0
+
+
+def test_spec_accept_fault_rows(d2):
+    rng = np.random.default_rng(14)
+    B, K, V = 6, 3, 5000
+    tb = synth.f32_to_bf16_bits(rng.standard_normal((B, K + 1, V)).astype(np.float32))
+    cand = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    q = np.full((B, K, 16), 1.0 / 16, np.float32)
+    tokens = cand[:, :, 0].copy()
+    tb[0, 1, 77] = 0x7FC0                 # NaN target -> bit 0
+    q[1, 0, 3] = np.nan                   # NaN q -> bit 2
+    q[2, 2] *= 0.5                        # wrong total -> bit 2
+    tokens[3, 1] = V + 4                  # out-of-range draft -> bit 1
+    q[4, 1, :] = 0.0                      # q(x) = 0 -> bit 2 (and wrong total)
+    q[4, 1, 5] = 1.0
+    tb[5, 0, 9] = 0x7F80                  # +inf target -> bit 0
+    o, n, st = d2.spec_accept(to_gpu_bits(tb), to_gpu(tokens), to_gpu(cand), to_gpu(q), 1.0, seed=3)
+    check_accept(tb, tokens, cand, q, 1.0, 3, cpu(o), cpu(n), cpu(st))
+    assert cpu(st).tolist() == [1, 4, 4, 2, 4, 1]
+
+
+def test_spec_accept_shared_target_matches_expanded(d2):
+    inp, w, out = _c4_draft(d2)
+    tb = inp["target_bits"][0]
+    tokens, cand, q = out["tokens"], out["cand_idx"], out["q"]
+    o1, n1, s1 = d2.spec_accept(to_gpu_bits(tb), tokens, cand, q, 1.0, seed=5, shared_target=True)
+    full = np.broadcast_to(tb, (w.B,) + tb.shape)
+    o2, n2, s2 = d2.spec_accept(to_gpu_bits(full), tokens, cand, q, 1.0, seed=5)
+    np.testing.assert_array_equal(cpu(o1), cpu(o2))
+    np.testing.assert_array_equal(cpu(n1), cpu(n2))
