@@ -11,7 +11,10 @@ using namespace df2;
 namespace {
 
 constexpr int64_t kMaxVocab = (int64_t)kMaxChunks * kChunkVec * 8;   // 2^19
-constexpr int64_t kMaxGridRows = (int64_t)1 << 30;
+// An AQL dispatch packet carries the grid size as a 32-bit count of work-items.
+constexpr int64_t kMaxItems = 0xffffffffLL;
+
+bool items_ok(int64_t blocks, int64_t threads) { return blocks >= 1 && blocks <= kMaxItems / threads; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,7 +25,7 @@ dflash2_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : 
 dflash2_status check_logits(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t ld) {
   if (!logits) return DFLASH2_ERR_NULL;
   if (rows < 1 || vocab < DFLASH2_NCAND || vocab > kMaxVocab || ld < vocab) return DFLASH2_ERR_SHAPE;
-  if (rows * topk_num_chunks(vocab) > kMaxGridRows) return DFLASH2_ERR_SHAPE;
+  if (rows > kMaxItems || !items_ok(rows * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
   if (!aligned16(logits) || (ld % 8) != 0) return DFLASH2_ERR_ALIGN;
   return DFLASH2_OK;
 }
@@ -38,7 +41,7 @@ dflash2_status check_emb(const void* a, const void* b, dflash2_dtype dt, int64_t
 
 dflash2_status check_bk(int64_t batch, int64_t K) {
   if (batch < 1 || batch >= ((int64_t)1 << 31) || K < 1 || K > DFLASH2_MAX_K) return DFLASH2_ERR_SHAPE;
-  if (batch * K > kMaxGridRows) return DFLASH2_ERR_SHAPE;
+  if (!items_ok(batch * K, 256)) return DFLASH2_ERR_SHAPE;
   return DFLASH2_OK;
 }
 
@@ -108,8 +111,11 @@ dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dty
   if (!h || !w_h || !H) return DFLASH2_ERR_NULL;
   if (w_dtype != DFLASH2_F32 && w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
   if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
-  if (rows < 1 || rows > kMaxGridRows || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24) ||
+  if (rows < 1 || rows > ((int64_t)1 << 30) || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24) ||
       !pow2_in(dim, 16, 1024))
+    return DFLASH2_ERR_SHAPE;
+  if (!items_ok((rows * dim + 255) / 256, 256) ||
+      (w_dtype == DFLASH2_BF16 && !items_ok(gate_grid_blocks(rows, hidden, dim), 256)))
     return DFLASH2_ERR_SHAPE;
   if (!aligned16(h) || !aligned16(w_h)) return DFLASH2_ERR_ALIGN;
   GateWs ws;
@@ -179,7 +185,9 @@ dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float
   if (!x || !x_prev || !taps || !y) return DFLASH2_ERR_NULL;
   if (sites < 1 || batch < 1 || K < 1 || K > DFLASH2_MAX_K || hidden < 1 || group < 1 || hidden % group != 0)
     return DFLASH2_ERR_SHAPE;
-  if (sites * batch * hidden > ((int64_t)1 << 40)) return DFLASH2_ERR_SHAPE;
+  if (sites > kMaxItems || batch > kMaxItems || hidden > kMaxItems || sites * batch > kMaxItems ||
+      !items_ok((sites * batch * hidden + 255) / 256, 256))
+    return DFLASH2_ERR_SHAPE;
   return hip_status(launch_conv2tap(x, x_prev, taps, sites, batch, (int)K, hidden, group, y, stream));
 }
 
@@ -202,6 +210,7 @@ dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, in
   if (st != DFLASH2_OK) return st;
   if (batch_stride < 0 || (batch_stride > 0 && batch_stride < (K + 1) * ld)) return DFLASH2_ERR_SHAPE;
   if (batch_stride % 8 != 0) return DFLASH2_ERR_ALIGN;
+  if (!items_ok(accept_stats_blocks(nrows, vocab), 256)) return DFLASH2_ERR_SHAPE;
   if (!tokens || !cand_idx || !out_tokens || !n_accepted) return DFLASH2_ERR_NULL;
   st = check_temp(temperature);
   if (st != DFLASH2_OK) return st;

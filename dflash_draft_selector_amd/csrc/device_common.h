@@ -167,48 +167,5 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// ---- cross-work-group publication ---------------------------------------------------
-// Data that one work-group hands to another inside the same launch is written with
-// agent-scope atomic stores and read with agent-scope atomic loads.  Those are
-// coherent across the XCDs' separate L2 caches on their own, so no agent-scope fence
-// (which writes back / invalidates a whole L2) is needed: a writer only waits for its
-// stores to complete before it is counted, and a reader issues its loads after it has
-// seen the count.
-
-template <typename T>
-__device__ __forceinline__ void st_agent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_agent(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Add one to `ticket`; true in the caller that brings it to `expected` (which then
-// resets it).  Call after the block's published stores completed (see arrive_last).
-__device__ __forceinline__ bool count_to(unsigned int* ticket, unsigned int expected) {
-  const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool last = prev + 1u == expected;
-  if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return last;
-}
-
-// Wait until this thread's published stores are complete, then join the block.
-__device__ __forceinline__ void publish_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-}
-
-// Count this work-group in `ticket` after every thread's published stores completed.
-// Returns true (uniformly across the block) in the work-group that completes the count;
-// that work-group resets the counter to zero for the next call.
-__device__ __forceinline__ bool arrive_last(unsigned int* ticket, unsigned int expected, int* s_flag) {
-  publish_barrier();
-  if (threadIdx.x == 0) *s_flag = count_to(ticket, expected) ? 1 : 0;
-  __syncthreads();
-  return *s_flag != 0;
-}
 
 }  // namespace df2

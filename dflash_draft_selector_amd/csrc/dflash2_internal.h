@@ -35,22 +35,20 @@ struct SelectWs {
 SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab);
 
 struct GateWs {
-  float* partial;                 // [nsplit][mtiles*16][dim]
-  unsigned int* ticket;           // [mtiles]
+  float* partial;                 // [nsplit][rows][dim] slice sums (nsplit > 1)
+  int nsplit;                     // slices of the hidden dimension
 };
-int gate_splits(int64_t rows, int64_t hidden);
+int gate_splits(int64_t rows, int64_t hidden, int64_t dim);
 GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim);
+int64_t gate_grid_blocks(int64_t rows, int64_t hidden, int64_t dim);
 
 struct AcceptWs {
-  float* chunk_max;               // [nrows][nchunks]
+  float* chunk_max;               // [nrows][nchunks]; NaN: a non-finite chunk
   float* chunk_sum;               // [nrows][nchunks]
   unsigned long long* chunk_arg;  // [nrows][nchunks] (greedy)
-  float* row_max;                 // [nrows]
-  float* row_sum;                 // [nrows]
-  unsigned long long* row_arg;    // [nrows]
-  unsigned int* row_ticket;       // [nrows]
 };
 AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab);
+int64_t accept_stats_blocks(int64_t nrows, int64_t vocab);
 
 hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld, int32_t* cand_idx,
                          float* cand_val, int32_t* row_status, TopkWs ws, hipStream_t s);

@@ -2,12 +2,14 @@
 // accept with min(1, p/q), on a reject resample from max(0, p - q); all-greedy keeps
 // the prefix match.  pegainfer issue "DFlash 2 proposer", "Proposal", phase 3).
 //
-// Pass 1 (k_accept_stats): split-vocabulary statistics of every target row -- max and
-// sum of exp((l - max)/T) per chunk and per row, or the row argmax when T == 0.
-// Pass 2 (k_accept_decide): one block per request runs the accept tests, then draws
-// the committed token by inverse CDF: the chunk is found from the pass-1 chunk masses
-// (minus the draft's mass at its candidates), and only that chunk is rescanned.
+// Pass 1 (k_accept_stats): split-vocabulary statistics of every target row -- per
+// chunk the max and the sum of exp((l - max)/T), or the chunk argmax when T == 0.
+// Pass 2 (k_accept_decide): one block per request merges its rows' chunk statistics
+// (fixed chunk order), runs the accept tests, then draws the committed token by
+// inverse CDF: the chunk is found from the chunk masses (minus the draft's mass at its
+// candidates), and only that chunk is rescanned.
 #include "device_common.h"
+#include "dflash2.h"
 #include "dflash2_internal.h"
 #include "topk_dev.h"
 
@@ -23,16 +25,14 @@ __host__ __device__ __forceinline__ int acc_num_chunks(long long vocab) {
   return (int)((nvec + kAccChunkVec - 1) / kAccChunkVec);
 }
 
+int64_t accept_stats_blocks(int64_t nrows, int64_t vocab) { return nrows * acc_num_chunks(vocab); }
+
 AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab) {
   AcceptWs w;
   const size_t n = (size_t)nrows * acc_num_chunks(vocab);
   w.chunk_max = c.take<float>(n);
   w.chunk_sum = c.take<float>(n);
   w.chunk_arg = c.take<unsigned long long>(n);
-  w.row_max = c.take<float>((size_t)nrows);
-  w.row_sum = c.take<float>((size_t)nrows);
-  w.row_arg = c.take<unsigned long long>((size_t)nrows);
-  w.row_ticket = c.take<unsigned int>((size_t)nrows);
   return w;
 }
 
@@ -61,7 +61,6 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
   __shared__ float s_redf[4];
   __shared__ int s_redi[4];
   __shared__ unsigned long long s_redu[4];
-  __shared__ int s_flag;
   const int tid = threadIdx.x;
   const int r = blockIdx.x / nchunks;
   const int c = blockIdx.x - r * nchunks;
@@ -110,16 +109,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
       }
     }
     best = block_reduce<unsigned long long>(best, s_redu, true);
-    if (tid == 0) st_agent(ws.chunk_arg + ci, best);
-    if (!arrive_last(ws.row_ticket + r, (unsigned)nchunks, &s_flag)) return;
-    if (tid == 0) {
-      unsigned long long m = 0ull;
-      for (int j = 0; j < nchunks; ++j) {
-        const unsigned long long a = ld_agent(ws.chunk_arg + (size_t)r * nchunks + j);
-        m = a > m ? a : m;
-      }
-      ws.row_arg[r] = m;
-    }
+    if (tid == 0) ws.chunk_arg[ci] = best;
     return;
   }
 
@@ -152,29 +142,15 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
   }
   sum = block_reduce<float>(sum, s_redf, false);
   if (tid == 0) {
-    st_agent(ws.chunk_max + ci, nonfinite ? __builtin_nanf("") : m_c);
-    st_agent(ws.chunk_sum + ci, sum);
-  }
-  if (!arrive_last(ws.row_ticket + r, (unsigned)nchunks, &s_flag)) return;
-  if (tid == 0) {
-    float m = -__builtin_inff();
-    bool bad = false;
-    for (int j = 0; j < nchunks; ++j) {
-      const float mj = ld_agent(ws.chunk_max + (size_t)r * nchunks + j);
-      if (__builtin_isnan(mj)) bad = true;
-      else m = fmaxf(m, mj);
-    }
-    float Z = 0.f;
-    for (int j = 0; j < nchunks; ++j) {
-      const float mj = ld_agent(ws.chunk_max + (size_t)r * nchunks + j);
-      if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ld_agent(ws.chunk_sum + (size_t)r * nchunks + j) * expf((mj - m) * inv_t);
-    }
-    ws.row_max[r] = m;
-    ws.row_sum[r] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
+    ws.chunk_max[ci] = nonfinite ? __builtin_nanf("") : m_c;
+    ws.chunk_sum[ci] = sum;
   }
 }
 
 struct DecideShared {
+  float row_max[DFLASH2_MAX_K + 1];     // merged statistics of the request's rows
+  float row_sum[DFLASH2_MAX_K + 1];     // NaN: a non-finite row
+  int row_arg[DFLASH2_MAX_K + 1];       // greedy: the row argmax
   int status;
   int tstar;
   int ids_bad;
@@ -190,15 +166,28 @@ struct DecideShared {
   float tsum[kAccThreads];
 };
 
-// Inverse-CDF draw from row `r` (stats index) of the target: weights p (residual ==
-// false) or max(0, p - q) with q supported on the request's candidates of that
-// position.  Block-wide; returns the token id (valid in every thread).
-__device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, int V, int nchunks, float inv_t, float u,
-                             bool residual, const int32_t* __restrict__ cand, const float* __restrict__ qrow,
-                             const AcceptWs& ws, DecideShared& sm) {
+// Weight of logit `id` of the draw: p, or max(0, p - q) at a candidate id (cl_id is
+// sorted; *ci walks it forward).
+__device__ __forceinline__ float draw_weight(uint32_t bits, int id, float m, float inv_t, float invZ,
+                                             const DecideShared& sm, int* ci) {
+  const float p = expf((bf16_to_f32(bits) - m) * inv_t) * invZ;
+  if (*ci < sm.ncl && sm.cl_id[*ci] == id) {
+    const float r = fmaxf(p - sm.cl_qf[*ci], 0.f);
+    ++*ci;
+    return r;
+  }
+  return p;
+}
+
+// Inverse-CDF draw from row `r` (stats index) of the target, whose merged max and sum
+// are m and Z: weights p (residual == false) or max(0, p - q) with q supported on the
+// request's candidates of that position.  Block-wide; returns the token id (valid in
+// every thread), or -1 for a residual without mass.
+__device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, float m, float Z, int V, int nchunks,
+                             float inv_t, float u, bool residual, const int32_t* __restrict__ cand,
+                             const float* __restrict__ qrow, const AcceptWs& ws, DecideShared& sm) {
   const int tid = threadIdx.x;
-  const float m = ws.row_max[r];
-  const float invZ = 1.f / ws.row_sum[r];
+  const float invZ = 1.f / Z;
   if (tid == 0) {
     int n = 0;
     if (residual) {
@@ -270,30 +259,21 @@ __device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, int V, in
   const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
   const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;   // <= 64
   const int a0 = e0 + tid * L;
-  float rv[64];
-  int ci = 0;
-  while (ci < sm.ncl && sm.cl_id[ci] < a0) ++ci;
+  int ci0 = 0;
+  while (ci0 < sm.ncl && sm.cl_id[ci0] < a0) ++ci0;
   float tsum = 0.f;
+  {
+    int ci = ci0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    u32x4 vec = {0u, 0u, 0u, 0u};
-    const int base = a0 + 8 * k;
-    if (8 * k < L && base + 8 <= e1) vec = *reinterpret_cast<const u32x4*>(rowp + base);
+    for (int k = 0; k < 8; ++k) {
+      const int base = a0 + 8 * k;
+      if (8 * k < L && base + 8 <= e1) {
+        const u32x4 vec = *reinterpret_cast<const u32x4*>(rowp + base);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int id = base + e;
-      float rr = 0.f;
-      if (8 * k < L && id < e1) {
-        const uint32_t bits = (base + 8 <= e1) ? elem_bits(vec, e) : (uint32_t)rowp[id];
-        const float p = expf((bf16_to_f32(bits) - m) * inv_t) * invZ;
-        rr = p;
-        if (ci < sm.ncl && sm.cl_id[ci] == id) {
-          rr = fmaxf(p - sm.cl_qf[ci], 0.f);
-          ++ci;
-        }
+        for (int e = 0; e < 8; ++e) tsum += draw_weight(elem_bits(vec, e), base + e, m, inv_t, invZ, sm, &ci);
+      } else if (8 * k < L) {
+        for (int id = base; id < base + 8 && id < e1; ++id) tsum += draw_weight(rowp[id], id, m, inv_t, invZ, sm, &ci);
       }
-      rv[8 * k + e] = rr;
-      tsum += rr;
     }
   }
   sm.tsum[tid] = tsum;
@@ -319,15 +299,14 @@ __device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, int V, in
   const int who = sm.status;
   const int lastpos = (int)sm.red[1];
   if (tid == who || (who < 0 && tid == lastpos)) {
+    // the same weights again, in the same order, now with the running sum
     float run = sm.red[0];
-    int pick = -1, lastp = -1;
-#pragma unroll
-    for (int e = 0; e < 64; ++e) {
-      if (e < L && a0 + e < e1) {
-        run += rv[e];
-        if (pick < 0 && who >= 0 && sm.rem < run) pick = a0 + e;
-        if (rv[e] > 0.f) lastp = a0 + e;
-      }
+    int pick = -1, lastp = -1, ci = ci0;
+    for (int id = a0; id < a0 + L && id < e1; ++id) {
+      const float w = draw_weight(rowp[id], id, m, inv_t, invZ, sm, &ci);
+      run += w;
+      if (pick < 0 && who >= 0 && sm.rem < run) pick = id;
+      if (w > 0.f) lastp = id;
     }
     sm.pick = pick >= 0 ? pick : lastp;
   }
@@ -357,6 +336,33 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     sm.q_bad = 0;
     sm.tstar = K;
   }
+  // merge the chunk statistics of rows rbase .. rbase + K (one thread per row, chunk order)
+  if (tid <= K) {
+    const size_t c0 = (size_t)(rbase + tid) * nchunks;
+    if (inv_t == 0.f) {
+      unsigned long long a = 0ull;
+      for (int j = 0; j < nchunks; ++j) {
+        const unsigned long long x = ws.chunk_arg[c0 + j];
+        a = x > a ? x : a;
+      }
+      sm.row_arg[tid] = rc_id(a);
+    } else {
+      float m = -__builtin_inff();
+      bool bad = false;
+      for (int j = 0; j < nchunks; ++j) {
+        const float mj = ws.chunk_max[c0 + j];
+        if (__builtin_isnan(mj)) bad = true;
+        else m = fmaxf(m, mj);
+      }
+      float Z = 0.f;
+      for (int j = 0; j < nchunks; ++j) {
+        const float mj = ws.chunk_max[c0 + j];
+        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ws.chunk_sum[c0 + j] * expf((mj - m) * inv_t);
+      }
+      sm.row_max[tid] = m;
+      sm.row_sum[tid] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
+    }
+  }
   __syncthreads();
   for (int e = tid; e < K * (kNC + 1); e += kAccThreads) {
     const int id = e < K ? tok_b[e] : cand_b[e - K];
@@ -371,12 +377,12 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     if (tid == 0) {
       int t = 0;
       while (t < K) {
-        const int g = rc_id(ws.row_arg[rbase + t]);
+        const int g = sm.row_arg[t];
         if (tok_b[t] != g) break;
         out_b[t] = g;
         ++t;
       }
-      out_b[t] = rc_id(ws.row_arg[rbase + t]);
+      out_b[t] = sm.row_arg[t];
       n_accepted[b] = t;
       if (row_status) row_status[b] = ids_bad ? 2 : 0;
     }
@@ -385,7 +391,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
 
   // non-finite target rows: commit nothing
   int nonfinite = 0;
-  for (int t = 0; t <= K; ++t) nonfinite |= !__builtin_isfinite(ws.row_sum[rbase + t]);
+  for (int t = 0; t <= K; ++t) nonfinite |= !__builtin_isfinite(sm.row_sum[t]);
   if (nonfinite) {
     if (tid == 0) {
       n_accepted[b] = 0;
@@ -415,7 +421,8 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
 
   if (ids_bad || q_bad) {
     const float u_res = word_to_uniform(philox4x32_10(0u, (uint32_t)b, 1u, 0u, k0, k1).x1);
-    const int v = draw_from_row(tb, rbase, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+    const int v = draw_from_row(tb, rbase, sm.row_max[0], sm.row_sum[0], V, nchunks, inv_t, u_res, false, nullptr,
+                                nullptr, ws, sm);
     if (tid == 0) {
       out_b[0] = v;
       n_accepted[b] = 0;
@@ -431,7 +438,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     float qx = 0.f;
     const float* qr = q + ((size_t)b * K + t) * kNC;
     for (int j = 0; j < kNC; ++j) qx += cand_b[t * kNC + j] == x ? qr[j] : 0.f;
-    const float px = expf((bf16_to_f32(tb[(size_t)t * ld + x]) - ws.row_max[rbase + t]) * inv_t) / ws.row_sum[rbase + t];
+    const float px = expf((bf16_to_f32(tb[(size_t)t * ld + x]) - sm.row_max[t]) * inv_t) / sm.row_sum[t];
     const float u_acc = word_to_uniform(philox4x32_10((uint32_t)t, (uint32_t)b, 1u, 0u, k0, k1).x0);
     if (!(u_acc * qx < px)) atomicMin(&sm.tstar, t);
   }
@@ -445,13 +452,15 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     const int32_t* cand_t = cand_b + tstar * kNC;
     const float* q_t = q + ((size_t)b * K + tstar) * kNC;
     // residual mass: 1 - sum over candidates of min(p, q) is positive after any reject
-    v = draw_from_row(rowp, rbase + tstar, V, nchunks, inv_t, u_res, true, cand_t, q_t, ws, sm);
+    const float m = sm.row_max[tstar], Z = sm.row_sum[tstar];
+    v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, inv_t, u_res, true, cand_t, q_t, ws, sm);
     if (v < 0) {
       status |= 8;
-      v = draw_from_row(rowp, rbase + tstar, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+      v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
     }
   } else {
-    v = draw_from_row(tb + (size_t)K * ld, rbase + K, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+    v = draw_from_row(tb + (size_t)K * ld, rbase + K, sm.row_max[K], sm.row_sum[K], V, nchunks, inv_t, u_res, false,
+                      nullptr, nullptr, ws, sm);
   }
   if (tid == 0) {
     out_b[tstar] = v;

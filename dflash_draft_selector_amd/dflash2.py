@@ -111,10 +111,9 @@ def _contig(t, name):
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
-# Workspaces: one zero-initialised buffer per (device, call kind, shape, stream).  The
-# kernels return every counter to zero, so a buffer stays valid for later calls of the
-# same kind and shape on the same stream; a different shape lays the workspace out
-# differently and gets its own buffer.
+# Workspaces: one buffer per (device, call kind, shape, stream).  A call writes every
+# workspace byte before it reads it, so no initialisation is needed; keeping one buffer
+# per stream keeps calls that may overlap in time off each other's scratch.
 _ws_cache: dict = {}
 
 
@@ -122,7 +121,7 @@ def workspace(kind: str, nbytes: int, device: torch.device, shape: tuple = ()) -
     key = (device.index, kind, tuple(shape), _stream())
     buf = _ws_cache.get(key)
     if buf is None:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 

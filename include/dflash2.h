@@ -12,15 +12,15 @@
  *  - bf16 data is passed as its uint16_t bit pattern.
  *  - The caller owns every buffer.  The library allocates no device memory and keeps
  *    no state between calls.  Scratch memory comes only from a caller-provided
- *    workspace sized by the matching *_workspace() query.  A workspace must be
- *    zero-filled once when first allocated; every call returns its counters to zero,
- *    so it stays valid for later calls of the SAME entry point with the SAME sizes.
- *    A call with other sizes lays the workspace out differently and needs its own
- *    (or a freshly zero-filled) buffer.  Calls that overlap in time must not share
- *    a workspace.
+ *    workspace sized by the matching *_workspace() query.  A workspace needs no
+ *    initialisation: a call writes every workspace byte it reads before reading it,
+ *    so a buffer may serve any later call whose query returns no more than its size.
+ *    Calls that overlap in time must not share a workspace.
  *  - Every call validates its arguments on the host, enqueues its kernels on `stream`
  *    and returns without synchronising.  Host-detectable errors are returned before
  *    anything is enqueued; nothing aborts, prints or reads the environment.
+ *  - Sizes whose kernels would need more than 2^32 - 1 work-items in one launch (the
+ *    limit of a dispatch packet) are rejected with DFLASH2_ERR_SHAPE.
  *  - Results are deterministic: bit-identical across runs for the same inputs.
  *  - Outputs must not alias inputs.
  *  - Per-row data faults are reported in optional int32 `row_status` arrays (pass
