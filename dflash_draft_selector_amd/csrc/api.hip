@@ -185,9 +185,9 @@ dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float
   if (!x || !x_prev || !taps || !y) return DFLASH2_ERR_NULL;
   if (sites < 1 || batch < 1 || K < 1 || K > DFLASH2_MAX_K || hidden < 1 || group < 1 || hidden % group != 0)
     return DFLASH2_ERR_SHAPE;
-  if (sites > kMaxItems || batch > kMaxItems || hidden > kMaxItems || sites * batch > kMaxItems ||
-      !items_ok((sites * batch * hidden + 255) / 256, 256))
-    return DFLASH2_ERR_SHAPE;
+  if (sites > kMaxItems || batch > kMaxItems / sites) return DFLASH2_ERR_SHAPE;
+  const int64_t rows = sites * batch * K;                 // one thread per channel and row at most
+  if (rows > kMaxItems || hidden > (kMaxItems - 255) / rows) return DFLASH2_ERR_SHAPE;
   return hip_status(launch_conv2tap(x, x_prev, taps, sites, batch, (int)K, hidden, group, y, stream));
 }
 

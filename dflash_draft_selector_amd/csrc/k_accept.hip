@@ -38,6 +38,13 @@ AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab) {
 
 __device__ __forceinline__ float order_to_float(int s) { return bf16_to_f32(order_to_bits(s)); }
 
+constexpr float kLog2e = 1.44269504088896341f;
+
+// exp((l - m) / T) formed as 2^((l - m) * c2) with c2 = log2(e) / T: one v_exp_f32 per
+// weight.  Every weight of the target distribution (chunk sums, the accept test and
+// the draws) is formed this one way.
+__device__ __forceinline__ float tweight(float l, float m, float c2) { return __builtin_amdgcn_exp2f((l - m) * c2); }
+
 template <typename T>
 __device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
   // fixed-order block reduction over 4 waves (deterministic)
@@ -94,6 +101,44 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
 
   const size_t ci = (size_t)r * nchunks + c;
   if (inv_t == 0.f) {
+    // Chunk argmax (largest order key, then lowest id; NaN lowest).  The maximum is
+    // found on packed signed-order halves, with +NaN clamped to +inf; the lanes then
+    // look for the lowest id whose key equals it.  A chunk whose only maxima were
+    // +NaN finds none and takes the exact composite scan.
+    int vmax[kAccVecPerThread];
+    int lmax = -32768;
+#pragma unroll
+    for (int k = 0; k < kAccVecPerThread; ++k) {
+      const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(signed_order2(d[k].x), signed_order2(d[k].y)),
+                                                 __builtin_elementwise_max(signed_order2(d[k].z), signed_order2(d[k].w)));
+      vmax[k] = max_halves(mx);
+      lmax = vmax[k] > lmax ? vmax[k] : lmax;
+    }
+    lmax = lmax > 0x7f80 ? 0x7f80 : lmax;
+    const int M = block_reduce<int>(lmax, s_redi, true);
+    const uint32_t mbits = order_to_bits(M);
+    const uint32_t mkey = bf16_key(mbits);
+    int best_id = 0x7fffffff;
+    // only vectors whose maximum reaches M - 1 can hold the key (-0 sits one order
+    // below +0 and shares its key); ids rise with k, so the first hit of a lane wins
+#pragma unroll
+    for (int k = 0; k < kAccVecPerThread; ++k) {
+      const int v = v0 + tid + k * kAccThreads;
+      if (best_id == 0x7fffffff && v < v1 && (vmax[k] > 0x7f80 ? 0x7f80 : vmax[k]) >= M - 1) {
+        for (int e = 0; e < 8; ++e) {
+          const int id = 8 * v + e;
+          if (id < V && bf16_key(elem_bits(d[k], e)) == mkey) {
+            best_id = id;
+            break;
+          }
+        }
+      }
+    }
+    best_id = -block_reduce<int>(-best_id, s_redi, true);
+    if (best_id != 0x7fffffff) {
+      if (tid == 0) ws.chunk_arg[ci] = make_rc(mkey, (unsigned)best_id, mbits);
+      return;
+    }
     unsigned long long best = 0ull;
 #pragma unroll
     for (int k = 0; k < kAccVecPerThread; ++k) {
@@ -131,12 +176,13 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
   const float m_c = order_to_float(smax > 32640 ? 32640 : smax);
   float sum = 0.f;
   if (!nonfinite && m_c != -__builtin_inff()) {
+    const float c2 = inv_t * kLog2e;
 #pragma unroll
     for (int k = 0; k < kAccVecPerThread; ++k) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        sum += expf((bf16_lo(d[k][w]) - m_c) * inv_t);
-        sum += expf((bf16_hi(d[k][w]) - m_c) * inv_t);
+        sum += tweight(bf16_lo(d[k][w]), m_c, c2);
+        sum += tweight(bf16_hi(d[k][w]), m_c, c2);
       }
     }
   }
@@ -157,157 +203,219 @@ struct DecideShared {
   int q_bad;
   int pick;
   int chunk;
+  int who;
+  int last;
   float rem;
+  float before;
   int ncl;
   int cl_id[kNC];
   float cl_qf[kNC];
   float R[kAccMaxChunks];
-  float red[4];
   float tsum[kAccThreads];
 };
 
-// Weight of logit `id` of the draw: p, or max(0, p - q) at a candidate id (cl_id is
-// sorted; *ci walks it forward).
-__device__ __forceinline__ float draw_weight(uint32_t bits, int id, float m, float inv_t, float invZ,
-                                             const DecideShared& sm, int* ci) {
-  const float p = expf((bf16_to_f32(bits) - m) * inv_t) * invZ;
-  if (*ci < sm.ncl && sm.cl_id[*ci] == id) {
-    const float r = fmaxf(p - sm.cl_qf[*ci], 0.f);
-    ++*ci;
-    return r;
+// Weight of logit `id` of the draw: p, or max(0, p - q) when id is a candidate.
+__device__ __forceinline__ float draw_weight(uint32_t bits, int id, bool is_cand, float m, float c2, float invZ,
+                                             const DecideShared& sm) {
+  const float p = tweight(bf16_to_f32(bits), m, c2) * invZ;
+  if (!is_cand) return p;
+  float qf = 0.f;
+  for (int i = 0; i < sm.ncl; ++i) qf = sm.cl_id[i] == id ? sm.cl_qf[i] : qf;
+  return fmaxf(p - qf, 0.f);
+}
+
+// Result of wave_find_crossing, the same in every lane of the wave.
+struct Crossing {
+  int idx;        // first index whose running sum exceeds the target, -1 if none
+  float before;   // the running sum before idx
+  int last;       // last index holding a positive value, -1 if none
+};
+
+// One whole wave over vals[0 .. n) (LDS, non-negative, n <= 256).  Lane l owns
+// vals[4l .. 4l + 3]; its offset is an inclusive scan of the lane sums over lanes, and
+// within the lane the sums run in index order.
+__device__ __forceinline__ Crossing wave_find_crossing(const float* vals, int n, float target) {
+  const int lane = threadIdx.x & 63;
+  float v[4], part[4];
+  float run = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * lane + j;
+    v[j] = i < n ? vals[i] : 0.f;
+    run += v[j];
+    part[j] = run;
   }
-  return p;
+  float inc = part[3];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  float excl = __shfl_up(inc, 1);
+  if (lane == 0) excl = 0.f;
+  int jhit = 0;
+  while (jhit < 3 && !(target < excl + part[jhit])) ++jhit;
+  const float bef = jhit == 0 ? excl : excl + part[jhit - 1];
+  int jlast = 3;
+  while (jlast > 0 && !(v[jlast] > 0.f)) --jlast;
+  const unsigned long long hit = __ballot(target < excl + part[3]);
+  const unsigned long long pos = __ballot(part[3] > 0.f);
+  Crossing cr = {-1, 0.f, -1};
+  if (hit) {
+    const int src = __builtin_ctzll(hit);
+    cr.idx = 4 * src + __builtin_amdgcn_readlane(jhit, src);
+    cr.before = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bef), src));
+  }
+  if (pos) {
+    const int src = 63 - __builtin_clzll(pos);
+    cr.last = 4 * src + __builtin_amdgcn_readlane(jlast, src);
+  }
+  return cr;
 }
 
 // Inverse-CDF draw from row `r` (stats index) of the target, whose merged max and sum
 // are m and Z: weights p (residual == false) or max(0, p - q) with q supported on the
 // request's candidates of that position.  Block-wide; returns the token id (valid in
 // every thread), or -1 for a residual without mass.
-__device__ int draw_from_row(const uint16_t* __restrict__ rowp, int r, float m, float Z, int V, int nchunks,
-                             float inv_t, float u, bool residual, const int32_t* __restrict__ cand,
+__device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restrict__ rowp, int r, float m, float Z, int V, int nchunks,
+                             float c2, float u, bool residual, const int32_t* __restrict__ cand,
                              const float* __restrict__ qrow, const AcceptWs& ws, DecideShared& sm) {
   const int tid = threadIdx.x;
   const float invZ = 1.f / Z;
-  if (tid == 0) {
-    int n = 0;
+  // residual: the distinct candidate ids with their total draft mass (summed in slot
+  // order), sorted by id -- lane j of wave 0 owns slot j & 15
+  if (tid < kWave) {
+    int ncl = 0;
     if (residual) {
-      // distinct candidate ids with their total draft mass, sorted by id
-      for (int j = 0; j < kNC; ++j) {
-        const int id = cand[j];
-        bool seen = false;
-        for (int i = 0; i < j; ++i) seen |= cand[i] == id;
-        if (seen) continue;
-        float qf = 0.f;
-        for (int i = 0; i < kNC; ++i) qf += cand[i] == id ? qrow[i] : 0.f;
-        int pos = n++;
-        while (pos > 0 && sm.cl_id[pos - 1] > id) {
-          sm.cl_id[pos] = sm.cl_id[pos - 1];
-          sm.cl_qf[pos] = sm.cl_qf[pos - 1];
-          --pos;
+      const int j = tid & (kNC - 1);
+      const int id = cand[j];
+      const float qv = qrow[j];
+      bool first = true;
+      float qf = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNC; ++i) {
+        const int oi = __shfl(id, i);
+        const float qi = __shfl(qv, i);
+        if (oi == id) {
+          qf += qi;
+          if (i < j) first = false;
         }
-        sm.cl_id[pos] = id;
-        sm.cl_qf[pos] = qf;
       }
+      int smaller = 0;
+#pragma unroll
+      for (int i = 0; i < kNC; ++i) {
+        const int oi = __shfl(id, i);
+        const int fi = __shfl(first ? 1 : 0, i);
+        if (fi && oi < id) ++smaller;
+      }
+      const unsigned long long fm = __ballot(tid < kNC && first);
+      if (tid < kNC && first) {
+        sm.cl_id[smaller] = id;
+        sm.cl_qf[smaller] = qf;
+      }
+      ncl = __popcll(fm);
     }
-    sm.ncl = n;
+    if (tid == 0) sm.ncl = ncl;
   }
   __syncthreads();
-  // coarse: mass of every chunk
+  // coarse: mass of every chunk, minus the draft's mass at the candidates it holds
   for (int c = tid; c < nchunks; c += kAccThreads) {
     const float mc = ws.chunk_max[(size_t)r * nchunks + c];
-    float P = mc == -__builtin_inff() ? 0.f : ws.chunk_sum[(size_t)r * nchunks + c] * expf((mc - m) * inv_t) * invZ;
+    float P = mc == -__builtin_inff() ? 0.f : ws.chunk_sum[(size_t)r * nchunks + c] * tweight(mc, m, c2) * invZ;
     const int e0 = 8 * chunk_begin(V, nchunks, c);
     const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
     for (int i = 0; i < sm.ncl; ++i) {
       const int id = sm.cl_id[i];
-      if (id >= e0 && id < e1) {
-        const float p = expf((bf16_to_f32(rowp[id]) - m) * inv_t) * invZ;
-        P -= fminf(p, sm.cl_qf[i]);
-      }
+      if (id >= e0 && id < e1) P -= fminf(tweight(bf16_to_f32(rowp[id]), m, c2) * invZ, sm.cl_qf[i]);
     }
     sm.R[c] = fmaxf(P, 0.f);
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < kWave) {
     float Zr = 0.f;
-    for (int c = 0; c < nchunks; ++c) Zr += sm.R[c];
+    for (int c = tid; c < nchunks; c += kWave) Zr += sm.R[c];
+    Zr = wave_sum(Zr);
     const float target = u * Zr;
-    float run = 0.f;
-    int pick = -1, lastpos = 0;
-    float before = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      if (pick < 0 && target < run + sm.R[c]) {
-        pick = c;
-        before = run;
+    const Crossing cr = wave_find_crossing(sm.R, nchunks, target);
+    int idx = cr.idx;
+    float before = cr.before;
+    const int last = cr.last;
+    if (tid == 0) {
+      if (idx < 0) {                       // rounding left the target past the total
+        idx = last;
+        before = 0.f;
+        for (int c = 0; c < last; ++c) before += sm.R[c];
       }
-      run += sm.R[c];
-      if (sm.R[c] > 0.f) lastpos = c;
+      sm.chunk = (residual && !(Zr > 0.f)) || idx < 0 ? -1 : idx;   // a residual without mass
+      sm.rem = target - before;
+      sm.pick = -1;
     }
-    if (pick < 0) {
-      pick = lastpos;
-      before = run - sm.R[lastpos];
-    }
-    sm.chunk = (residual && !(Zr > 0.f)) ? -1 : pick;   // a residual without mass
-    sm.rem = target - before;
-    sm.pick = -1;
   }
   __syncthreads();
   if (sm.chunk < 0) return -1;
-  // fine: rescan the chosen chunk; thread i owns a contiguous run of L logits
+  // fine: rescan the chosen chunk; thread i owns a contiguous run of L <= 64 logits,
+  // loaded once into registers
   const int c = sm.chunk;
   const int e0 = 8 * chunk_begin(V, nchunks, c);
   const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
-  const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;   // <= 64
+  const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;
   const int a0 = e0 + tid * L;
-  int ci0 = 0;
-  while (ci0 < sm.ncl && sm.cl_id[ci0] < a0) ++ci0;
-  float tsum = 0.f;
-  {
-    int ci = ci0;
+  u32x4 raw[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int base = a0 + 8 * k;
-      if (8 * k < L && base + 8 <= e1) {
-        const u32x4 vec = *reinterpret_cast<const u32x4*>(rowp + base);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tsum += draw_weight(elem_bits(vec, e), base + e, m, inv_t, invZ, sm, &ci);
-      } else if (8 * k < L) {
-        for (int id = base; id < base + 8 && id < e1; ++id) tsum += draw_weight(rowp[id], id, m, inv_t, invZ, sm, &ci);
-      }
+  for (int k = 0; k < 8; ++k) {
+    const int base = a0 + 8 * k;
+    raw[k] = (u32x4){0u, 0u, 0u, 0u};
+    if (8 * k < L && base + 8 <= e1) {
+      raw[k] = *reinterpret_cast<const u32x4*>(rowp + base);
+    } else if (8 * k < L && base < e1) {
+      uint32_t w4[4] = {0u, 0u, 0u, 0u};
+      for (int e = 0; e < 8 && base + e < e1; ++e) w4[e >> 1] |= (uint32_t)rowp[base + e] << ((e & 1) * 16);
+      raw[k] = (u32x4){w4[0], w4[1], w4[2], w4[3]};
     }
   }
+  // which of this thread's logits are candidates (bit = offset from a0)
+  unsigned long long cmask = 0ull;
+  for (int i = 0; i < sm.ncl; ++i) {
+    const int off = sm.cl_id[i] - a0;
+    if (off >= 0 && off < L) cmask |= 1ull << off;
+  }
+  float tsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int off = 8 * k + e;
+      if (8 * k < L && a0 + off < e1)
+        tsum += draw_weight(elem_bits(raw[k], e), a0 + off, (cmask >> off) & 1ull, m, c2, invZ, sm);
+    }
   sm.tsum[tid] = tsum;
   __syncthreads();
-  if (tid == 0) {
-    // exclusive scan in thread order; first thread whose run crosses the remainder
-    float run = 0.f;
-    int who = -1, lastpos = -1;
-    float before = 0.f;
-    for (int i = 0; i < kAccThreads; ++i) {
-      if (who < 0 && sm.rem < run + sm.tsum[i]) {
-        who = i;
-        before = run;
-      }
-      run += sm.tsum[i];
-      if (sm.tsum[i] > 0.f) lastpos = i;
+  if (tid < kWave) {
+    const Crossing cr = wave_find_crossing(sm.tsum, kAccThreads, sm.rem);
+    if (tid == 0) {
+      sm.who = cr.idx >= 0 ? cr.idx : cr.last;
+      sm.before = cr.idx >= 0 ? cr.before : 0.f;
+      sm.last = cr.idx < 0 ? 1 : 0;        // no crossing: take the last positive weight
     }
-    sm.status = who;               // borrowed as scratch: crossing thread
-    sm.red[0] = before;
-    sm.red[1] = (float)lastpos;
   }
   __syncthreads();
-  const int who = sm.status;
-  const int lastpos = (int)sm.red[1];
-  if (tid == who || (who < 0 && tid == lastpos)) {
+  if (tid == sm.who) {
     // the same weights again, in the same order, now with the running sum
-    float run = sm.red[0];
-    int pick = -1, lastp = -1, ci = ci0;
-    for (int id = a0; id < a0 + L && id < e1; ++id) {
-      const float w = draw_weight(rowp[id], id, m, inv_t, invZ, sm, &ci);
-      run += w;
-      if (pick < 0 && who >= 0 && sm.rem < run) pick = id;
-      if (w > 0.f) lastp = id;
-    }
+    float run = sm.before;
+    int pick = -1, lastp = -1;
+    const bool take_last = sm.last != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int off = 8 * k + e;
+        if (8 * k < L && a0 + off < e1) {
+          const float w = draw_weight(elem_bits(raw[k], e), a0 + off, (cmask >> off) & 1ull, m, c2, invZ, sm);
+          run += w;
+          if (pick < 0 && !take_last && sm.rem < run) pick = a0 + off;
+          if (w > 0.f) lastp = a0 + off;
+        }
+      }
     sm.pick = pick >= 0 ? pick : lastp;
   }
   __syncthreads();
@@ -330,6 +438,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   const int rbase = batch_stride == 0 ? 0 : b * (K + 1);
   int32_t* out_b = out_tokens + (size_t)b * (K + 1);
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const float c2 = inv_t * kLog2e;
 
   if (tid == 0) {
     sm.ids_bad = 0;
@@ -341,6 +450,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     const size_t c0 = (size_t)(rbase + tid) * nchunks;
     if (inv_t == 0.f) {
       unsigned long long a = 0ull;
+#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
         const unsigned long long x = ws.chunk_arg[c0 + j];
         a = x > a ? x : a;
@@ -349,15 +459,17 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     } else {
       float m = -__builtin_inff();
       bool bad = false;
+#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
         const float mj = ws.chunk_max[c0 + j];
         if (__builtin_isnan(mj)) bad = true;
         else m = fmaxf(m, mj);
       }
       float Z = 0.f;
+#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
         const float mj = ws.chunk_max[c0 + j];
-        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ws.chunk_sum[c0 + j] * expf((mj - m) * inv_t);
+        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ws.chunk_sum[c0 + j] * tweight(mj, m, c2);
       }
       sm.row_max[tid] = m;
       sm.row_sum[tid] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
@@ -421,7 +533,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
 
   if (ids_bad || q_bad) {
     const float u_res = word_to_uniform(philox4x32_10(0u, (uint32_t)b, 1u, 0u, k0, k1).x1);
-    const int v = draw_from_row(tb, rbase, sm.row_max[0], sm.row_sum[0], V, nchunks, inv_t, u_res, false, nullptr,
+    const int v = draw_from_row(tb, rbase, sm.row_max[0], sm.row_sum[0], V, nchunks, c2, u_res, false, nullptr,
                                 nullptr, ws, sm);
     if (tid == 0) {
       out_b[0] = v;
@@ -438,7 +550,7 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     float qx = 0.f;
     const float* qr = q + ((size_t)b * K + t) * kNC;
     for (int j = 0; j < kNC; ++j) qx += cand_b[t * kNC + j] == x ? qr[j] : 0.f;
-    const float px = expf((bf16_to_f32(tb[(size_t)t * ld + x]) - sm.row_max[t]) * inv_t) / sm.row_sum[t];
+    const float px = tweight(bf16_to_f32(tb[(size_t)t * ld + x]), sm.row_max[t], c2) / sm.row_sum[t];
     const float u_acc = word_to_uniform(philox4x32_10((uint32_t)t, (uint32_t)b, 1u, 0u, k0, k1).x0);
     if (!(u_acc * qx < px)) atomicMin(&sm.tstar, t);
   }
@@ -453,13 +565,13 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     const float* q_t = q + ((size_t)b * K + tstar) * kNC;
     // residual mass: 1 - sum over candidates of min(p, q) is positive after any reject
     const float m = sm.row_max[tstar], Z = sm.row_sum[tstar];
-    v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, inv_t, u_res, true, cand_t, q_t, ws, sm);
+    v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, c2, u_res, true, cand_t, q_t, ws, sm);
     if (v < 0) {
       status |= 8;
-      v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, inv_t, u_res, false, nullptr, nullptr, ws, sm);
+      v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, c2, u_res, false, nullptr, nullptr, ws, sm);
     }
   } else {
-    v = draw_from_row(tb + (size_t)K * ld, rbase + K, sm.row_max[K], sm.row_sum[K], V, nchunks, inv_t, u_res, false,
+    v = draw_from_row(tb + (size_t)K * ld, rbase + K, sm.row_max[K], sm.row_sum[K], V, nchunks, c2, u_res, false,
                       nullptr, nullptr, ws, sm);
   }
   if (tid == 0) {

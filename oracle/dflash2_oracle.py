@@ -347,9 +347,14 @@ def target_probs(bits_row, temperature: float) -> np.ndarray:
 
 
 def bf16_argmax(bits_row) -> int:
-    """Lowest token id holding the largest bf16 logit (NaN ranks lowest)."""
+    """Lowest token id holding the largest bf16 logit.  NaN ranks below every number,
+    -inf included (the candidate order's reading); an all-NaN row gives token 0."""
     l = bf16_to_f64(bits_row)
-    return int(np.argmax(np.where(np.isnan(l), -np.inf, l))) if not np.all(np.isnan(l)) else 0
+    ok = ~np.isnan(l)
+    if not ok.any():
+        return 0
+    m = l[ok].max()
+    return int(np.flatnonzero(ok & (l == m))[0])
 
 
 def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int = 0,

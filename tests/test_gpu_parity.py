@@ -383,6 +383,40 @@ def test_spec_accept_fault_rows(d2):
     assert cpu(st).tolist() == [1, 4, 4, 2, 4, 1]
 
 
+@pytest.mark.parametrize("V", [5003, 40000])
+def test_spec_accept_greedy_edge_rows(d2, V):
+    """Greedy verify = argmax prefix match with NaN lowest, -0 == +0 and ties to the
+    lowest id, on target rows built to hit every branch of the chunk argmax."""
+    rng = np.random.default_rng(21)
+    B, K = 8, 3
+    vals = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    tb = synth.f32_to_bf16_bits(vals)
+    tb[0, 0, 11] = 0x7FC0                                # +NaN above every value: not the argmax
+    tb[0, 1, :] = 0x7FC0                                 # all NaN: argmax = token 0
+    tb[0, 1, 5::7] = 0xFFC1                              # with some -NaN
+    tb[1, 0, :] = 0x8000                                 # all -0 ...
+    tb[1, 0, 3000 % V] = 0x0000                          # ... one +0: ties with -0, lowest id wins
+    tb[1, 1, :] = 0xFF80                                 # all -inf
+    tb[2, 0, [17, 400, V - 1]] = 0x4400                  # tied maxima (value 512)
+    tb[2, 1, V - 1] = 0x7F80                             # +inf in the ragged tail
+    tb[3, 0, :] = 0xC000                                 # all -2 ...
+    tb[3, 0, V // 2:] = 0x7FC0                           # ... and +NaN on the right half: fallback path
+    tb[3, 1, :] = 0xFFC0                                 # all -NaN
+    cand = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    q = np.full((B, K, 16), 1.0 / 16, np.float32)
+    g = np.array([[int(oracle.bf16_argmax(tb[b, t])) for t in range(K + 1)] for b in range(B)])
+    tokens = cand[:, :, 0].copy()
+    for b in range(B):                                   # prefixes of several lengths
+        n = b % (K + 1)
+        tokens[b, :n] = g[b, :n]
+    ld = (V + 7) // 8 * 8                                # rows padded to the 16-byte stride rule
+    buf = np.zeros((B, K + 1, ld), np.uint16)
+    buf[..., :V] = tb
+    print(f"greedy verify edge rows V={V} ld={ld}", flush=True)
+    o, n, st = d2.spec_accept(to_gpu_bits(buf)[..., :V], to_gpu(tokens), to_gpu(cand), to_gpu(q), 0.0, seed=1)
+    check_accept(tb, tokens, cand, q, 0.0, 1, cpu(o), cpu(n), cpu(st))
+
+
 def test_spec_accept_shared_target_matches_expanded(d2):
     inp, w, out = _c4_draft(d2)
     tb = inp["target_bits"][0]

@@ -431,6 +431,16 @@ def test_spec_accept_resample_never_returns_rejected_draft():
     assert hits > 150
 
 
+def test_bf16_argmax_order():
+    # NaN below -inf, -0 == +0 (lowest id wins), ties to the lowest id
+    nan, ninf, pz, nz = 0x7FC0, 0xFF80, 0x0000, 0x8000
+    assert oracle.bf16_argmax(np.array([nan, ninf, nan], np.uint16)) == 1
+    assert oracle.bf16_argmax(np.array([nan, 0xFFC0, nan], np.uint16)) == 0
+    assert oracle.bf16_argmax(np.array([ninf, nz, pz, nz], np.uint16)) == 1
+    assert oracle.bf16_argmax(np.array([0x3F80, 0x4000, 0x3F80, 0x4000], np.uint16)) == 1
+    assert oracle.bf16_argmax(np.array([0x4000, 0x7FC0, 0x7F80], np.uint16)) == 2
+
+
 def test_spec_accept_greedy_prefix_match():
     V, K = 50, 4
     rng = np.random.default_rng(13)
