@@ -10,7 +10,8 @@ using namespace df2;
 
 namespace {
 
-constexpr int64_t kMaxVocab = (int64_t)kMaxChunks * kChunkVec * 8;   // 2^19
+constexpr int64_t kMaxVocab = (int64_t)1 << 19;
+static_assert((int64_t)kMaxChunks * kChunkVec * 8 >= kMaxVocab, "top-16 chunking must cover the vocabulary limit");
 // An AQL dispatch packet carries the grid size as a 32-bit count of work-items.
 constexpr int64_t kMaxItems = 0xffffffffLL;
 

@@ -23,7 +23,7 @@ struct Carver {
 };
 
 struct TopkWs {
-  unsigned long long* partials;   // [rows][nchunks * 4 waves][16] sorted candidate lists
+  unsigned long long* partials;   // [rows][nchunks][16] chunk top-16s, best first
 };
 TopkWs carve_topk(Carver& c, int64_t rows, int64_t vocab);
 

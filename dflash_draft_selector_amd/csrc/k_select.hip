@@ -1,15 +1,15 @@
 // Top-16, pair-score and walk kernels, and the proposer step built from them.
 //
 // The proposer step (dflash2_select) runs as three back-to-back kernels on one stream:
-//   1. k_chunk_lists  streams the logits; every wave publishes a candidate list holding
-//                     the best 16 of the logits its lanes loaded (no block-level or
-//                     cross-block sync);
-//   2. k_positions    one block per draft position: merges the lists of rows t-1 and t,
-//                     writes row t's candidates, computes the 16 x 16 scores of t and
-//                     the successor table (slot taken from each predecessor slot);
+//   1. k_chunk_lists  streams the logits (two 512-thread blocks per row at V = 151936)
+//                     and writes each chunk's sorted top-16;
+//   2. k_positions    one block per draft position: merges the chunk top-16s of rows
+//                     t - 1 and t, writes row t's candidates, computes the 16 x 16
+//                     scores of t and the successor table (the slot taken from each
+//                     predecessor slot);
 //   3. k_walk_tables  one block per request: chases the tables from the verified row
 //                     and writes tokens, slots and q.
-// Kernel boundaries replace every cross-work-group handoff, so no work-group ever
+// Kernel boundaries replace every cross-work-group hand-off, so no work-group ever
 // waits for another and no workspace counter exists.
 #include "dflash2_internal.h"
 #include "pair_dev.h"
@@ -17,13 +17,11 @@
 
 namespace df2 {
 
-constexpr int kListsPerChunk = kTopkWaves;        // one candidate list per wave
-
-__host__ __device__ __forceinline__ int lists_per_row(long long vocab) { return topk_num_chunks(vocab) * kListsPerChunk; }
+constexpr int kMergeRows = 16;                    // rows per block of the standalone top-16 merge
 
 TopkWs carve_topk(Carver& c, int64_t rows, int64_t vocab) {
   TopkWs w;
-  w.partials = c.take<unsigned long long>((size_t)rows * lists_per_row(vocab) * kListLen);
+  w.partials = c.take<unsigned long long>((size_t)rows * topk_num_chunks(vocab) * kNC);
   return w;
 }
 
@@ -35,47 +33,36 @@ SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab) {
   return w;
 }
 
-// Row merge state of up to two rows; their list entries sit in dynamic LDS.
-struct MergeShared {
-  unsigned long long cbuf[2][kMergeCandCap + 8];
-  unsigned long long top[2][kNC];
-  int bits;
-};
-
-// 16-byte aligned: the lists are copied in with 16-byte LDS stores.
-extern __shared__ __attribute__((aligned(16))) unsigned long long dyn_lists[];
-
-// ---- stage 1: per-wave candidate lists -------------------------------------------------
+// ---- stage 1: chunk top-16s ---------------------------------------------------------------
 
 __global__ void __launch_bounds__(kTopkThreads) k_chunk_lists(const uint16_t* __restrict__ logits, int64_t ld, int V,
                                                               int nchunks, unsigned long long* __restrict__ partials) {
   __shared__ ChunkShared sm;
   const int row = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - row * nchunks;
-  const int wave = threadIdx.x >> 6;
-  wave_list(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1),
-            sm.w[wave], partials + (((size_t)row * nchunks + chunk) * kListsPerChunk + wave) * kListLen);
+  chunk_top16(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1), sm,
+              partials + ((size_t)row * nchunks + chunk) * kNC);
 }
 
-// ---- top-16: merge each row's lists (one wave per row) ---------------------------------
+// ---- top-16: merge each row's chunk top-16s (one 16-lane row per logits row) ----------
 
-__global__ void __launch_bounds__(kWave) k_merge_lists(const unsigned long long* __restrict__ partials, int nlists,
-                                                       int32_t* __restrict__ cand_idx, float* __restrict__ cand_val,
-                                                       int32_t* __restrict__ row_status) {
-  __shared__ MergeShared ms;
-  const int lane = threadIdx.x;
-  const int row = blockIdx.x;
-  const int n = nlists * kListLen;
-  wave_stage_lists(partials + (size_t)row * n, n, dyn_lists);
-  wave_merge_lists(dyn_lists, n, ms.cbuf[0], ms.top[0]);
-  const unsigned long long rc = ms.top[0][lane & 15];
+__global__ void __launch_bounds__(kMergeRows * kNC) k_merge_lists(const unsigned long long* __restrict__ partials,
+                                                                  int rows, int nchunks,
+                                                                  int32_t* __restrict__ cand_idx,
+                                                                  float* __restrict__ cand_val,
+                                                                  int32_t* __restrict__ row_status) {
+  const int i = threadIdx.x & 15;
+  const int row_raw = blockIdx.x * kMergeRows + (threadIdx.x >> 4);
+  const int row = row_raw < rows ? row_raw : rows - 1;   // spare lanes redo the last row, every lane merges
+  const unsigned long long rc = row16_merge_chunks(partials + (size_t)row * nchunks * kNC, nchunks);
   const float v = bf16_to_f32(rc_bits(rc));
-  if (lane < kNC) {
-    cand_idx[(size_t)row * kNC + lane] = rc ? rc_id(rc) : 0;
-    cand_val[(size_t)row * kNC + lane] = v;
+  const unsigned long long bad = __ballot(!__builtin_isfinite(v));
+  if (row_raw < rows) {
+    cand_idx[(size_t)row * kNC + i] = rc ? rc_id(rc) : 0;
+    cand_val[(size_t)row * kNC + i] = v;
+    const int sh = (threadIdx.x & 63) & ~15;
+    if (row_status && i == 0) row_status[row] = ((bad >> sh) & 0xffffull) ? 1 : 0;
   }
-  const unsigned long long bad = __ballot(lane < kNC && !__builtin_isfinite(v));
-  if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
 }
 
 // ---- pair scores ------------------------------------------------------------------------
@@ -149,9 +136,8 @@ __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ nex
   if (tid == 0) {
     int i = 0;
     for (int t = 0; t < K; ++t) {
-      const int j = sm.next[t * kNC + i];
-      sm.path[t] = j;
-      i = j;
+      i = sm.next[t * kNC + i];
+      sm.path[t] = i;
     }
   }
   __syncthreads();
@@ -169,8 +155,8 @@ __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ nex
 // ---- stage 2 of the proposer step -------------------------------------------------------
 
 template <int DIM, bool BF16>
-__global__ void __launch_bounds__(kPairThreads) k_positions(const unsigned long long* __restrict__ partials, int nlists,
-                                                            int K, const int32_t* __restrict__ verified,
+__global__ void __launch_bounds__(kPairThreads) k_positions(const unsigned long long* __restrict__ partials,
+                                                            int nchunks, int K, const int32_t* __restrict__ verified,
                                                             const void* __restrict__ emb_a,
                                                             const void* __restrict__ emb_b, int V,
                                                             const float* __restrict__ H, float inv_t, uint64_t seed,
@@ -178,37 +164,34 @@ __global__ void __launch_bounds__(kPairThreads) k_positions(const unsigned long 
                                                             float* __restrict__ cand_val, float* __restrict__ S,
                                                             int* __restrict__ next, float* __restrict__ qtab,
                                                             int32_t* __restrict__ row_status) {
-  __shared__ MergeShared ms;
   __shared__ PairShared ps;
+  __shared__ int s_bits;
   const int pos = blockIdx.x;
   const int b = pos / K, p = pos - b * K;
   const int tid = threadIdx.x;
-  // wave 0 merges row pos, wave 1 row pos - 1 (the predecessors)
-  const int wave = tid >> 6;
-  const int n = nlists * kListLen;
-  if (wave < (p > 0 ? 2 : 1)) {
-    wave_stage_lists(partials + (size_t)(pos - wave) * n, n, dyn_lists + wave * n);
-    wave_merge_lists(dyn_lists + wave * n, n, ms.cbuf[wave], ms.top[wave]);
-  }
-  if (tid == 0) ms.bits = 0;
-  __syncthreads();
-  if (tid < kNC) {
-    const unsigned long long rc = ms.top[0][tid];
-    const int id = rc ? rc_id(rc) : 0;
+  if (tid < kWave) {
+    // rows 0 and 2 of wave 0 merge row pos, rows 1 and 3 row pos - 1 (the predecessors)
+    const int i = tid & 15;
+    const bool pred = (tid & 16) != 0;
+    const int r = pred && p > 0 ? pos - 1 : pos;
+    const unsigned long long rc = row16_merge_chunks(partials + (size_t)r * nchunks * kNC, nchunks);
     const float v = bf16_to_f32(rc_bits(rc));
-    cand_idx[(size_t)pos * kNC + tid] = id;
-    cand_val[(size_t)pos * kNC + tid] = v;
-    ps.cur[tid] = id;
-    ps.U[tid] = v;
-    const unsigned long long rp = ms.top[1][tid];
-    ps.prev[tid] = p == 0 ? verified[b] : (rp ? rc_id(rp) : 0);
-    if (!__builtin_isfinite(v)) atomicOr(&ms.bits, 1);
+    const bool bad = __ballot(tid < kNC && !__builtin_isfinite(v)) != 0ull;
+    if (tid < kNC) {
+      cand_idx[(size_t)pos * kNC + i] = rc ? rc_id(rc) : 0;
+      cand_val[(size_t)pos * kNC + i] = v;
+      ps.cur[i] = rc ? rc_id(rc) : 0;
+      ps.U[i] = v;
+    } else if (tid < 2 * kNC) {
+      ps.prev[i] = p == 0 ? verified[b] : (rc ? rc_id(rc) : 0);
+    }
+    if (tid == 0) s_bits = bad ? 1 : 0;
   }
   __syncthreads();
   const int pbits = pair_tile<DIM, BF16>(emb_a, emb_b, V, H + (size_t)pos * DIM, S + (size_t)pos * kNC * kNC, ps);
   const float u = inv_t == 0.f ? 0.f : walk_uniform(seed, (uint32_t)b, (uint32_t)p);
   tile_successors(ps, inv_t, u, next + (size_t)pos * kNC, inv_t == 0.f ? nullptr : qtab + (size_t)pos * kNC * kNC);
-  if (row_status && tid == 0) row_status[pos] = ms.bits | pbits;
+  if (row_status && tid == 0) row_status[pos] = s_bits | pbits;
 }
 
 // ---- launchers -----------------------------------------------------------------------
@@ -218,9 +201,8 @@ hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld
   const int nchunks = topk_num_chunks(vocab);
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(rows * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
                      nchunks, ws.partials);
-  const int nlists = nchunks * kListsPerChunk;
-  hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)rows), dim3(kWave), (size_t)nlists * kListLen * 8, s, ws.partials,
-                     nlists, cand_idx, cand_val, row_status);
+  hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)), dim3(kMergeRows * kNC),
+                     0, s, ws.partials, rows, nchunks, cand_idx, cand_val, row_status);
   return hipGetLastError();
 }
 
@@ -263,11 +245,11 @@ hipError_t launch_walk(const float* S, const int32_t* cand_idx, int batch, int K
 }
 
 template <int DIM, bool BF16>
-static void positions_launch(dim3 grid, hipStream_t s, const unsigned long long* partials, int nlists, int K,
+static void positions_launch(dim3 grid, hipStream_t s, const unsigned long long* partials, int nchunks, int K,
                              const int32_t* verified, const void* a, const void* b, int V, const float* H, float inv_t,
                              uint64_t seed, int32_t* ci, float* cv, float* S, int* next, float* qtab, int32_t* st) {
-  hipLaunchKernelGGL((k_positions<DIM, BF16>), grid, dim3(kPairThreads), (size_t)2 * nlists * kListLen * 8, s, partials,
-                     nlists, K, verified, a, b, V, H, inv_t, seed, ci, cv, S, next, qtab, st);
+  hipLaunchKernelGGL((k_positions<DIM, BF16>), grid, dim3(kPairThreads), 0, s, partials, nchunks, K, verified, a, b, V,
+                     H, inv_t, seed, ci, cv, S, next, qtab, st);
 }
 
 hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
@@ -275,19 +257,18 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
                          float temperature, uint64_t seed, int32_t* cand_idx, float* cand_val, float* S,
                          int32_t* tokens, int32_t* slots, float* q, int32_t* row_status, SelectWs ws, hipStream_t s) {
   const int nchunks = topk_num_chunks(vocab);
-  const int nlists = nchunks * kListsPerChunk;
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(batch * K * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
                      nchunks, ws.topk.partials);
   const dim3 grid((unsigned)(batch * K));
-#define DF2_POS(D)                                                                                                   \
-  case D:                                                                                                            \
-    if (bf16)                                                                                                        \
-      positions_launch<D, true>(grid, s, ws.topk.partials, nlists, K, verified, emb_a, emb_b, vocab, H, inv_t, seed, \
-                                cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                                         \
-    else                                                                                                             \
-      positions_launch<D, false>(grid, s, ws.topk.partials, nlists, K, verified, emb_a, emb_b, vocab, H, inv_t,      \
-                                 seed, cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                                  \
+#define DF2_POS(D)                                                                                                    \
+  case D:                                                                                                             \
+    if (bf16)                                                                                                         \
+      positions_launch<D, true>(grid, s, ws.topk.partials, nchunks, K, verified, emb_a, emb_b, vocab, H, inv_t, seed, \
+                                cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                                 \
+    else                                                                                                              \
+      positions_launch<D, false>(grid, s, ws.topk.partials, nchunks, K, verified, emb_a, emb_b, vocab, H, inv_t,      \
+                                 seed, cand_idx, cand_val, S, ws.next, ws.qtab, row_status);                          \
     break;
   switch (dim) {
     DF2_POS(64)

@@ -26,42 +26,6 @@ struct WalkShared {
   int path[64];
 };
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <int N>
-__device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ p, float (&out)[N]) {
-  if constexpr (N % 8 == 0) {
-#pragma unroll
-    for (int i = 0; i < N / 8; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p + 8 * i);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        out[8 * i + 2 * w] = bf16_lo(v[w]);
-        out[8 * i + 2 * w + 1] = bf16_hi(v[w]);
-      }
-    }
-  } else {
-    static_assert(N == 4, "selector dim / 16 must be 4 or a multiple of 8");
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    out[0] = bf16_lo(v.x);
-    out[1] = bf16_hi(v.x);
-    out[2] = bf16_lo(v.y);
-    out[3] = bf16_hi(v.y);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void load_row_f32(const float* __restrict__ p, float (&out)[N]) {
-#pragma unroll
-  for (int i = 0; i < N / 4; ++i) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * i);
-    out[4 * i] = v.x;
-    out[4 * i + 1] = v.y;
-    out[4 * i + 2] = v.z;
-    out[4 * i + 3] = v.w;
-  }
-}
-
 __device__ __forceinline__ int clamp_id(int id, int V, int* bad) {
   if (id < 0 || id >= V) {
     *bad = 1;
@@ -71,20 +35,22 @@ __device__ __forceinline__ int clamp_id(int id, int V, int* bad) {
 }
 
 // One position's 16 x 16 scores from sm.prev (predecessor ids), sm.cur (candidate ids)
-// and sm.U (candidate logits), all set by the caller and visible to the block.  Writes
-// the tile to sm.S and (agent-coherently) to S_out[256]; returns the row-status bits
-// (block-uniform): 2 = an id outside [0, V) (clamped), 1 = a non-finite score.
+// and sm.U (candidate logits), all set by the caller and visible to the block (all 256
+// threads call it).  Writes the tile to sm.S and to S_out[256]; returns the row-status
+// bits (block-uniform): 2 = an id outside [0, V) (clamped), 1 = a non-finite score.
 //
 // MFMA mapping (v_mfma_f32_16x16x4_f32, wave64): lane l feeds A[i = l % 16][k = l / 16]
 // and B[k = l / 16][j = l % 16]; step s of wave w uses, for k-group g = l / 16, the
 // selector dim d = w * DIM/4 + g * DIM/16 + s, so each lane reads one contiguous
 // DIM/16-wide slice of its table rows.  The product over d is order-free, so this
-// permutation of the contraction is exact up to fp32 rounding order.  The four
-// waves' partial tiles are summed in a fixed order.
+// permutation of the contraction is exact up to fp32 rounding order.  A scheduling
+// barrier keeps every gather ahead of the first MFMA (one memory round trip), and the
+// four waves' partial tiles are summed in a fixed order.
 template <int DIM, bool BF16>
 __device__ __forceinline__ int pair_tile(const void* __restrict__ emb_a, const void* __restrict__ emb_b, int V,
                                          const float* __restrict__ Hrow, float* __restrict__ S_out, PairShared& sm) {
-  constexpr int ND = DIM / 16;
+  constexpr int ND = DIM / 16;                       // dims per lane
+  constexpr int NV = BF16 ? (ND + 7) / 8 : ND / 4;   // 16-byte loads per table slice (ND >= 4)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -95,19 +61,20 @@ __device__ __forceinline__ int pair_tile(const void* __restrict__ emb_a, const v
   int bad = 0;
   const int prev = clamp_id(sm.prev[r16], V, &bad);
   const int cur = clamp_id(sm.cur[r16], V, &bad);
-
   if (tid == 0) sm.flags = 0;
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* hp = Hrow + d0;
+  f32x4 hq[ND / 4];
+#pragma unroll
+  for (int i = 0; i < ND / 4; ++i) hq[i] = *reinterpret_cast<const f32x4*>(Hrow + d0 + 4 * i);
   if constexpr (BF16) {
     // table slices stay packed (two bf16 per register) until their MFMA step
-    constexpr int NW = ND / 2;
-    uint32_t aw[NW], bw[NW];
+    uint32_t aw[ND / 2], bw[ND / 2];
     const uint16_t* ap = static_cast<const uint16_t*>(emb_a) + (size_t)prev * DIM + d0;
     const uint16_t* bp = static_cast<const uint16_t*>(emb_b) + (size_t)cur * DIM + d0;
-    if constexpr (NW >= 4) {
+    if constexpr (ND >= 8) {
 #pragma unroll
-      for (int i = 0; i < NW / 4; ++i) {
+      for (int i = 0; i < NV; ++i) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(ap + 8 * i);
         const u32x4 y = *reinterpret_cast<const u32x4*>(bp + 8 * i);
 #pragma unroll
@@ -117,13 +84,15 @@ __device__ __forceinline__ int pair_tile(const void* __restrict__ emb_a, const v
         }
       }
     } else {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 x = *reinterpret_cast<const u32x2*>(ap);
       const u32x2 y = *reinterpret_cast<const u32x2*>(bp);
-      aw[0] = x.x; aw[1] = x.y; bw[0] = y.x; bw[1] = y.y;
+      aw[0] = x.x;
+      aw[1] = x.y;
+      bw[0] = y.x;
+      bw[1] = y.y;
     }
-    f32x4 hq[ND / 4];
-#pragma unroll
-    for (int i = 0; i < ND / 4; ++i) hq[i] = *reinterpret_cast<const f32x4*>(hp + 4 * i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < ND; ++s) {
       const float a = (s & 1) ? bf16_hi(aw[s >> 1]) : bf16_lo(aw[s >> 1]);
@@ -131,16 +100,18 @@ __device__ __forceinline__ int pair_tile(const void* __restrict__ emb_a, const v
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a * hq[s >> 2][s & 3], bb, acc, 0, 0, 0);
     }
   } else {
+    f32x4 x[NV], y[NV];
     const float* ap = static_cast<const float*>(emb_a) + (size_t)prev * DIM + d0;
     const float* bp = static_cast<const float*>(emb_b) + (size_t)cur * DIM + d0;
 #pragma unroll
-    for (int i = 0; i < ND / 4; ++i) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(ap + 4 * i);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(bp + 4 * i);
-      const f32x4 h = *reinterpret_cast<const f32x4*>(hp + 4 * i);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[c] * h[c], y[c], acc, 0, 0, 0);
+    for (int i = 0; i < NV; ++i) {
+      x[i] = *reinterpret_cast<const f32x4*>(ap + 4 * i);
+      y[i] = *reinterpret_cast<const f32x4*>(bp + 4 * i);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < ND; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s >> 2][s & 3] * hq[s >> 2][s & 3], y[s >> 2][s & 3], acc, 0, 0, 0);
   }
 
   // D layout: lane l, register r holds D[4 * (l / 16) + r][l % 16]

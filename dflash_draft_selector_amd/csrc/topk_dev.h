@@ -1,6 +1,10 @@
-// Split-vocabulary top-16 over bf16 logits rows.  Every wave of the streaming pass
-// reduces the logits its lanes load to a short candidate list that contains the wave's
-// best 16; the lists of a row are then merged into the row's top-16.
+// Split-vocabulary top-16 over bf16 logits rows.  A work-group streams one chunk of a
+// row.  Its waves sort their lanes' maxima, and the 16th largest of the block's 512 lane
+// maxima bounds the chunk's 16th best logit from below (16 lanes hold a logit at least
+// that large), so only the few logits at or above it are gathered, with exact keys, and
+// one wave ranks them into the chunk's sorted top-16.  When too few or too many survive,
+// every wave selects its own top-16 exactly and one wave merges the eight lists with a
+// bitonic network.  The chunks of a row are merged afterwards with the same network.
 // Selection order: value descending, token id ascending, -0 == +0, NaN below -inf
 // (pegainfer issue "DFlash 2 proposer", section "What upstream shipped", item 1: keep
 // the top-16 candidates per position).
@@ -10,20 +14,15 @@
 
 namespace df2 {
 
-constexpr int kTopkThreads = 256;                            // 4 waves
+constexpr int kTopkThreads = 512;                            // 8 waves
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkVecPerThread = 16;                        // 16 x 16 B loads in flight per lane
-constexpr int kChunkVec = kTopkThreads * kTopkVecPerThread;  // 4096 vectors = 32768 logits
+constexpr int kTopkVecPerThread = 19;                        // 19 x 16 B loads in flight per lane
+constexpr int kChunkVec = kTopkThreads * kTopkVecPerThread;  // 9728 vectors = 77824 logits
 constexpr int kWaveCapVec = 64;                              // candidate vectors kept per wave
-constexpr int kWaveCapCand = 128;                            // candidate logits kept per wave
-constexpr int kListLen = 32;                                 // entries of a wave's candidate list
-constexpr int kMaxChunks = 16;                               // vocab <= 16 * 32768 = 2^19
-constexpr int kMaxLists = kMaxChunks * kTopkWaves;           // candidate lists per row (64)
-constexpr int kMaxListEntries = kMaxLists * kListLen;        // 2048
-constexpr int kMergeCandCap = 2 * kWave;                     // merge survivors ranked in LDS
+constexpr int kBlockCapCand = 128;                           // candidate logits kept per block
+constexpr int kMaxChunks = 7;                                // vocab <= 7 * 77824 (2^19 and more)
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 // Row composite of a logit: (order key << 48) | ((0xfffff - token id) << 28) | bf16 bits.
 // Larger = better (higher value, then lower id); unique per token; 0 = empty slot.
@@ -33,17 +32,14 @@ __device__ __forceinline__ unsigned long long make_rc(uint32_t key, uint32_t id,
 __device__ __forceinline__ int rc_id(unsigned long long rc) { return (int)(0xfffffu - (uint32_t)((rc >> 28) & 0xfffffu)); }
 __device__ __forceinline__ uint32_t rc_bits(unsigned long long rc) { return (uint32_t)(rc & 0xffffu); }
 
-// Per-wave scratch of the chunk selection (each wave uses only its own slot, so the
-// waves of a block never wait for one another).
-struct WaveSelShared {
-  u32x4 vec_data[kWaveCapVec];
-  unsigned int vec_pos[kWaveCapVec];
-  unsigned long long cand[kWaveCapCand + 8];
-  unsigned long long top[kNC];
-};
-
 struct ChunkShared {
-  WaveSelShared w[kTopkWaves];
+  u32x4 vec_data[kTopkWaves][kWaveCapVec];                  // each wave's candidate vectors
+  unsigned int vec_pos[kTopkWaves][kWaveCapVec];            // and their positions in the chunk
+  int lane_top[2][kTopkWaves][kNC];                         // sorted lane maxima (raw, signed order)
+  unsigned long long cand[kBlockCapCand + 8];               // the block's candidate logits
+  unsigned long long lists[kTopkWaves * kNC];               // exact per-wave top-16s (fallback)
+  unsigned int ncand;
+  unsigned int overflow;
 };
 
 // Signed 16-bit order of a bf16 pattern, two per word: flip the magnitude bits of
@@ -85,63 +81,145 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// rank[i] = number of entries of list[0..n) larger than mine_i, for the (up to) two
-// keys a lane owns.  `list` is in LDS and zero-padded to a multiple of 8 (a zero is
-// never larger); all lanes read the same address in each step (a broadcast), and eight
-// independent reads are in flight per step.
-__device__ __forceinline__ void rank2(const unsigned long long* list, unsigned int n, unsigned long long mine0,
-                                      unsigned long long mine1, unsigned int& r0, unsigned int& r1) {
-  r0 = 0;
-  r1 = 0;
-  for (unsigned int j = 0; j < n; j += 8) {
-    unsigned long long x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = list[j + u];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      r0 += x[u] > mine0 ? 1u : 0u;
-      r1 += x[u] > mine1 ? 1u : 0u;
-    }
-  }
+// ---- bitonic merging of sorted top-16 lists ------------------------------------------
+// A 16-lane row of a wave holds one list, slot i in lane i (row lane = lane & 15).
+// The 64-bit moves use DPP within a row and ds_bpermute across rows.
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// 16th largest of the lanes' values v (signed 16-bit range): a radix select on ballots.
-__device__ __forceinline__ int lane_threshold(int v) {
-  const uint32_t u = (uint32_t)(v + 32768);
-  uint32_t T = 0;
-#pragma unroll
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t c = T | (1u << bit);
-    if (__popcll(__ballot(u >= c)) >= kNC) T = c;
-  }
-  return (int)T - 32768;
+// Value of lane (lane ^ m) of the wave.
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v, int m) {
+  const int addr = ((threadIdx.x & 63) ^ m) << 2;
+  const int lo = __builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(v >> 32));
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Candidate list of the logits this wave's lanes load from the chunk of vectors
-// [v0, v1) of `row` (lane L of wave w loads vectors v0 + 64 w + L + 256 k, so a
-// block's loads are contiguous); vector v holds logits 8v..8v+7, only those < V
-// exist.  Writes kListLen row composites to list[] (lanes < kListLen): a set that
-// contains the wave's best 16, in no particular order, zero-padded.  Called by every
-// wave of the block; no wave waits for another.
-//
-// The wave finds the 16th largest of its lanes' maxima (a radix select on ballots):
-// at least 16 of its logits reach it, so only logits at or above it can be among the
-// wave's best 16.  Those few are gathered with exact keys (ballot compaction); when
-// they fit the list they are the list, otherwise they are ranked and the best 16 kept.
-// If fewer than 16 or too many survive (NaN-heavy, constant or heavily tied data), an
-// exact 16-round selection over the wave's logits decides instead.
-__device__ __forceinline__ void wave_list(const uint16_t* __restrict__ row, int V, int v0, int v1, WaveSelShared& sm,
-                                          unsigned long long* __restrict__ list) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
+// Compare-exchange with the partner's value: the lane keeps the larger when keep_max.
+__device__ __forceinline__ unsigned long long cmpx(unsigned long long x, unsigned long long p, bool keep_max) {
+  return ((x > p) == keep_max) ? x : p;
+}
+
+// Sorts, largest first, a bitonic sequence held by each 16-lane row: half-cleaners at
+// distances 8, 4, 2, 1 (Batcher's bitonic sorter).
+__device__ __forceinline__ unsigned long long row16_bitonic_sort(unsigned long long x) {
+  const int i = threadIdx.x & 15;
+  x = cmpx(x, dpp_u64<0x128>(x), (i & 8) == 0);                       // row_ror:8 = lane ^ 8
+  const unsigned long long up = dpp_u64<0x12C>(x);                    // row_ror:12 = lane + 4
+  const unsigned long long dn = dpp_u64<0x124>(x);                    // row_ror:4 = lane - 4
+  x = cmpx(x, (i & 4) ? dn : up, (i & 4) == 0);
+  x = cmpx(x, dpp_u64<0x4e>(x), (i & 2) == 0);                        // quad_perm [2,3,0,1]
+  x = cmpx(x, dpp_u64<0xb1>(x), (i & 1) == 0);                        // quad_perm [1,0,3,2]
+  return x;
+}
+
+// Top-16, sorted, of the union of two disjoint sorted lists a (slot i) and b (slot
+// 15 - i in this lane): the elementwise maximum of a list and the other reversed holds
+// the 16 largest of both and is bitonic.
+__device__ __forceinline__ unsigned long long merge16(unsigned long long a, unsigned long long b_rev) {
+  return row16_bitonic_sort(a > b_rev ? a : b_rev);
+}
+
+// 32-bit forms for the lanes' own values.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int xor_lane_i32(int v, int m) {
+  return __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ m) << 2, v);
+}
+__device__ __forceinline__ int cmpx_i32(int x, int p, bool keep_max) { return keep_max ? max(x, p) : min(x, p); }
+
+// Partner of a lane at distance j (1, 2, 4 or 8) inside its 16-lane row.
+template <int J>
+__device__ __forceinline__ int row_partner_i32(int x) {
+  if constexpr (J == 8) return dpp_i32<0x128>(x);                    // row_ror:8
+  if constexpr (J == 2) return dpp_i32<0x4e>(x);                     // quad_perm [2,3,0,1]
+  if constexpr (J == 1) return dpp_i32<0xb1>(x);                     // quad_perm [1,0,3,2]
+  const int up = dpp_i32<0x12C>(x), dn = dpp_i32<0x124>(x);          // row_ror:12 / row_ror:4
+  return (threadIdx.x & 4) ? dn : up;
+}
+
+// One stage of Batcher's bitonic sort on the rows: blocks of K lanes ordered largest
+// first where lane bit K is clear (and for K = 16), partners at distance J.
+template <int K, int J>
+__device__ __forceinline__ int bitonic_stage_i32(int x) {
+  const int i = threadIdx.x & 15;
+  const bool desc = K >= 16 || (i & K) == 0;
+  return cmpx_i32(x, row_partner_i32<J>(x), ((i & J) == 0) == desc);
+}
+
+// Half-cleaners at distances 8, 4, 2, 1: sorts, largest first, a bitonic sequence held
+// by each 16-lane row.
+__device__ __forceinline__ int row16_bitonic_sort_i32(int x) {
+  x = bitonic_stage_i32<16, 8>(x);
+  x = bitonic_stage_i32<16, 4>(x);
+  x = bitonic_stage_i32<16, 2>(x);
+  return bitonic_stage_i32<16, 1>(x);
+}
+
+// Keeps in each row the best 16 of it and its partner row (lane ^ m, m = 16 or 32),
+// sorted: the elementwise maximum with the mirrored partner row is bitonic.
+__device__ __forceinline__ int row16_merge_rows_i32(int x, int m) {
+  return row16_bitonic_sort_i32(max(x, xor_lane_i32(dpp_i32<0x140>(x), m)));   // row_mirror
+}
+
+// The 16 largest of the wave's lane values, largest first, in lanes 0..15 (each row
+// sorted by a full bitonic sort, then the rows merged pairwise).  All on the vector unit.
+__device__ __forceinline__ int wave_top16_i32(int x) {
+  x = bitonic_stage_i32<2, 1>(x);
+  x = bitonic_stage_i32<4, 2>(x);
+  x = bitonic_stage_i32<4, 1>(x);
+  x = bitonic_stage_i32<8, 4>(x);
+  x = bitonic_stage_i32<8, 2>(x);
+  x = bitonic_stage_i32<8, 1>(x);
+  x = row16_bitonic_sort_i32(x);
+  x = row16_merge_rows_i32(x, 16);
+  return row16_merge_rows_i32(x, 32);
+}
+
+// 16th largest of the union of kTopkWaves sorted top-16 lists (LDS, 16 each), taken by
+// every wave that calls it: lists merge pairwise in the four rows, then the rows.
+__device__ __forceinline__ int block_kth16(const int* lists) {
+  static_assert(kTopkWaves == 8, "the merge tree assumes eight wave lists");
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4, i = lane & 15;
+  int x = row16_bitonic_sort_i32(max(lists[(2 * r) * kNC + i], lists[(2 * r + 1) * kNC + (kNC - 1 - i)]));
+  x = row16_merge_rows_i32(x, 16);
+  x = row16_merge_rows_i32(x, 32);
+  return __builtin_amdgcn_readlane(x, 15);
+}
+
+// Top-16, best first, of the block's kTopkWaves sorted wave lists (LDS, 16 each) by one
+// whole wave: pairs of lists merge in the four rows, then pairs of rows (through the
+// mirrored partner row), twice.  Lane i < 16 returns slot i.
+__device__ __forceinline__ unsigned long long wave_merge_block(const unsigned long long* lists) {
+  static_assert(kTopkWaves == 8, "the merge tree assumes eight wave lists");
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 4, i = lane & 15;
+  unsigned long long x = merge16(lists[(2 * r) * kNC + i], lists[(2 * r + 1) * kNC + (kNC - 1 - i)]);
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 16));                // row_mirror, then the row above/below
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 32));
+  return x;
+}
+
+// ---- one chunk of a row -------------------------------------------------------------
+// Lane L of wave w loads vectors v0 + 64 w + L + kTopkThreads k of the chunk [v0, v1)
+// of `row`, so a block's loads are contiguous; vector v holds logits 8v..8v+7, only
+// those < V exist, the rest read as -NaN (below every logit).
+
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ row, int V, int v0, int v1,
+                                           u32x4 (&d)[kTopkVecPerThread]) {
   const int nfull = V >> 3;
   const u32x4* __restrict__ rowv = reinterpret_cast<const u32x4*>(row);
-
-  // ---- stream: every lane issues all its 16-byte loads before using any ----------
-  u32x4 d[kTopkVecPerThread];
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
-    const int v = v0 + tid + k * kTopkThreads;
+    const int v = v0 + (int)threadIdx.x + k * kTopkThreads;
     if (v < v1 && v < nfull) {
       d[k] = __builtin_nontemporal_load(rowv + v);
     } else {
@@ -158,220 +236,203 @@ __device__ __forceinline__ void wave_list(const uint16_t* __restrict__ row, int 
       d[k] = (u32x4){w4[0], w4[1], w4[2], w4[3]};
     }
   }
+}
 
-  // ---- pass 1: per-vector and per-lane maxima --------------------------------------
-  // First on the raw patterns read as signed 16-bit integers: on non-negative values
-  // (and +NaN, above +inf) that is the value order, and every negative value sits
-  // below +0, so a threshold above +0 found in it is exact.  Otherwise the pass is
-  // redone in the signed order, which follows the value order everywhere.
-  int vmax[kTopkVecPerThread];
+// Per-vector maxima and the lane maximum, on the raw patterns read as signed 16-bit
+// integers (SIGNED = false) or in the signed order (SIGNED = true).  On non-negative
+// values (and +NaN, above +inf) the raw order is the value order and every negative
+// value sits below +0, so a threshold above +0 found in it is exact; the signed order
+// follows the value order everywhere (-0 one below +0).
+template <bool SIGNED>
+__device__ __forceinline__ int vector_maxima(const u32x4 (&d)[kTopkVecPerThread], int (&vmax)[kTopkVecPerThread]) {
   int lmax = -32768;
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
-    const s16x2 a = __builtin_elementwise_max(raw_order2(d[k].x), raw_order2(d[k].y));
-    const s16x2 b = __builtin_elementwise_max(raw_order2(d[k].z), raw_order2(d[k].w));
+    s16x2 a, b;
+    if constexpr (SIGNED) {
+      a = __builtin_elementwise_max(signed_order2(d[k].x), signed_order2(d[k].y));
+      b = __builtin_elementwise_max(signed_order2(d[k].z), signed_order2(d[k].w));
+    } else {
+      a = __builtin_elementwise_max(raw_order2(d[k].x), raw_order2(d[k].y));
+      b = __builtin_elementwise_max(raw_order2(d[k].z), raw_order2(d[k].w));
+    }
     vmax[k] = max_halves(__builtin_elementwise_max(a, b));
     lmax = vmax[k] > lmax ? vmax[k] : lmax;
   }
-  int tau = lane_threshold(lmax);
-  const bool raw = tau > 0;
-  if (!raw) {
-    lmax = -32768;
-#pragma unroll
+  return lmax;
+}
+
+// Exact top-16 of the logits this wave's lanes load, best first, into list[] (LDS),
+// zero-padded when the wave holds fewer than 16: sixteen rounds of a wave maximum below
+// the previous one.  It re-reads the logits (cache-resident by now) so that the common
+// path keeps its register budget.
+__device__ __noinline__ void wave_exact_list(const uint16_t* __restrict__ row, int V, int v0, int v1,
+                                             unsigned long long* list) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int nfull = V >> 3;
+  const u32x4* __restrict__ rowv = reinterpret_cast<const u32x4*>(row);
+  unsigned long long prev = ~0ull;
+  for (int r = 0; r < kNC; ++r) {
+    unsigned long long best = 0ull;
+#pragma unroll 1
     for (int k = 0; k < kTopkVecPerThread; ++k) {
-      const s16x2 a = __builtin_elementwise_max(signed_order2(d[k].x), signed_order2(d[k].y));
-      const s16x2 b = __builtin_elementwise_max(signed_order2(d[k].z), signed_order2(d[k].w));
-      vmax[k] = max_halves(__builtin_elementwise_max(a, b));
-      lmax = vmax[k] > lmax ? vmax[k] : lmax;
+      const int v = v0 + tid + k * kTopkThreads;
+      if (v >= v1) break;
+      u32x4 x;
+      if (v < nfull) {
+        x = rowv[v];
+      } else {
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (8 * v + e < V) {
+            const uint32_t b = row[8 * v + e];
+            w4[e >> 1] |= (e & 1) ? (b << 16) : b;
+          }
+        }
+        x = (u32x4){w4[0], w4[1], w4[2], w4[3]};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (8 * v + e < V) {
+          const uint32_t bits = elem_bits(x, e);
+          const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)(8 * v + e), bits);
+          if (comp < prev && comp > best) best = comp;
+        }
+      }
     }
-    tau = lane_threshold(lmax);
+    best = wave_max_u64(best);
+    if (lane == 0) list[r] = best;
+    prev = best;
+  }
+}
+
+// The chunk's top-16 row composites, best first, written to out[0..16) (global memory),
+// zero-padded when the chunk holds fewer than 16 logits.  The whole block calls it.
+__device__ __forceinline__ void chunk_top16(const uint16_t* __restrict__ row, int V, int v0, int v1, ChunkShared& sm,
+                                            unsigned long long* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  if (tid == 0) {
+    sm.ncand = 0;
+    sm.overflow = 0;
+  }
+
+  // ---- stream: every lane issues all its 16-byte loads before using any ------------
+  u32x4 d[kTopkVecPerThread];
+  load_chunk(row, V, v0, v1, d);
+
+  // ---- the block's 16th largest lane maximum, first in the raw order ----------------
+  int vmax[kTopkVecPerThread];
+  const int lmax_raw = vector_maxima<false>(d, vmax);
+  int t = wave_top16_i32(lmax_raw);
+  if (lane < kNC) sm.lane_top[0][wave][lane] = t;
+  __syncthreads();
+  int tau = block_kth16(&sm.lane_top[0][0][0]);
+  const bool raw = tau > 0;                      // the same in every wave
+  if (!raw) {
+    t = wave_top16_i32(vector_maxima<true>(d, vmax));
+    if (lane < kNC) sm.lane_top[1][wave][lane] = t;
+    __syncthreads();
+    tau = block_kth16(&sm.lane_top[1][0][0]);
   }
   if (tau > 0x7f80) tau = 0x7f80;                // never above +inf
   const uint32_t tau_key = bf16_key(raw ? (uint32_t)tau : order_to_bits(tau));
   const int slack = raw ? 0 : 1;                 // signed order: -0 sits one below +0
 
-  // ---- vectors that may hold a logit >= tau (ballot compaction) -------------------
-  unsigned int nv = 0;
+  // ---- this wave's vectors that may hold a logit >= tau -----------------------------
+  // Few qualify, so each slot k costs one ballot and a wave-uniform branch unless some
+  // lane's vector k does.
+  uint32_t nv = 0;
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const bool f = vmax[k] >= tau - slack;
     const unsigned long long m = __ballot(f);
-    if (f) {
-      const unsigned int slot = nv + (unsigned)__popcll(m & lanemask_lt());
-      if (slot < (unsigned)kWaveCapVec) {
-        sm.vec_data[slot] = d[k];
-        sm.vec_pos[slot] = (unsigned)(tid + k * kTopkThreads);
+    if (m != 0ull) {
+      const uint32_t slot = nv + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (f && slot < (uint32_t)kWaveCapVec) {
+        sm.vec_data[wave][slot] = d[k];
+        sm.vec_pos[wave][slot] = (unsigned)(tid + k * kTopkThreads);
       }
+      nv += (uint32_t)__popcll(m);
     }
-    nv += (unsigned)__popcll(m);
   }
   wave_lds_sync();
 
-  // ---- their logits >= tau, with exact keys ---------------------------------------
-  unsigned int nc = 0;
-  bool exact = nv > (unsigned)kWaveCapVec;
-  if (!exact) {
-    for (unsigned int base = 0; base < nv * 8u; base += kWave) {
-      const unsigned int e = base + (unsigned)lane;
+  // ---- their logits >= tau, with exact keys, into the block's candidates -----------
+  if (nv > (uint32_t)kWaveCapVec) {
+    if (lane == 0) sm.overflow = 1u;
+  } else {
+    for (uint32_t base = 0; base < nv * 8u; base += kWave) {
+      const uint32_t e = base + (uint32_t)lane;
       bool f = false;
       unsigned long long comp = 0ull;
       if (e < nv * 8u) {
-        const unsigned int slot = e >> 3;
-        const uint32_t w = reinterpret_cast<const uint32_t*>(&sm.vec_data[slot])[(e & 7u) >> 1];
+        const uint32_t slot = e >> 3;
+        const uint32_t pos = sm.vec_pos[wave][slot];
+        const uint32_t w = reinterpret_cast<const uint32_t*>(&sm.vec_data[wave][slot])[(e & 7u) >> 1];
         const uint32_t bits = (e & 1u) ? (w >> 16) : (w & 0xffffu);
         const uint32_t key = bf16_key(bits);
         f = key != 0u && key >= tau_key;
-        comp = make_rc(key, (unsigned)v0 * 8u + sm.vec_pos[slot] * 8u + (e & 7u), bits);
+        comp = make_rc(key, (uint32_t)v0 * 8u + pos * 8u + (e & 7u), bits);
       }
       const unsigned long long m = __ballot(f);
-      if (f) {
-        const unsigned int slot = nc + (unsigned)__popcll(m & lanemask_lt());
-        if (slot < (unsigned)kWaveCapCand) sm.cand[slot] = comp;
+      if (m != 0ull) {
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
+        at = __builtin_amdgcn_readfirstlane(at);
+        const uint32_t slot = at + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (f && slot < (uint32_t)kBlockCapCand) sm.cand[slot] = comp;
       }
-      nc += (unsigned)__popcll(m);
     }
-    exact = nc < (unsigned)kNC || nc > (unsigned)kWaveCapCand;
   }
-  if (!exact && nc <= (unsigned)kListLen) {
-    // ---- the survivors are the list ----------------------------------------------------
-    if (lane < kListLen) list[lane] = (unsigned)lane < nc ? sm.cand[lane] : 0ull;
+  __syncthreads();
+
+  // ---- rank the candidates: every wave takes two at a time, one per half-wave, and --
+  // counts the larger ones by ballot, 32 at a time; ranks 0..15 each occur once.
+  const uint32_t n = sm.ncand;
+  if (sm.overflow == 0u && n >= (uint32_t)kNC && n <= (uint32_t)kBlockCapCand) {
+    const int half = lane >> 5, j = lane & 31;
+    for (uint32_t c0 = 0; c0 < n; c0 += 2 * kTopkWaves) {
+      const uint32_t c = c0 + 2u * (uint32_t)wave + (uint32_t)half;
+      const unsigned long long mine = c < n ? sm.cand[c] : 0ull;
+      uint32_t rank = 0;
+      for (uint32_t j0 = 0; j0 < n; j0 += 32) {
+        const uint32_t jj = j0 + (uint32_t)j;
+        const bool gt = jj < n && sm.cand[jj] > mine;
+        const unsigned long long m = __ballot(gt);
+        rank += (uint32_t)__popc((uint32_t)(m >> (32 * half)));
+      }
+      if (j == 0 && c < n && rank < (uint32_t)kNC) out[rank] = mine;
+    }
     return;
   }
-  if (!exact) {
-    // ---- rank the survivors (at most two per lane) ---------------------------------
-    const unsigned int npad = (nc + 7u) & ~7u;
-    for (unsigned int c = nc + (unsigned)lane; c < npad; c += kWave) sm.cand[c] = 0ull;
-    wave_lds_sync();
-    const unsigned long long m0 = (unsigned)lane < nc ? sm.cand[lane] : 0ull;
-    const unsigned long long m1 = (unsigned)lane + kWave < nc ? sm.cand[lane + kWave] : 0ull;
-    unsigned int r0, r1;
-    rank2(sm.cand, npad, m0, m1, r0, r1);
-    if (m0 && r0 < (unsigned)kNC) sm.top[r0] = m0;
-    if (m1 && r1 < (unsigned)kNC) sm.top[r1] = m1;
-  } else {
-    // ---- exact 16-round selection over the wave's logits -----------------------------
-    // It re-reads them from memory (cache-resident by now) so that the common path
-    // keeps its register budget.
-    unsigned long long prev = ~0ull;
-    for (int r = 0; r < kNC; ++r) {
-      unsigned long long best = 0ull;
-#pragma unroll 1
-      for (int k = 0; k < kTopkVecPerThread; ++k) {
-        const int v = v0 + tid + k * kTopkThreads;
-        if (v >= v1) break;
-        u32x4 x;
-        if (v < nfull) {
-          x = rowv[v];
-        } else {
-          uint32_t w4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (8 * v + e < V) {
-              const uint32_t b = row[8 * v + e];
-              w4[e >> 1] |= (e & 1) ? (b << 16) : b;
-            }
-          }
-          x = (u32x4){w4[0], w4[1], w4[2], w4[3]};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (8 * v + e < V) {
-            const uint32_t bits = elem_bits(x, e);
-            const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)(8 * v + e), bits);
-            if (comp < prev && comp > best) best = comp;
-          }
-        }
-      }
-      best = wave_max_u64(best);
-      if (lane == 0) sm.top[r] = best;
-      prev = best;
-    }
+
+  // ---- fallback (NaN-heavy, constant, heavily tied or tiny chunks) -------------------
+  wave_exact_list(row, V, v0, v1, sm.lists + wave * kNC);
+  __syncthreads();
+  if (wave == 0) {
+    const unsigned long long top = wave_merge_block(sm.lists);
+    if (lane < kNC) out[lane] = top;
   }
-  wave_lds_sync();
-  if (lane < kListLen) list[lane] = lane < kNC ? sm.top[lane] : 0ull;
 }
 
-// Copy a row's candidate lists (n composites, n a multiple of 128, at most
-// kMaxListEntries) from global memory to dst (LDS).  One whole wave; every load is
-// issued before the first store.
-__device__ __forceinline__ void wave_stage_lists(const unsigned long long* __restrict__ src, int n,
-                                                 unsigned long long* dst) {
-  constexpr int kPer = kMaxListEntries / 2 / kWave;
-  const int lane = threadIdx.x & 63;
-  const int nvec = n / 2;                               // a multiple of 64
-  const u64x2* __restrict__ s2 = reinterpret_cast<const u64x2*>(src);
-  u64x2* d2 = reinterpret_cast<u64x2*>(dst);
-  u64x2 x[kPer];
+// Top-16, best first, of a row's nchunks <= kMaxChunks sorted chunk lists (global
+// memory, kNC entries each): the 16 lanes of a row load them all, then merge them one
+// after another.  Every lane of each 16-lane row must take part.  Lane i returns slot i.
+__device__ __forceinline__ unsigned long long row16_merge_chunks(const unsigned long long* __restrict__ src,
+                                                                 int nchunks) {
+  const int i = threadIdx.x & 15;
+  unsigned long long y[kMaxChunks];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    if (k * kWave < nvec) x[k] = s2[lane + k * kWave];
+  for (int c = 0; c < kMaxChunks; ++c) y[c] = c < nchunks ? src[c * kNC + (c == 0 ? i : kNC - 1 - i)] : 0ull;
+  unsigned long long x = y[0];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    if (k * kWave < nvec) d2[lane + k * kWave] = x[k];
-  wave_lds_sync();
-}
-
-// Top-16 of a row, best first, from its n candidate-list entries ent[] (LDS; row
-// composites in no order, zero-padded) into out16[] (LDS).  One whole wave; lane l
-// looks at entries l + 64 j.  The 16th largest lane-maximum order key T bounds the
-// row's 16th best from below (16 lanes hold an entry at least that large), so only
-// entries with key >= T are compacted into cbuf (LDS, kMergeCandCap + 8) and ranked
-// among themselves.  Rows where fewer than 16 lanes see a key above the NaN key, or
-// with too many survivors, take an exact 16-round selection over all entries.
-__device__ __forceinline__ void wave_merge_lists(const unsigned long long* ent, int n, unsigned long long* cbuf,
-                                                 unsigned long long* out16) {
-  const int lane = threadIdx.x & 63;
-  const int m = n / kWave;
-  uint32_t lmax = 0;
-#pragma unroll 4
-  for (int j = 0; j < m; ++j) {
-    const uint32_t k = (uint32_t)(ent[lane + kWave * j] >> 48);
-    lmax = k > lmax ? k : lmax;
-  }
-  uint32_t T = 0;
-#pragma unroll
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t c = T | (1u << bit);
-    if (__popcll(__ballot(lmax >= c)) >= kNC) T = c;
-  }
-  unsigned int nc = 0;
-  if (T != 0u) {
-#pragma unroll 4
-    for (int j = 0; j < m; ++j) {
-      const unsigned long long x = ent[lane + kWave * j];
-      const bool f = (uint32_t)(x >> 48) >= T;
-      const unsigned long long mk = __ballot(f);
-      if (f) {
-        const unsigned int slot = nc + (unsigned)__popcll(mk & lanemask_lt());
-        if (slot < (unsigned)kMergeCandCap) cbuf[slot] = x;
-      }
-      nc += (unsigned)__popcll(mk);
-    }
-  }
-  if (T != 0u && nc <= (unsigned)kMergeCandCap) {
-    const unsigned int npad = (nc + 7u) & ~7u;
-    for (unsigned int c = nc + (unsigned)lane; c < npad; c += kWave) cbuf[c] = 0ull;
-    wave_lds_sync();
-    const unsigned long long m0 = (unsigned)lane < nc ? cbuf[lane] : 0ull;
-    const unsigned long long m1 = (unsigned)lane + kWave < nc ? cbuf[lane + kWave] : 0ull;
-    unsigned int r0, r1;
-    rank2(cbuf, npad, m0, m1, r0, r1);
-    if (m0 && r0 < (unsigned)kNC) out16[r0] = m0;
-    if (m1 && r1 < (unsigned)kNC) out16[r1] = m1;
-  } else {
-    unsigned long long prev = ~0ull;
-    for (int r = 0; r < kNC; ++r) {
-      unsigned long long best = 0ull;
-      for (int j = 0; j < m; ++j) {
-        const unsigned long long x = ent[lane + kWave * j];
-        if (x < prev && x > best) best = x;
-      }
-      best = wave_max_u64(best);
-      if (lane == 0) out16[r] = best;
-      prev = best;
-    }
-  }
-  wave_lds_sync();
+  for (int c = 1; c < kMaxChunks; ++c)
+    if (c < nchunks) x = merge16(x, y[c]);
+  return x;
 }
 
 // Chunking of a row: n chunks of near-equal vector counts, each <= kChunkVec.
