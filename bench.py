@@ -1,9 +1,9 @@
 """Throughput of the DFlash 2 proposer hot path on one MI355X.
 
-One step = the whole path over one batch: context gate -> select (top-16 -> pair
-score -> walk: one C call, three back-to-back kernels) -> two-tap conv -> verify, on
-the batched greedy
-workload (B=15, K=7, V=151936, hidden 5120, selector dim 256).  Inputs are synthetic
+One step = the whole path over one batch: the gated select (context gate, top-16, pair
+score and walk in one C call: the gate's tiles run inside the launch that streams the
+logits, then two more kernels) -> two-tap conv -> greedy verify, on the batched
+greedy workload (B=15, K=7, V=151936, hidden 5120, selector dim 256).  Inputs are synthetic
 and already resident in HBM; logits and target logits rotate through >= 16 buffers
 (> 2x the 256 MB Infinity Cache) so the streams come from HBM.  The step sequence is
 captured once in a HIP graph (one graph = one pass over every rotating buffer) and
@@ -118,8 +118,7 @@ def main():
     }
 
     def step(i):
-        H.copy_(dflash2.context_gate(h, Wh, bias))
-        dflash2.select(logits[i], verified, A, Bt, H, 0.0, 0, out=sel)
+        dflash2.select_gated(logits[i], verified, A, Bt, h, Wh, bias, "sigmoid", 0.0, 0, out=sel, H_out=H)
         dflash2.conv2tap(x, xp, taps, y=y)
         dflash2.spec_accept(targets[i], sel["tokens"], sel["cand_idx"], sel["q"], 0.0, 0)
 
@@ -200,7 +199,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "c2: batched greedy B=15 K=7 V=151936, hidden 5120, selector dim 256, bf16 logits "
-                               "and tables; step = gate + select + conv2tap + greedy verify",
+                               "and tables; step = gated select (gate + top-16 + pair score + walk) + conv2tap + greedy verify",
                    "global_batch": w.B, "draft_positions_per_step": positions, "rotating_buffers": nbuf},
         "select_only": {"positions_per_s": round(positions / (select_us * 1e-6), 1), "avg_launch_us": round(select_us, 3),
                         "hbm_frac": roofline["frac"]},

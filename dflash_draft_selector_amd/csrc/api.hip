@@ -181,6 +181,47 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
                                   row_status, ws, stream));
 }
 
+size_t dflash2_select_gated_workspace(int64_t batch, int64_t K, int64_t vocab, int64_t hidden, int64_t dim) {
+  if (batch < 1 || K < 1 || vocab < 1 || hidden < 1 || dim < 1) return 0;
+  Carver c(nullptr);
+  carve_select_gated(c, batch, K, vocab, hidden, dim);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                                    const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab, int64_t dim,
+                                    const float* h, const void* w_h, dflash2_dtype w_dtype, const float* bias,
+                                    int64_t hidden, dflash2_gate_act act, int64_t batch, int64_t K,
+                                    float temperature, uint64_t seed, float* H_out, int32_t* cand_idx,
+                                    float* cand_val, float* S, int32_t* tokens, int32_t* slots, float* q,
+                                    int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  st = check_logits(logits, batch * K, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
+  if (st != DFLASH2_OK) return st;
+  if (!verified || !h || !w_h || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
+  if (w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
+  if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
+  if (hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24)) return DFLASH2_ERR_SHAPE;
+  const int64_t rows = batch * K;
+  if (!items_ok(rows * topk_num_chunks(vocab) + fused_gate_blocks(rows, hidden, dim), kTopkThreads))
+    return DFLASH2_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_h)) return DFLASH2_ERR_ALIGN;
+  st = check_temp(temperature);
+  if (st != DFLASH2_OK) return st;
+  SelectGatedWs ws;
+  st = carve_checked(workspace, workspace_bytes,
+                     [&](Carver& c) { return carve_select_gated(c, batch, K, vocab, hidden, dim); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_select_gated(logits, ld, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab,
+                                        (int)dim, h, static_cast<const uint16_t*>(w_h), bias, (int)hidden, (int)act,
+                                        (int)batch, (int)K, temperature, seed, H_out, cand_idx, cand_val, S, tokens,
+                                        slots, q, row_status, ws, stream));
+}
+
 dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float* taps, int64_t sites, int64_t batch,
                                 int64_t K, int64_t hidden, int64_t group, float* y, hipStream_t stream) {
   if (!x || !x_prev || !taps || !y) return DFLASH2_ERR_NULL;

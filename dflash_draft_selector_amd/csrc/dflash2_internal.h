@@ -34,6 +34,14 @@ struct SelectWs {
 };
 SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab);
 
+struct SelectGatedWs {
+  SelectWs sel;
+  float* partial;                 // [nsplit][rows][dim] gate partial sums
+  int nsplit;
+};
+SelectGatedWs carve_select_gated(Carver& c, int64_t batch, int64_t K, int64_t vocab, int64_t hidden, int64_t dim);
+int64_t fused_gate_blocks(int64_t rows, int64_t hidden, int64_t dim);
+
 struct GateWs {
   float* partial;                 // [nsplit][rows][dim] slice sums (nsplit > 1)
   int nsplit;                     // slices of the hidden dimension
@@ -65,6 +73,13 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
                          float temperature, uint64_t seed, int32_t* cand_idx, float* cand_val, float* S,
                          int32_t* tokens, int32_t* slots, float* q, int32_t* row_status, SelectWs ws,
                          hipStream_t s);
+
+hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                               const void* emb_b, bool bf16, int vocab, int dim, const float* h,
+                               const uint16_t* w_h, const float* bias, int hidden, int act, int batch, int K,
+                               float temperature, uint64_t seed, float* H_out, int32_t* cand_idx, float* cand_val,
+                               float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
+                               SelectGatedWs ws, hipStream_t s);
 
 hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden,
                        int dim, int act, float* H, GateWs ws, hipStream_t s);

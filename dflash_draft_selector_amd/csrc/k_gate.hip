@@ -1,20 +1,10 @@
-// Context gate H = act(W_H h + b) (pegainfer issue "DFlash 2 proposer", section
-// "What upstream shipped", item 1: 256-dim token embeddings + context gate).
-//
-// bf16 weight: h is rounded to bf16 (nearest even) as it is loaded and the product
-// runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  A block owns a 16-row x
-// (up to) 64-column output tile over one slice of the hidden dimension; its four
-// waves take interleaved 32-wide steps of the slice and are summed in LDS in a fixed
-// order.  With several slices, each block stores its tile as a partial sum and a
-// second kernel adds the slices in slice order, then the bias and the activation, so
-// results never depend on scheduling.  fp32 weight: plain fp32 FMA, one thread per
-// output.
-#include "device_common.h"
+// Context gate kernels: the standalone bf16 path (tiles of gate_dev.h, four waves per
+// work-group, then a kernel adding the slices) and the fp32-weight path (plain fp32
+// FMA, one thread per output).
 #include "dflash2_internal.h"
+#include "gate_dev.h"
 
 namespace df2 {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGateThreads = 256;
 constexpr int kGateTargetBlocks = 288;
@@ -48,92 +38,19 @@ GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim) {
   return w;
 }
 
-__device__ __forceinline__ float gate_act(float x, int act) { return act == 0 ? 1.f / (1.f + expf(-x)) : x; }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
-
 // NB = 16-column blocks of the tile (tile width 16 * NB = min(dim, 64)).
 template <int NB>
 __global__ void __launch_bounds__(kGateThreads) k_gate_bf16(const float* __restrict__ h, const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int rows, int hidden,
                                                             int dim, int act, int ntiles, int nsplit,
                                                             float* __restrict__ H, float* __restrict__ partial) {
-  constexpr int kCols = 16 * NB;
-  __shared__ float red[4][16][kCols];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
+  __shared__ float red[4 * 16 * 16 * NB];
   const int per = ntiles * nsplit;
   const int mt = blockIdx.x / per;
   const int rem = blockIdx.x - mt * per;
   const int nt = rem / nsplit;
   const int split = rem - nt * nsplit;
-  const int nsteps = (hidden + 31) / 32;
-  const int s0 = (int)((long long)nsteps * split / nsplit), s1 = (int)((long long)nsteps * (split + 1) / nsplit);
-
-  const int arow = mt * 16 + r16;
-  const bool arow_ok = arow < rows;
-  const float* hrow = h + (size_t)(arow_ok ? arow : 0) * hidden;
-  const uint16_t* wcol[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) wcol[j] = w + (size_t)(nt * kCols + j * 16 + r16) * hidden;
-
-  f32x4 acc[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  for (int base = s0 + wv; base < s1; base += 4 * kGateRound) {
-    f32x4 x0[kGateRound], x1[kGateRound];
-    u32x4 bw[kGateRound][NB];
-#pragma unroll
-    for (int i = 0; i < kGateRound; ++i) {
-      const int st = base + 4 * i;
-      const int k = st * 32 + g * 8;
-      const bool kok = st < s1 && k < hidden;
-      x0[i] = x1[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (kok && arow_ok) {
-        x0[i] = *reinterpret_cast<const f32x4*>(hrow + k);
-        x1[i] = *reinterpret_cast<const f32x4*>(hrow + k + 4);
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        bw[i][j] = (u32x4){0u, 0u, 0u, 0u};
-        if (kok) bw[i][j] = *reinterpret_cast<const u32x4*>(wcol[j] + k);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kGateRound; ++i) {
-      u32x4 a;
-      a.x = pack_bf16x2(x0[i].x, x0[i].y);
-      a.y = pack_bf16x2(x0[i].z, x0[i].w);
-      a.z = pack_bf16x2(x1[i].x, x1[i].y);
-      a.w = pack_bf16x2(x1[i].z, x1[i].w);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                         __builtin_bit_cast(bf16x8, bw[i][j]), acc[j], 0, 0, 0);
-    }
-  }
-
-  // D layout: lane l, register r -> row 4 * (l / 16) + r, column l % 16 of each block
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wv][4 * g + r][j * 16 + r16] = acc[j][r];
-  __syncthreads();
-  for (int e = tid; e < 16 * kCols; e += kGateThreads) {
-    const int rr = e / kCols, c = e - rr * kCols;
-    const int row = mt * 16 + rr;
-    if (row >= rows) continue;
-    const int n = nt * kCols + c;
-    const float sum = ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c];
-    if (nsplit == 1)
-      H[(size_t)row * dim + n] = gate_act(sum + (bias ? bias[n] : 0.f), act);
-    else
-      partial[((size_t)split * rows + row) * dim + n] = sum;
-  }
+  gate_tile<NB, 4, kGateRound>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H, partial);
 }
 
 // Sum of the slices in slice order, then bias and activation: one thread per output.
@@ -142,11 +59,8 @@ __global__ void __launch_bounds__(256) k_gate_finish(const float* __restrict__ p
                                                      float* __restrict__ H) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n_out) return;
-  const int n = (int)(e % dim);
-  float sum = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < nsplit; ++sp) sum += partial[(size_t)sp * n_out + e];
-  H[e] = gate_act(sum + (bias ? bias[n] : 0.f), act);
+  const int row = (int)(e / dim), n = (int)(e - (long long)row * dim);
+  H[e] = gate_finish(partial, bias, (int)(n_out / dim), dim, nsplit, act, row, n);
 }
 
 // fp32 weight: one thread per (row, column); four interleaved partial sums.

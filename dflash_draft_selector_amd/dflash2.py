@@ -45,6 +45,10 @@ _SIGNATURES = {
     "dflash2_select_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_select": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _f32, _u64,
                         _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_select_gated_workspace": ([_i64, _i64, _i64, _i64, _i64], _size),
+    "dflash2_select_gated": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _c_ptr, _int, _c_ptr,
+                              _i64, _int, _i64, _i64, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                              _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_conv2tap": ([_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i64, _i64, _c_ptr, _c_ptr], _int),
     "dflash2_spec_accept_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_spec_accept": ([_c_ptr, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _f32, _u64, _c_ptr,
@@ -165,8 +169,11 @@ def topk16(logits: torch.Tensor, row_status: bool = False):
     return (idx, val, st) if row_status else (idx, val)
 
 
-def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None = None, act: str = "sigmoid"):
-    """H = act(W_H h + b) for h [..., hidden] (fp32) and W_H [dim, hidden] (fp32 or bf16)."""
+def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None = None, act: str = "sigmoid",
+                 out: torch.Tensor | None = None):
+    """H = act(W_H h + b) for h [..., hidden] (fp32) and W_H [dim, hidden] (fp32 or bf16).
+
+    `out` may supply a contiguous fp32 tensor of shape [..., dim] to write H into."""
     lib = load_library()
     _contig(_need(h, "h", (torch.float32,)), "h")
     _contig(_need(w_h, "w_h", (torch.float32,) + _BF16_LIKE, h.device), "w_h")
@@ -176,7 +183,12 @@ def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None =
     if h.shape[-1] != hidden:
         raise ValueError("h and w_h disagree on the hidden size")
     rows = h.numel() // hidden
-    H = torch.empty(h.shape[:-1] + (dim,), dtype=torch.float32, device=h.device)
+    if out is None:
+        H = torch.empty(h.shape[:-1] + (dim,), dtype=torch.float32, device=h.device)
+    else:
+        H = _contig(_need(out, "out", (torch.float32,), h.device), "out")
+        if tuple(H.shape) != tuple(h.shape[:-1]) + (dim,):
+            raise ValueError("out must have shape h.shape[:-1] + (dim,)")
     wdt = F32 if w_h.dtype == torch.float32 else BF16
     a = {"sigmoid": GATE_SIGMOID, "identity": GATE_IDENTITY}[act]
     nbytes = lib.dflash2_context_gate_workspace(rows, hidden, dim)
@@ -260,6 +272,55 @@ def select(logits, verified, emb_a, emb_b, H, temperature: float = 0.0, seed: in
                               _ptr(out["cand_val"]), _ptr(out["S"]), _ptr(out["tokens"]), _ptr(out["slots"]),
                               _ptr(out["q"]), _ptr(out["row_status"]), _ptr(ws), ws.numel(), _stream()),
            "dflash2_select")
+    return out
+
+
+def select_gated(logits, verified, emb_a, emb_b, h, w_h, bias=None, act: str = "sigmoid", temperature: float = 0.0,
+                 seed: int = 0, out: dict | None = None, H_out: torch.Tensor | None = None):
+    """Context gate + select in one call: h [B, K, hidden] fp32, w_h [dim, hidden] bf16.
+
+    Returns the dict of select(); H_out (fp32 [B, K, dim]) receives the gate values the
+    scores used when given.
+    """
+    lib = load_library()
+    dev = logits.device
+    _need(logits, "logits", _BF16_LIKE)
+    rows, V, ld = _rows_view(logits, "logits")
+    B, K = logits.shape[0], logits.shape[1]
+    _contig(_need(verified, "verified", (torch.int32,), dev), "verified")
+    _contig(_need(emb_a, "emb_a", (torch.float32,) + _BF16_LIKE, dev), "emb_a")
+    _contig(_need(emb_b, "emb_b", (torch.float32,) + _BF16_LIKE, dev), "emb_b")
+    _contig(_need(h, "h", (torch.float32,), dev), "h")
+    _contig(_need(w_h, "w_h", _BF16_LIKE, dev), "w_h")
+    if bias is not None:
+        _contig(_need(bias, "bias", (torch.float32,), dev), "bias")
+    dim = emb_a.shape[1]
+    hidden = h.shape[-1]
+    if tuple(h.shape) != (B, K, hidden) or tuple(w_h.shape) != (dim, hidden):
+        raise ValueError("h must be [B, K, hidden] and w_h [dim, hidden] with dim = emb_a.shape[1]")
+    if H_out is not None:
+        _contig(_need(H_out, "H_out", (torch.float32,), dev), "H_out")
+        if tuple(H_out.shape) != (B, K, dim):
+            raise ValueError("H_out must be [B, K, dim]")
+    if out is None:
+        out = {
+            "cand_idx": torch.empty((B, K, NCAND), dtype=torch.int32, device=dev),
+            "cand_val": torch.empty((B, K, NCAND), dtype=torch.float32, device=dev),
+            "S": torch.empty((B, K, NCAND, NCAND), dtype=torch.float32, device=dev),
+            "tokens": torch.empty((B, K), dtype=torch.int32, device=dev),
+            "slots": torch.empty((B, K), dtype=torch.int32, device=dev),
+            "q": torch.empty((B, K, NCAND), dtype=torch.float32, device=dev),
+            "row_status": torch.empty((B, K), dtype=torch.int32, device=dev),
+        }
+    a = {"sigmoid": GATE_SIGMOID, "identity": GATE_IDENTITY}[act]
+    nbytes = lib.dflash2_select_gated_workspace(B, K, V, hidden, dim)
+    ws = workspace("select_gated", nbytes, dev, (B, K, V, hidden, dim))
+    _check(lib.dflash2_select_gated(_ptr(logits), ld, _ptr(verified), _ptr(emb_a), _ptr(emb_b),
+                                    _emb_dtype(emb_a, emb_b), V, dim, _ptr(h), _ptr(w_h), BF16, _ptr(bias), hidden, a,
+                                    B, K, float(temperature), int(seed) & (2 ** 64 - 1), _ptr(H_out),
+                                    _ptr(out["cand_idx"]), _ptr(out["cand_val"]), _ptr(out["S"]), _ptr(out["tokens"]),
+                                    _ptr(out["slots"]), _ptr(out["q"]), _ptr(out["row_status"]), _ptr(ws), ws.numel(),
+                                    _stream()), "dflash2_select_gated")
     return out
 
 

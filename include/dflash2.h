@@ -153,10 +153,11 @@ dflash2_status dflash2_walk(const float* S, const int32_t* cand_idx, int64_t bat
                             float* q, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
- * Fused proposer step: topk16 -> pair_score -> walk in ONE kernel launch.
- * Same passages as the three calls above; the outputs are bit-identical to calling
- * dflash2_topk16 on every position's logits row, then dflash2_pair_score, then
- * dflash2_walk.  logits rows are addressed as logits[(b*K + t)*ld + v].
+ * Fused proposer step: topk16 -> pair_score -> walk in one call (three back-to-back
+ * kernels on `stream`, no host synchronisation).  Same passages as the three calls
+ * above; the outputs are bit-identical to calling dflash2_topk16 on every position's
+ * logits row, then dflash2_pair_score, then dflash2_walk.  logits rows are addressed
+ * as logits[(b*K + t)*ld + v].
  *
  * row_status int32 [batch, K] or NULL (the union of the top-16 and pair-score bits).
  * Errors: the union of the three calls' checks, plus workspace.
@@ -169,6 +170,34 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
                               float* S, int32_t* tokens, int32_t* slots, float* q,
                               int32_t* row_status, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Gated proposer step: context gate -> topk16 -> pair_score -> walk in one call.
+ * The passages of dflash2_context_gate and dflash2_select.  The gate's bf16 matrix
+ * product runs inside the launch that streams the logits (on compute units the stream
+ * leaves idle or shares), and each draft position adds its own row's gate slices, so
+ * H never makes a separate round trip.
+ *
+ * h float [batch, K, hidden]; w_h [dim, hidden] in w_dtype, which must be
+ * DFLASH2_BF16 (h rounded to bf16 as in dflash2_context_gate); bias float [dim] or
+ * NULL; act as in dflash2_context_gate.  H_out float [batch, K, dim] or NULL: the gate
+ * values the scores used.  They equal dflash2_context_gate's up to the fp32 summation
+ * order over `hidden` (deterministic, not bit-identical to it); every other output is
+ * bit-identical to dflash2_select called with H = H_out.
+ * Errors: the checks of dflash2_select and dflash2_context_gate, w_dtype other than
+ *         DFLASH2_BF16 (DFLASH2_ERR_DTYPE), workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_select_gated_workspace(int64_t batch, int64_t K, int64_t vocab, int64_t hidden,
+                                      int64_t dim);
+dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified,
+                                    const void* emb_a, const void* emb_b, dflash2_dtype emb_dtype,
+                                    int64_t vocab, int64_t dim, const float* h, const void* w_h,
+                                    dflash2_dtype w_dtype, const float* bias, int64_t hidden,
+                                    dflash2_gate_act act, int64_t batch, int64_t K,
+                                    float temperature, uint64_t seed, float* H_out,
+                                    int32_t* cand_idx, float* cand_val, float* S, int32_t* tokens,
+                                    int32_t* slots, float* q, int32_t* row_status, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * Two-tap dynamic depthwise convolution, at `sites` independent sublayer sites.

@@ -96,6 +96,18 @@ def test_host_validation_before_any_launch():
                               FAKE, FAKE, NULL, ws, 16, NULL) == 5
     assert lib.dflash2_select(FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 0, 0.0, 0, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, NULL, ws, big, NULL) == 2
+    # gated select: the select checks, then the gate's
+    sg = lambda w_dtype=1, hidden=512, act=0, h=FAKE, wsb=big, K=7: lib.dflash2_select_gated(
+        FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, h, FAKE, w_dtype, NULL, hidden, act, 1, K, 0.0, 0, NULL, FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, NULL, ws, wsb, NULL)
+    assert sg(K=0) == 2
+    assert sg(h=NULL) == 1
+    assert sg(w_dtype=0) == 4
+    assert sg(act=5) == 4
+    assert sg(hidden=500) == 2
+    assert sg(h=MIS) == 3
+    assert lib.dflash2_select_gated_workspace(1, 7, 4096, 512, 256) > lib.dflash2_select_workspace(1, 7, 4096)
+    assert sg(wsb=lib.dflash2_select_gated_workspace(1, 7, 4096, 512, 256) - 257) == 5
     # conv
     assert lib.dflash2_conv2tap(FAKE, FAKE, FAKE, 1, 1, 7, 512, 3, FAKE, NULL) == 2
     assert lib.dflash2_conv2tap(FAKE, NULL, FAKE, 1, 1, 7, 512, 1, FAKE, NULL) == 1

@@ -243,6 +243,60 @@ def test_select_vs_oracle(d2, wl):
     print(f"c{wl} walk stats", stats, flush=True)
 
 
+@pytest.mark.parametrize("wl", [0, 1, 2, 4])
+def test_select_gated(d2, wl):
+    """The gated select's H_out follows the oracle gate, and every other output is
+    bit-identical to dflash2_select called with that H."""
+    import torch
+    inp = inputs(wl)
+    w = synth.workload(wl)
+    if "w_h_bits" not in inp:
+        pytest.skip("the gated select takes a bf16 gate weight")
+    print(f"gated select c{wl}", flush=True)
+    A64, B64, Ag, Bg = tables(inp)
+    W64, Wg, _ = gate_w(inp)
+    hg = to_gpu(inp["h"].reshape(w.B, w.K, w.D))
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    Hout = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=hg.device)
+    out = d2.select_gated(logits, ver, Ag, Bg, hg, Wg, to_gpu(inp["bias"]), "sigmoid", w.temperature, w.walk_seed,
+                          H_out=Hout)
+    Href, _, pre_abs = oracle.context_gate(inp["h"].reshape(-1, w.D), W64, inp["bias"], True)
+    scale = 0.25 * pre_abs          # |d sigmoid / dx| <= 1/4
+    assert_close_scaled(cpu(Hout).reshape(-1, w.dim), Href, scale, what="gated H")
+    ref = d2.select(logits, ver, Ag, Bg, Hout, w.temperature, w.walk_seed)
+    for k in ref:
+        a, b = cpu(out[k]), cpu(ref[k])
+        np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                      b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+    ridx, _ = oracle.topk16(inp["logits_bits"])
+    np.testing.assert_array_equal(cpu(out["cand_idx"]), ridx)
+
+
+def test_select_gated_ragged(d2):
+    """Rows not a multiple of 16, a hidden size that is not a multiple of 32, dim 64, a
+    bias, the identity activation and a sampled walk."""
+    import torch
+    w = synth.workload(0, B=3, K=5, V=5000, D=200, dim=64, bf16_params=True)
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(11)
+    bias = rng.normal(0.0, 0.5, size=w.dim).astype(np.float32)
+    A64, B64, Ag, Bg = tables(inp)
+    W64, Wg, _ = gate_w(inp)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    for act, T in (("identity", 0.0), ("sigmoid", 0.7)):
+        print(f"gated select ragged act={act} T={T}", flush=True)
+        Hout = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=logits.device)
+        out = d2.select_gated(logits, ver, Ag, Bg, to_gpu(inp["h"]), Wg, to_gpu(bias), act, T, 9, H_out=Hout)
+        Href, _, pre_abs = oracle.context_gate(inp["h"].reshape(-1, w.D), W64, bias, True, act=act)
+        assert_close_scaled(cpu(Hout).reshape(-1, w.dim), Href, pre_abs * (0.25 if act == "sigmoid" else 1.0),
+                            what=f"gated H {act}")
+        ref = d2.select(logits, ver, Ag, Bg, Hout, T, 9)
+        for k in ref:
+            a, b = cpu(out[k]), cpu(ref[k])
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+
+
 def test_select_c3_sampled_rows(d2):
     w = synth.workload(3)
     inp = inputs(3)
