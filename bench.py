@@ -39,6 +39,31 @@ def algorithmic_select_bytes(B, K, V, dim, table_bytes=2):
     return logits + gathers + h
 
 
+SELECT_SOURCES = ("k_select.hip", "topk_dev.h", "pair_dev.h", "gate_dev.h", "device_common.h", "dflash2_internal.h")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "select_c2_memory_counters.md")
+
+
+def measured_select_traffic():
+    """HBM bytes per dflash2_select launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel of known size), or None when the
+    select's kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None
+    m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_h = re.search(r"^select_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not (m_t and m_h):
+        return None
+    h = hashlib.sha256()
+    for f in SELECT_SOURCES:
+        with open(os.path.join(ROOT, "dflash_draft_selector_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m_t.group(1)) if h.hexdigest() == m_h.group(1) else None
+
+
 def cpu_baseline(inp, w, budget_s=12.0):
     """Time the CPU oracle (top-16 -> pair score -> walk) on whole requests of the same
     workload until ~budget_s of work, single-threaded."""
@@ -77,6 +102,8 @@ def main():
     ap.add_argument("--nbuf", type=int, default=17)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select-only", action="store_true", help="time only the select graph (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy a 1 GiB buffer three times (a kernel of known traffic, to scale memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "libdflash2 runs on one GPU per process; multi-GPU runs are not supported, use --gpus 1"}))
@@ -89,6 +116,14 @@ def main():
 
     dflash2.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.workload(2)
     inp = synth.make_inputs(w)
     target = synth.make_target(w, seed=102)
@@ -153,7 +188,8 @@ def main():
     achieved = sel_bytes / (select_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "dflash2_select = k_chunk_lists + k_positions + k_walk_tables",
                 "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_select_traffic(),
                 "bytes_per_launch": sel_bytes, "avg_launch_us": round(select_us, 3)}
 
     if args.select_only:

@@ -109,12 +109,22 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
   }
 }
 
-// Gate value of (row, n) from the nsplit partial sums, added in slice order.
+// Gate value of (row, n) from the nsplit partial sums, added in slice order.  Loads
+// go out sixteen at a time, so up to sixteen slices cost one memory round trip.
 __device__ __forceinline__ float gate_finish(const float* __restrict__ partial, const float* __restrict__ bias,
                                              int rows, int dim, int nsplit, int act, int row, int n) {
+  constexpr int kBatch = 16;
+  const size_t stride = (size_t)rows * dim;
+  const float* p = partial + (size_t)row * dim + n;
   float sum = 0.f;
-#pragma unroll 4
-  for (int sp = 0; sp < nsplit; ++sp) sum += partial[((size_t)sp * rows + row) * dim + n];
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) v[i] = s0 + i < nsplit ? p[(size_t)(s0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (s0 + i < nsplit) sum += v[i];
+  }
   return gate_act(sum + (bias ? bias[n] : 0.f), act);
 }
 

@@ -2,8 +2,9 @@
 // accept with min(1, p/q), on a reject resample from max(0, p - q); all-greedy keeps
 // the prefix match.  pegainfer issue "DFlash 2 proposer", "Proposal", phase 3).
 //
-// Pass 1 (k_accept_stats): split-vocabulary statistics of every target row -- per
-// chunk the max and the sum of exp((l - max)/T), or the chunk argmax when T == 0.
+// Pass 1: split-vocabulary statistics of every target row -- per chunk the max and
+// the sum of exp((l - max)/T) (k_accept_stats), or the chunk argmax when T == 0
+// (k_greedy_argmax).
 // Pass 2 (k_accept_decide): one block per request merges its rows' chunk statistics
 // (fixed chunk order), runs the accept tests, then draws the committed token by
 // inverse CDF: the chunk is found from the chunk masses (minus the draft's mass at its
@@ -62,12 +63,12 @@ __device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
   return r;
 }
 
+// Sampled statistics (T > 0) of one chunk of a target row.
 __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __restrict__ target, int64_t ld,
                                                               int64_t batch_stride, int K, int V, int nchunks,
                                                               float inv_t, AcceptWs ws) {
   __shared__ float s_redf[4];
   __shared__ int s_redi[4];
-  __shared__ unsigned long long s_redu[4];
   const int tid = threadIdx.x;
   const int r = blockIdx.x / nchunks;
   const int c = blockIdx.x - r * nchunks;
@@ -100,64 +101,6 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
   }
 
   const size_t ci = (size_t)r * nchunks + c;
-  if (inv_t == 0.f) {
-    // Chunk argmax (largest order key, then lowest id; NaN lowest).  The maximum is
-    // found on packed signed-order halves, with +NaN clamped to +inf; the lanes then
-    // look for the lowest id whose key equals it.  A chunk whose only maxima were
-    // +NaN finds none and takes the exact composite scan.
-    int vmax[kAccVecPerThread];
-    int lmax = -32768;
-#pragma unroll
-    for (int k = 0; k < kAccVecPerThread; ++k) {
-      const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(signed_order2(d[k].x), signed_order2(d[k].y)),
-                                                 __builtin_elementwise_max(signed_order2(d[k].z), signed_order2(d[k].w)));
-      vmax[k] = max_halves(mx);
-      lmax = vmax[k] > lmax ? vmax[k] : lmax;
-    }
-    lmax = lmax > 0x7f80 ? 0x7f80 : lmax;
-    const int M = block_reduce<int>(lmax, s_redi, true);
-    const uint32_t mbits = order_to_bits(M);
-    const uint32_t mkey = bf16_key(mbits);
-    int best_id = 0x7fffffff;
-    // only vectors whose maximum reaches M - 1 can hold the key (-0 sits one order
-    // below +0 and shares its key); ids rise with k, so the first hit of a lane wins
-#pragma unroll
-    for (int k = 0; k < kAccVecPerThread; ++k) {
-      const int v = v0 + tid + k * kAccThreads;
-      if (best_id == 0x7fffffff && v < v1 && (vmax[k] > 0x7f80 ? 0x7f80 : vmax[k]) >= M - 1) {
-        for (int e = 0; e < 8; ++e) {
-          const int id = 8 * v + e;
-          if (id < V && bf16_key(elem_bits(d[k], e)) == mkey) {
-            best_id = id;
-            break;
-          }
-        }
-      }
-    }
-    best_id = -block_reduce<int>(-best_id, s_redi, true);
-    if (best_id != 0x7fffffff) {
-      if (tid == 0) ws.chunk_arg[ci] = make_rc(mkey, (unsigned)best_id, mbits);
-      return;
-    }
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int k = 0; k < kAccVecPerThread; ++k) {
-      const int v = v0 + tid + k * kAccThreads;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int id = 8 * v + e;
-        if (v < v1 && id < V) {
-          const uint32_t bits = elem_bits(d[k], e);
-          const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)id, bits);
-          best = comp > best ? comp : best;
-        }
-      }
-    }
-    best = block_reduce<unsigned long long>(best, s_redu, true);
-    if (tid == 0) ws.chunk_arg[ci] = best;
-    return;
-  }
-
   // signed-order max / min (to find +inf and NaN) and the chunk maximum
   int smax = -32768, smin = 32767;
 #pragma unroll
@@ -190,6 +133,90 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
   if (tid == 0) {
     ws.chunk_max[ci] = nonfinite ? __builtin_nanf("") : m_c;
     ws.chunk_sum[ci] = sum;
+  }
+}
+
+// ---- greedy pass 1: the argmax of every target row -----------------------------------
+// Rows are split like the top-16 chunks (two 512-thread blocks per row at V = 151936,
+// 19 loads of 16 bytes in flight per lane).  A block's chunk argmax: the maximum of
+// the packed signed-order halves (+NaN clamped to +inf), reduced over the block; then
+// the lowest id whose key equals it, searched only in vectors whose maximum reaches it
+// (-0 sits one order below +0 and shares its key).  A chunk whose only maxima were
+// +NaN finds none and takes the exact composite maximum.
+__global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* __restrict__ target, int64_t ld,
+                                                                int64_t batch_stride, int K, int V, int nchunks,
+                                                                unsigned long long* __restrict__ chunk_arg) {
+  __shared__ int s_red[kTopkWaves];
+  __shared__ unsigned long long s_redu[kTopkWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const int r = blockIdx.x / nchunks;
+  const int c = blockIdx.x - r * nchunks;
+  const int b = batch_stride == 0 ? 0 : r / (K + 1);
+  const int t = batch_stride == 0 ? r : r - b * (K + 1);
+  const uint16_t* rowp = target + (size_t)b * batch_stride + (size_t)t * ld;
+  const int v0 = chunk_begin(V, nchunks, c), v1 = chunk_begin(V, nchunks, c + 1);
+
+  u32x4 d[kTopkVecPerThread];
+  load_chunk(rowp, V, v0, v1, d);                  // missing logits read as -NaN (lowest)
+  int vmax[kTopkVecPerThread];
+  int lmax = vector_maxima<true>(d, vmax);
+  lmax = lmax > 0x7f80 ? 0x7f80 : lmax;
+  lmax = wave_max_i32(lmax);
+  if (lane == 0) s_red[wave] = lmax;
+  __syncthreads();
+  int M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) M = max(M, s_red[w]);
+  const uint32_t mbits = order_to_bits(M);
+  const uint32_t mkey = bf16_key(mbits);
+  int best = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < kTopkVecPerThread; ++k) {
+    const int v = v0 + tid + k * kTopkThreads;
+    if (best == 0x7fffffff && v < v1 && (vmax[k] > 0x7f80 ? 0x7f80 : vmax[k]) >= M - 1) {
+      for (int e = 0; e < 8; ++e) {
+        const int id = 8 * v + e;
+        if (id < V && bf16_key(elem_bits(d[k], e)) == mkey) {
+          best = id;
+          break;
+        }
+      }
+    }
+  }
+  best = -wave_max_i32(-best);
+  __syncthreads();                                 // every wave has read s_red
+  if (lane == 0) s_red[wave] = best;
+  __syncthreads();
+  best = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) best = min(best, s_red[w]);
+  const size_t ci = (size_t)r * nchunks + c;
+  if (best != 0x7fffffff) {
+    if (tid == 0) chunk_arg[ci] = make_rc(mkey, (unsigned)best, mbits);
+    return;
+  }
+  unsigned long long comp = 0ull;
+#pragma unroll
+  for (int k = 0; k < kTopkVecPerThread; ++k) {
+    const int v = v0 + tid + k * kTopkThreads;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int id = 8 * v + e;
+      if (v < v1 && id < V) {
+        const uint32_t bits = elem_bits(d[k], e);
+        const unsigned long long x = make_rc(bf16_key(bits), (unsigned)id, bits);
+        comp = x > comp ? x : comp;
+      }
+    }
+  }
+  comp = wave_max_u64(comp);
+  if (lane == 0) s_redu[wave] = comp;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long m = s_redu[0];
+    for (int w = 1; w < kTopkWaves; ++w) m = s_redu[w] > m ? s_redu[w] : m;
+    chunk_arg[ci] = m;
   }
 }
 
@@ -585,11 +612,18 @@ hipError_t launch_spec_accept(const uint16_t* target, int64_t ld, int64_t batch_
                               const int32_t* cand_idx, const float* q, int batch, int K, int vocab, float temperature,
                               uint64_t seed, int32_t* out_tokens, int32_t* n_accepted, int32_t* row_status, AcceptWs ws,
                               hipStream_t s) {
-  const int nchunks = acc_num_chunks(vocab);
   const int nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
-  hipLaunchKernelGGL(k_accept_stats, dim3((unsigned)(nrows * nchunks)), dim3(kAccThreads), 0, s, target, ld,
-                     batch_stride, K, vocab, nchunks, inv_t, ws);
+  int nchunks;
+  if (inv_t == 0.f) {
+    nchunks = topk_num_chunks(vocab);          // <= acc_num_chunks(vocab): fits the workspace
+    hipLaunchKernelGGL(k_greedy_argmax, dim3((unsigned)(nrows * nchunks)), dim3(kTopkThreads), 0, s, target, ld,
+                       batch_stride, K, vocab, nchunks, ws.chunk_arg);
+  } else {
+    nchunks = acc_num_chunks(vocab);
+    hipLaunchKernelGGL(k_accept_stats, dim3((unsigned)(nrows * nchunks)), dim3(kAccThreads), 0, s, target, ld,
+                       batch_stride, K, vocab, nchunks, inv_t, ws);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_accept_decide, dim3((unsigned)batch), dim3(kAccThreads), 0, s, target, ld, batch_stride, tokens,

@@ -154,6 +154,18 @@ __device__ __forceinline__ int bitonic_stage_i32(int x) {
   return cmpx_i32(x, row_partner_i32<J>(x), ((i & J) == 0) == desc);
 }
 
+// Maximum of the lanes' values over the whole wave (DPP within each 16-lane row, then
+// the four row results through readlane); every lane gets it.
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, dpp_i32<0xb1>(x));                                      // quad_perm [1,0,3,2]
+  x = max(x, dpp_i32<0x4e>(x));                                      // quad_perm [2,3,0,1]
+  x = max(x, dpp_i32<0x141>(x));                                     // row_half_mirror
+  x = max(x, dpp_i32<0x140>(x));                                     // row_mirror
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return max(a, b);
+}
+
 // Half-cleaners at distances 8, 4, 2, 1: sorts, largest first, a bitonic sequence held
 // by each 16-lane row.
 __device__ __forceinline__ int row16_bitonic_sort_i32(int x) {
