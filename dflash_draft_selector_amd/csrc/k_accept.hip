@@ -170,17 +170,26 @@ __global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* 
   for (int w = 1; w < kTopkWaves; ++w) M = max(M, s_red[w]);
   const uint32_t mbits = order_to_bits(M);
   const uint32_t mkey = bf16_key(mbits);
-  int best = 0x7fffffff;
+  // Only the vectors holding the maximum reach M - 1: usually one lane of one wave.
+  // Each lane marks its own on the vector unit; a wave with none skips the search.
+  const int nfull = V >> 3;
+  uint32_t q = 0;
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const int v = v0 + tid + k * kTopkThreads;
-    if (best == 0x7fffffff && v < v1 && (vmax[k] > 0x7f80 ? 0x7f80 : vmax[k]) >= M - 1) {
-      for (int e = 0; e < 8; ++e) {
-        const int id = 8 * v + e;
-        if (id < V && bf16_key(elem_bits(d[k], e)) == mkey) {
-          best = id;
-          break;
-        }
+    q |= (v < v1 && (vmax[k] > 0x7f80 ? 0x7f80 : vmax[k]) >= M - 1) ? (1u << k) : 0u;
+  }
+  int best = 0x7fffffff;
+  if (__ballot(q != 0u) != 0ull) {
+#pragma unroll
+    for (int k = 0; k < kTopkVecPerThread; ++k) {
+      if ((q >> k) & 1u) {
+        const int v = v0 + tid + k * kTopkThreads;
+        const int lim = v < nfull ? 8 : V - 8 * v;     // logits of the vector that exist
+        int e_hit = 8;
+#pragma unroll
+        for (int e = 7; e >= 0; --e) e_hit = (e < lim && bf16_key(elem_bits(d[k], e)) == mkey) ? e : e_hit;
+        if (e_hit < 8) best = min(best, 8 * v + e_hit);
       }
     }
   }
@@ -220,11 +229,25 @@ __global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* 
   }
 }
 
+constexpr int kMaxStatRows = DFLASH2_MAX_K + 1;
+
 struct DecideShared {
-  float row_max[DFLASH2_MAX_K + 1];     // merged statistics of the request's rows
-  float row_sum[DFLASH2_MAX_K + 1];     // NaN: a non-finite row
-  int row_arg[DFLASH2_MAX_K + 1];       // greedy: the row argmax
-  int status;
+  // the request's inputs, loaded once at entry
+  int tok[DFLASH2_MAX_K];
+  int cand[DFLASH2_MAX_K * kNC];
+  float q[DFLASH2_MAX_K * kNC];
+  uint32_t xbits[DFLASH2_MAX_K];          // target logit (bits) of each drafted token
+  uint32_t cbits[DFLASH2_MAX_K * kNC];    // target logit (bits) of each candidate
+  union {
+    struct {
+      float max[kMaxStatRows * kAccMaxChunks];
+      float sum[kMaxStatRows * kAccMaxChunks];
+    } st;                                 // sampled: chunk statistics of the request's rows
+    unsigned long long arg[kMaxStatRows * kMaxChunks];   // greedy: chunk argmax composites
+  } cs;
+  float row_max[kMaxStatRows];            // merged statistics of the request's rows
+  float row_sum[kMaxStatRows];            // NaN: a non-finite row
+  int row_arg[kMaxStatRows];              // greedy: the row argmax
   int tstar;
   int ids_bad;
   int q_bad;
@@ -237,19 +260,10 @@ struct DecideShared {
   int ncl;
   int cl_id[kNC];
   float cl_qf[kNC];
+  float cl_p[kNC];
   float R[kAccMaxChunks];
   float tsum[kAccThreads];
 };
-
-// Weight of logit `id` of the draw: p, or max(0, p - q) when id is a candidate.
-__device__ __forceinline__ float draw_weight(uint32_t bits, int id, bool is_cand, float m, float c2, float invZ,
-                                             const DecideShared& sm) {
-  const float p = tweight(bf16_to_f32(bits), m, c2) * invZ;
-  if (!is_cand) return p;
-  float qf = 0.f;
-  for (int i = 0; i < sm.ncl; ++i) qf = sm.cl_id[i] == id ? sm.cl_qf[i] : qf;
-  return fmaxf(p - qf, 0.f);
-}
 
 // Result of wave_find_crossing, the same in every lane of the wave.
 struct Crossing {
@@ -300,23 +314,28 @@ __device__ __forceinline__ Crossing wave_find_crossing(const float* vals, int n,
   return cr;
 }
 
-// Inverse-CDF draw from row `r` (stats index) of the target, whose merged max and sum
-// are m and Z: weights p (residual == false) or max(0, p - q) with q supported on the
-// request's candidates of that position.  Block-wide; returns the token id (valid in
-// every thread), or -1 for a residual without mass.
-__device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restrict__ rowp, int r, float m, float Z, int V, int nchunks,
-                             float c2, float u, bool residual, const int32_t* __restrict__ cand,
-                             const float* __restrict__ qrow, const AcceptWs& ws, DecideShared& sm) {
+// Inverse-CDF draw from target row t of the request (row pointer rowp), whose merged
+// max and sum are m and Z: weights p (residual == false) or max(0, p - q) with q
+// supported on the request's candidates of position t (in LDS).  Block-wide; returns
+// the token id (valid in every thread), or -1 for a residual without mass.  Inlined
+// at a single call site, so that `sm` stays a known LDS object (ds_* accesses).
+constexpr int kFineVec = kAccChunkVec / kAccThreads;    // 16-byte vectors per thread of a chunk rescan
+constexpr int kFineLen = 8 * kFineVec;                  // logits per thread
+
+__device__ __forceinline__ int draw_from_row(const uint16_t* __restrict__ rowp, int t, float m, float Z,
+                                                       int V, int nchunks, float c2, float u, bool residual,
+                                                       DecideShared& sm) {
   const int tid = threadIdx.x;
   const float invZ = 1.f / Z;
   // residual: the distinct candidate ids with their total draft mass (summed in slot
-  // order), sorted by id -- lane j of wave 0 owns slot j & 15
+  // order) and their p, sorted by id -- lane j of wave 0 owns slot j & 15
   if (tid < kWave) {
     int ncl = 0;
     if (residual) {
       const int j = tid & (kNC - 1);
-      const int id = cand[j];
-      const float qv = qrow[j];
+      const int id = sm.cand[t * kNC + j];
+      const float qv = sm.q[t * kNC + j];
+      const float pv = tweight(bf16_to_f32(sm.cbits[t * kNC + j]), m, c2) * invZ;
       bool first = true;
       float qf = 0.f;
 #pragma unroll
@@ -339,6 +358,7 @@ __device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restric
       if (tid < kNC && first) {
         sm.cl_id[smaller] = id;
         sm.cl_qf[smaller] = qf;
+        sm.cl_p[smaller] = pv;
       }
       ncl = __popcll(fm);
     }
@@ -347,13 +367,13 @@ __device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restric
   __syncthreads();
   // coarse: mass of every chunk, minus the draft's mass at the candidates it holds
   for (int c = tid; c < nchunks; c += kAccThreads) {
-    const float mc = ws.chunk_max[(size_t)r * nchunks + c];
-    float P = mc == -__builtin_inff() ? 0.f : ws.chunk_sum[(size_t)r * nchunks + c] * tweight(mc, m, c2) * invZ;
+    const float mc = sm.cs.st.max[t * nchunks + c];
+    float P = mc == -__builtin_inff() ? 0.f : sm.cs.st.sum[t * nchunks + c] * tweight(mc, m, c2) * invZ;
     const int e0 = 8 * chunk_begin(V, nchunks, c);
     const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
     for (int i = 0; i < sm.ncl; ++i) {
       const int id = sm.cl_id[i];
-      if (id >= e0 && id < e1) P -= fminf(tweight(bf16_to_f32(rowp[id]), m, c2) * invZ, sm.cl_qf[i]);
+      if (id >= e0 && id < e1) P -= fminf(sm.cl_p[i], sm.cl_qf[i]);
     }
     sm.R[c] = fmaxf(P, 0.f);
   }
@@ -380,21 +400,26 @@ __device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restric
   }
   __syncthreads();
   if (sm.chunk < 0) return -1;
-  // fine: rescan the chosen chunk; thread i owns a contiguous run of L <= 64 logits,
-  // loaded once into registers
+  // fine: rescan the chosen chunk; thread i owns a contiguous run of L <= kFineLen
+  // logits.  All its loads go out at once (a vector not wholly inside the chunk reads
+  // the chunk's first vector and is replaced), and its weights stay in registers.
   const int c = sm.chunk;
   const int e0 = 8 * chunk_begin(V, nchunks, c);
   const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
   const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;
   const int a0 = e0 + tid * L;
-  u32x4 raw[8];
+  u32x4 raw[kFineVec];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kFineVec; ++k) {
     const int base = a0 + 8 * k;
-    raw[k] = (u32x4){0u, 0u, 0u, 0u};
-    if (8 * k < L && base + 8 <= e1) {
-      raw[k] = *reinterpret_cast<const u32x4*>(rowp + base);
-    } else if (8 * k < L && base < e1) {
+    const bool full = 8 * k < L && base + 8 <= e1;
+    raw[k] = *reinterpret_cast<const u32x4*>(rowp + (full ? base : e0));
+    if (!full) raw[k] = (u32x4){0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < kFineVec; ++k) {
+    const int base = a0 + 8 * k;
+    if (8 * k < L && base < e1 && base + 8 > e1) {     // the row's ragged last vector
       uint32_t w4[4] = {0u, 0u, 0u, 0u};
       for (int e = 0; e < 8 && base + e < e1; ++e) w4[e >> 1] |= (uint32_t)rowp[base + e] << ((e & 1) * 16);
       raw[k] = (u32x4){w4[0], w4[1], w4[2], w4[3]};
@@ -406,15 +431,30 @@ __device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restric
     const int off = sm.cl_id[i] - a0;
     if (off >= 0 && off < L) cmask |= 1ull << off;
   }
+  // weights p of every logit, branch-free; then, only in the threads that need it,
+  // zero the logits outside the chunk and replace candidates' weights by max(0, p - q)
+  float w[kFineLen];
+#pragma unroll
+  for (int k = 0; k < kFineVec; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[8 * k + e] = tweight(bf16_to_f32(elem_bits(raw[k], e)), m, c2) * invZ;
+  if (!(L == kFineLen && a0 + kFineLen <= e1)) {
+#pragma unroll
+    for (int off = 0; off < kFineLen; ++off)
+      if (!(off < L && a0 + off < e1)) w[off] = 0.f;
+  }
+  if (cmask != 0ull) {
+#pragma unroll
+    for (int off = 0; off < kFineLen; ++off)
+      if ((cmask >> off) & 1ull) {
+        float qf = 0.f;
+        for (int i = 0; i < sm.ncl; ++i) qf = sm.cl_id[i] == a0 + off ? sm.cl_qf[i] : qf;
+        w[off] = fmaxf(w[off] - qf, 0.f);
+      }
+  }
   float tsum = 0.f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int off = 8 * k + e;
-      if (8 * k < L && a0 + off < e1)
-        tsum += draw_weight(elem_bits(raw[k], e), a0 + off, (cmask >> off) & 1ull, m, c2, invZ, sm);
-    }
+  for (int off = 0; off < kFineLen; ++off) tsum += w[off];
   sm.tsum[tid] = tsum;
   __syncthreads();
   if (tid < kWave) {
@@ -427,22 +467,18 @@ __device__ __attribute__((noinline)) int draw_from_row(const uint16_t* __restric
   }
   __syncthreads();
   if (tid == sm.who) {
-    // the same weights again, in the same order, now with the running sum
+    // the same weights, in the same order, now with the running sum
     float run = sm.before;
     int pick = -1, lastp = -1;
     const bool take_last = sm.last != 0;
+    const float rem = sm.rem;
+    // (weights outside the chunk are 0: they neither cross nor count as positive)
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int off = 8 * k + e;
-        if (8 * k < L && a0 + off < e1) {
-          const float w = draw_weight(elem_bits(raw[k], e), a0 + off, (cmask >> off) & 1ull, m, c2, invZ, sm);
-          run += w;
-          if (pick < 0 && !take_last && sm.rem < run) pick = a0 + off;
-          if (w > 0.f) lastp = a0 + off;
-        }
-      }
+    for (int off = 0; off < kFineLen; ++off) {
+      run += w[off];
+      if (pick < 0 && !take_last && rem < run) pick = a0 + off;
+      if (w[off] > 0.f) lastp = a0 + off;
+    }
     sm.pick = pick >= 0 ? pick : lastp;
   }
   __syncthreads();
@@ -466,58 +502,81 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   int32_t* out_b = out_tokens + (size_t)b * (K + 1);
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const float c2 = inv_t * kLog2e;
+  const bool sampled = inv_t != 0.f;
 
+  // ---- everything the decision reads, in at most two dependent memory round trips ----
+  for (int e = tid; e < K * kNC; e += kAccThreads) {
+    const int id = cand_b[e];
+    sm.cand[e] = id;
+    if (sampled) {
+      sm.q[e] = q[(size_t)b * K * kNC + e];
+      const int idc = id < 0 ? 0 : (id >= V ? V - 1 : id);          // read in bounds; flagged below
+      sm.cbits[e] = tb[(size_t)(e / kNC) * ld + idc];
+    }
+  }
+  for (int e = tid; e < K; e += kAccThreads) {
+    const int x = tok_b[e];
+    sm.tok[e] = x;
+    if (sampled) sm.xbits[e] = tb[(size_t)e * ld + (x < 0 ? 0 : (x >= V ? V - 1 : x))];
+  }
+  const int nst = (K + 1) * nchunks;
+  const size_t s0 = (size_t)rbase * nchunks;
+  for (int e = tid; e < nst; e += kAccThreads) {
+    if (sampled) {
+      sm.cs.st.max[e] = ws.chunk_max[s0 + e];
+      sm.cs.st.sum[e] = ws.chunk_sum[s0 + e];
+    } else {
+      sm.cs.arg[e] = ws.chunk_arg[s0 + e];
+    }
+  }
   if (tid == 0) {
     sm.ids_bad = 0;
     sm.q_bad = 0;
     sm.tstar = K;
   }
-  // merge the chunk statistics of rows rbase .. rbase + K (one thread per row, chunk order)
+  __syncthreads();
+
+  // ---- merge the chunk statistics of the request's rows (one thread per row, chunk order)
   if (tid <= K) {
-    const size_t c0 = (size_t)(rbase + tid) * nchunks;
-    if (inv_t == 0.f) {
+    const int c0 = tid * nchunks;
+    if (!sampled) {
       unsigned long long a = 0ull;
-#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
-        const unsigned long long x = ws.chunk_arg[c0 + j];
+        const unsigned long long x = sm.cs.arg[c0 + j];
         a = x > a ? x : a;
       }
       sm.row_arg[tid] = rc_id(a);
     } else {
       float m = -__builtin_inff();
       bool bad = false;
-#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
-        const float mj = ws.chunk_max[c0 + j];
+        const float mj = sm.cs.st.max[c0 + j];
         if (__builtin_isnan(mj)) bad = true;
         else m = fmaxf(m, mj);
       }
       float Z = 0.f;
-#pragma unroll 8
       for (int j = 0; j < nchunks; ++j) {
-        const float mj = ws.chunk_max[c0 + j];
-        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += ws.chunk_sum[c0 + j] * tweight(mj, m, c2);
+        const float mj = sm.cs.st.max[c0 + j];
+        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += sm.cs.st.sum[c0 + j] * tweight(mj, m, c2);
       }
       sm.row_max[tid] = m;
       sm.row_sum[tid] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
     }
   }
-  __syncthreads();
   for (int e = tid; e < K * (kNC + 1); e += kAccThreads) {
-    const int id = e < K ? tok_b[e] : cand_b[e - K];
+    const int id = e < K ? sm.tok[e] : sm.cand[e - K];
     if (id < 0 || id >= V) atomicOr(&sm.ids_bad, 1);
   }
+  for (int e = tid; e <= K; e += kAccThreads) out_b[e] = -1;
   __syncthreads();
   const bool ids_bad = sm.ids_bad != 0;
-  for (int e = tid; e <= K; e += kAccThreads) out_b[e] = -1;
 
-  if (inv_t == 0.f) {
-    __syncthreads();
+  if (!sampled) {
     if (tid == 0) {
       int t = 0;
       while (t < K) {
         const int g = sm.row_arg[t];
-        if (tok_b[t] != g) break;
+        if (sm.tok[t] != g) break;
         out_b[t] = g;
         ++t;
       }
@@ -541,14 +600,13 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
 
   // validity of the draft distributions
   if (tid < K) {
-    const float* qr = q + ((size_t)b * K + tid) * kNC;
     float s = 0.f, qx = 0.f;
     bool ok = true;
     for (int j = 0; j < kNC; ++j) {
-      const float v = qr[j];
+      const float v = sm.q[tid * kNC + j];
       ok &= __builtin_isfinite(v) && v >= 0.f;
       s += v;
-      qx += cand_b[tid * kNC + j] == tok_b[tid] ? v : 0.f;
+      qx += sm.cand[tid * kNC + j] == sm.tok[tid] ? v : 0.f;
     }
     ok &= fabsf(s - 1.f) <= 1e-3f;
     if (!ids_bad) ok &= qx > 0.f;
@@ -558,52 +616,38 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   const bool q_bad = sm.q_bad != 0;
   int status = (ids_bad ? 2 : 0) | (q_bad ? 4 : 0);
 
-  if (ids_bad || q_bad) {
-    const float u_res = word_to_uniform(philox4x32_10(0u, (uint32_t)b, 1u, 0u, k0, k1).x1);
-    const int v = draw_from_row(tb, rbase, sm.row_max[0], sm.row_sum[0], V, nchunks, c2, u_res, false, nullptr,
-                                nullptr, ws, sm);
-    if (tid == 0) {
-      out_b[0] = v;
-      n_accepted[b] = 0;
-      if (row_status) row_status[b] = status;
-    }
-    return;
-  }
-
-  // accept tests (all positions at once; the first reject decides)
-  if (tid < K) {
+  // accept tests (all positions at once; the first reject decides); skipped when the
+  // ids or the draft distributions are invalid, which commits one token from p_0
+  const bool fault = ids_bad || q_bad;
+  if (!fault && tid < K) {
     const int t = tid;
-    const int x = tok_b[t];
+    const int x = sm.tok[t];
     float qx = 0.f;
-    const float* qr = q + ((size_t)b * K + t) * kNC;
-    for (int j = 0; j < kNC; ++j) qx += cand_b[t * kNC + j] == x ? qr[j] : 0.f;
-    const float px = tweight(bf16_to_f32(tb[(size_t)t * ld + x]), sm.row_max[t], c2) / sm.row_sum[t];
+    for (int j = 0; j < kNC; ++j) qx += sm.cand[t * kNC + j] == x ? sm.q[t * kNC + j] : 0.f;
+    const float px = tweight(bf16_to_f32(sm.xbits[t]), sm.row_max[t], c2) / sm.row_sum[t];
     const float u_acc = word_to_uniform(philox4x32_10((uint32_t)t, (uint32_t)b, 1u, 0u, k0, k1).x0);
     if (!(u_acc * qx < px)) atomicMin(&sm.tstar, t);
   }
   __syncthreads();
-  const int tstar = sm.tstar;
-  for (int t = tid; t < tstar; t += kAccThreads) out_b[t] = tok_b[t];
+  const int tstar = fault ? 0 : sm.tstar;
+  if (!fault)
+    for (int t = tid; t < tstar; t += kAccThreads) out_b[t] = sm.tok[t];
   const float u_res = word_to_uniform(philox4x32_10((uint32_t)tstar, (uint32_t)b, 1u, 0u, k0, k1).x1);
-  int v;
-  if (tstar < K) {
-    const uint16_t* rowp = tb + (size_t)tstar * ld;
-    const int32_t* cand_t = cand_b + tstar * kNC;
-    const float* q_t = q + ((size_t)b * K + tstar) * kNC;
-    // residual mass: 1 - sum over candidates of min(p, q) is positive after any reject
-    const float m = sm.row_max[tstar], Z = sm.row_sum[tstar];
-    v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, c2, u_res, true, cand_t, q_t, ws, sm);
-    if (v < 0) {
-      status |= 8;
-      v = draw_from_row(rowp, rbase + tstar, m, Z, V, nchunks, c2, u_res, false, nullptr, nullptr, ws, sm);
-    }
-  } else {
-    v = draw_from_row(tb + (size_t)K * ld, rbase + K, sm.row_max[K], sm.row_sum[K], V, nchunks, c2, u_res, false,
-                      nullptr, nullptr, ws, sm);
+  // the residual max(0, p - q) at a reject (p instead when it has no mass), else p of
+  // the bonus row (or of row 0 after a fault)
+  const int trow = fault ? 0 : tstar;
+  bool residual = !fault && tstar < K;
+  const uint16_t* rowp = tb + (size_t)trow * ld;
+  int v = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    v = draw_from_row(rowp, trow, sm.row_max[trow], sm.row_sum[trow], V, nchunks, c2, u_res, residual, sm);
+    if (v >= 0 || !residual) break;
+    status |= 8;
+    residual = false;
   }
   if (tid == 0) {
     out_b[tstar] = v;
-    n_accepted[b] = tstar;
+    n_accepted[b] = fault ? 0 : tstar;
     if (row_status) row_status[b] = status;
   }
 }
