@@ -170,19 +170,24 @@ def main():
                 fn(i)
         return graph
 
-    sel_graph = capture(lambda i: dflash2.select(logits[i], verified, A, Bt, H, 0.0, 0, out=sel))
-    reps_sel = max(1, args.steps // nbuf)
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup // nbuf)):
-            sel_graph.replay()
+    def time_graph(fn, reps, warm):
+        """Microseconds per call of fn, over `reps` replays of a graph of nbuf calls."""
+        graph = capture(fn)
+        with torch.cuda.stream(stream):
+            for _ in range(warm):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps_sel):
-            sel_graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    select_us = e0.elapsed_time(e1) * 1e3 / (reps_sel * nbuf)
+        return e0.elapsed_time(e1) * 1e3 / (reps * nbuf)
+
+    reps_sel = max(1, args.steps // nbuf)
+    select_us = time_graph(lambda i: dflash2.select(logits[i], verified, A, Bt, H, 0.0, 0, out=sel), reps_sel,
+                           max(1, args.warmup // nbuf))
 
     sel_bytes = algorithmic_select_bytes(w.B, w.K, w.V, w.dim)
     achieved = sel_bytes / (select_us * 1e-6) / 1e9
@@ -195,6 +200,33 @@ def main():
     if args.select_only:
         print(json.dumps({"metric": METRIC, "select_us": select_us, "roofline": roofline}))
         return
+
+    # every entry point on the same workload, each as its own graph of nbuf calls
+    sel_t = {k: torch.empty_like(v) for k, v in sel.items()}
+    Hs = torch.empty_like(H)
+    y2 = torch.empty_like(y)
+    comp_fns = {
+        "context_gate": lambda i: dflash2.context_gate(h, Wh, bias, out=Hs),
+        "select_greedy": lambda i: dflash2.select(logits[i], verified, A, Bt, H, 0.0, 0, out=sel_t),
+        "select_sampled_T1": lambda i: dflash2.select(logits[i], verified, A, Bt, H, 1.0, 7, out=sel_t),
+        "select_gated_greedy": lambda i: dflash2.select_gated(logits[i], verified, A, Bt, h, Wh, bias, "sigmoid", 0.0, 0,
+                                                              out=sel_t, H_out=Hs),
+        "conv2tap": lambda i: dflash2.conv2tap(x, xp, taps, y=y2),
+        "spec_accept_greedy": lambda i: dflash2.spec_accept(targets[i], sel["tokens"], sel["cand_idx"], sel["q"], 0.0, 0),
+        "spec_accept_sampled_T1": lambda i: dflash2.spec_accept(targets[i], sel_t["tokens"], sel_t["cand_idx"],
+                                                                sel_t["q"], 1.0, 7),
+    }
+    dflash2.select(logits[0], verified, A, Bt, H, 1.0, 7, out=sel_t)   # a sampled draft for the sampled verify
+    components = {}
+    for name, fn in comp_fns.items():
+        with torch.cuda.stream(stream):
+            for i in range(nbuf):
+                fn(i)
+        torch.cuda.synchronize()
+        if name == "spec_accept_sampled_T1":
+            dflash2.select(logits[0], verified, A, Bt, H, 1.0, 7, out=sel_t)
+            torch.cuda.synchronize()
+        components[name] = round(time_graph(fn, 3, 1), 2)
 
     step_graph = capture(step)
     reps = max(1, args.steps // nbuf)
@@ -240,6 +272,7 @@ def main():
         "select_only": {"positions_per_s": round(positions / (select_us * 1e-6), 1), "avg_launch_us": round(select_us, 3),
                         "hbm_frac": roofline["frac"]},
         "roofline": roofline,
+        "components_us_per_call": components,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
