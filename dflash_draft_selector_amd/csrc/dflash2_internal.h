@@ -48,6 +48,7 @@ struct GateWs {
 };
 int gate_splits(int64_t rows, int64_t hidden, int64_t dim);
 GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim);
+constexpr int kGateBlockThreads = 512;    // threads of a standalone gate work-group
 int64_t gate_grid_blocks(int64_t rows, int64_t hidden, int64_t dim);
 
 struct AcceptWs {

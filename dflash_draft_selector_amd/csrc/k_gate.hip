@@ -1,4 +1,4 @@
-// Context gate kernels: the standalone bf16 path (tiles of gate_dev.h, four waves per
+// Context gate kernels: the standalone bf16 path (tiles of gate_dev.h, eight waves per
 // work-group, then a kernel adding the slices) and the fp32-weight path (plain fp32
 // FMA, one thread per output).
 #include "dflash2_internal.h"
@@ -6,9 +6,10 @@
 
 namespace df2 {
 
-constexpr int kGateThreads = 256;
-constexpr int kGateTargetBlocks = 288;
-constexpr int kGateRound = 4;             // 32-wide steps per wave with loads in flight together
+constexpr int kGateThreads = kGateBlockThreads;
+constexpr int kGateWaves = kGateThreads / 64;
+constexpr int kGateTargetBlocks = 144;
+constexpr int kGateRound = 2;             // 32-wide steps per wave with loads in flight together
 
 static int gate_coltile(int64_t dim) { return dim < 64 ? (int)dim : 64; }
 
@@ -44,13 +45,13 @@ __global__ void __launch_bounds__(kGateThreads) k_gate_bf16(const float* __restr
                                                             const float* __restrict__ bias, int rows, int hidden,
                                                             int dim, int act, int ntiles, int nsplit,
                                                             float* __restrict__ H, float* __restrict__ partial) {
-  __shared__ float red[4 * 16 * 16 * NB];
+  __shared__ float red[kGateWaves * 16 * 16 * NB];
   const int per = ntiles * nsplit;
   const int mt = blockIdx.x / per;
   const int rem = blockIdx.x - mt * per;
   const int nt = rem / nsplit;
   const int split = rem - nt * nsplit;
-  gate_tile<NB, 4, kGateRound>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H, partial);
+  gate_tile<NB, kGateWaves, kGateRound>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H, partial);
 }
 
 // Sum of the slices in slice order, then bias and activation: one thread per output.
