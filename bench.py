@@ -94,6 +94,113 @@ def cpu_baseline(inp, w, budget_s=12.0):
                       f"with {len(os.sched_getaffinity(0))} cores visible"}
 
 
+def per_config_throughput(dflash2, torch, dev, stream, min_bytes=600 << 20):
+    """Every synthetic workload (c0..c4) on the same GPU: the select (and the gated select
+    where the gate weight is bf16), the conv and the verify, each as a graph of calls over
+    enough rotating input buffers to exceed 2x the 256 MB Infinity Cache where a buffer
+    set that large stays within 512 calls (c0 and c1 are smaller: partly cache-resident).
+    The conv rotates its own input sets the same way.  Inputs are drawn on the GPU with
+    the workloads' shapes and distributions (logits
+    N(0, 3^2) in bf16 plus the planted peaks, tables N(0, 1/256), h N(0, 1), W_H
+    N(0, 1/D), conv x N(0, 1) and taps U(-1, 1), target logits N(0, 3^2))."""
+    from dflash_draft_selector_amd import synth
+    out = {}
+    gen = torch.Generator(device=dev)
+    for idx in sorted(synth.WORKLOADS):
+        w = synth.workload(idx)
+        gen.manual_seed(1000 + idx)
+        B, K, V, D, dim = w.B, w.K, w.V, w.D, w.dim
+        row_bytes = B * K * V * 2
+        nb = int(min(512, max(4, -(-min_bytes // row_bytes))))
+
+        def bf16(t):
+            return t.to(torch.bfloat16).view(torch.int16)
+
+        def logits_buf():
+            x = torch.randn((B, K, V), generator=gen, device=dev) * 3.0
+            if w.peak != "none":
+                pidx = torch.randint(0, V, (B, K), generator=gen, device=dev)
+                bump = torch.full((B, K), 8.0, device=dev)
+                if w.peak == "decay":
+                    bump = bump - torch.arange(K, device=dev, dtype=torch.float32)[None, :]
+                x.scatter_add_(2, pidx[..., None], bump[..., None])
+            return bf16(x)
+
+        logits = [logits_buf() for _ in range(nb)]
+        targets = [bf16(torch.randn((B, K + 1, V), generator=gen, device=dev) * 3.0) for _ in range(nb)]
+        tdt = torch.float32 if not w.bf16_params else torch.bfloat16
+        A = (torch.randn((V, dim), generator=gen, device=dev) / 16.0).to(tdt)
+        Bt = (torch.randn((V, dim), generator=gen, device=dev) / 16.0).to(tdt)
+        if w.bf16_params:
+            A, Bt = A.view(torch.int16), Bt.view(torch.int16)
+        h = torch.randn((B, K, D), generator=gen, device=dev)
+        Wh = torch.randn((dim, D), generator=gen, device=dev) * (1.0 / D) ** 0.5
+        Wh = bf16(Wh) if w.bf16_params else Wh
+        bias = torch.zeros(dim, device=dev)
+        verified = torch.randint(0, V, (B,), generator=gen, device=dev, dtype=torch.int32)
+        conv_set = w.sites * B * (K * D + D + K * 2 * (D // w.group)) * 4
+        nbc = int(min(512, max(4, -(-min_bytes // conv_set))))
+        xs = [torch.randn((w.sites, B, K, D), generator=gen, device=dev) for _ in range(nbc)]
+        xps = [torch.randn((w.sites, B, D), generator=gen, device=dev) for _ in range(nbc)]
+        tapss = [torch.rand((w.sites, B, K, 2, D // w.group), generator=gen, device=dev) * 2.0 - 1.0
+                 for _ in range(nbc)]
+        y = torch.empty_like(xs[0])
+        H = dflash2.context_gate(h, Wh, bias)
+        T = w.temperature
+        sel = dflash2.select(logits[0], verified, A, Bt, H, T, w.walk_seed)
+        Hc = torch.empty_like(H)
+        fns = {"context_gate": lambda i: dflash2.context_gate(h, Wh, bias, out=Hc),
+               "select": lambda i: dflash2.select(logits[i], verified, A, Bt, H, T, w.walk_seed, out=sel),
+               "conv2tap": lambda i: dflash2.conv2tap(xs[i], xps[i], tapss[i], group=w.group, y=y),
+               "spec_accept": lambda i: dflash2.spec_accept(targets[i], sel["tokens"], sel["cand_idx"], sel["q"], T,
+                                                            w.walk_seed)}
+        if w.bf16_params:
+            Hg = torch.empty_like(H)
+            fns["select_gated"] = lambda i: dflash2.select_gated(logits[i], verified, A, Bt, h, Wh, bias, "sigmoid", T,
+                                                                 w.walk_seed, out=sel, H_out=Hg)
+        res = {"B": B, "K": K, "V": V, "hidden": D, "temperature": T, "rotating_buffers": nb,
+               "conv_rotating_sets": nbc}
+        for name, fn in fns.items():
+            n = nbc if name == "conv2tap" else (16 if name == "context_gate" else nb)
+            with torch.cuda.stream(stream):
+                for i in range(n):
+                    fn(i)
+            torch.cuda.synchronize()
+            if name == "spec_accept":
+                dflash2.select(logits[0], verified, A, Bt, H, T, w.walk_seed, out=sel)
+                torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(i)
+            reps = max(2, 64 // n)
+            with torch.cuda.stream(stream):
+                g.replay()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+            res[name + "_us"] = round(us, 2)
+        tb = 4 if not w.bf16_params else 2
+        sel_bytes = algorithmic_select_bytes(B, K, V, dim, table_bytes=tb)
+        res["select_positions_per_s"] = round(B * K / (res["select_us"] * 1e-6), 1)
+        res["select_hbm_frac"] = round(sel_bytes / (res["select_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        conv_bytes = w.sites * B * (K * D * 4 * 2 + K * 2 * (D // w.group) * 4 + D * 4)
+        gate_bytes = B * K * D * 4 + dim * D * (2 if w.bf16_params else 4) + B * K * dim * 4
+        res["context_gate_hbm_frac"] = round(gate_bytes / (res["context_gate_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        res["context_gate_tflops"] = round(2.0 * B * K * dim * D / (res["context_gate_us"] * 1e-6) / 1e12, 2)
+        res["conv2tap_hbm_frac"] = round(conv_bytes / (res["conv2tap_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        ver_bytes = B * (K + 1) * V * 2
+        res["spec_accept_hbm_frac"] = round(ver_bytes / (res["spec_accept_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        out[w.name] = res
+        del logits, targets, xs, xps, tapss
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +208,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=34)
     ap.add_argument("--nbuf", type=int, default=17)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload throughput table")
     ap.add_argument("--select-only", action="store_true", help="time only the select graph (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 1 GiB buffer three times (a kernel of known traffic, to scale memory counters)")
@@ -275,6 +383,8 @@ def main():
         "components_us_per_call": components,
         "wall_s": round(wall, 3),
     }
+    if not args.no_configs:
+        result["per_config"] = per_config_throughput(dflash2, torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(result), flush=True)
