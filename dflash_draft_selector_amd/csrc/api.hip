@@ -115,8 +115,7 @@ dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dty
   if (rows < 1 || rows > ((int64_t)1 << 30) || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24) ||
       !pow2_in(dim, 16, 1024))
     return DFLASH2_ERR_SHAPE;
-  if (!items_ok((rows * dim + 255) / 256, 256) ||
-      (w_dtype == DFLASH2_BF16 && !items_ok(gate_grid_blocks(rows, hidden, dim), kGateBlockThreads)))
+  if (!items_ok((rows * dim + 255) / 256, 256) || !items_ok(gate_grid_blocks(rows, hidden, dim), kGateBlockThreads))
     return DFLASH2_ERR_SHAPE;
   if (!aligned16(h) || !aligned16(w_h)) return DFLASH2_ERR_ALIGN;
   GateWs ws;

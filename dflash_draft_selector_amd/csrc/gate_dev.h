@@ -109,6 +109,78 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
   }
 }
 
+// fp32 weight: the same tiling on v_mfma_f32_16x16x4f32 with 16-wide steps of hidden.
+// In step st lane l loads h[row][16 st + 4 g .. + 3] and W[col][16 st + 4 g .. + 3]
+// (g = l / 16, row / col = l % 16 of the tile) and feeds component j of both to MFMA j,
+// so the four MFMAs of a step contract over all 16 of its hidden indices (a permutation
+// of the sum, exact up to fp32 rounding order).
+template <int NB, int NW, int ROUND>
+__device__ __forceinline__ void gate_tile_f32(const float* __restrict__ h, const float* __restrict__ w,
+                                              const float* __restrict__ bias, int rows, int hidden, int dim,
+                                              int act, int mt, int nt, int split, int nsplit, float* red,
+                                              float* __restrict__ H, float* __restrict__ partial) {
+  constexpr int kCols = 16 * NB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int nsteps = (hidden + 15) / 16;
+  const int s0 = (int)((long long)nsteps * split / nsplit), s1 = (int)((long long)nsteps * (split + 1) / nsplit);
+
+  const int arow = mt * 16 + r16;
+  const bool arow_ok = arow < rows;
+  const float* hrow = h + (size_t)(arow_ok ? arow : 0) * hidden;
+  const float* wcol[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) wcol[j] = w + (size_t)(nt * kCols + j * 16 + r16) * hidden;
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int base = s0 + wv; base < s1; base += NW * ROUND) {
+    f32x4 x[ROUND];
+    f32x4 y[ROUND][NB];
+#pragma unroll
+    for (int i = 0; i < ROUND; ++i) {
+      const int st = base + NW * i;
+      const int k = st * 16 + g * 4;
+      const bool kok = st < s1 && k < hidden;
+      x[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (kok && arow_ok) x[i] = *reinterpret_cast<const f32x4*>(hrow + k);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        y[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (kok) y[i][j] = *reinterpret_cast<const f32x4*>(wcol[j] + k);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ROUND; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[i][c], y[i][j][c], acc[j], 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wv * 16 + 4 * g + r) * kCols + j * 16 + r16] = acc[j][r];
+  __syncthreads();
+  for (int e = tid; e < 16 * kCols; e += NW * 64) {
+    const int rr = e / kCols, c = e - rr * kCols;
+    const int row = mt * 16 + rr;
+    if (row >= rows) continue;
+    const int n = nt * kCols + c;
+    float sum = red[rr * kCols + c];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) sum += red[(v * 16 + rr) * kCols + c];
+    if (H != nullptr && nsplit == 1)
+      H[(size_t)row * dim + n] = gate_act(sum + (bias ? bias[n] : 0.f), act);
+    else
+      partial[((size_t)split * rows + row) * dim + n] = sum;
+  }
+}
+
 // Gate value of (row, n) from the nsplit partial sums, added in slice order.  Loads
 // go out sixteen at a time, so up to sixteen slices cost one memory round trip.
 __device__ __forceinline__ float gate_finish(const float* __restrict__ partial, const float* __restrict__ bias,

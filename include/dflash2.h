@@ -96,7 +96,7 @@ dflash2_status dflash2_topk16(const uint16_t* logits, int64_t rows, int64_t voca
  * h        float [rows, hidden].
  * w_h      [dim, hidden] in w_dtype.  With DFLASH2_BF16 each h value is first rounded
  *          to bf16 (nearest, ties to even) and the product runs on bf16 MFMA with
- *          fp32 accumulation; with DFLASH2_F32 it runs in fp32.
+ *          fp32 accumulation; with DFLASH2_F32 it runs on fp32 MFMA.
  * bias     float [dim] or NULL (= 0).
  * H        float [rows, dim].
  * Errors: NULL pointers, rows < 1, hidden < 8 or hidden % 8 != 0, dim not a power of

@@ -122,7 +122,8 @@ def test_context_gate(d2, wl):
 
 def test_context_gate_ragged(d2):
     rng = np.random.default_rng(4)
-    for rows, hidden, dim in ((1, 8, 16), (17, 520, 64), (33, 1000, 128), (5, 4096, 1024)):
+    for rows, hidden, dim in ((1, 8, 16), (17, 520, 64), (33, 1000, 128), (5, 4096, 1024), (300, 200, 128),
+                              (257, 1032, 256)):
         h = rng.standard_normal((rows, hidden)).astype(np.float32)
         w = (rng.standard_normal((dim, hidden)) / np.sqrt(hidden)).astype(np.float32)
         wb = synth.f32_to_bf16_bits(w)
@@ -295,6 +296,29 @@ def test_select_gated_ragged(d2):
             a, b = cpu(out[k]), cpu(ref[k])
             np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                           b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+
+
+def test_select_gated_many_rows(d2):
+    """The gated select at c3's 960 rows: H_out within tolerance on
+    sampled rows, and every output bit-identical to dflash2_select on that H."""
+    import torch
+    w = synth.workload(3)
+    inp = inputs(3)
+    print("gated select c3 (960 rows)", flush=True)
+    A64, B64, Ag, Bg = tables(inp)
+    W64, Wg, _ = gate_w(inp)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    Hout = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=logits.device)
+    out = d2.select_gated(logits, ver, Ag, Bg, to_gpu(inp["h"]), Wg, to_gpu(inp["bias"]), "sigmoid", 0.0, 0,
+                          H_out=Hout)
+    rows = np.r_[0:40, 400:440, 920:960]
+    Href, _, pre_abs = oracle.context_gate(inp["h"].reshape(-1, w.D)[rows], W64, inp["bias"], True)
+    assert_close_scaled(cpu(Hout).reshape(-1, w.dim)[rows], Href, 0.25 * pre_abs, what="gated H c3")
+    ref = d2.select(logits, ver, Ag, Bg, Hout, 0.0, 0)
+    for k in ref:
+        a, b = cpu(out[k]), cpu(ref[k])
+        np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                      b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
 
 
 def test_select_c3_sampled_rows(d2):
