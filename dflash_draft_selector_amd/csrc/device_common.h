@@ -26,13 +26,6 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t b16) {
   return (b16 & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
 }
 
-// Smallest float whose bf16_key is `key` (key 0 -> -inf, i.e. no threshold).
-__device__ __forceinline__ float key_to_float(uint32_t key) {
-  if (key == 0u) return -__builtin_inff();
-  const uint32_t b16 = key >= 0x8000u ? key - 0x8000u : (0x8000u | (0x8000u - key));
-  return __uint_as_float(b16 << 16);
-}
-
 // Round-to-nearest-even fp32 -> bf16 for finite and infinite inputs (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -142,15 +135,6 @@ __device__ __forceinline__ int row16_pick(float s, float inv_t, float u, float* 
 
 // ---- wave / block helpers ----------------------------------------------------------
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const T other = __shfl_xor(v, o);
-    v = other > v ? other : v;
-  }
-  return v;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -9,6 +9,9 @@
 //                     predecessor slot);
 //   3. k_walk_tables  one block per request: chases the tables from the verified row
 //                     and writes tokens, slots and q.
+// The gated step (dflash2_select_gated) launches k_chunk_gate in place of stage 1 (the
+// same blocks plus the context gate's tiles as extra work-groups), and its stage 2
+// adds each row's gate slices before the scores.
 // Kernel boundaries replace every cross-work-group hand-off, so no work-group ever
 // waits for another and no workspace counter exists.
 #include "dflash2_internal.h"

@@ -69,11 +69,6 @@ __device__ __forceinline__ uint32_t elem_bits(const u32x4& d, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-__device__ __forceinline__ unsigned long long lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
