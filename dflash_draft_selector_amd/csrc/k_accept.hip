@@ -205,15 +205,18 @@ __global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* 
     if (tid == 0) chunk_arg[ci] = make_rc(mkey, (unsigned)best, mbits);
     return;
   }
+  // exact composite maximum (only when the block maximum was +NaN): a rolled loop that
+  // re-reads the chunk, to keep the common path's code small
   unsigned long long comp = 0ull;
-#pragma unroll
+#pragma unroll 1
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const int v = v0 + tid + k * kTopkThreads;
-#pragma unroll
+    if (v >= v1) break;
+#pragma unroll 1
     for (int e = 0; e < 8; ++e) {
       const int id = 8 * v + e;
-      if (v < v1 && id < V) {
-        const uint32_t bits = elem_bits(d[k], e);
+      if (id < V) {
+        const uint32_t bits = rowp[id];
         const unsigned long long x = make_rc(bf16_key(bits), (unsigned)id, bits);
         comp = x > comp ? x : comp;
       }

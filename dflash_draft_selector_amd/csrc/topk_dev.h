@@ -224,24 +224,29 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ row, int
                                            u32x4 (&d)[kTopkVecPerThread]) {
   const int nfull = V >> 3;
   const u32x4* __restrict__ rowv = reinterpret_cast<const u32x4*>(row);
+  // whole vectors, branch-free: a slot past the chunk or the row reads the chunk's first
+  // vector (always whole) and is replaced by -NaN padding
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const int v = v0 + (int)threadIdx.x + k * kTopkThreads;
-    if (v < v1 && v < nfull) {
-      d[k] = __builtin_nontemporal_load(rowv + v);
-    } else {
-      uint32_t w4[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // -NaN padding
-      if (v < v1) {                                                            // ragged last vector
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (8 * v + e < V) {
-            const uint32_t b = row[8 * v + e];
-            w4[e >> 1] = (e & 1) ? ((w4[e >> 1] & 0xffffu) | (b << 16)) : ((w4[e >> 1] & 0xffff0000u) | b);
-          }
-        }
-      }
-      d[k] = (u32x4){w4[0], w4[1], w4[2], w4[3]};
+    const bool whole = v < v1 && v < nfull;
+    d[k] = __builtin_nontemporal_load(rowv + (whole ? v : v0));
+    if (!whole) d[k] = (u32x4){0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  }
+  // the row's ragged last vector (V % 8 != 0), in the one lane that owns it
+  const int vr = nfull - v0;
+  if ((V & 7) != 0 && nfull < v1 && vr >= 0 && (int)threadIdx.x == vr % kTopkThreads) {
+    uint32_t w4[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+#pragma unroll 1
+    for (int e = 0; e < (V & 7); ++e) {
+      const uint32_t b = row[8 * nfull + e];
+      w4[e >> 1] = (e & 1) ? ((w4[e >> 1] & 0xffffu) | (b << 16)) : ((w4[e >> 1] & 0xffff0000u) | b);
     }
+    const u32x4 x = (u32x4){w4[0], w4[1], w4[2], w4[3]};
+    const int kr = vr / kTopkThreads;
+#pragma unroll
+    for (int k = 0; k < kTopkVecPerThread; ++k)
+      if (k == kr) d[k] = x;
   }
 }
 
