@@ -188,7 +188,10 @@ __global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* 
         const int lim = v < nfull ? 8 : V - 8 * v;     // logits of the vector that exist
         int e_hit = 8;
 #pragma unroll
-        for (int e = 7; e >= 0; --e) e_hit = (e < lim && bf16_key(elem_bits(d[k], e)) == mkey) ? e : e_hit;
+        for (int e = 7; e >= 0; --e) {
+          const int hit = (int)(e < lim) & (int)(bf16_key(elem_bits(d[k], e)) == mkey);   // no short circuit
+          e_hit = hit ? e : e_hit;
+        }
         if (e_hit < 8) best = min(best, 8 * v + e_hit);
       }
     }
