@@ -52,12 +52,11 @@ constexpr int kGateBlockThreads = 512;    // threads of a standalone gate work-g
 int64_t gate_grid_blocks(int64_t rows, int64_t hidden, int64_t dim);
 
 struct AcceptWs {
-  float* chunk_max;               // [nrows][nchunks]; NaN: a non-finite chunk
-  float* chunk_sum;               // [nrows][nchunks]
+  float* chunk_max;               // [nrows][8 * nchunks] sub-chunk max; NaN: non-finite
+  float* chunk_sum;               // [nrows][8 * nchunks] sub-chunk sum of weights
   unsigned long long* chunk_arg;  // [nrows][nchunks] (greedy)
 };
 AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab);
-int64_t accept_stats_blocks(int64_t nrows, int64_t vocab);
 
 hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld, int32_t* cand_idx,
                          float* cand_val, int32_t* row_status, TopkWs ws, hipStream_t s);

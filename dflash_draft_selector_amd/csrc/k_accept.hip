@@ -2,13 +2,15 @@
 // accept with min(1, p/q), on a reject resample from max(0, p - q); all-greedy keeps
 // the prefix match.  pegainfer issue "DFlash 2 proposer", "Proposal", phase 3).
 //
-// Pass 1: split-vocabulary statistics of every target row -- per chunk the max and
-// the sum of exp((l - max)/T) (k_accept_stats), or the chunk argmax when T == 0
-// (k_greedy_argmax).
-// Pass 2 (k_accept_decide): one block per request merges its rows' chunk statistics
-// (fixed chunk order), runs the accept tests, then draws the committed token by
-// inverse CDF: the chunk is found from the chunk masses (minus the draft's mass at its
-// candidates), and only that chunk is rescanned.
+// Pass 1 streams every target row once, split like the top-16 stream (512-thread
+// work-groups, 19 loads of 16 bytes in flight per lane).  T > 0 (k_accept_stats): each
+// wave owns a contiguous sub-chunk of its work-group's vectors and writes the sub-chunk's
+// max and sum of exp((l - max)/T).  T == 0 (k_greedy_argmax): the chunk argmax.
+// Pass 2, one work-group per request.  Greedy (k_greedy_decide, one wave): the row
+// argmaxes and the prefix match.  Sampled (k_accept_decide): one wave merges the rows'
+// statistics (fixed sub-chunk order), runs the accept tests and finds the sub-chunk in
+// which the inverse-CDF draw lands (sub-chunk masses minus the draft's mass at its
+// candidates); the whole work-group then rescans that one sub-chunk.
 #include "device_common.h"
 #include "dflash2.h"
 #include "dflash2_internal.h"
@@ -16,23 +18,28 @@
 
 namespace df2 {
 
-constexpr int kAccThreads = 256;
-constexpr int kAccVecPerThread = 8;                          // 8 x 16 B loads in flight per lane
-constexpr int kAccChunkVec = kAccThreads * kAccVecPerThread;  // 2048 vectors = 16384 logits
-constexpr int kAccMaxChunks = 32;                            // vocab <= 2^19
+constexpr int kSubPerChunk = kTopkWaves;                  // one contiguous sub-chunk per wave
+constexpr int kMaxSub = kMaxChunks * kSubPerChunk;       // sub-chunks of the longest row
+constexpr int kSubVec = kTopkVecPerThread * kWave;       // 1216 vectors: the longest sub-chunk
+static_assert(kChunkVec == kSubPerChunk * kSubVec, "a chunk is its waves' sub-chunks");
+static_assert(kMaxSub <= kWave, "one sub-chunk per lane of the deciding wave");
 
-__host__ __device__ __forceinline__ int acc_num_chunks(long long vocab) {
-  const long long nvec = (vocab + 7) / 8;
-  return (int)((nvec + kAccChunkVec - 1) / kAccChunkVec);
+// First vector of sub-chunk s = 8c + j (wave j's share of chunk c); s = 8 * nchunks gives
+// the row's end.  Every sub-chunk but a chunk's last has ceil(len / 8) vectors.
+__host__ __device__ __forceinline__ int sub_begin(int V, int nchunks, int s) {
+  const int c = s / kSubPerChunk, j = s - c * kSubPerChunk;
+  const int a = chunk_begin(V, nchunks, c);
+  if (j == 0) return a;
+  const int b = chunk_begin(V, nchunks, c + 1);
+  const int span = (b - a + kSubPerChunk - 1) / kSubPerChunk;
+  return a + j * span < b ? a + j * span : b;
 }
-
-int64_t accept_stats_blocks(int64_t nrows, int64_t vocab) { return nrows * acc_num_chunks(vocab); }
 
 AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab) {
   AcceptWs w;
-  const size_t n = (size_t)nrows * acc_num_chunks(vocab);
-  w.chunk_max = c.take<float>(n);
-  w.chunk_sum = c.take<float>(n);
+  const size_t n = (size_t)nrows * topk_num_chunks(vocab);
+  w.chunk_max = c.take<float>(n * kSubPerChunk);
+  w.chunk_sum = c.take<float>(n * kSubPerChunk);
   w.chunk_arg = c.take<unsigned long long>(n);
   return w;
 }
@@ -42,69 +49,58 @@ __device__ __forceinline__ float order_to_float(int s) { return bf16_to_f32(orde
 constexpr float kLog2e = 1.44269504088896341f;
 
 // exp((l - m) / T) formed as 2^((l - m) * c2) with c2 = log2(e) / T: one v_exp_f32 per
-// weight.  Every weight of the target distribution (chunk sums, the accept test and
+// weight.  Every weight of the target distribution (sub-chunk sums, the accept test and
 // the draws) is formed this one way.
 __device__ __forceinline__ float tweight(float l, float m, float c2) { return __builtin_amdgcn_exp2f((l - m) * c2); }
 
-template <typename T>
-__device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
-  // fixed-order block reduction over 4 waves (deterministic)
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const T other = __shfl_xor(v, o);
-    v = is_max ? (other > v ? other : v) : v + other;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  T r = red[0];
-  for (int w = 1; w < kAccThreads / 64; ++w) r = is_max ? (red[w] > r ? red[w] : r) : r + red[w];
-  return r;
-}
-
-// Sampled statistics (T > 0) of one chunk of a target row.
-__global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __restrict__ target, int64_t ld,
-                                                              int64_t batch_stride, int K, int V, int nchunks,
-                                                              float inv_t, AcceptWs ws) {
-  __shared__ float s_redf[4];
-  __shared__ int s_redi[4];
-  const int tid = threadIdx.x;
+// ---- sampled pass 1: max and sum of weights of every sub-chunk ------------------------
+// Wave j of work-group (row, c) reads sub-chunk 8c + j: lane l holds its vectors l,
+// l + 64, ... (each load instruction covers 1 KB of the row).  Missing logits read as
+// -inf (weight 0).  A sub-chunk holding +inf or NaN is marked by a NaN max.  No LDS and
+// no barrier: each wave writes its own pair.
+__global__ void __launch_bounds__(kTopkThreads) k_accept_stats(const uint16_t* __restrict__ target, int64_t ld,
+                                                               int64_t batch_stride, int K, int V, int nchunks,
+                                                               float inv_t, AcceptWs ws) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int r = blockIdx.x / nchunks;
   const int c = blockIdx.x - r * nchunks;
   const int b = batch_stride == 0 ? 0 : r / (K + 1);
   const int t = batch_stride == 0 ? r : r - b * (K + 1);
   const uint16_t* rowp = target + (size_t)b * batch_stride + (size_t)t * ld;
-  const u32x4* rowv = reinterpret_cast<const u32x4*>(rowp);
-  const int v0 = chunk_begin(V, nchunks, c), v1 = chunk_begin(V, nchunks, c + 1);
+  const u32x4* __restrict__ rowv = reinterpret_cast<const u32x4*>(rowp);
+  const int s = c * kSubPerChunk + wave;
+  const int s0 = sub_begin(V, nchunks, s), s1 = sub_begin(V, nchunks, s + 1);
+  const int safe = chunk_begin(V, nchunks, c);            // the chunk's first vector: whole
   const int nfull = V >> 3;
 
-  u32x4 d[kAccVecPerThread];
+  u32x4 d[kTopkVecPerThread];
 #pragma unroll
-  for (int k = 0; k < kAccVecPerThread; ++k) {
-    const int v = v0 + tid + k * kAccThreads;
-    if (v < v1 && v < nfull) {
-      d[k] = __builtin_nontemporal_load(rowv + v);
-    } else {
-      uint32_t wds[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};   // -inf padding
-      if (v < v1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (8 * v + e < V) {
-            const uint32_t bb = rowp[8 * v + e];
-            wds[e >> 1] = (e & 1) ? ((wds[e >> 1] & 0xffffu) | (bb << 16)) : ((wds[e >> 1] & 0xffff0000u) | bb);
-          }
-        }
-      }
-      d[k] = (u32x4){wds[0], wds[1], wds[2], wds[3]};
+  for (int k = 0; k < kTopkVecPerThread; ++k) {
+    const int v = s0 + lane + k * kWave;
+    const bool whole = v < s1 && v < nfull;
+    d[k] = __builtin_nontemporal_load(rowv + (whole ? v : safe));
+    if (!whole) d[k] = (u32x4){0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+  }
+  // the row's ragged last vector (V % 8 != 0), in the one lane that owns it
+  const int vr = nfull - s0;
+  if ((V & 7) != 0 && nfull < s1 && vr >= 0 && lane == (vr & (kWave - 1))) {
+    uint32_t w4[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+#pragma unroll 1
+    for (int e = 0; e < (V & 7); ++e) {
+      const uint32_t bb = rowp[8 * nfull + e];
+      w4[e >> 1] = (e & 1) ? ((w4[e >> 1] & 0xffffu) | (bb << 16)) : ((w4[e >> 1] & 0xffff0000u) | bb);
     }
+    const u32x4 x = (u32x4){w4[0], w4[1], w4[2], w4[3]};
+    const int kr = vr / kWave;
+#pragma unroll
+    for (int k = 0; k < kTopkVecPerThread; ++k)
+      if (k == kr) d[k] = x;
   }
 
-  const size_t ci = (size_t)r * nchunks + c;
-  // signed-order max / min (to find +inf and NaN) and the chunk maximum
+  // signed-order max and min (to find +inf and NaN) of the sub-chunk
   int smax = -32768, smin = 32767;
 #pragma unroll
-  for (int k = 0; k < kAccVecPerThread; ++k) {
+  for (int k = 0; k < kTopkVecPerThread; ++k) {
     const s16x2 a = signed_order2(d[k].x), bq = signed_order2(d[k].y);
     const s16x2 cq = signed_order2(d[k].z), dq = signed_order2(d[k].w);
     const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, bq), __builtin_elementwise_max(cq, dq));
@@ -113,26 +109,27 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_stats(const uint16_t* __
     const int lo = mn.x < mn.y ? (int)mn.x : (int)mn.y;
     smin = lo < smin ? lo : smin;
   }
-  smax = block_reduce<int>(smax, s_redi, true);
-  smin = -block_reduce<int>(-smin, s_redi, true);
+  smax = wave_max_i32(smax);
+  smin = -wave_max_i32(-smin);
   const bool nonfinite = smax >= 32640 || smin < -32641;       // +inf / +NaN, or -NaN
-  const float m_c = order_to_float(smax > 32640 ? 32640 : smax);
+  const float m = order_to_float(smax > 32640 ? 32640 : smax);
   float sum = 0.f;
-  if (!nonfinite && m_c != -__builtin_inff()) {
+  if (!nonfinite && m != -__builtin_inff()) {
     const float c2 = inv_t * kLog2e;
 #pragma unroll
-    for (int k = 0; k < kAccVecPerThread; ++k) {
+    for (int k = 0; k < kTopkVecPerThread; ++k) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        sum += tweight(bf16_lo(d[k][w]), m_c, c2);
-        sum += tweight(bf16_hi(d[k][w]), m_c, c2);
+        sum += tweight(bf16_lo(d[k][w]), m, c2);
+        sum += tweight(bf16_hi(d[k][w]), m, c2);
       }
     }
   }
-  sum = block_reduce<float>(sum, s_redf, false);
-  if (tid == 0) {
-    ws.chunk_max[ci] = nonfinite ? __builtin_nanf("") : m_c;
-    ws.chunk_sum[ci] = sum;
+  sum = wave_sum(sum);
+  if (lane == 0) {
+    const size_t si = (size_t)r * (nchunks * kSubPerChunk) + s;
+    ws.chunk_max[si] = nonfinite ? __builtin_nanf("") : m;
+    ws.chunk_sum[si] = sum;
   }
 }
 
@@ -235,6 +232,67 @@ __global__ void __launch_bounds__(kTopkThreads) k_greedy_argmax(const uint16_t* 
   }
 }
 
+// ---- greedy pass 2: one wave per request ----------------------------------------------
+// Lane t takes the argmax of row t (and lane 0 that of row 64 when K = 64): the maximum
+// of its chunks' composites.  The first position whose draft differs from the argmax
+// ends the prefix; the row argmax there is the committed token.
+__global__ void __launch_bounds__(kWave) k_greedy_decide(const int32_t* __restrict__ tokens,
+                                                         const int32_t* __restrict__ cand_idx, int64_t batch_stride,
+                                                         int K, int V, int nchunks,
+                                                         const unsigned long long* __restrict__ chunk_arg,
+                                                         int32_t* __restrict__ out_tokens,
+                                                         int32_t* __restrict__ n_accepted,
+                                                         int32_t* __restrict__ row_status) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  const int rbase = batch_stride == 0 ? 0 : b * (K + 1);
+  int32_t* out_b = out_tokens + (size_t)b * (K + 1);
+  int g[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = lane + i * kWave;
+    if (row <= K) {
+      const unsigned long long* a = chunk_arg + (size_t)(rbase + row) * nchunks;
+      unsigned long long mx = 0ull;
+#pragma unroll
+      for (int j = 0; j < kMaxChunks; ++j) {
+        const unsigned long long x = j < nchunks ? a[j] : 0ull;
+        mx = x > mx ? x : mx;
+      }
+      g[i] = rc_id(mx);
+    }
+  }
+  bool bad = false;
+  int x = 0;
+  if (lane < K) {
+    x = tokens[(size_t)b * K + lane];
+    bad = x < 0 || x >= V;
+    const int32_t* cb = cand_idx + ((size_t)b * K + lane) * kNC;
+#pragma unroll
+    for (int j = 0; j < kNC; ++j) {
+      const int id = cb[j];
+      bad |= id < 0 || id >= V;
+    }
+  }
+  const bool ids_bad = __ballot(bad) != 0ull;
+  const unsigned long long miss = __ballot(lane < K && x != g[0]);
+  const int tstar = miss != 0ull ? __builtin_ctzll(miss) : K;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = lane + i * kWave;
+    if (row <= K) out_b[row] = row <= tstar ? g[i] : -1;
+  }
+  if (lane == 0) {
+    n_accepted[b] = tstar;
+    if (row_status) row_status[b] = ids_bad ? 2 : 0;
+  }
+}
+
+// ---- sampled pass 2 -------------------------------------------------------------------
+constexpr int kAccThreads = 256;
+constexpr int kAccWaves = kAccThreads / kWave;
+constexpr int kFineVec = (kSubVec + kAccThreads - 1) / kAccThreads;   // 16-byte vectors per thread of a rescan
+constexpr int kFineLen = 8 * kFineVec;                                // logits per thread
 constexpr int kMaxStatRows = DFLASH2_MAX_K + 1;
 
 struct DecideShared {
@@ -244,174 +302,102 @@ struct DecideShared {
   float q[DFLASH2_MAX_K * kNC];
   uint32_t xbits[DFLASH2_MAX_K];          // target logit (bits) of each drafted token
   uint32_t cbits[DFLASH2_MAX_K * kNC];    // target logit (bits) of each candidate
-  union {
-    struct {
-      float max[kMaxStatRows * kAccMaxChunks];
-      float sum[kMaxStatRows * kAccMaxChunks];
-    } st;                                 // sampled: chunk statistics of the request's rows
-    unsigned long long arg[kMaxStatRows * kMaxChunks];   // greedy: chunk argmax composites
-  } cs;
-  float row_max[kMaxStatRows];            // merged statistics of the request's rows
-  float row_sum[kMaxStatRows];            // NaN: a non-finite row
-  int row_arg[kMaxStatRows];              // greedy: the row argmax
-  int tstar;
-  int ids_bad;
-  int q_bad;
+  float smax[kMaxStatRows * kMaxSub];     // sub-chunk statistics of the request's rows
+  float ssum[kMaxStatRows * kMaxSub];
+  // the draw, as the deciding wave leaves it
+  int done;                               // the request is finished (a non-finite row)
+  int trow;                               // the row drawn from
+  int sub;                                // the sub-chunk to rescan
+  float rem;                              // the draw's target minus the mass before it
+  float m, invZ;                          // the drawn row's max and 1 / sum of weights
+  int residual;                           // draw from max(0, p - q) (else from p)
+  int cl_id[kNC];                         // the drawn position's candidates: an id at its
+  float cl_qf[kNC];                       // first slot (else -1) and its total draft mass
+  float wtot[kAccWaves];                  // rescan: the weight of each wave's logits
   int pick;
-  int chunk;
-  int who;
-  int last;
-  float rem;
-  float before;
-  int ncl;
-  int cl_id[kNC];
-  float cl_qf[kNC];
-  float cl_p[kNC];
-  float R[kAccMaxChunks];
-  float tsum[kAccThreads];
 };
 
-// Result of wave_find_crossing, the same in every lane of the wave.
-struct Crossing {
-  int idx;        // first index whose running sum exceeds the target, -1 if none
-  float before;   // the running sum before idx
-  int last;       // last index holding a positive value, -1 if none
-};
-
-// One whole wave over vals[0 .. n) (LDS, non-negative, n <= 256).  Lane l owns
-// vals[4l .. 4l + 3]; its offset is an inclusive scan of the lane sums over lanes, and
-// within the lane the sums run in index order.
-__device__ __forceinline__ Crossing wave_find_crossing(const float* vals, int n, float target) {
-  const int lane = threadIdx.x & 63;
-  float v[4], part[4];
-  float run = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * lane + j;
-    v[j] = i < n ? vals[i] : 0.f;
-    run += v[j];
-    part[j] = run;
-  }
-  float inc = part[3];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  float excl = __shfl_up(inc, 1);
-  if (lane == 0) excl = 0.f;
-  int jhit = 0;
-  while (jhit < 3 && !(target < excl + part[jhit])) ++jhit;
-  const float bef = jhit == 0 ? excl : excl + part[jhit - 1];
-  int jlast = 3;
-  while (jlast > 0 && !(v[jlast] > 0.f)) --jlast;
-  const unsigned long long hit = __ballot(target < excl + part[3]);
-  const unsigned long long pos = __ballot(part[3] > 0.f);
-  Crossing cr = {-1, 0.f, -1};
-  if (hit) {
-    const int src = __builtin_ctzll(hit);
-    cr.idx = 4 * src + __builtin_amdgcn_readlane(jhit, src);
-    cr.before = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bef), src));
-  }
-  if (pos) {
-    const int src = 63 - __builtin_clzll(pos);
-    cr.last = 4 * src + __builtin_amdgcn_readlane(jlast, src);
-  }
-  return cr;
+// Inverse-CDF step over one non-negative value per lane (incl: their inclusive scan):
+// the first lane holding a positive value whose running sum exceeds x (in exact
+// arithmetic the first lane whose running sum exceeds x holds one), or the last positive
+// lane when rounding leaves x at or past the total (x = +inf asks for that).  -1 when no
+// lane is positive.  The whole wave calls it.
+__device__ __forceinline__ int wave_pick_lane(float v, float incl, float x) {
+  const unsigned long long pos = __ballot(v > 0.f);
+  if (pos == 0ull) return -1;
+  const unsigned long long hit = __ballot(x < incl) & pos;
+  return hit != 0ull ? __builtin_ctzll(hit) : 63 - __builtin_clzll(pos);
 }
 
-// Inverse-CDF draw from target row t of the request (row pointer rowp), whose merged
-// max and sum are m and Z: weights p (residual == false) or max(0, p - q) with q
-// supported on the request's candidates of position t (in LDS).  Block-wide; returns
-// the token id (valid in every thread), or -1 for a residual without mass.  Inlined
-// at a single call site, so that `sm` stays a known LDS object (ds_* accesses).
-constexpr int kFineVec = kAccChunkVec / kAccThreads;    // 16-byte vectors per thread of a chunk rescan
-constexpr int kFineLen = 8 * kFineVec;                  // logits per thread
+// Inclusive scan over the wave's lanes (every lane must be active).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
 
-__device__ __forceinline__ int draw_from_row(const uint16_t* __restrict__ rowp, int t, float m, float Z,
-                                                       int V, int nchunks, float c2, float u, bool residual,
-                                                       DecideShared& sm) {
-  const int tid = threadIdx.x;
-  const float invZ = 1.f / Z;
-  // residual: the distinct candidate ids with their total draft mass (summed in slot
-  // order) and their p, sorted by id -- lane j of wave 0 owns slot j & 15
-  if (tid < kWave) {
-    int ncl = 0;
-    if (residual) {
-      const int j = tid & (kNC - 1);
-      const int id = sm.cand[t * kNC + j];
-      const float qv = sm.q[t * kNC + j];
-      const float pv = tweight(bf16_to_f32(sm.cbits[t * kNC + j]), m, c2) * invZ;
-      bool first = true;
-      float qf = 0.f;
+// The scan's exclusive form.  The cross-lane read runs in every lane: a lane that reads
+// from an inactive one gets 0.
+__device__ __forceinline__ float wave_excl_from_incl(float incl) {
+  const float y = __shfl_up(incl, 1);
+  return (threadIdx.x & (kWave - 1)) == 0 ? 0.f : y;
+}
+
+struct CoarsePick {
+  int sub;      // -1: no mass
+  float rem;
+};
+
+// The deciding wave's step over the sub-chunks of row `trow` (lane s owns sub-chunk s):
+// each sub-chunk's mass, less the draft's mass min(p, q) at the candidates it holds when
+// `residual` (cid / csub: lane j & 15 holds slot j, an id at its first slot else -1),
+// then the sub-chunk whose running sum first exceeds u times the total.
+__device__ __forceinline__ CoarsePick coarse_pick(const DecideShared& sm, int trow, int nsub, int V, int nchunks,
+                                                  float m, float invZ, float c2, float u, bool residual, int cid,
+                                                  float csub) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float P = 0.f;
+  if (lane < nsub) {
+    const float mc = sm.smax[trow * nsub + lane];
+    P = mc == -__builtin_inff() ? 0.f : sm.ssum[trow * nsub + lane] * tweight(mc, m, c2) * invZ;
+  }
+  if (residual) {
+    const int e0 = 8 * sub_begin(V, nchunks, lane);
+    const int e1 = min(8 * sub_begin(V, nchunks, lane + 1), V);
 #pragma unroll
-      for (int i = 0; i < kNC; ++i) {
-        const int oi = __shfl(id, i);
-        const float qi = __shfl(qv, i);
-        if (oi == id) {
-          qf += qi;
-          if (i < j) first = false;
-        }
-      }
-      int smaller = 0;
-#pragma unroll
-      for (int i = 0; i < kNC; ++i) {
-        const int oi = __shfl(id, i);
-        const int fi = __shfl(first ? 1 : 0, i);
-        if (fi && oi < id) ++smaller;
-      }
-      const unsigned long long fm = __ballot(tid < kNC && first);
-      if (tid < kNC && first) {
-        sm.cl_id[smaller] = id;
-        sm.cl_qf[smaller] = qf;
-        sm.cl_p[smaller] = pv;
-      }
-      ncl = __popcll(fm);
-    }
-    if (tid == 0) sm.ncl = ncl;
-  }
-  __syncthreads();
-  // coarse: mass of every chunk, minus the draft's mass at the candidates it holds
-  for (int c = tid; c < nchunks; c += kAccThreads) {
-    const float mc = sm.cs.st.max[t * nchunks + c];
-    float P = mc == -__builtin_inff() ? 0.f : sm.cs.st.sum[t * nchunks + c] * tweight(mc, m, c2) * invZ;
-    const int e0 = 8 * chunk_begin(V, nchunks, c);
-    const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
-    for (int i = 0; i < sm.ncl; ++i) {
-      const int id = sm.cl_id[i];
-      if (id >= e0 && id < e1) P -= fminf(sm.cl_p[i], sm.cl_qf[i]);
-    }
-    sm.R[c] = fmaxf(P, 0.f);
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    float Zr = 0.f;
-    for (int c = tid; c < nchunks; c += kWave) Zr += sm.R[c];
-    Zr = wave_sum(Zr);
-    const float target = u * Zr;
-    const Crossing cr = wave_find_crossing(sm.R, nchunks, target);
-    int idx = cr.idx;
-    float before = cr.before;
-    const int last = cr.last;
-    if (tid == 0) {
-      if (idx < 0) {                       // rounding left the target past the total
-        idx = last;
-        before = 0.f;
-        for (int c = 0; c < last; ++c) before += sm.R[c];
-      }
-      sm.chunk = (residual && !(Zr > 0.f)) || idx < 0 ? -1 : idx;   // a residual without mass
-      sm.rem = target - before;
-      sm.pick = -1;
+    for (int i = 0; i < kNC; ++i) {
+      const int id = __shfl(cid, i);
+      const float x = __shfl(csub, i);
+      P -= (id >= e0 && id < e1) ? x : 0.f;
     }
   }
-  __syncthreads();
-  if (sm.chunk < 0) return -1;
-  // fine: rescan the chosen chunk; thread i owns a contiguous run of L <= kFineLen
-  // logits.  All its loads go out at once (a vector not wholly inside the chunk reads
-  // the chunk's first vector and is replaced), and its weights stay in registers.
-  const int c = sm.chunk;
-  const int e0 = 8 * chunk_begin(V, nchunks, c);
-  const int e1 = min(8 * chunk_begin(V, nchunks, c + 1), V);
+  const float R = lane < nsub ? fmaxf(P, 0.f) : 0.f;
+  const float target = u * wave_sum(R);
+  const float incl = wave_incl_scan(R);
+  const float excl = wave_excl_from_incl(incl);
+  CoarsePick cp;
+  cp.sub = wave_pick_lane(R, incl, target);
+  cp.rem = cp.sub < 0 ? 0.f : target - __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), cp.sub < 0 ? 0 : cp.sub));
+  return cp;
+}
+
+// The draw inside sub-chunk sm.sub of row rowp, by the whole work-group: thread i owns a
+// contiguous run of L <= kFineLen logits; every load goes out at once (a vector not wholly
+// inside the sub-chunk reads the row's first vector and is replaced) and the weights stay
+// in registers.  Returns the token id (the same in every thread), -1 if no weight is
+// positive.
+__device__ __forceinline__ int fine_pick(const uint16_t* __restrict__ rowp, int V, int nchunks, float c2,
+                                         DecideShared& sm) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int s = sm.sub;
+  const float m = sm.m, invZ = sm.invZ, rem = sm.rem;
+  const bool residual = sm.residual != 0;
+  const int e0 = 8 * sub_begin(V, nchunks, s);
+  const int e1 = min(8 * sub_begin(V, nchunks, s + 1), V);
   const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;
   const int a0 = e0 + tid * L;
   u32x4 raw[kFineVec];
@@ -419,7 +405,7 @@ __device__ __forceinline__ int draw_from_row(const uint16_t* __restrict__ rowp, 
   for (int k = 0; k < kFineVec; ++k) {
     const int base = a0 + 8 * k;
     const bool full = 8 * k < L && base + 8 <= e1;
-    raw[k] = *reinterpret_cast<const u32x4*>(rowp + (full ? base : e0));
+    raw[k] = *reinterpret_cast<const u32x4*>(rowp + (full ? base : 0));
     if (!full) raw[k] = (u32x4){0u, 0u, 0u, 0u};
   }
 #pragma unroll
@@ -433,12 +419,15 @@ __device__ __forceinline__ int draw_from_row(const uint16_t* __restrict__ rowp, 
   }
   // which of this thread's logits are candidates (bit = offset from a0)
   unsigned long long cmask = 0ull;
-  for (int i = 0; i < sm.ncl; ++i) {
-    const int off = sm.cl_id[i] - a0;
-    if (off >= 0 && off < L) cmask |= 1ull << off;
+  if (residual) {
+#pragma unroll
+    for (int i = 0; i < kNC; ++i) {
+      const int off = sm.cl_id[i] - a0;               // an unused slot holds -1: off < 0
+      if (off >= 0 && off < L) cmask |= 1ull << off;
+    }
   }
-  // weights p of every logit, branch-free; then, only in the threads that need it,
-  // zero the logits outside the chunk and replace candidates' weights by max(0, p - q)
+  // weights p of every logit, branch-free; then, only in the threads that need it, zero
+  // the logits outside the sub-chunk and replace candidates' weights by max(0, p - q)
   float w[kFineLen];
 #pragma unroll
   for (int k = 0; k < kFineVec; ++k)
@@ -454,38 +443,54 @@ __device__ __forceinline__ int draw_from_row(const uint16_t* __restrict__ rowp, 
     for (int off = 0; off < kFineLen; ++off)
       if ((cmask >> off) & 1ull) {
         float qf = 0.f;
-        for (int i = 0; i < sm.ncl; ++i) qf = sm.cl_id[i] == a0 + off ? sm.cl_qf[i] : qf;
+        for (int i = 0; i < kNC; ++i) qf = sm.cl_id[i] == a0 + off ? sm.cl_qf[i] : qf;
         w[off] = fmaxf(w[off] - qf, 0.f);
       }
   }
   float tsum = 0.f;
 #pragma unroll
   for (int off = 0; off < kFineLen; ++off) tsum += w[off];
-  sm.tsum[tid] = tsum;
+  const float incl = wave_incl_scan(tsum);
+  const float excl = wave_excl_from_incl(incl);
+  if (lane == kWave - 1) sm.wtot[wave] = incl;
   __syncthreads();
-  if (tid < kWave) {
-    const Crossing cr = wave_find_crossing(sm.tsum, kAccThreads, sm.rem);
-    if (tid == 0) {
-      sm.who = cr.idx >= 0 ? cr.idx : cr.last;
-      sm.before = cr.idx >= 0 ? cr.before : 0.f;
-      sm.last = cr.idx < 0 ? 1 : 0;        // no crossing: take the last positive weight
-    }
-  }
-  __syncthreads();
-  if (tid == sm.who) {
-    // the same weights, in the same order, now with the running sum
-    float run = sm.before;
-    int pick = -1, lastp = -1;
-    const bool take_last = sm.last != 0;
-    const float rem = sm.rem;
-    // (weights outside the chunk are 0: they neither cross nor count as positive)
+  // the wave whose logits hold the crossing (the same in every thread)
+  float off = 0.f, offw = 0.f, offlast = 0.f;
+  int W = -1, wlast = -1;
 #pragma unroll
-    for (int off = 0; off < kFineLen; ++off) {
-      run += w[off];
-      if (pick < 0 && !take_last && rem < run) pick = a0 + off;
-      if (w[off] > 0.f) lastp = a0 + off;
+  for (int i = 0; i < kAccWaves; ++i) {
+    const float t = sm.wtot[i];
+    if (W < 0 && t > 0.f && rem < off + t) {
+      W = i;
+      offw = off;
     }
-    sm.pick = pick >= 0 ? pick : lastp;
+    if (t > 0.f) {
+      wlast = i;
+      offlast = off;
+    }
+    off += t;
+  }
+  const bool take_last = W < 0;               // rounding left the target past the total
+  if (take_last) {
+    W = wlast;
+    offw = offlast;
+  }
+  if (W < 0) return -1;                       // no positive weight (uniform)
+  if (wave == W) {
+    const float local = rem - offw;
+    const int l = wave_pick_lane(tsum, incl, take_last ? __builtin_inff() : local);
+    if (lane == l) {
+      // the same weights, in the same order, now with the running sum
+      float run = excl;
+      int pick = -1, lastp = -1;
+#pragma unroll
+      for (int o = 0; o < kFineLen; ++o) {
+        run += w[o];
+        if (pick < 0 && !take_last && local < run) pick = a0 + o;
+        if (w[o] > 0.f) lastp = a0 + o;
+      }
+      sm.pick = pick >= 0 ? pick : lastp;     // the lane holds a positive weight
+    }
   }
   __syncthreads();
   return sm.pick;
@@ -499,157 +504,189 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
                                                                int32_t* __restrict__ n_accepted,
                                                                int32_t* __restrict__ row_status, AcceptWs ws) {
   __shared__ DecideShared sm;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int b = blockIdx.x;
   const int32_t* tok_b = tokens + (size_t)b * K;
   const int32_t* cand_b = cand_idx + (size_t)b * K * kNC;
   const uint16_t* tb = target + (size_t)b * batch_stride;
   const int rbase = batch_stride == 0 ? 0 : b * (K + 1);
   int32_t* out_b = out_tokens + (size_t)b * (K + 1);
-  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const float c2 = inv_t * kLog2e;
-  const bool sampled = inv_t != 0.f;
+  const int nsub = nchunks * kSubPerChunk;
 
-  // ---- everything the decision reads, in at most two dependent memory round trips ----
+  // ---- everything the decision reads, in two dependent memory round trips ------------
   for (int e = tid; e < K * kNC; e += kAccThreads) {
     const int id = cand_b[e];
     sm.cand[e] = id;
-    if (sampled) {
-      sm.q[e] = q[(size_t)b * K * kNC + e];
-      const int idc = id < 0 ? 0 : (id >= V ? V - 1 : id);          // read in bounds; flagged below
-      sm.cbits[e] = tb[(size_t)(e / kNC) * ld + idc];
-    }
+    sm.q[e] = q[(size_t)b * K * kNC + e];
+    const int idc = id < 0 ? 0 : (id >= V ? V - 1 : id);          // read in bounds; flagged below
+    sm.cbits[e] = tb[(size_t)(e / kNC) * ld + idc];
   }
   for (int e = tid; e < K; e += kAccThreads) {
     const int x = tok_b[e];
     sm.tok[e] = x;
-    if (sampled) sm.xbits[e] = tb[(size_t)e * ld + (x < 0 ? 0 : (x >= V ? V - 1 : x))];
+    sm.xbits[e] = tb[(size_t)e * ld + (x < 0 ? 0 : (x >= V ? V - 1 : x))];
   }
-  const int nst = (K + 1) * nchunks;
-  const size_t s0 = (size_t)rbase * nchunks;
+  const int nst = (K + 1) * nsub;
+  const size_t s0 = (size_t)rbase * nsub;
   for (int e = tid; e < nst; e += kAccThreads) {
-    if (sampled) {
-      sm.cs.st.max[e] = ws.chunk_max[s0 + e];
-      sm.cs.st.sum[e] = ws.chunk_sum[s0 + e];
-    } else {
-      sm.cs.arg[e] = ws.chunk_arg[s0 + e];
-    }
-  }
-  if (tid == 0) {
-    sm.ids_bad = 0;
-    sm.q_bad = 0;
-    sm.tstar = K;
+    sm.smax[e] = ws.chunk_max[s0 + e];
+    sm.ssum[e] = ws.chunk_sum[s0 + e];
   }
   __syncthreads();
 
-  // ---- merge the chunk statistics of the request's rows (one thread per row, chunk order)
-  if (tid <= K) {
-    const int c0 = tid * nchunks;
-    if (!sampled) {
-      unsigned long long a = 0ull;
-      for (int j = 0; j < nchunks; ++j) {
-        const unsigned long long x = sm.cs.arg[c0 + j];
-        a = x > a ? x : a;
+  // ---- the decision, in wave 0 alone: lane t owns position t and row t (lane 0 also
+  // row 64 when K = 64); flags and the first reject come from ballots
+  int tstar = 0, trow = 0, status = 0;
+  bool fault = false, residual = false;
+  float m = 0.f, invZ = 0.f, u_res = 0.f;
+  if (wave == 0) {
+    float mr[2] = {0.f, 0.f}, zr[2] = {1.f, 1.f};
+    bool nonfinite = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = lane + i * kWave;
+      if (row <= K) {
+        const float* mx = sm.smax + row * nsub;
+        const float* sx = sm.ssum + row * nsub;
+        float mm = -__builtin_inff();
+        bool bad = false;
+        for (int j = 0; j < nsub; ++j) {
+          const float mj = mx[j];
+          if (__builtin_isnan(mj)) bad = true;
+          else mm = fmaxf(mm, mj);
+        }
+        float Z = 0.f;
+        for (int j = 0; j < nsub; ++j) {
+          const float mj = mx[j];
+          if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += sx[j] * tweight(mj, mm, c2);
+        }
+        mr[i] = mm;
+        zr[i] = (bad || mm == -__builtin_inff()) ? __builtin_nanf("") : Z;
+        nonfinite |= !__builtin_isfinite(zr[i]);
       }
-      sm.row_arg[tid] = rc_id(a);
-    } else {
-      float m = -__builtin_inff();
-      bool bad = false;
-      for (int j = 0; j < nchunks; ++j) {
-        const float mj = sm.cs.st.max[c0 + j];
-        if (__builtin_isnan(mj)) bad = true;
-        else m = fmaxf(m, mj);
-      }
-      float Z = 0.f;
-      for (int j = 0; j < nchunks; ++j) {
-        const float mj = sm.cs.st.max[c0 + j];
-        if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += sm.cs.st.sum[c0 + j] * tweight(mj, m, c2);
-      }
-      sm.row_max[tid] = m;
-      sm.row_sum[tid] = (bad || m == -__builtin_inff()) ? __builtin_nanf("") : Z;
     }
-  }
-  for (int e = tid; e < K * (kNC + 1); e += kAccThreads) {
-    const int id = e < K ? sm.tok[e] : sm.cand[e - K];
-    if (id < 0 || id >= V) atomicOr(&sm.ids_bad, 1);
-  }
-  for (int e = tid; e <= K; e += kAccThreads) out_b[e] = -1;
-  __syncthreads();
-  const bool ids_bad = sm.ids_bad != 0;
-
-  if (!sampled) {
-    if (tid == 0) {
-      int t = 0;
-      while (t < K) {
-        const int g = sm.row_arg[t];
-        if (sm.tok[t] != g) break;
-        out_b[t] = g;
-        ++t;
-      }
-      out_b[t] = sm.row_arg[t];
-      n_accepted[b] = t;
-      if (row_status) row_status[b] = ids_bad ? 2 : 0;
-    }
-    return;
-  }
-
-  // non-finite target rows: commit nothing
-  int nonfinite = 0;
-  for (int t = 0; t <= K; ++t) nonfinite |= !__builtin_isfinite(sm.row_sum[t]);
-  if (nonfinite) {
-    if (tid == 0) {
-      n_accepted[b] = 0;
-      if (row_status) row_status[b] = 1;
-    }
-    return;
-  }
-
-  // validity of the draft distributions
-  if (tid < K) {
-    float s = 0.f, qx = 0.f;
-    bool ok = true;
-    for (int j = 0; j < kNC; ++j) {
-      const float v = sm.q[tid * kNC + j];
-      ok &= __builtin_isfinite(v) && v >= 0.f;
-      s += v;
-      qx += sm.cand[tid * kNC + j] == sm.tok[tid] ? v : 0.f;
-    }
-    ok &= fabsf(s - 1.f) <= 1e-3f;
-    if (!ids_bad) ok &= qx > 0.f;
-    if (!ok) atomicOr(&sm.q_bad, 1);
-  }
-  __syncthreads();
-  const bool q_bad = sm.q_bad != 0;
-  int status = (ids_bad ? 2 : 0) | (q_bad ? 4 : 0);
-
-  // accept tests (all positions at once; the first reject decides); skipped when the
-  // ids or the draft distributions are invalid, which commits one token from p_0
-  const bool fault = ids_bad || q_bad;
-  if (!fault && tid < K) {
-    const int t = tid;
-    const int x = sm.tok[t];
+    // ids in range, and a valid draft distribution at every position
+    bool bad = false, qok = true;
     float qx = 0.f;
-    for (int j = 0; j < kNC; ++j) qx += sm.cand[t * kNC + j] == x ? sm.q[t * kNC + j] : 0.f;
-    const float px = tweight(bf16_to_f32(sm.xbits[t]), sm.row_max[t], c2) / sm.row_sum[t];
-    const float u_acc = word_to_uniform(philox4x32_10((uint32_t)t, (uint32_t)b, 1u, 0u, k0, k1).x0);
-    if (!(u_acc * qx < px)) atomicMin(&sm.tstar, t);
+    int x = 0;
+    if (lane < K) {
+      x = sm.tok[lane];
+      bad = x < 0 || x >= V;
+      float sq = 0.f;
+      for (int j = 0; j < kNC; ++j) {
+        const int id = sm.cand[lane * kNC + j];
+        const float v = sm.q[lane * kNC + j];
+        bad |= id < 0 || id >= V;
+        qok &= __builtin_isfinite(v) && v >= 0.f;
+        sq += v;
+        qx += id == x ? v : 0.f;
+      }
+      qok &= fabsf(sq - 1.f) <= 1e-3f;
+    }
+    const bool ids_bad = __ballot(bad) != 0ull;
+    const bool q_bad = __ballot(lane < K && !(qok && (ids_bad || qx > 0.f))) != 0ull;
+    status = (ids_bad ? 2 : 0) | (q_bad ? 4 : 0);
+    fault = ids_bad || q_bad;
+    if (__ballot(nonfinite) != 0ull) {
+      // a non-finite target row: commit nothing
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (lane + i * kWave <= K) out_b[lane + i * kWave] = -1;
+      if (lane == 0) {
+        n_accepted[b] = 0;
+        if (row_status) row_status[b] = 1;
+        sm.done = 1;
+      }
+    } else {
+      // accept tests at every position (the first reject decides); skipped when the ids
+      // or the draft distributions are invalid, which commits one token from p_0
+      const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+      bool rej = false;
+      if (!fault && lane < K) {
+        const float px = tweight(bf16_to_f32(sm.xbits[lane]), mr[0], c2) / zr[0];
+        const float u_acc = word_to_uniform(philox4x32_10((uint32_t)lane, (uint32_t)b, 1u, 0u, k0, k1).x0);
+        rej = !(u_acc * qx < px);
+      }
+      const unsigned long long rejm = __ballot(rej);
+      tstar = fault ? 0 : (rejm != 0ull ? __builtin_ctzll(rejm) : K);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = lane + i * kWave;
+        if (t <= K && t != tstar) out_b[t] = t < tstar ? sm.tok[t] : -1;
+      }
+      u_res = word_to_uniform(philox4x32_10((uint32_t)tstar, (uint32_t)b, 1u, 0u, k0, k1).x1);
+      // the residual max(0, p - q) at a reject (p instead when it has no mass), else p of
+      // the bonus row (or of row 0 after a fault)
+      trow = fault ? 0 : tstar;
+      residual = !fault && tstar < K;
+      const int hi = trow >> 6, src = trow & (kWave - 1);
+      m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi ? mr[1] : mr[0]), src));
+      invZ = 1.f / __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi ? zr[1] : zr[0]), src));
+      // the drawn position's distinct candidates, their total draft mass (slot order)
+      int cid = -1;
+      float cqf = 0.f, csub = 0.f;
+      if (residual) {
+        const int j = lane & (kNC - 1);
+        const int id = sm.cand[trow * kNC + j];
+        const float qv = sm.q[trow * kNC + j];
+        const float pv = tweight(bf16_to_f32(sm.cbits[trow * kNC + j]), m, c2) * invZ;
+        bool first = true;
+#pragma unroll
+        for (int i = 0; i < kNC; ++i) {
+          const int oi = __shfl(id, i);
+          const float qi = __shfl(qv, i);
+          if (oi == id) {
+            cqf += qi;
+            if (i < j) first = false;
+          }
+        }
+        cid = first ? id : -1;
+        csub = first ? fminf(pv, cqf) : 0.f;
+      }
+      CoarsePick cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, residual, cid, csub);
+      if (cp.sub < 0 && residual) {           // the residual has no mass: draw from p
+        status |= 8;
+        residual = false;
+        cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, false, -1, 0.f);
+      }
+      if (lane < kNC) {
+        sm.cl_id[lane] = cid;
+        sm.cl_qf[lane] = cqf;
+      }
+      if (lane == 0) {
+        sm.done = 0;
+        sm.sub = cp.sub;
+        sm.rem = cp.rem;
+        sm.trow = trow;
+        sm.m = m;
+        sm.invZ = invZ;
+        sm.residual = residual ? 1 : 0;
+      }
+    }
   }
   __syncthreads();
-  const int tstar = fault ? 0 : sm.tstar;
-  if (!fault)
-    for (int t = tid; t < tstar; t += kAccThreads) out_b[t] = sm.tok[t];
-  const float u_res = word_to_uniform(philox4x32_10((uint32_t)tstar, (uint32_t)b, 1u, 0u, k0, k1).x1);
-  // the residual max(0, p - q) at a reject (p instead when it has no mass), else p of
-  // the bonus row (or of row 0 after a fault)
-  const int trow = fault ? 0 : tstar;
-  bool residual = !fault && tstar < K;
-  const uint16_t* rowp = tb + (size_t)trow * ld;
-  int v = -1;
-  for (int pass = 0; pass < 2; ++pass) {
-    v = draw_from_row(rowp, trow, sm.row_max[trow], sm.row_sum[trow], V, nchunks, c2, u_res, residual, sm);
-    if (v >= 0 || !residual) break;
-    status |= 8;
-    residual = false;
+  if (sm.done) return;
+
+  // ---- the rescan of one sub-chunk by the whole work-group --------------------------
+  const uint16_t* rowp = tb + (size_t)sm.trow * ld;
+  bool res = sm.residual != 0;
+  int v;
+  for (;;) {
+    v = sm.sub >= 0 ? fine_pick(rowp, V, nchunks, c2, sm) : -1;
+    if (v >= 0 || !res) break;
+    // the residual had mass in the sub-chunk sums but none in the rescan: draw from p
+    res = false;
+    if (wave == 0) {
+      status |= 8;
+      const CoarsePick cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, false, -1, 0.f);
+      if (lane == 0) {
+        sm.sub = cp.sub;
+        sm.rem = cp.rem;
+        sm.residual = 0;
+      }
+    }
+    __syncthreads();
   }
   if (tid == 0) {
     out_b[tstar] = v;
@@ -664,16 +701,18 @@ hipError_t launch_spec_accept(const uint16_t* target, int64_t ld, int64_t batch_
                               hipStream_t s) {
   const int nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
-  int nchunks;
+  const int nchunks = topk_num_chunks(vocab);
   if (inv_t == 0.f) {
-    nchunks = topk_num_chunks(vocab);          // <= acc_num_chunks(vocab): fits the workspace
     hipLaunchKernelGGL(k_greedy_argmax, dim3((unsigned)(nrows * nchunks)), dim3(kTopkThreads), 0, s, target, ld,
                        batch_stride, K, vocab, nchunks, ws.chunk_arg);
-  } else {
-    nchunks = acc_num_chunks(vocab);
-    hipLaunchKernelGGL(k_accept_stats, dim3((unsigned)(nrows * nchunks)), dim3(kAccThreads), 0, s, target, ld,
-                       batch_stride, K, vocab, nchunks, inv_t, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_greedy_decide, dim3((unsigned)batch), dim3(kWave), 0, s, tokens, cand_idx, batch_stride, K,
+                       vocab, nchunks, ws.chunk_arg, out_tokens, n_accepted, row_status);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(k_accept_stats, dim3((unsigned)(nrows * nchunks)), dim3(kTopkThreads), 0, s, target, ld,
+                     batch_stride, K, vocab, nchunks, inv_t, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_accept_decide, dim3((unsigned)batch), dim3(kAccThreads), 0, s, target, ld, batch_stride, tokens,
