@@ -25,15 +25,18 @@ static_assert(kChunkVec == kSubPerChunk * kSubVec, "a chunk is its waves' sub-ch
 static_assert(kMaxSub <= kWave, "one sub-chunk per lane of the deciding wave");
 
 // First vector of sub-chunk s = 8c + j (wave j's share of chunk c); s = 8 * nchunks gives
-// the row's end.  Every sub-chunk but a chunk's last has ceil(len / 8) vectors.
+// the row's end.  Chunk c starts at vector floor(nvec * c / nchunks), as in the top-16
+// split (32-bit arithmetic: nvec <= 2^16, c <= 8); every sub-chunk but a chunk's last has
+// ceil(len / 8) vectors.
 __host__ __device__ __forceinline__ int sub_begin(int V, int nchunks, int s) {
-  const int c = s / kSubPerChunk, j = s - c * kSubPerChunk;
-  const int a = chunk_begin(V, nchunks, c);
-  if (j == 0) return a;
-  const int b = chunk_begin(V, nchunks, c + 1);
-  const int span = (b - a + kSubPerChunk - 1) / kSubPerChunk;
-  return a + j * span < b ? a + j * span : b;
+  const unsigned nvec = ((unsigned)V + 7u) >> 3;
+  const unsigned c = (unsigned)s / kSubPerChunk, j = (unsigned)s % kSubPerChunk;
+  const unsigned a = nvec * c / (unsigned)nchunks;
+  const unsigned b = nvec * (c + 1u) / (unsigned)nchunks;
+  const unsigned span = (b - a + kSubPerChunk - 1) / kSubPerChunk;
+  return (int)(a + j * span < b ? a + j * span : b);
 }
+static_assert((int64_t)kMaxChunks * kChunkVec * (kWave / kSubPerChunk + 1) < (1ll << 32), "sub_begin's products fit 32 bits");
 
 AcceptWs carve_accept(Carver& c, int64_t nrows, int64_t vocab) {
   AcceptWs w;
@@ -53,11 +56,50 @@ constexpr float kLog2e = 1.44269504088896341f;
 // the draws) is formed this one way.
 __device__ __forceinline__ float tweight(float l, float m, float c2) { return __builtin_amdgcn_exp2f((l - m) * c2); }
 
+// ---- wave-wide sums on DPP ------------------------------------------------------------
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f32(float x) {
+  // lanes whose source lies outside the pattern (or in a row outside ROWS) read 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive sum over the wave's lanes: within each 16-lane row by shifts of 1, 2, 4 and
+// 8 lanes, then across rows by broadcasting lane 15 into rows 1 and 3 and lane 31 into
+// rows 2 and 3.  Every lane must be active.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x += dpp_f32<0x111>(x);           // row_shr:1
+  x += dpp_f32<0x112>(x);           // row_shr:2
+  x += dpp_f32<0x114>(x);           // row_shr:4
+  x += dpp_f32<0x118>(x);           // row_shr:8
+  x += dpp_f32<0x142, 0xa>(x);      // row_bcast:15
+  x += dpp_f32<0x143, 0xc>(x);      // row_bcast:31
+  return x;
+}
+
+// The scan's exclusive form (wave_shr:1; lane 0 reads 0).
+__device__ __forceinline__ float wave_excl_from_incl(float incl) { return dpp_f32<0x138>(incl); }
+
+// The wave's total, the same in every lane (lane 63 of the inclusive scan).
+__device__ __forceinline__ float wave_total(float x) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan(x)), kWave - 1));
+}
+
 // ---- sampled pass 1: max and sum of weights of every sub-chunk ------------------------
 // Wave j of work-group (row, c) reads sub-chunk 8c + j: lane l holds its vectors l,
 // l + 64, ... (each load instruction covers 1 KB of the row).  Missing logits read as
-// -inf (weight 0).  A sub-chunk holding +inf or NaN is marked by a NaN max.  No LDS and
-// no barrier: each wave writes its own pair.
+// -inf (weight 0).  Each lane folds every vector in as soon as its load lands: a running
+// max m and the sum of weights relative to it (rescaled when m grows), so the weights are
+// formed while the rest of the row is still streaming in.  A sub-chunk holding +inf or
+// NaN (a raw half >= 0x7f80 read as signed, or > 0xff80 read as unsigned) gets a NaN max.
+// No LDS and no barrier: each wave writes its own pair.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int float_order(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float order_float(int o) { return __int_as_float(o ^ ((o >> 31) & 0x7fffffff)); }
+
 __global__ void __launch_bounds__(kTopkThreads) k_accept_stats(const uint16_t* __restrict__ target, int64_t ld,
                                                                int64_t batch_stride, int K, int V, int nchunks,
                                                                float inv_t, AcceptWs ws) {
@@ -70,17 +112,22 @@ __global__ void __launch_bounds__(kTopkThreads) k_accept_stats(const uint16_t* _
   const u32x4* __restrict__ rowv = reinterpret_cast<const u32x4*>(rowp);
   const int s = c * kSubPerChunk + wave;
   const int s0 = sub_begin(V, nchunks, s), s1 = sub_begin(V, nchunks, s + 1);
-  const int safe = chunk_begin(V, nchunks, c);            // the chunk's first vector: whole
+  const int safe = sub_begin(V, nchunks, c * kSubPerChunk);   // the chunk's first vector: whole
   const int nfull = V >> 3;
 
   u32x4 d[kTopkVecPerThread];
+  unsigned whole = 0u;
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const int v = s0 + lane + k * kWave;
-    const bool whole = v < s1 && v < nfull;
-    d[k] = __builtin_nontemporal_load(rowv + (whole ? v : safe));
-    if (!whole) d[k] = (u32x4){0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    const bool w = v < s1 && v < nfull;
+    d[k] = __builtin_nontemporal_load(rowv + (w ? v : safe));
+    whole |= (w ? 1u : 0u) << k;
   }
+  // every load is issued before any is used: the fold below consumes the vectors in
+  // order (a slot that is not whole as -inf), and without this fence the scheduler
+  // trades loads in flight for registers
+  __builtin_amdgcn_sched_barrier(0);
   // the row's ragged last vector (V % 8 != 0), in the one lane that owns it
   const int vr = nfull - s0;
   if ((V & 7) != 0 && nfull < s1 && vr >= 0 && lane == (vr & (kWave - 1))) {
@@ -95,40 +142,48 @@ __global__ void __launch_bounds__(kTopkThreads) k_accept_stats(const uint16_t* _
 #pragma unroll
     for (int k = 0; k < kTopkVecPerThread; ++k)
       if (k == kr) d[k] = x;
+    whole |= 1u << kr;
   }
 
-  // signed-order max and min (to find +inf and NaN) of the sub-chunk
-  int smax = -32768, smin = 32767;
+  const float c2 = inv_t * kLog2e;
+  float m = -__builtin_inff(), S = 0.f;
+  s16x2 hs = (s16x2){-32768, -32768};
+  u16x2 hu = (u16x2){0, 0};
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
-    const s16x2 a = signed_order2(d[k].x), bq = signed_order2(d[k].y);
-    const s16x2 cq = signed_order2(d[k].z), dq = signed_order2(d[k].w);
-    const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, bq), __builtin_elementwise_max(cq, dq));
-    const s16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(a, bq), __builtin_elementwise_min(cq, dq));
-    smax = max_halves(mx) > smax ? max_halves(mx) : smax;
-    const int lo = mn.x < mn.y ? (int)mn.x : (int)mn.y;
-    smin = lo < smin ? lo : smin;
-  }
-  smax = wave_max_i32(smax);
-  smin = -wave_max_i32(-smin);
-  const bool nonfinite = smax >= 32640 || smin < -32641;       // +inf / +NaN, or -NaN
-  const float m = order_to_float(smax > 32640 ? 32640 : smax);
-  float sum = 0.f;
-  if (!nonfinite && m != -__builtin_inff()) {
-    const float c2 = inv_t * kLog2e;
+    const u32x4 x = ((whole >> k) & 1u) ? d[k] : (u32x4){0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    const s16x2 a0 = __builtin_bit_cast(s16x2, x.x), a1 = __builtin_bit_cast(s16x2, x.y);
+    const s16x2 a2 = __builtin_bit_cast(s16x2, x.z), a3 = __builtin_bit_cast(s16x2, x.w);
+    hs = __builtin_elementwise_max(hs, __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                                 __builtin_elementwise_max(a2, a3)));
+    const u16x2 b0 = __builtin_bit_cast(u16x2, x.x), b1 = __builtin_bit_cast(u16x2, x.y);
+    const u16x2 b2 = __builtin_bit_cast(u16x2, x.z), b3 = __builtin_bit_cast(u16x2, x.w);
+    hu = __builtin_elementwise_max(hu, __builtin_elementwise_max(__builtin_elementwise_max(b0, b1),
+                                                                 __builtin_elementwise_max(b2, b3)));
+    float f[8];
 #pragma unroll
-    for (int k = 0; k < kTopkVecPerThread; ++k) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        sum += tweight(bf16_lo(d[k][w]), m, c2);
-        sum += tweight(bf16_hi(d[k][w]), m, c2);
-      }
+    for (int w = 0; w < 4; ++w) {
+      f[2 * w] = bf16_lo(x[w]);
+      f[2 * w + 1] = bf16_hi(x[w]);
     }
+    // (NaN is ignored by the max; its sub-chunk is marked non-finite below)
+    const float vm = fmaxf(fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])), fmaxf(fmaxf(f[4], f[5]), fmaxf(f[6], f[7])));
+    const float mn = fmaxf(m, vm);
+    const float mref = mn == -__builtin_inff() ? 0.f : mn;   // every logit so far -inf: weights 0
+    S *= mn == m ? 1.f : tweight(m, mref, c2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S += tweight(f[e], mref, c2);
+    m = mn;
   }
-  sum = wave_sum(sum);
+  // the wave's pair: its max, and the lanes' sums rescaled to it
+  const int hmax = hs.x > hs.y ? (int)hs.x : (int)hs.y;
+  const int umax = hu.x > hu.y ? (int)hu.x : (int)hu.y;
+  const bool nonfinite = __ballot(hmax >= 0x7f80 || umax > 0xff80) != 0ull;
+  const float mw = order_float(wave_max_i32(float_order(m)));
+  const float sum = wave_total(m == -__builtin_inff() ? 0.f : S * tweight(m, mw, c2));
   if (lane == 0) {
     const size_t si = (size_t)r * (nchunks * kSubPerChunk) + s;
-    ws.chunk_max[si] = nonfinite ? __builtin_nanf("") : m;
+    ws.chunk_max[si] = nonfinite ? __builtin_nanf("") : mw;
     ws.chunk_sum[si] = sum;
   }
 }
@@ -289,26 +344,28 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(const int32_t* __restri
 }
 
 // ---- sampled pass 2 -------------------------------------------------------------------
-constexpr int kAccThreads = 256;
+constexpr int kAccThreads = 512;
 constexpr int kAccWaves = kAccThreads / kWave;
 constexpr int kFineVec = (kSubVec + kAccThreads - 1) / kAccThreads;   // 16-byte vectors per thread of a rescan
 constexpr int kFineLen = 8 * kFineVec;                                // logits per thread
 constexpr int kMaxStatRows = DFLASH2_MAX_K + 1;
+constexpr int kNCP = kNC + 1;            // LDS pitch of a position's candidates (odd: lanes
+constexpr int kSubP = kMaxSub + 1;       // reading one position or row each hit distinct banks)
 
 struct DecideShared {
   // the request's inputs, loaded once at entry
   int tok[DFLASH2_MAX_K];
-  int cand[DFLASH2_MAX_K * kNC];
-  float q[DFLASH2_MAX_K * kNC];
+  int cand[DFLASH2_MAX_K * kNCP];
+  float q[DFLASH2_MAX_K * kNCP];
   uint32_t xbits[DFLASH2_MAX_K];          // target logit (bits) of each drafted token
-  uint32_t cbits[DFLASH2_MAX_K * kNC];    // target logit (bits) of each candidate
-  float smax[kMaxStatRows * kMaxSub];     // sub-chunk statistics of the request's rows
-  float ssum[kMaxStatRows * kMaxSub];
+  uint32_t cbits[DFLASH2_MAX_K * kNCP];   // target logit (bits) of each candidate
+  float smax[kMaxStatRows * kSubP];       // sub-chunk j of row r at r * (nsub + 1) + j
+  float ssum[kMaxStatRows * kSubP];
   // the draw, as the deciding wave leaves it
   int done;                               // the request is finished (a non-finite row)
   int trow;                               // the row drawn from
-  int sub;                                // the sub-chunk to rescan
-  float rem;                              // the draw's target minus the mass before it
+  int e0, e1;                             // the logits [e0, e1) to rescan
+  float rem;                              // the draw's target minus the mass before e0
   float m, invZ;                          // the drawn row's max and 1 / sum of weights
   int residual;                           // draw from max(0, p - q) (else from p)
   int cl_id[kNC];                         // the drawn position's candidates: an id at its
@@ -316,6 +373,10 @@ struct DecideShared {
   float wtot[kAccWaves];                  // rescan: the weight of each wave's logits
   int pick;
 };
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 
 // Inverse-CDF step over one non-negative value per lane (incl: their inclusive scan):
 // the first lane holding a positive value whose running sum exceeds x (in exact
@@ -329,22 +390,30 @@ __device__ __forceinline__ int wave_pick_lane(float v, float incl, float x) {
   return hit != 0ull ? __builtin_ctzll(hit) : 63 - __builtin_clzll(pos);
 }
 
-// Inclusive scan over the wave's lanes (every lane must be active).
-__device__ __forceinline__ float wave_incl_scan(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
+// Merged statistics of one row from its sub-chunks, in sub-chunk order: the max, and the
+// sum of weights relative to it (NaN when a sub-chunk is non-finite or no logit is
+// finite).  nsub is a multiple of 8; the loads of 8 sub-chunks go out together.
+__device__ __forceinline__ void merge_row(const float* mx, const float* sx, int nsub, float c2, float& m_out,
+                                          float& z_out) {
+  float mm = -__builtin_inff();
+  bool bad = false;
+#pragma unroll 1
+  for (int j0 = 0; j0 < nsub; j0 += kSubPerChunk) {
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float y = __shfl_up(v, o);
-    if (lane >= o) v += y;
+    for (int u = 0; u < kSubPerChunk; ++u) {
+      const float v = mx[j0 + u];
+      bad |= v != v;
+      mm = fmaxf(mm, v);                  // a NaN is skipped (and flagged)
+    }
   }
-  return v;
-}
-
-// The scan's exclusive form.  The cross-lane read runs in every lane: a lane that reads
-// from an inactive one gets 0.
-__device__ __forceinline__ float wave_excl_from_incl(float incl) {
-  const float y = __shfl_up(incl, 1);
-  return (threadIdx.x & (kWave - 1)) == 0 ? 0.f : y;
+  float Z = 0.f;
+#pragma unroll 1
+  for (int j0 = 0; j0 < nsub; j0 += kSubPerChunk) {
+#pragma unroll
+    for (int u = 0; u < kSubPerChunk; ++u) Z += sx[j0 + u] * tweight(mx[j0 + u], mm, c2);   // -inf max: 0 * 0
+  }
+  m_out = mm;
+  z_out = (bad || mm == -__builtin_inff()) ? __builtin_nanf("") : Z;
 }
 
 struct CoarsePick {
@@ -352,52 +421,48 @@ struct CoarsePick {
   float rem;
 };
 
-// The deciding wave's step over the sub-chunks of row `trow` (lane s owns sub-chunk s):
-// each sub-chunk's mass, less the draft's mass min(p, q) at the candidates it holds when
-// `residual` (cid / csub: lane j & 15 holds slot j, an id at its first slot else -1),
-// then the sub-chunk whose running sum first exceeds u times the total.
-__device__ __forceinline__ CoarsePick coarse_pick(const DecideShared& sm, int trow, int nsub, int V, int nchunks,
+// The deciding wave's step over the sub-chunks of row `trow` (lane s owns sub-chunk s,
+// whose logits are [e0, e1)): each sub-chunk's mass, less the draft's mass min(p, q) at
+// the candidates it holds when `residual` (cid / csub: lane j < 16 holds slot j, an id at
+// its first slot else -1), then the sub-chunk whose running sum first exceeds u times the
+// total.
+__device__ __forceinline__ CoarsePick coarse_pick(const DecideShared& sm, int trow, int nsub, int e0, int e1,
                                                   float m, float invZ, float c2, float u, bool residual, int cid,
                                                   float csub) {
   const int lane = threadIdx.x & (kWave - 1);
   float P = 0.f;
   if (lane < nsub) {
-    const float mc = sm.smax[trow * nsub + lane];
-    P = mc == -__builtin_inff() ? 0.f : sm.ssum[trow * nsub + lane] * tweight(mc, m, c2) * invZ;
+    const float mc = sm.smax[trow * (nsub + 1) + lane];
+    P = mc == -__builtin_inff() ? 0.f : sm.ssum[trow * (nsub + 1) + lane] * tweight(mc, m, c2) * invZ;
   }
   if (residual) {
-    const int e0 = 8 * sub_begin(V, nchunks, lane);
-    const int e1 = min(8 * sub_begin(V, nchunks, lane + 1), V);
 #pragma unroll
     for (int i = 0; i < kNC; ++i) {
-      const int id = __shfl(cid, i);
-      const float x = __shfl(csub, i);
+      const int id = __builtin_amdgcn_readlane(cid, i);
+      const float x = readlane_f(csub, i);
       P -= (id >= e0 && id < e1) ? x : 0.f;
     }
   }
   const float R = lane < nsub ? fmaxf(P, 0.f) : 0.f;
-  const float target = u * wave_sum(R);
   const float incl = wave_incl_scan(R);
   const float excl = wave_excl_from_incl(incl);
+  const float target = u * readlane_f(incl, kWave - 1);
   CoarsePick cp;
   cp.sub = wave_pick_lane(R, incl, target);
-  cp.rem = cp.sub < 0 ? 0.f : target - __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), cp.sub < 0 ? 0 : cp.sub));
+  cp.rem = target - readlane_f(excl, cp.sub < 0 ? 0 : cp.sub);
   return cp;
 }
 
-// The draw inside sub-chunk sm.sub of row rowp, by the whole work-group: thread i owns a
-// contiguous run of L <= kFineLen logits; every load goes out at once (a vector not wholly
-// inside the sub-chunk reads the row's first vector and is replaced) and the weights stay
-// in registers.  Returns the token id (the same in every thread), -1 if no weight is
+// The draw inside logits [sm.e0, sm.e1) of row rowp, by the whole work-group: thread i
+// owns a contiguous run of L <= kFineLen logits; every load goes out at once (a vector not
+// wholly inside the range reads the row's first vector and is replaced) and the weights
+// stay in registers.  Returns the token id (the same in every thread), -1 if no weight is
 // positive.
-__device__ __forceinline__ int fine_pick(const uint16_t* __restrict__ rowp, int V, int nchunks, float c2,
-                                         DecideShared& sm) {
+__device__ __forceinline__ int fine_pick(const uint16_t* __restrict__ rowp, float c2, DecideShared& sm) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int s = sm.sub;
+  const int e0 = sm.e0, e1 = sm.e1;
   const float m = sm.m, invZ = sm.invZ, rem = sm.rem;
   const bool residual = sm.residual != 0;
-  const int e0 = 8 * sub_begin(V, nchunks, s);
-  const int e1 = min(8 * sub_begin(V, nchunks, s + 1), V);
   const int L = (((e1 - e0) + kAccThreads * 8 - 1) / (kAccThreads * 8)) * 8;
   const int a0 = e0 + tid * L;
   u32x4 raw[kFineVec];
@@ -418,16 +483,16 @@ __device__ __forceinline__ int fine_pick(const uint16_t* __restrict__ rowp, int 
     }
   }
   // which of this thread's logits are candidates (bit = offset from a0)
-  unsigned long long cmask = 0ull;
+  unsigned cmask = 0u;
   if (residual) {
 #pragma unroll
     for (int i = 0; i < kNC; ++i) {
       const int off = sm.cl_id[i] - a0;               // an unused slot holds -1: off < 0
-      if (off >= 0 && off < L) cmask |= 1ull << off;
+      if (off >= 0 && off < L) cmask |= 1u << off;
     }
   }
   // weights p of every logit, branch-free; then, only in the threads that need it, zero
-  // the logits outside the sub-chunk and replace candidates' weights by max(0, p - q)
+  // the logits outside the range and replace candidates' weights by max(0, p - q)
   float w[kFineLen];
 #pragma unroll
   for (int k = 0; k < kFineVec; ++k)
@@ -438,10 +503,10 @@ __device__ __forceinline__ int fine_pick(const uint16_t* __restrict__ rowp, int 
     for (int off = 0; off < kFineLen; ++off)
       if (!(off < L && a0 + off < e1)) w[off] = 0.f;
   }
-  if (cmask != 0ull) {
+  if (cmask != 0u) {
 #pragma unroll
     for (int off = 0; off < kFineLen; ++off)
-      if ((cmask >> off) & 1ull) {
+      if ((cmask >> off) & 1u) {
         float qf = 0.f;
         for (int i = 0; i < kNC; ++i) qf = sm.cl_id[i] == a0 + off ? sm.cl_qf[i] : qf;
         w[off] = fmaxf(w[off] - qf, 0.f);
@@ -513,14 +578,16 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   int32_t* out_b = out_tokens + (size_t)b * (K + 1);
   const float c2 = inv_t * kLog2e;
   const int nsub = nchunks * kSubPerChunk;
+  const int pitch = nsub + 1;
 
   // ---- everything the decision reads, in two dependent memory round trips ------------
   for (int e = tid; e < K * kNC; e += kAccThreads) {
+    const int t = e >> 4, j = e & (kNC - 1);
     const int id = cand_b[e];
-    sm.cand[e] = id;
-    sm.q[e] = q[(size_t)b * K * kNC + e];
+    sm.cand[t * kNCP + j] = id;
+    sm.q[t * kNCP + j] = q[(size_t)b * K * kNC + e];
     const int idc = id < 0 ? 0 : (id >= V ? V - 1 : id);          // read in bounds; flagged below
-    sm.cbits[e] = tb[(size_t)(e / kNC) * ld + idc];
+    sm.cbits[t * kNCP + j] = tb[(size_t)t * ld + idc];
   }
   for (int e = tid; e < K; e += kAccThreads) {
     const int x = tok_b[e];
@@ -530,53 +597,52 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   const int nst = (K + 1) * nsub;
   const size_t s0 = (size_t)rbase * nsub;
   for (int e = tid; e < nst; e += kAccThreads) {
-    sm.smax[e] = ws.chunk_max[s0 + e];
-    sm.ssum[e] = ws.chunk_sum[s0 + e];
+    const int row = (int)((unsigned)e / (unsigned)nsub);
+    const int at = e + row;                                     // row * pitch + (e - row * nsub)
+    sm.smax[at] = ws.chunk_max[s0 + e];
+    sm.ssum[at] = ws.chunk_sum[s0 + e];
   }
   __syncthreads();
 
   // ---- the decision, in wave 0 alone: lane t owns position t and row t (lane 0 also
   // row 64 when K = 64); flags and the first reject come from ballots
   int tstar = 0, trow = 0, status = 0;
-  bool fault = false, residual = false;
+  bool fault = false;
   float m = 0.f, invZ = 0.f, u_res = 0.f;
+  int se0 = 0, se1 = 0;
   if (wave == 0) {
-    float mr[2] = {0.f, 0.f}, zr[2] = {1.f, 1.f};
+    // the logits of sub-chunk `lane`
+    se0 = 8 * sub_begin(V, nchunks, lane);
+    se1 = min(8 * sub_begin(V, nchunks, lane + 1), V);
+    float mr0 = 0.f, zr0 = 1.f, mr1 = 0.f, zr1 = 1.f;
     bool nonfinite = false;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+#pragma unroll 1
+    for (int i = 0; i < (K >= kWave ? 2 : 1); ++i) {
       const int row = lane + i * kWave;
       if (row <= K) {
-        const float* mx = sm.smax + row * nsub;
-        const float* sx = sm.ssum + row * nsub;
-        float mm = -__builtin_inff();
-        bool bad = false;
-        for (int j = 0; j < nsub; ++j) {
-          const float mj = mx[j];
-          if (__builtin_isnan(mj)) bad = true;
-          else mm = fmaxf(mm, mj);
+        float mm, zz;
+        merge_row(sm.smax + row * pitch, sm.ssum + row * pitch, nsub, c2, mm, zz);
+        nonfinite |= !__builtin_isfinite(zz);
+        if (i == 0) {
+          mr0 = mm;
+          zr0 = zz;
+        } else {
+          mr1 = mm;
+          zr1 = zz;
         }
-        float Z = 0.f;
-        for (int j = 0; j < nsub; ++j) {
-          const float mj = mx[j];
-          if (!__builtin_isnan(mj) && mj != -__builtin_inff()) Z += sx[j] * tweight(mj, mm, c2);
-        }
-        mr[i] = mm;
-        zr[i] = (bad || mm == -__builtin_inff()) ? __builtin_nanf("") : Z;
-        nonfinite |= !__builtin_isfinite(zr[i]);
       }
     }
     // ids in range, and a valid draft distribution at every position
     bool bad = false, qok = true;
     float qx = 0.f;
-    int x = 0;
     if (lane < K) {
-      x = sm.tok[lane];
+      const int x = sm.tok[lane];
       bad = x < 0 || x >= V;
       float sq = 0.f;
+#pragma unroll
       for (int j = 0; j < kNC; ++j) {
-        const int id = sm.cand[lane * kNC + j];
-        const float v = sm.q[lane * kNC + j];
+        const int id = sm.cand[lane * kNCP + j];
+        const float v = sm.q[lane * kNCP + j];
         bad |= id < 0 || id >= V;
         qok &= __builtin_isfinite(v) && v >= 0.f;
         sq += v;
@@ -590,10 +656,9 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
     fault = ids_bad || q_bad;
     if (__ballot(nonfinite) != 0ull) {
       // a non-finite target row: commit nothing
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (lane + i * kWave <= K) out_b[lane + i * kWave] = -1;
+      if (lane <= K) out_b[lane] = -1;
       if (lane == 0) {
+        if (K >= kWave) out_b[kWave] = -1;
         n_accepted[b] = 0;
         if (row_status) row_status[b] = 1;
         sm.done = 1;
@@ -604,38 +669,36 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
       const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
       bool rej = false;
       if (!fault && lane < K) {
-        const float px = tweight(bf16_to_f32(sm.xbits[lane]), mr[0], c2) / zr[0];
+        const float px = tweight(bf16_to_f32(sm.xbits[lane]), mr0, c2) / zr0;
         const float u_acc = word_to_uniform(philox4x32_10((uint32_t)lane, (uint32_t)b, 1u, 0u, k0, k1).x0);
         rej = !(u_acc * qx < px);
       }
       const unsigned long long rejm = __ballot(rej);
       tstar = fault ? 0 : (rejm != 0ull ? __builtin_ctzll(rejm) : K);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = lane + i * kWave;
-        if (t <= K && t != tstar) out_b[t] = t < tstar ? sm.tok[t] : -1;
-      }
+      if (lane <= K && lane != tstar) out_b[lane] = lane < tstar ? sm.tok[lane] : -1;
+      if (lane == 0 && K >= kWave && tstar != kWave) out_b[kWave] = -1;      // row 64 lies past tstar
       u_res = word_to_uniform(philox4x32_10((uint32_t)tstar, (uint32_t)b, 1u, 0u, k0, k1).x1);
       // the residual max(0, p - q) at a reject (p instead when it has no mass), else p of
       // the bonus row (or of row 0 after a fault)
       trow = fault ? 0 : tstar;
-      residual = !fault && tstar < K;
-      const int hi = trow >> 6, src = trow & (kWave - 1);
-      m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi ? mr[1] : mr[0]), src));
-      invZ = 1.f / __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi ? zr[1] : zr[0]), src));
+      bool residual = !fault && tstar < K;
+      const bool hi = trow >= kWave;
+      const int src = trow & (kWave - 1);
+      m = readlane_f(hi ? mr1 : mr0, src);
+      invZ = 1.f / readlane_f(hi ? zr1 : zr0, src);
       // the drawn position's distinct candidates, their total draft mass (slot order)
       int cid = -1;
       float cqf = 0.f, csub = 0.f;
       if (residual) {
         const int j = lane & (kNC - 1);
-        const int id = sm.cand[trow * kNC + j];
-        const float qv = sm.q[trow * kNC + j];
-        const float pv = tweight(bf16_to_f32(sm.cbits[trow * kNC + j]), m, c2) * invZ;
+        const int id = sm.cand[trow * kNCP + j];
+        const float qv = sm.q[trow * kNCP + j];
+        const float pv = tweight(bf16_to_f32(sm.cbits[trow * kNCP + j]), m, c2) * invZ;
         bool first = true;
 #pragma unroll
         for (int i = 0; i < kNC; ++i) {
-          const int oi = __shfl(id, i);
-          const float qi = __shfl(qv, i);
+          const int oi = __builtin_amdgcn_readlane(id, i);
+          const float qi = readlane_f(qv, i);
           if (oi == id) {
             cqf += qi;
             if (i < j) first = false;
@@ -644,21 +707,25 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
         cid = first ? id : -1;
         csub = first ? fminf(pv, cqf) : 0.f;
       }
-      CoarsePick cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, residual, cid, csub);
+      CoarsePick cp = coarse_pick(sm, trow, nsub, se0, se1, m, invZ, c2, u_res, residual, cid, csub);
       if (cp.sub < 0 && residual) {           // the residual has no mass: draw from p
         status |= 8;
         residual = false;
-        cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, false, -1, 0.f);
+        cp = coarse_pick(sm, trow, nsub, se0, se1, m, invZ, c2, u_res, false, -1, 0.f);
       }
       if (lane < kNC) {
         sm.cl_id[lane] = cid;
         sm.cl_qf[lane] = cqf;
       }
+      // (no mass at all cannot happen for p of a finite row; an empty range then draws -1)
+      const int ce0 = cp.sub < 0 ? 0 : __builtin_amdgcn_readlane(se0, cp.sub);
+      const int ce1 = cp.sub < 0 ? 0 : __builtin_amdgcn_readlane(se1, cp.sub);
       if (lane == 0) {
         sm.done = 0;
-        sm.sub = cp.sub;
-        sm.rem = cp.rem;
         sm.trow = trow;
+        sm.e0 = ce0;
+        sm.e1 = ce1;
+        sm.rem = cp.rem;
         sm.m = m;
         sm.invZ = invZ;
         sm.residual = residual ? 1 : 0;
@@ -673,15 +740,18 @@ __global__ void __launch_bounds__(kAccThreads) k_accept_decide(const uint16_t* _
   bool res = sm.residual != 0;
   int v;
   for (;;) {
-    v = sm.sub >= 0 ? fine_pick(rowp, V, nchunks, c2, sm) : -1;
+    v = fine_pick(rowp, c2, sm);
     if (v >= 0 || !res) break;
     // the residual had mass in the sub-chunk sums but none in the rescan: draw from p
     res = false;
     if (wave == 0) {
       status |= 8;
-      const CoarsePick cp = coarse_pick(sm, trow, nsub, V, nchunks, m, invZ, c2, u_res, false, -1, 0.f);
+      const CoarsePick cp = coarse_pick(sm, trow, nsub, se0, se1, m, invZ, c2, u_res, false, -1, 0.f);
+      const int ce0 = cp.sub < 0 ? 0 : __builtin_amdgcn_readlane(se0, cp.sub);
+      const int ce1 = cp.sub < 0 ? 0 : __builtin_amdgcn_readlane(se1, cp.sub);
       if (lane == 0) {
-        sm.sub = cp.sub;
+        sm.e0 = ce0;
+        sm.e1 = ce1;
         sm.rem = cp.rem;
         sm.residual = 0;
       }
