@@ -461,6 +461,33 @@ def test_spec_accept_fault_rows(d2):
     assert cpu(st).tolist() == [1, 4, 4, 2, 4, 1]
 
 
+@pytest.mark.parametrize("V", [16, 23, 77, 1003, 9729])
+@pytest.mark.parametrize("temperature", [1.0, 0.3])
+def test_spec_accept_sampled_small_and_ragged_vocab(d2, V, temperature):
+    """Sampled verify where the vocabulary leaves sub-chunks empty (V = 16, 23), short,
+    ragged (V % 8 != 0) or one vector past a whole sub-chunk (9729); the drafts are
+    the target's own top candidates so accepts, residual draws and bonus draws occur."""
+    rng = np.random.default_rng(V)
+    B, K = 6, 4
+    vals = rng.standard_normal((B, K + 1, V)).astype(np.float32) * 2.0
+    tb = synth.f32_to_bf16_bits(vals)
+    p = np.stack([[oracle.target_probs(tb[b, t], temperature) for t in range(K + 1)] for b in range(B)])
+    cand = np.argsort(-p[:, :K], axis=-1, kind="stable")[..., :16].astype(np.int32)
+    q = np.take_along_axis(p[:, :K], cand.astype(np.int64), axis=-1)
+    q = (q / q.sum(-1, keepdims=True)).astype(np.float32)
+    q = (0.5 * q + 0.5 * rng.dirichlet(np.ones(16), size=(B, K))).astype(np.float32)   # off the target's
+    q /= q.sum(-1, keepdims=True)
+    tokens = cand[:, :, 0].copy()
+    ld = (V + 7) // 8 * 8                                # rows padded to the 16-byte stride rule
+    buf = np.zeros((B, K + 1, ld), np.uint16)
+    buf[..., :V] = tb
+    print(f"sampled verify V={V} T={temperature}", flush=True)
+    o, n, st = d2.spec_accept(to_gpu_bits(buf)[..., :V], to_gpu(tokens), to_gpu(cand), to_gpu(q.astype(np.float32)),
+                              temperature, seed=V)
+    stats = check_accept(tb, tokens, cand, q, temperature, V, cpu(o), cpu(n), cpu(st))
+    print("verify stats", stats, "accepted", cpu(n).tolist(), flush=True)
+
+
 @pytest.mark.parametrize("V", [5003, 40000])
 def test_spec_accept_greedy_edge_rows(d2, V):
     """Greedy verify = argmax prefix match with NaN lowest, -0 == +0 and ties to the
