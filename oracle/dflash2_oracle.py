@@ -346,6 +346,40 @@ def target_probs(bits_row, temperature: float) -> np.ndarray:
     return w / w.sum()
 
 
+def filtered_target_probs(bits_row, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                          margin: list | None = None) -> np.ndarray:
+    """p after the sampling filters, applied in the order the [FT] runs name them
+    ("Speed" and "All settings": temperature, then top_p = 0.95 and top_k = 20).
+
+    Readings (the pages name the settings, not their tie or boundary rules):
+      - top-k keeps exactly top_k tokens, the largest logits by (value desc, token id
+        asc), the candidate order used everywhere else on this path; top_k = 0 keeps all;
+      - p over the kept tokens is softmax(l / T) renormalised over them;
+      - top-p walks the kept tokens in that same order and keeps each one whose
+        preceding cumulative mass is below top_p (the token that reaches top_p is
+        kept, so at least one token is); top_p >= 1 cuts nothing (no rounding of the
+        running sum up to 1 may drop the tail);
+      - the surviving masses are renormalised; every other token has p = 0.
+    `margin`, when given, receives |cumulative mass before a token - top_p| at the two
+    tokens on either side of the top-p cut (how close the cut is to moving).
+    """
+    l = bf16_to_f64(bits_row)
+    V = l.size
+    order = np.lexsort((np.arange(V), -l))            # value desc, id asc
+    kept = order[:top_k] if top_k > 0 else order
+    z = l[kept] / temperature
+    w = np.exp(z - z.max())
+    pk = w / w.sum()
+    before = np.concatenate([[0.0], np.cumsum(pk)[:-1]])
+    keep = before < top_p if top_p < 1.0 else np.ones(before.size, dtype=bool)   # top_p >= 1: no cut
+    n = int(keep.sum())
+    if margin is not None:
+        margin.append(min(abs(before[i] - top_p) for i in (n - 1, n) if i < before.size))
+    p = np.zeros(V)
+    p[kept[:n]] = pk[:n] / pk[:n].sum()
+    return p
+
+
 def bf16_argmax(bits_row) -> int:
     """Lowest token id holding the largest bf16 logit.  NaN ranks below every number,
     -inf included (the candidate order's reading); an all-NaN row gives token 0."""
@@ -358,7 +392,7 @@ def bf16_argmax(bits_row) -> int:
 
 
 def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int = 0,
-                return_trace: bool = False):
+                return_trace: bool = False, top_k: int = 0, top_p: float = 1.0):
     """Lossless verify of K drafted tokens against target logits [B, K+1, V].
 
     [FT] "Details", sampled verify: accept with min(1, p/q); on a reject resample
@@ -375,6 +409,9 @@ def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int 
       p_K with u_res of position K.
     T = 0: g_t = argmax l_t; accept while tokens[t] == g_t; commit g at the first
     mismatch, or the bonus g_K.
+    With top_k > 0 or top_p < 1 (T > 0 only), p_t is the filtered target distribution
+    of `filtered_target_probs` throughout: the accept test, the residual max(0, p - q),
+    the bonus and the fallbacks.  Without them the rule is the one above unchanged.
 
     Readings taken for malformed rows (status bits):
       bit 0  a target row of the request holds NaN or +inf (T > 0): nothing is committed.
@@ -399,7 +436,7 @@ def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int 
     if temperature != 0.0:
         U_acc, U_res = verify_uniforms(seed, np.arange(B_)[:, None], np.arange(K + 1)[None, :])
     for b in range(B_):
-        tr = {"accepts": [], "resample": None}
+        tr = {"accepts": [], "resample": None, "topp_margin": []}
         traces.append(tr)
         ids_bad = np.any((tokens[b] < 0) | (tokens[b] >= V)) or np.any((cand_idx[b] < 0) | (cand_idx[b] >= V))
         if temperature == 0.0:
@@ -419,7 +456,11 @@ def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int 
         if np.any(np.isnan(logits) | (logits == np.inf)):
             status[b] |= 1
             continue
-        p = np.stack([target_probs(target_bits[b, t], temperature) for t in range(K + 1)])
+        if top_k > 0 or top_p < 1.0:
+            p = np.stack([filtered_target_probs(target_bits[b, t], temperature, top_k, top_p, tr["topp_margin"])
+                          for t in range(K + 1)])
+        else:
+            p = np.stack([target_probs(target_bits[b, t], temperature) for t in range(K + 1)])
         qb = np.asarray(q[b], dtype=np.float64)
         q_bad = False
         for t in range(K):

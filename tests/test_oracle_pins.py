@@ -507,6 +507,115 @@ def test_spec_accept_monte_carlo_marginals():
     assert (n_acc >= 1).mean() > 0.2                  # the accept path is exercised too
 
 
+# ---------------------------------------------------------------- filtered verify --
+
+
+def test_filtered_probs_hand_fixture():
+    # logits 2, 0, 1, 3, 1, -1 (all exact in bf16); order by (value desc, id asc): 3, 0, 2, 4, 1, 5
+    bits = synth.f32_to_bf16_bits(np.array([2, 0, 1, 3, 1, -1], np.float32))
+    e = np.e
+    p = oracle.filtered_target_probs(bits, 1.0, top_k=3)
+    np.testing.assert_allclose(p, np.array([e ** 2, 0, e, e ** 3, 0, 0]) / (e ** 3 + e ** 2 + e), rtol=1e-14)
+    # top-p 0.7 over those three: p(3) = 0.665 < 0.7, so token 0 is kept too; the mass
+    # before token 2 is 0.910 >= 0.7, so it is dropped
+    p = oracle.filtered_target_probs(bits, 1.0, top_k=3, top_p=0.7)
+    np.testing.assert_allclose(p, np.array([1 / (1 + e), 0, 0, 1 / (1 + 1 / e), 0, 0]), rtol=1e-14)
+    # top-p alone: p(3) = e^3 / (e^3 + e^2 + 2e + 1 + 1/e) = 0.586 >= 0.5 keeps token 3 only
+    p = oracle.filtered_target_probs(bits, 1.0, top_p=0.5)
+    np.testing.assert_array_equal(p, np.array([0, 0, 0, 1.0, 0, 0]))
+    # temperature 2, top-k 2: p(3) : p(0) = e^1.5 : e^1
+    p = oracle.filtered_target_probs(bits, 2.0, top_k=2)
+    np.testing.assert_allclose(p, np.array([1 / (1 + e ** 0.5), 0, 0, 1 / (1 + e ** -0.5), 0, 0]), rtol=1e-14)
+    # the tie at value 1 goes to the lower id: top-k 3 keeps token 2, not token 4;
+    # top-k 4 keeps both, and not token 1 (value 0)
+    p = oracle.filtered_target_probs(bits, 1.0, top_k=3)
+    assert p[4] == 0 and p[2] > 0
+    p = oracle.filtered_target_probs(bits, 1.0, top_k=4)
+    assert p[4] > 0 and p[2] == p[4] and p[1] == 0 and p[5] == 0
+    # the margin to the top-p cut: |0.665 - 0.7| (token 0 kept) and |0.910 - 0.7| (token 2 dropped)
+    m = []
+    oracle.filtered_target_probs(bits, 1.0, top_k=3, top_p=0.7, margin=m)
+    assert abs(m[0] - abs(e ** 3 / (e ** 3 + e ** 2 + e) - 0.7)) < 1e-14
+
+
+def test_filtered_probs_without_filters_is_the_softmax():
+    rng = np.random.default_rng(31)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal(300).astype(np.float32) * 3)
+    for T in (1.0, 0.4):
+        np.testing.assert_allclose(oracle.filtered_target_probs(bits, T), oracle.target_probs(bits, T),
+                                   rtol=1e-12, atol=1e-300)
+        np.testing.assert_allclose(oracle.filtered_target_probs(bits, T, top_k=300, top_p=1.0),
+                                   oracle.target_probs(bits, T), rtol=1e-12, atol=1e-300)
+        p = oracle.filtered_target_probs(bits, T, top_k=20, top_p=0.9)
+        assert abs(p.sum() - 1) < 1e-12 and 1 <= np.count_nonzero(p) <= 20
+        # the kept set is a prefix of the value order, and its mass before the last kept
+        # token is below 0.9 while the full top-20 mass reaches it
+        order = np.lexsort((np.arange(300), -oracle.bf16_to_f64(bits)))
+        n = np.count_nonzero(p)
+        assert np.all(p[order[:n]] > 0)
+        p20 = oracle.filtered_target_probs(bits, T, top_k=20)
+        cum = np.cumsum(p20[order[:20]])
+        assert (n == 1 or cum[n - 2] < 0.9) and (n == 20 or cum[n - 1] >= 0.9)
+
+
+def test_filtered_verify_with_top1_is_the_greedy_prefix_match():
+    # top-k 1 (or a tiny top-p) leaves a one-hot p at the argmax: a draft equal to it is
+    # always accepted, any other is rejected and the residual's only mass is the argmax
+    rng = np.random.default_rng(32)
+    B_, K, V = 40, 4, 64
+    bits = synth.f32_to_bf16_bits(rng.standard_normal((B_, K + 1, V)).astype(np.float32))
+    g = np.array([[oracle.bf16_argmax(bits[b, t]) for t in range(K + 1)] for b in range(B_)])
+    cand = np.stack([np.stack([rng.choice(V, 16, replace=False) for _ in range(K)]) for _ in range(B_)])
+    for b in range(B_):
+        for t in range(K):
+            if rng.random() < 0.7:
+                cand[b, t, rng.integers(16)] = g[b, t] if g[b, t] not in cand[b, t] else cand[b, t, 0]
+    q = rng.dirichlet(np.ones(16), size=(B_, K))
+    tokens = cand[:, :, 0].copy()
+    for b in range(B_):                               # prefixes of several lengths
+        for t in range(b % (K + 1)):
+            if g[b, t] in cand[b, t]:
+                tokens[b, t] = g[b, t]
+    ref, ref_n, _ = oracle.spec_accept(bits, tokens, cand, None, 0.0)
+    for kw in ({"top_k": 1}, {"top_p": 1e-12}, {"top_k": 7, "top_p": 1e-12}):
+        out, n, st = oracle.spec_accept(bits, tokens, cand, q, 1.0, seed=5, **kw)
+        assert np.all(st == 0)
+        np.testing.assert_array_equal(out, ref)
+        np.testing.assert_array_equal(n, ref_n)
+
+
+def test_filtered_verify_monte_carlo_marginals():
+    # The speculative-sampling theorem with the filtered target: conditional on reaching
+    # position t, the committed token is distributed as the filtered p_t, which is 0
+    # outside the kept set.  10^5 requests, V = 24, top-k 6, top-p 0.8.
+    rng = np.random.default_rng(33)
+    V, K, T, nreq, top_k, top_p = 24, 2, 1.0, 100000, 6, 0.8
+    draft = rng.standard_normal((K, V)).astype(np.float32) * 1.5
+    target = (draft + 0.7 * rng.standard_normal((K, V))).astype(np.float32)
+    target = np.concatenate([target, rng.standard_normal((1, V)).astype(np.float32)])
+    tbits = synth.f32_to_bf16_bits(target)
+    cand = np.stack([np.argsort(-draft[t], kind="stable")[:16] for t in range(K)])
+    S = np.zeros((K, 16, 16))
+    for t in range(K):
+        S[t] = draft[t, cand[t]][None, :] + 0.3 * rng.standard_normal((16, 16))
+    tokens, slots, q = oracle.walk(np.broadcast_to(S, (nreq, K, 16, 16)), np.broadcast_to(cand, (nreq, K, 16)), T,
+                                   seed=41)
+    out, n_acc, st = oracle.spec_accept(np.broadcast_to(tbits, (nreq, K + 1, V)), tokens,
+                                        np.broadcast_to(cand, (nreq, K, 16)), q, T, seed=42, top_k=top_k, top_p=top_p)
+    assert np.all(st == 0)
+    tol = 5e-3 * np.sqrt(10)
+    for t in range(K + 1):
+        reach = out[:, t] >= 0
+        if reach.sum() < 10000:
+            continue
+        p = oracle.filtered_target_probs(tbits[t], T, top_k, top_p)
+        assert 2 <= np.count_nonzero(p) < top_k       # the cut is active at this position
+        freq = np.bincount(out[reach, t], minlength=V) / reach.sum()
+        assert np.all(freq[p == 0] == 0)
+        assert np.abs(freq - p).max() < tol, (t, np.abs(freq - p).max())
+    assert (n_acc >= 1).mean() > 0.1
+
+
 def test_philox_matches_rocrand_header_engine(tmp_path):
     # rocRAND ships an independent Philox4x32-10 as a header; compile a host program
     # against it and compare whole output blocks on random counters and keys.
