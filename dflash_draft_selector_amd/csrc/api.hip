@@ -4,6 +4,7 @@
 
 #include "dflash2.h"
 #include "dflash2_internal.h"
+#include "filter.h"
 #include "topk_dev.h"
 
 using namespace df2;
@@ -47,6 +48,17 @@ dflash2_status check_bk(int64_t batch, int64_t K) {
 }
 
 dflash2_status check_temp(float t) { return (t >= 0.f && !isnan(t) && !isinf(t)) ? DFLASH2_OK : DFLASH2_ERR_VALUE; }
+
+struct FilteredWs {
+  AcceptWs acc;      // the greedy path (temperature 0)
+  FilterWs filt;
+};
+FilteredWs carve_filtered(Carver& c, int64_t nrows, int64_t vocab) {
+  FilteredWs w;
+  w.acc = carve_accept(c, nrows, vocab);
+  w.filt = carve_filter(c, nrows, vocab);
+  return w;
+}
 
 template <typename WsT, typename F>
 dflash2_status carve_checked(void* ws, size_t bytes, F&& carve, WsT* out) {
@@ -261,6 +273,43 @@ dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, in
   if (st != DFLASH2_OK) return st;
   return hip_status(launch_spec_accept(target_logits, ld, batch_stride, tokens, cand_idx, q, (int)batch, (int)K,
                                        (int)vocab, temperature, seed, out_tokens, n_accepted, row_status, ws, stream));
+}
+
+size_t dflash2_spec_accept_filtered_workspace(int64_t batch, int64_t K, int64_t vocab) {
+  if (batch < 1 || K < 1 || vocab < 1) return 0;
+  Carver c(nullptr);
+  carve_filtered(c, batch * (K + 1), vocab);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_spec_accept_filtered(const uint16_t* target_logits, int64_t ld, int64_t batch_stride,
+                                            const int32_t* tokens, const int32_t* cand_idx, const float* q,
+                                            int64_t batch, int64_t K, int64_t vocab, float temperature,
+                                            int32_t top_k, float top_p, uint64_t seed, int32_t* out_tokens,
+                                            int32_t* n_accepted, int32_t* row_status, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  const int64_t nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
+  st = check_logits(target_logits, nrows, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  if (batch_stride < 0 || (batch_stride > 0 && batch_stride < (K + 1) * ld)) return DFLASH2_ERR_SHAPE;
+  if (batch_stride % 8 != 0) return DFLASH2_ERR_ALIGN;
+  if (!items_ok(nrows * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
+  if (!tokens || !cand_idx || !out_tokens || !n_accepted) return DFLASH2_ERR_NULL;
+  st = check_temp(temperature);
+  if (st != DFLASH2_OK) return st;
+  if (top_k < 1 || top_k > DFLASH2_MAX_TOPK || !(top_p > 0.f && top_p <= 1.f)) return DFLASH2_ERR_VALUE;
+  if (temperature > 0.f && !q) return DFLASH2_ERR_NULL;
+  FilteredWs ws;
+  st = carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_filtered(c, nrows, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  if (temperature == 0.f)
+    return hip_status(launch_spec_accept(target_logits, ld, batch_stride, tokens, cand_idx, q, (int)batch, (int)K,
+                                         (int)vocab, 0.f, seed, out_tokens, n_accepted, row_status, ws.acc, stream));
+  return hip_status(launch_spec_accept_filtered(target_logits, ld, batch_stride, tokens, cand_idx, q, (int)batch,
+                                                (int)K, (int)vocab, temperature, top_k, top_p, seed, out_tokens,
+                                                n_accepted, row_status, ws.filt, stream));
 }
 
 }  // extern "C"

@@ -53,6 +53,10 @@ _SIGNATURES = {
     "dflash2_spec_accept_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_spec_accept": ([_c_ptr, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _f32, _u64, _c_ptr,
                              _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_spec_accept_filtered_workspace": ([_i64, _i64, _i64], _size),
+    "dflash2_spec_accept_filtered": ([_c_ptr, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _f32,
+                                      ctypes.c_int32, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr],
+                                     _int),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -342,6 +346,17 @@ def conv2tap(x, x_prev, taps, group: int = 1, y=None):
 def spec_accept(target_logits, tokens, cand_idx, q, temperature: float, seed: int = 0, shared_target: bool = False):
     """Verify drafts [B, K] against target logits [B, K+1, V] (or [K+1, V] shared by every
     request when shared_target).  Returns (out_tokens [B, K+1], n_accepted [B], row_status [B])."""
+    return _spec_accept(target_logits, tokens, cand_idx, q, temperature, seed, shared_target, None, None)
+
+
+def spec_accept_filtered(target_logits, tokens, cand_idx, q, temperature: float, top_k: int, top_p: float,
+                         seed: int = 0, shared_target: bool = False):
+    """spec_accept against the target distribution after top-k (1..32) then top-p (0, 1]
+    filtering; same layouts and outputs."""
+    return _spec_accept(target_logits, tokens, cand_idx, q, temperature, seed, shared_target, top_k, top_p)
+
+
+def _spec_accept(target_logits, tokens, cand_idx, q, temperature, seed, shared_target, top_k, top_p):
     lib = load_library()
     dev = tokens.device
     _need(target_logits, "target_logits", _BF16_LIKE, dev)
@@ -365,9 +380,18 @@ def spec_accept(target_logits, tokens, cand_idx, q, temperature: float, seed: in
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     st = torch.empty((B,), dtype=torch.int32, device=dev)
-    nbytes = lib.dflash2_spec_accept_workspace(1 if shared_target else B, K, V)
-    ws = workspace("spec_accept", nbytes, dev, (B if not shared_target else -1, K, V))
-    _check(lib.dflash2_spec_accept(_ptr(target_logits), ld, bstride, _ptr(tokens), _ptr(cand_idx), _ptr(q), B, K, V,
-                                   float(temperature), int(seed) & (2 ** 64 - 1), _ptr(out), _ptr(nacc), _ptr(st),
-                                   _ptr(ws), ws.numel(), _stream()), "dflash2_spec_accept")
+    seed = int(seed) & (2 ** 64 - 1)
+    if top_k is None:
+        nbytes = lib.dflash2_spec_accept_workspace(1 if shared_target else B, K, V)
+        ws = workspace("spec_accept", nbytes, dev, (B if not shared_target else -1, K, V))
+        _check(lib.dflash2_spec_accept(_ptr(target_logits), ld, bstride, _ptr(tokens), _ptr(cand_idx), _ptr(q), B, K,
+                                       V, float(temperature), seed, _ptr(out), _ptr(nacc), _ptr(st), _ptr(ws),
+                                       ws.numel(), _stream()), "dflash2_spec_accept")
+    else:
+        nbytes = lib.dflash2_spec_accept_filtered_workspace(1 if shared_target else B, K, V)
+        ws = workspace("spec_accept_filtered", nbytes, dev, (B if not shared_target else -1, K, V))
+        _check(lib.dflash2_spec_accept_filtered(_ptr(target_logits), ld, bstride, _ptr(tokens), _ptr(cand_idx),
+                                                _ptr(q), B, K, V, float(temperature), int(top_k), float(top_p), seed,
+                                                _ptr(out), _ptr(nacc), _ptr(st), _ptr(ws), ws.numel(), _stream()),
+                                       "dflash2_spec_accept_filtered")
     return out, nacc, st

@@ -46,6 +46,7 @@ extern "C" {
 #define DFLASH2_ABI_VERSION 1
 #define DFLASH2_NCAND 16       /* candidates per draft position */
 #define DFLASH2_MAX_K 64       /* draft positions per request */
+#define DFLASH2_MAX_TOPK 32    /* largest top_k of the filtered verify */
 
 typedef enum dflash2_status {
   DFLASH2_OK = 0,
@@ -251,6 +252,32 @@ dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, in
                                    uint64_t seed, int32_t* out_tokens, int32_t* n_accepted,
                                    int32_t* row_status, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* ---- dflash2_spec_accept_filtered ---------------------------------------------
+ * The verify of dflash2_spec_accept against the filtered target distribution of the
+ * FreeToken runs' sampling settings (FreeToken PR "Adds DFlash 2", "Speed" and "All
+ * settings": temperature 1.0, top_p 0.95, top_k 20; "Known gaps": the sparse-q verify
+ * with top-k + top-p).  For temperature > 0, p_t of target row t is:
+ *   the top_k largest logits of the row (value desc, lowest id first on ties), exactly
+ *   top_k of them; softmax(l / T) over those; then, walking them in that order, every
+ *   token whose preceding mass is below top_p (the token reaching top_p is kept;
+ *   top_p >= 1 cuts nothing); renormalised.  Every other token has p = 0.
+ * That p replaces softmax(l / T) everywhere in the rule of dflash2_spec_accept: the
+ * accept test, the residual max(0, p - q), the bonus token and the fallbacks, with the
+ * same Philox counters, status bits and outputs.  temperature == 0 is the greedy
+ * prefix match of dflash2_spec_accept (the filters keep the argmax).
+ * Arguments and layouts as dflash2_spec_accept, plus top_k in [1, DFLASH2_MAX_TOPK] and
+ * top_p in (0, 1].  The workspace (dflash2_spec_accept_filtered_workspace bytes, any
+ * contents) holds each 1/8 chunk's top_k and is rewritten by every call.
+ * Errors: as dflash2_spec_accept; top_k or top_p out of range -> DFLASH2_ERR_VALUE.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_spec_accept_filtered_workspace(int64_t batch, int64_t K, int64_t vocab);
+dflash2_status dflash2_spec_accept_filtered(const uint16_t* target_logits, int64_t ld, int64_t batch_stride,
+                                            const int32_t* tokens, const int32_t* cand_idx, const float* q,
+                                            int64_t batch, int64_t K, int64_t vocab, float temperature,
+                                            int32_t top_k, float top_p, uint64_t seed, int32_t* out_tokens,
+                                            int32_t* n_accepted, int32_t* row_status, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

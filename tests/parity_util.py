@@ -85,11 +85,11 @@ def check_walk(S_ref, cand_idx, tokens, slots, q, temperature, seed):
     return stats
 
 
-def check_accept(target_bits, tokens, cand_idx, q, temperature, seed, out, n_acc, status):
+def check_accept(target_bits, tokens, cand_idx, q, temperature, seed, out, n_acc, status, top_k=0, top_p=1.0):
     """Compare a verify with the oracle; differences are allowed only where the oracle's
-    own accept test or inverse-CDF draw lies within BAND of a boundary."""
+    own accept test, inverse-CDF draw or top-p cut lies within BAND of a boundary."""
     ref_out, ref_n, ref_st, traces = oracle.spec_accept(target_bits, tokens, cand_idx, q, temperature, seed,
-                                                        return_trace=True)
+                                                        return_trace=True, top_k=top_k, top_p=top_p)
     stats = {"requests": int(tokens.shape[0]), "band": 0}
     np.testing.assert_array_equal(status, ref_st)
     for b in range(tokens.shape[0]):
@@ -100,10 +100,13 @@ def check_accept(target_bits, tokens, cand_idx, q, temperature, seed, out, n_acc
         for (t, u, qx, px, acc) in tr["accepts"]:
             if abs(u * qx - px) <= BAND * max(px, u * qx):
                 near = True
+        if any(m <= BAND for m in tr.get("topp_margin", [])):
+            near = True
         if tr["resample"] is not None and not near:
             t, kind, u = tr["resample"]
             bits = np.asarray(target_bits[b, t])
-            p = oracle.target_probs(bits, temperature)
+            p = (oracle.filtered_target_probs(bits, temperature, top_k, top_p) if top_k > 0 or top_p < 1.0
+                 else oracle.target_probs(bits, temperature))
             if kind == "residual":
                 qfull = np.zeros(p.size)
                 np.add.at(qfull, cand_idx[b, t], q[b, t])

@@ -29,7 +29,7 @@ def _declared():
 def test_header_declares_the_six_calls_and_the_fused_step():
     names = _declared()
     for n in ("dflash2_topk16", "dflash2_context_gate", "dflash2_pair_score", "dflash2_walk", "dflash2_conv2tap",
-              "dflash2_spec_accept", "dflash2_select"):
+              "dflash2_spec_accept", "dflash2_select", "dflash2_spec_accept_filtered"):
         assert n in names
 
 
@@ -118,6 +118,18 @@ def test_host_validation_before_any_launch():
                                    NULL) == 2
     assert lib.dflash2_spec_accept(FAKE, 4096, 8 * 4096 + 4, FAKE, FAKE, FAKE, 2, 7, 4096, 1.0, 0, FAKE, FAKE, NULL, ws,
                                    big, NULL) == 3
+    # filtered verify: the spec_accept checks, then top_k in [1, 32] and top_p in (0, 1]
+    fv = lambda top_k=20, top_p=0.95, q=FAKE, T=1.0, wsb=big, K=7: lib.dflash2_spec_accept_filtered(
+        FAKE, 4096, 8 * 4096, FAKE, FAKE, q, 2, K, 4096, T, top_k, top_p, 0, FAKE, FAKE, NULL, ws, wsb, NULL)
+    assert fv(K=65) == 2
+    assert fv(T=-1.0) == 6
+    for bad_k, bad_p in ((0, 0.95), (33, 0.95), (-1, 0.95), (20, 0.0), (20, 1.5), (20, float("nan")), (20, -0.1)):
+        assert fv(top_k=bad_k, top_p=bad_p) == 6, (bad_k, bad_p)
+    assert fv(q=NULL) == 1
+    assert fv(q=NULL, T=0.0, wsb=16) == 5               # q may be NULL when greedy; the workspace is still checked
+    need = lib.dflash2_spec_accept_filtered_workspace(2, 7, 4096)
+    assert need > lib.dflash2_spec_accept_workspace(2, 7, 4096)
+    assert fv(wsb=need - 257) == 5
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
