@@ -323,6 +323,12 @@ def main():
         "spec_accept_greedy": lambda i: dflash2.spec_accept(targets[i], sel["tokens"], sel["cand_idx"], sel["q"], 0.0, 0),
         "spec_accept_sampled_T1": lambda i: dflash2.spec_accept(targets[i], sel_t["tokens"], sel_t["cand_idx"],
                                                                 sel_t["q"], 1.0, 7),
+        # the FreeToken runs' sampling filters (T 1, top-k 20, top-p 0.95); also at the
+        # pages' sparse-q verify microbenchmark shape of 4 requests
+        "spec_accept_filtered_T1_k20_p095": lambda i: dflash2.spec_accept_filtered(
+            targets[i], sel_t["tokens"], sel_t["cand_idx"], sel_t["q"], 1.0, 20, 0.95, 7),
+        "spec_accept_filtered_B4_T1_k20_p095": lambda i: dflash2.spec_accept_filtered(
+            targets[i][:4], sel_t["tokens"][:4], sel_t["cand_idx"][:4], sel_t["q"][:4], 1.0, 20, 0.95, 7),
     }
     dflash2.select(logits[0], verified, A, Bt, H, 1.0, 7, out=sel_t)   # a sampled draft for the sampled verify
     components = {}
@@ -331,7 +337,7 @@ def main():
             for i in range(nbuf):
                 fn(i)
         torch.cuda.synchronize()
-        if name == "spec_accept_sampled_T1":
+        if name.startswith("spec_accept_sampled") or name.startswith("spec_accept_filtered"):
             dflash2.select(logits[0], verified, A, Bt, H, 1.0, 7, out=sel_t)
             torch.cuda.synchronize()
         components[name] = round(time_graph(fn, 3, 1), 2)

@@ -12,7 +12,7 @@
 // maxima (at least top_k logits reach it); it gathers the logits at or above the bound
 // and ranks them.  No LDS is shared between waves and there is no barrier.
 // Pass 2 (k_filter_decide), one work-group per request: each wave merges one row's
-// sub-chunk lists into the row's top_k (pruned by the largest list's top_k-th entry),
+// sub-chunk lists into the row's top_k (pruned by a bound from the lists' heads),
 // forms the filtered p over them; wave 0 runs the accept tests and the draw over at most
 // top_k tokens, in token-id order.
 #include "dflash2.h"
@@ -24,6 +24,7 @@
 namespace df2 {
 
 constexpr int kFiltCap = 128;                  // logits a wave gathers before its exact path
+constexpr int kFiltVecCap = 64;                // candidate vectors a wave stages
 constexpr int kFiltThreads = 512;              // pass 2
 constexpr int kFiltWaves = kFiltThreads / kWave;
 constexpr int kFiltRowCap = 256;               // pruned list entries a deciding wave keeps
@@ -104,25 +105,31 @@ __device__ __forceinline__ int gather_vector(unsigned long long* cw, int n, unsi
 // Rare sub-chunks with more than kFiltCap logits at or above the bound (ties at it): the
 // bound rises to the top_k-th best of the kFiltCap logits kept, which at least top_k
 // logits still reach, and the sub-chunk is gathered again from memory; each round leaves
-// out the kFiltCap - top_k kept logits below the new bound.  Rolled and out of line, to
-// keep the common path small.  Returns the count gathered (<= kFiltCap).
+// out the kFiltCap - top_k kept logits below the new bound.  With `regather` (more
+// candidate vectors than were staged) the first round gathers at `thr` itself.  Rolled
+// and out of line, to keep the common path small.  Returns the count gathered
+// (<= kFiltCap).
 __device__ __noinline__ int gather_raised(const uint16_t* __restrict__ rowp, int V, int s0, int s1, int top_k,
-                                          unsigned long long* cw, unsigned long long* thr_slot) {
+                                          unsigned long long thr, bool regather, unsigned long long* cw,
+                                          unsigned long long* thr_slot) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nfull = V >> 3;
   int n;
 #pragma unroll 1
   for (;;) {
-    wave_lds_sync();
-    for (int i = lane; i < kFiltCap; i += kWave) {
-      const unsigned long long x = cw[i];
-      int rank = 0;
-      for (int j = 0; j < kFiltCap; ++j) rank += cw[j] > x ? 1 : 0;
-      if (rank == top_k - 1) *thr_slot = x;
+    if (!regather) {
+      wave_lds_sync();
+      for (int i = lane; i < kFiltCap; i += kWave) {
+        const unsigned long long x = cw[i];
+        int rank = 0;
+        for (int j = 0; j < kFiltCap; ++j) rank += cw[j] > x ? 1 : 0;
+        if (rank == top_k - 1) *thr_slot = x;
+      }
+      wave_lds_sync();
+      thr = *thr_slot;
+      wave_lds_sync();
     }
-    wave_lds_sync();
-    const unsigned long long thr = *thr_slot;
-    wave_lds_sync();
+    regather = false;
     n = 0;
 #pragma unroll 1
     for (int k = 0; k < kTopkVecPerThread; ++k) {
@@ -150,6 +157,8 @@ __global__ void __launch_bounds__(kTopkThreads) k_filter_topk(const uint16_t* __
                                                               int* __restrict__ flags) {
   __shared__ unsigned long long s_cand[kTopkWaves][kFiltCap];
   __shared__ unsigned long long s_thr[kTopkWaves];
+  __shared__ u32x4 s_vec[kTopkWaves][kFiltVecCap];
+  __shared__ int s_vpos[kTopkWaves][kFiltVecCap];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int r = blockIdx.x / nchunks;
   const int c = blockIdx.x - r * nchunks;
@@ -212,26 +221,51 @@ __global__ void __launch_bounds__(kTopkThreads) k_filter_topk(const uint16_t* __
   tau = tau > 0x7f80 ? 0x7f80 : tau;                           // never above +inf
   const int tkey = (int)bf16_key(order_to_bits(tau));
 
-  // ---- gather every logit whose key reaches the bound (the sub-chunk's top_k all do);
-  // a vector can hold one only if its signed maximum reaches tau - 1 (-0 sits one below
-  // +0 and shares its key)
+  // ---- gather every logit whose key reaches the bound (the sub-chunk's top_k all do):
+  // first the vectors that can hold one (signed maximum >= tau - 1: -0 sits one below
+  // +0 and shares its key) are staged in LDS, a few instructions per slot; then each
+  // lane tests the elements of one staged vector
   unsigned long long* cw = s_cand[wave];
-  int n = 0;
+  int nv = 0;
 #pragma unroll
   for (int k = 0; k < kTopkVecPerThread; ++k) {
     const int v = s0 + lane + k * kWave;
     const bool f = v < s1 && vmax[k] >= tau - 1;
-    if (__ballot(f) != 0ull) {
-      unsigned m8 = 0u;
-      if (f) {
-        const int lim = v < nfull ? 8 : V - 8 * v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m8 |= (unsigned)((e < lim) & ((int)bf16_key(elem_bits(d[k], e)) >= tkey)) << e;
+    const unsigned long long bal = __ballot(f);
+    if (bal != 0ull) {
+      const int at = nv + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (f && at < kFiltVecCap) {
+        s_vec[wave][at] = d[k];
+        s_vpos[wave][at] = v;
       }
-      n = gather_vector(cw, n, m8, d[k], v, kFiltCap);
+      nv += __popcll(bal);
     }
   }
-  if (n > kFiltCap) n = gather_raised(rowp, V, s0, s1, top_k, cw, &s_thr[wave]);
+  int n;
+  if (nv <= kFiltVecCap) {
+    wave_lds_sync();
+    n = 0;
+    for (int i0 = 0; i0 < nv; i0 += kWave) {          // uniform trip count
+      const int i = i0 + lane;
+      unsigned m8 = 0u;
+      u32x4 x = (u32x4){0u, 0u, 0u, 0u};
+      int v = 0;
+      if (i < nv) {
+        x = s_vec[wave][i];
+        v = s_vpos[wave][i];
+        const int lim = v < nfull ? 8 : V - 8 * v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m8 |= (unsigned)((e < lim) & ((int)bf16_key(elem_bits(x, e)) >= tkey)) << e;
+      }
+      n = gather_vector(cw, n, m8, x, v, kFiltCap);
+    }
+  } else {
+    n = kFiltCap + 1;                                 // more vectors than staged: gather from memory
+    s_thr[wave] = 0ull;
+  }
+  if (n > kFiltCap) n = gather_raised(rowp, V, s0, s1, top_k, (unsigned long long)tkey << 48, nv > kFiltVecCap, cw,
+                                      &s_thr[wave]);
   wave_lds_sync();
 
   // ---- rank the gathered logits (distinct composites); the best top_k, best first ---
@@ -259,7 +293,7 @@ struct FilterShared {
   unsigned long long thr[kFiltWaves];
   int draw_id[DFLASH2_MAX_TOPK];
   float draw_w[DFLASH2_MAX_TOPK];
-  int nonfinite;
+  int nonfinite_w[kFiltWaves];                   // each wave: one of its rows holds +inf or NaN
 };
 
 // Row `row` of the request: merge its sub-chunk lists into the row's top_k (by one wave),
@@ -269,16 +303,29 @@ __device__ __forceinline__ bool filter_row(const unsigned long long* __restrict_
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int nent = nsub * top_k;
   wave_lds_sync();                               // the previous row's reads of pool / top are done
-  // every list entry in flight at once (at most kFiltMaxEnt per lane)
+  // the sub-chunk flags, the list heads and every list entry (at most kFiltMaxEnt per
+  // lane), all in flight at once
+  const int per = kWave / nsub;
+  const int ls = lane / per, lj = lane - ls * per;
+  const bool head = ls < nsub && lj < top_k;
+  const int fl = F[lane < nsub ? lane : 0];
+  const unsigned long long hx = L[head ? ls * top_k + lj : 0];
   unsigned long long e[kFiltMaxEnt];
 #pragma unroll
   for (int j = 0; j < kFiltMaxEnt; ++j) {
     const int i = lane + j * kWave;
-    e[j] = i < nent ? L[i] : 0ull;
+    e[j] = L[i < nent ? i : 0];
   }
-  const bool nonfinite = __ballot(lane < nsub && F[lane] != 0) != 0ull;
-  // the bound: the largest top_k-th entry of a list (the row's top_k all reach it)
-  unsigned long long lb = wave_max_u64(lane < nsub ? L[lane * top_k + top_k - 1] : 0ull);
+  __builtin_amdgcn_sched_barrier(0);                 // every load issued before any is used
+#pragma unroll
+  for (int j = 0; j < kFiltMaxEnt; ++j)
+    if (lane + j * kWave >= nent) e[j] = 0ull;
+  const bool nonfinite = __ballot(lane < nsub && fl != 0) != 0ull;
+  // the bound: the top_k-th largest key among the best 64 / nsub entries of every
+  // list (at least top_k of the row's logits reach it, so its top_k all do; the
+  // row's best logits sit near the heads of the lists, so few others do)
+  const int hk = head ? (int)(hx >> 48) : 0;
+  unsigned long long lb = (unsigned long long)__builtin_amdgcn_readlane(wave_sort64_desc(hk), top_k - 1) << 48;
   unsigned long long* pool = sm.pool[wave];
   unsigned long long* top = sm.top[wave];
   for (;;) {
@@ -294,6 +341,20 @@ __device__ __forceinline__ bool filter_row(const unsigned long long* __restrict_
       np += __popcll(bal);
     }
     wave_lds_sync();
+    if (np <= kWave) {
+      // the usual case: one pooled entry per lane, ranked against the others through
+      // readlane (no LDS round trip per comparison)
+      const unsigned long long x = lane < np ? pool[lane] : 0ull;
+      const uint32_t xl = (uint32_t)x, xh = (uint32_t)(x >> 32);
+      int rank = 0;
+      for (int j = 0; j < np; ++j) {
+        const uint32_t yl = __builtin_amdgcn_readlane(xl, j), yh = __builtin_amdgcn_readlane(xh, j);
+        rank += (yh > xh || (yh == xh && yl > xl)) ? 1 : 0;
+      }
+      if (lane < np && rank < top_k) top[rank] = x;
+      for (int i = np + lane; i < top_k; i += kWave) top[i] = 0ull;
+      break;
+    }
     const int ns = np < kFiltRowCap ? np : kFiltRowCap;
     for (int i = lane; i < ns; i += kWave) {
       const unsigned long long x = pool[i];
@@ -355,25 +416,40 @@ __global__ void __launch_bounds__(kFiltThreads) k_filter_decide(const int32_t* _
   const float c2 = inv_t * kLog2e;
   const int nsub = nchunks * kSubPerChunk;
 
-  for (int e = tid; e < K * kNC; e += kFiltThreads) {
-    const int t = e >> 4, j = e & (kNC - 1);
-    sm.cand[t * kFiltNCP + j] = cand_idx[(size_t)b * K * kNC + e];
-    sm.q[t * kFiltNCP + j] = q[(size_t)b * K * kNC + e];
+  // the drafts, loaded into registers first so that their loads overlap the rows' list
+  // loads, and stored to LDS after
+  constexpr int kPer = DFLASH2_MAX_K * kNC / kFiltThreads;
+  int cv[kPer];
+  float qv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kFiltThreads;
+    const int ec = e < K * kNC ? e : 0;
+    cv[j] = cand_idx[(size_t)b * K * kNC + ec];
+    qv[j] = q[(size_t)b * K * kNC + ec];
   }
-  for (int e = tid; e < K; e += kFiltThreads) sm.tok[e] = tokens[(size_t)b * K + e];
-  if (tid == 0) sm.nonfinite = 0;
-  __syncthreads();
+  const int tv = tokens[(size_t)b * K + (tid < K ? tid : 0)];
   bool nf = false;
   for (int row = wave; row <= K; row += kFiltWaves) {
     const size_t at = (size_t)(rbase + row) * nsub;
     nf |= filter_row(lists + at * top_k, flags + at, nsub, top_k, top_p, c2, row, sm);
   }
-  if (lane == 0 && nf) atomicOr(&sm.nonfinite, 1);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kFiltThreads;
+    if (e < K * kNC) {
+      sm.cand[(e >> 4) * kFiltNCP + (e & (kNC - 1))] = cv[j];
+      sm.q[(e >> 4) * kFiltNCP + (e & (kNC - 1))] = qv[j];
+    }
+  }
+  if (tid < K) sm.tok[tid] = tv;
+  if (lane == 0) sm.nonfinite_w[wave] = nf ? 1 : 0;
   __syncthreads();
   if (wave != 0) return;
 
   // ---- the decision, in wave 0: lane t owns position t -------------------------------
-  if (sm.nonfinite) {                           // a target row holds +inf or NaN: commit nothing
+  if (__ballot(lane < kFiltWaves && sm.nonfinite_w[lane < kFiltWaves ? lane : 0] != 0) != 0ull) {
+    // a target row holds +inf or NaN: commit nothing
     for (int t = lane; t <= K; t += kWave) out_b[t] = -1;
     if (lane == 0) {
       n_accepted[b] = 0;
@@ -398,7 +474,9 @@ __global__ void __launch_bounds__(kFiltThreads) k_filter_decide(const int32_t* _
     }
     qok &= fabsf(sq - 1.f) <= 1e-3f;
     const int nk = sm.nkeep[lane];
-    for (int i = 0; i < nk; ++i) px = sm.keep_id[lane * kFiltKP + i] == x ? sm.keep_p[lane * kFiltKP + i] : px;
+#pragma unroll
+    for (int i = 0; i < DFLASH2_MAX_TOPK; ++i)
+      px = (i < nk && sm.keep_id[lane * kFiltKP + i] == x) ? sm.keep_p[lane * kFiltKP + i] : px;
   }
   const bool ids_bad = __ballot(bad) != 0ull;
   const bool q_bad = __ballot(lane < K && !(qok && (ids_bad || qx > 0.f))) != 0ull;
@@ -432,7 +510,8 @@ __global__ void __launch_bounds__(kFiltThreads) k_filter_decide(const int32_t* _
   }
   // token-id order: lane i's rank among the kept ids, then the weights in that order
   int rank = 0;
-  for (int j = 0; j < nk; ++j) rank += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
+#pragma unroll
+  for (int j = 0; j < DFLASH2_MAX_TOPK; ++j) rank += (j < nk && __builtin_amdgcn_readlane(id, j) < id) ? 1 : 0;
   if (lane < nk) {
     sm.draw_id[rank] = id;
     sm.draw_w[rank] = rv;
