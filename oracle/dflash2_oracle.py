@@ -507,3 +507,41 @@ def spec_accept(target_bits, tokens, cand_idx, q, temperature: float, seed: int 
     if return_trace:
         return out, n_acc, status, traces
     return out, n_acc, status
+
+
+# ----------------------------------------------------------------------------------
+# LM head with the top-16 taken from its output (the draft side's adjacent step)
+# ----------------------------------------------------------------------------------
+
+
+def bf16_bits_of(values) -> np.ndarray:
+    """bf16 bit patterns of values that are already bf16 numbers (exact, no rounding)."""
+    v = np.asarray(values, dtype=np.float64).astype(np.float32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def lmhead_logits(h_bits, w_bits):
+    """Draft logits of a shared LM head: l[r, v] = bf16( sum_d h[r, d] * W[v, d] ).
+
+    [FT] "Details", runtime: one draft forward over the block, then the target's LM
+    head gives the 16 candidates of every slot; [RFC] "Questions", item 4: the draft
+    shares the target's embedding and LM head.  The pages do not state the head's
+    arithmetic.  Reading: the product of bf16 hidden rows and a bf16 weight [V, D],
+    and logits stored as bf16, as the draft's logits are everywhere else on this
+    path.  The oracle rounds the exact dot product once (float64 sums of exact bf16
+    products are exact to about 1e-12 relative here), ties to even.
+
+    h_bits uint16 [R, D], w_bits uint16 [V, D].  Returns (exact float64 [R, V],
+    logit bits uint16 [R, V]).
+    """
+    h = bf16_to_f64(h_bits)
+    w = bf16_to_f64(w_bits)
+    exact = h @ w.T
+    return exact, bf16_bits_of(round_to_bf16(exact))
+
+
+def lmhead_topk16(h_bits, w_bits):
+    """The top-16 candidates of every draft slot straight from the LM head's inputs:
+    topk16 of lmhead_logits (same order: value desc, token id asc)."""
+    _, bits = lmhead_logits(h_bits, w_bits)
+    return topk16(bits)

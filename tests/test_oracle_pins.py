@@ -638,3 +638,47 @@ def test_philox_matches_rocrand_header_engine(tmp_path):
     ref = np.array([[int(v) for v in line.split()] for line in res.stdout.strip().splitlines()], dtype=np.uint64)
     got = np.stack(oracle.philox4x32_10(*cases.T), axis=1)
     np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- LM head + top-16 --
+
+
+def test_lmhead_identity_weight_reduces_to_topk16():
+    # W = I: the logits are the hidden row itself, so the result is the (pinned) top-16
+    rng = np.random.default_rng(5)
+    D = 48
+    h = synth.f32_to_bf16_bits(rng.normal(0, 3, (3, D)).astype(np.float32))
+    eye = synth.f32_to_bf16_bits(np.eye(D, dtype=np.float32))
+    _, bits = oracle.lmhead_logits(h, eye)
+    assert np.array_equal(bits, h)
+    idx, val = oracle.lmhead_topk16(h, eye)
+    ridx, rval = oracle.topk16(h)
+    assert np.array_equal(idx, ridx) and np.array_equal(val, rval)
+
+
+def test_lmhead_hand_fixture_nonsquare_with_ties():
+    # V = 48, D = 16, W[v] = (1 + v // 16) * e_(v % 16): logit v = (1 + v // 16) h[v % 16].
+    # Worked by hand: the three scaled copies of h, largest 16, ties (12 at ids 27 and
+    # 37, 7 at 15 and 25, 6 at 11, 17, 40) toward the lower id.  A transposed weight or
+    # a dropped scale changes the list.
+    h = np.array([0.5, 3, 1, 2.5, 0.25, 4, 1.5, 0.75, 2, 3.5, 0.125, 6, 5, 1.25, 0.375, 7], dtype=np.float32)
+    W = np.zeros((48, 16), dtype=np.float32)
+    for v in range(48):
+        W[v, v % 16] = 1 + v // 16
+    idx, val = oracle.lmhead_topk16(synth.f32_to_bf16_bits(h)[None, :], synth.f32_to_bf16_bits(W))
+    assert idx[0].tolist() == [47, 43, 44, 31, 27, 37, 41, 28, 33, 21, 35, 15, 25, 11, 17, 40]
+    assert val[0].tolist() == [21, 18, 15, 14, 12, 12, 10.5, 10, 9, 8, 7.5, 7, 7, 6, 6, 6]
+
+
+def test_lmhead_rounds_the_exact_sum_once():
+    # h = (1, 1, 1); each weight row's sum is worked by hand:
+    #   1 + 2^-8               halfway between 1 and 1 + 2^-7      -> even: 1       0x3F80
+    #   1 + 2^-7 + 2^-8        halfway between 1+2^-7 and 1+2^-6   -> even: 1+2^-6  0x3F82
+    #   1 + 2^-8 + 2^-30       just above halfway                  -> 1 + 2^-7      0x3F81
+    #                          (rounding to fp32 first would lose 2^-30 and give 1)
+    #   -(1 + 2^-8 + 2^-30)                                        -> -(1 + 2^-7)   0xBF81
+    h = synth.f32_to_bf16_bits(np.ones((1, 3), dtype=np.float32))
+    W = np.array([[1, 2.0**-8, 0], [1 + 2.0**-7, 2.0**-8, 0], [1, 2.0**-8, 2.0**-30],
+                  [-1, -(2.0**-8), -(2.0**-30)]], dtype=np.float32)
+    _, bits = oracle.lmhead_logits(h, synth.f32_to_bf16_bits(W))
+    assert bits[0].tolist() == [0x3F80, 0x3F82, 0x3F81, 0xBF81]
