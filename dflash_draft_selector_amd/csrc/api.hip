@@ -111,6 +111,29 @@ dflash2_status dflash2_topk16(const uint16_t* logits, int64_t rows, int64_t voca
   return hip_status(launch_topk16(logits, (int)rows, (int)vocab, ld, cand_idx, cand_val, row_status, ws, stream));
 }
 
+size_t dflash2_lmhead_topk16_workspace(int64_t rows, int64_t vocab) {
+  if (rows < 1 || vocab < 1) return 0;
+  Carver c(nullptr);
+  carve_lmhead(c, rows, vocab);
+  return c.off + 256;
+}
+
+dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64_t rows, int64_t hidden,
+                                     int64_t vocab, int32_t* cand_idx, float* cand_val, int32_t* row_status,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!h || !w || !cand_idx || !cand_val) return DFLASH2_ERR_NULL;
+  if (rows < 1 || rows > kMaxItems / 1024 || hidden < 256 || hidden % 256 != 0 || hidden > ((int64_t)1 << 20) ||
+      vocab < DFLASH2_NCAND || vocab > kMaxVocab)
+    return DFLASH2_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w)) return DFLASH2_ERR_ALIGN;
+  LmheadWs ws;
+  dflash2_status st =
+      carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_lmhead(c, rows, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_lmhead_topk16(h, w, (int)rows, (int)hidden, (int)vocab, cand_idx, cand_val, row_status,
+                                         ws, stream));
+}
+
 size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim) {
   if (rows < 1 || hidden < 1 || dim < 1) return 0;
   Carver c(nullptr);

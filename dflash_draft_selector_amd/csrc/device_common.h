@@ -11,6 +11,7 @@ constexpr int kWave = 64;     // CDNA wavefront width
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---- bf16 -------------------------------------------------------------------------
 

@@ -42,6 +42,13 @@ struct SelectGatedWs {
 SelectGatedWs carve_select_gated(Carver& c, int64_t batch, int64_t K, int64_t vocab, int64_t hidden, int64_t dim);
 int64_t fused_gate_blocks(int64_t rows, int64_t hidden, int64_t dim);
 
+struct LmheadWs {
+  unsigned long long* partials;   // [rows][tiles][16] per 256-column tile top-16s, best first
+};
+constexpr int kLmMaxRows = 128;   // rows per LM-head tile launch (eight 16-row MFMA tiles)
+int lmhead_tiles(int64_t vocab);
+LmheadWs carve_lmhead(Carver& c, int64_t rows, int64_t vocab);
+
 struct GateWs {
   float* partial;                 // [nsplit][rows][dim] slice sums (nsplit > 1)
   int nsplit;                     // slices of the hidden dimension
@@ -80,6 +87,10 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
                                float temperature, uint64_t seed, float* H_out, int32_t* cand_idx, float* cand_val,
                                float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
                                SelectGatedWs ws, hipStream_t s);
+
+hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+                                int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
+                                hipStream_t s);
 
 hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden,
                        int dim, int act, float* H, GateWs ws, hipStream_t s);

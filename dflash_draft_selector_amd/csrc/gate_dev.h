@@ -14,8 +14,6 @@
 
 namespace df2 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 __device__ __forceinline__ float gate_act(float x, int act) { return act == 0 ? 1.f / (1.f + expf(-x)) : x; }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -1,0 +1,274 @@
+// LM head with the top-16 taken in its epilogue: the draft logits
+// l[r, v] = bf16(sum_d h[r, d] W[v, d]) never reach memory, only every row's
+// top-16 per 256-column tile does ([FT] "Details", runtime: the target's LM head gives
+// 16 candidates per slot; [RFC] "Questions", item 4: the draft shares the target's LM
+// head).
+//
+// Stage 1, k_lmhead_tiles: one 512-thread work-group per 256 vocabulary columns (and
+// per group of up to 128 rows).  Each wave owns two 16-column tiles for every 16-row
+// tile, on v_mfma_f32_16x16x32_bf16 with fp32 accumulators.  W rows go straight from
+// HBM into the MFMA B operand (each lane 16 contiguous bytes of one W row per step),
+// loaded up to eight steps ahead in a register ring; the hidden rows (read by every
+// work-group, so cache-resident) are staged 256 dims at a time through LDS with an XOR
+// swizzle, so the 16 rows a wave reads per instruction sit in distinct banks.  The
+// epilogue rounds the accumulators to bf16, sorts each row's 32 columns per wave with
+// DPP bitonic networks and merges the eight wave lists of every row through LDS.
+// Stage 2, k_lmhead_merge: one work-group per row merges the row's sorted tile lists.
+//
+// Selection order: value descending, token id ascending, NaN below -inf (the order of
+// dflash2_topk16).
+#include "dflash2_internal.h"
+#include "topk_dev.h"
+
+namespace df2 {
+
+constexpr int kLmThreads = 512;                       // 8 waves
+constexpr int kLmWaves = kLmThreads / kWave;
+constexpr int kLmCols = kLmWaves * 2 * 16;            // 256 vocabulary columns per work-group
+constexpr int kLmSteps = 8;                           // 32-wide MFMA steps per LDS stage
+constexpr int kLmStageDims = kLmSteps * 32;           // 256 hidden dims per stage
+constexpr int kLmSlots = kLmStageDims / 8;            // 16-byte slots per staged row (32)
+constexpr int kLmMergeThreads = 1024;
+constexpr int kLmBurst = 2;                           // W ring refills per burst (steps)
+static_assert(kLmSteps % kLmBurst == 0, "bursts must tile a stage");
+
+int lmhead_tiles(int64_t vocab) { return (int)((vocab + kLmCols - 1) / kLmCols); }
+
+LmheadWs carve_lmhead(Carver& c, int64_t rows, int64_t vocab) {
+  LmheadWs w;
+  w.partials = c.take<unsigned long long>((size_t)rows * lmhead_tiles(vocab) * kNC);
+  return w;
+}
+
+// Byte offset of 16-byte slot c of staged row r: slot c ^ (r % 16) within each group of
+// 16 slots, so rows r..r+15 at one slot land on 16 different bank groups.
+__device__ __forceinline__ int lm_lds_off(int r, int c) { return r * (kLmSlots * 16) + ((c ^ (r & 15)) << 4); }
+
+// Signed 32-bit rank of a logit in tile column lc (0..255): order key in the high half
+// (offset to signed), 0xffff - lc in the low half.  INT_MIN marks a column past the
+// vocabulary (below every logit, NaN included).
+__device__ __forceinline__ int lm_rank(float x, int lc, bool valid) {
+  const int key = (int)bf16_key(f32_to_bf16_rne(x));
+  return valid ? (int)(((unsigned)(key - 0x8000) << 16) | (unsigned)(0xffff - lc)) : (int)0x80000000;
+}
+
+// Full descending sort of the 16 values held by each 16-lane row (Batcher's bitonic
+// sort: blocks of 2, 4, 8, then the 16-lane half-cleaners).
+__device__ __forceinline__ int row16_full_sort_i32(int x) {
+  x = bitonic_stage_i32<2, 1>(x);
+  x = bitonic_stage_i32<4, 2>(x);
+  x = bitonic_stage_i32<4, 1>(x);
+  x = bitonic_stage_i32<8, 4>(x);
+  x = bitonic_stage_i32<8, 2>(x);
+  x = bitonic_stage_i32<8, 1>(x);
+  return row16_bitonic_sort_i32(x);
+}
+
+// Tile list entry -> row composite of dflash2_topk16 (0 = empty).
+__device__ __forceinline__ unsigned long long lm_rank_to_rc(int rank, int col0) {
+  if (rank == (int)0x80000000) return 0ull;
+  const uint32_t key = (uint32_t)((rank >> 16) + 0x8000);
+  const uint32_t id = (uint32_t)(col0 + (0xffff - (rank & 0xffff)));
+  uint32_t bits;
+  if (key == 0u)
+    bits = 0x7fc0u;                                   // NaN
+  else if (key >= 0x8000u)
+    bits = key - 0x8000u;                             // +0 and positive values
+  else
+    bits = 0x8000u | (0x8000u - key);                 // negative values
+  return make_rc(key, id, bits);
+}
+
+template <int MT>
+__global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
+                                                              const uint16_t* __restrict__ w, int rows, int hidden,
+                                                              int vocab, int row0, int ntiles,
+                                                              unsigned long long* __restrict__ partials) {
+  // the staged hidden rows; reused by the epilogue for the waves' sorted lists
+  __shared__ __align__(16) unsigned char lds[MT * 16 * kLmSlots * 16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int tile = blockIdx.x;
+  const int col0 = tile * kLmCols;
+  const int nstages = hidden / kLmStageDims;
+
+  // this lane's two W rows (a column past the vocabulary reads the last row, unused)
+  const uint16_t* wrow[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int col = col0 + 32 * wv + 16 * nt + i16;
+    wrow[nt] = w + (size_t)(col < vocab ? col : vocab - 1) * hidden + 8 * g;
+  }
+
+  // staging of one 256-dim stage of the hidden rows: thread slot e covers row
+  // (tid + 512 e) / 32, 16-byte slot (tid + 512 e) % 32; rows past the group are zero
+  auto load_h = [&](int st, u32x4 (&hp)[MT]) {
+#pragma unroll
+    for (int e = 0; e < MT; ++e) {
+      const int idx = tid + kLmThreads * e;
+      const int r = idx / kLmSlots, c = idx % kLmSlots;
+      const int grow = row0 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(h + (size_t)(grow < rows ? grow : rows - 1) * hidden +
+                                                      st * kLmStageDims + 8 * c);
+      hp[e] = grow < rows ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_h = [&](const u32x4 (&hp)[MT]) {
+#pragma unroll
+    for (int e = 0; e < MT; ++e) {
+      const int idx = tid + kLmThreads * e;
+      *reinterpret_cast<u32x4*>(lds + lm_lds_off(idx / kLmSlots, idx % kLmSlots)) = hp[e];
+    }
+  };
+
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[m][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // W ring: slot s holds step s of the current stage, refilled with step s of the next
+  u32x4 wr[kLmSteps][2];
+#pragma unroll
+  for (int s = 0; s < kLmSteps; ++s)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) wr[s][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + 32 * s);
+
+  u32x4 hp[MT];
+  load_h(0, hp);
+  store_h(hp);
+  __syncthreads();
+
+  for (int st = 0; st < nstages; ++st) {
+    const int nx = st + 1 < nstages ? st + 1 : st;     // the last stage reloads itself (unused)
+    load_h(nx, hp);
+#pragma unroll
+    for (int s = 0; s < kLmSteps; ++s) {
+      u32x4 a[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) a[m] = *reinterpret_cast<const u32x4*>(lds + lm_lds_off(16 * m + i16, 4 * s + g));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]),
+                                                               __builtin_bit_cast(bf16x8, wr[s][nt]), acc[m][nt],
+                                                               0, 0, 0);
+      // refill the ring kLmBurst steps at a time, so the two 64-byte halves of every
+      // 128-byte line of a W row are requested back to back (plain loads: the line
+      // stays in L2 for its second half; non-temporal loads measured 25% slower)
+      if ((s + 1) % kLmBurst == 0) {
+#pragma unroll
+        for (int b = s + 1 - kLmBurst; b <= s; ++b)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            wr[b][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)nx * kLmStageDims + 32 * b);
+      }
+    }
+    __syncthreads();
+    if (st + 1 < nstages) {
+      store_h(hp);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: per-row top-16 of the tile ---------------------------------------
+  // acc[m][nt][r] is row 16 m + 4 g + r, column 32 wv + 16 nt + i16 of the tile.
+  int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lc0 = 32 * wv + i16, lc1 = lc0 + 16;
+      int a = row16_full_sort_i32(lm_rank(acc[m][0][r], lc0, col0 + lc0 < vocab));
+      int b = row16_full_sort_i32(lm_rank(acc[m][1][r], lc1, col0 + lc1 < vocab));
+      const int x = row16_bitonic_sort_i32(max(a, dpp_i32<0x140>(b)));   // row_mirror: b ascending
+      lists[((16 * m + 4 * g + r) * kLmWaves + wv) * kNC + i16] = x;
+    }
+  }
+  __syncthreads();
+  // every wave merges the eight lists of rows wv, wv + 8, ...: lane row q takes lists
+  // 2q and 2q + 1 (the second reversed), then the rows merge pairwise
+  for (int rl = wv; rl < MT * 16; rl += kLmWaves) {
+    const int* L = lists + rl * kLmWaves * kNC;
+    int x = row16_bitonic_sort_i32(max(L[(2 * g) * kNC + i16], L[(2 * g + 1) * kNC + (kNC - 1 - i16)]));
+    x = row16_merge_rows_i32(x, 16);
+    x = row16_merge_rows_i32(x, 32);
+    const int grow = row0 + rl;
+    if (lane < kNC && grow < rows) partials[((size_t)grow * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x, col0);
+  }
+}
+
+// Top-16 of a row's ntiles sorted tile lists: 64 lane rows each merge every 64th list
+// in registers, the waves merge their four rows, and wave 0 the sixteen wave lists.
+__global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned long long* __restrict__ partials,
+                                                                   int ntiles, int32_t* __restrict__ cand_idx,
+                                                                   float* __restrict__ cand_val,
+                                                                   int32_t* __restrict__ row_status) {
+  constexpr int kGroups = kLmMergeThreads / kNC;      // 64 lane rows
+  constexpr int kBatch = 8;                           // lists loaded before merging
+  __shared__ unsigned long long wl[kLmMergeThreads / kWave][kNC];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int grp = tid >> 4, i = tid & 15;
+  const unsigned long long* src = partials + (size_t)row * ntiles * kNC;
+  unsigned long long x = 0ull;
+  for (int base = grp; base < ntiles; base += kGroups * kBatch) {
+    unsigned long long y[kBatch];
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+      const int t = base + kGroups * c;
+      y[c] = t < ntiles ? src[(size_t)t * kNC + (kNC - 1 - i)] : 0ull;   // reversed: merge16 takes b reversed
+    }
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) x = merge16(x, y[c]);
+  }
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 16));
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 32));
+  if (lane < kNC) wl[wv][lane] = x;
+  __syncthreads();
+  if (wv != 0) return;
+  const int q = lane >> 4;
+  x = wl[4 * q][i];
+#pragma unroll
+  for (int c = 1; c < 4; ++c) x = merge16(x, wl[4 * q + c][kNC - 1 - i]);
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 16));
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 32));
+  const float v = bf16_to_f32(rc_bits(x));
+  const bool bad = __ballot(lane < kNC && !__builtin_isfinite(v)) != 0ull;
+  if (lane < kNC) {
+    cand_idx[(size_t)row * kNC + lane] = x ? rc_id(x) : 0;
+    cand_val[(size_t)row * kNC + lane] = v;
+  }
+  if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
+}
+
+template <int MT>
+static void lmhead_tiles_launch(int ntiles, hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden,
+                                int vocab, int row0, unsigned long long* partials) {
+  hipLaunchKernelGGL((k_lmhead_tiles<MT>), dim3((unsigned)ntiles), dim3(kLmThreads), 0, s, h, w, rows, hidden, vocab,
+                     row0, ntiles, partials);
+}
+
+hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+                                int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
+                                hipStream_t s) {
+  const int ntiles = lmhead_tiles(vocab);
+  for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
+    const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
+    if (n <= 16)
+      lmhead_tiles_launch<1>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+    else if (n <= 32)
+      lmhead_tiles_launch<2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+    else if (n <= 64)
+      lmhead_tiles_launch<4>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+    else
+      lmhead_tiles_launch<8>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+  }
+  hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)rows), dim3(kLmMergeThreads), 0, s, ws.partials, ntiles, cand_idx,
+                     cand_val, row_status);
+  return hipGetLastError();
+}
+
+}  // namespace df2

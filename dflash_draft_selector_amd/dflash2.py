@@ -37,6 +37,8 @@ _SIGNATURES = {
     "dflash2_status_str": ([_int], ctypes.c_char_p),
     "dflash2_topk16_workspace": ([_i64, _i64], _size),
     "dflash2_topk16": ([_c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_lmhead_topk16_workspace": ([_i64, _i64], _size),
+    "dflash2_lmhead_topk16": ([_c_ptr, _c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_context_gate_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_context_gate": ([_c_ptr, _c_ptr, _int, _c_ptr, _i64, _i64, _i64, _int, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_pair_score": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr,
@@ -170,6 +172,27 @@ def topk16(logits: torch.Tensor, row_status: bool = False):
     ws = workspace("topk16", nbytes, dev, (rows, V))
     _check(lib.dflash2_topk16(_ptr(logits), rows, V, ld, _ptr(idx), _ptr(val), _ptr(st), _ptr(ws), ws.numel(),
                               _stream()), "dflash2_topk16")
+    return (idx, val, st) if row_status else (idx, val)
+
+
+def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
+    """Top-16 candidates of the bf16 logits h @ w.T without writing them: h bf16 [rows, D]
+    (or [..., D]), w bf16 [V, D].  Returns (idx int32 [..., 16], val f32 [..., 16])."""
+    lib = load_library()
+    _contig(_need(h, "h", _BF16_LIKE), "h")
+    _contig(_need(w, "w", _BF16_LIKE, h.device), "w")
+    if h.dim() < 2 or w.dim() != 2 or w.shape[1] != h.shape[-1]:
+        raise ValueError("lmhead_topk16: h [..., D] and w [V, D] must share D")
+    D, V = h.shape[-1], w.shape[0]
+    rows = h.numel() // D
+    dev = h.device
+    idx = torch.empty(h.shape[:-1] + (NCAND,), dtype=torch.int32, device=dev)
+    val = torch.empty(h.shape[:-1] + (NCAND,), dtype=torch.float32, device=dev)
+    st = torch.empty(h.shape[:-1], dtype=torch.int32, device=dev) if row_status else None
+    nbytes = lib.dflash2_lmhead_topk16_workspace(rows, V)
+    ws = workspace("lmhead_topk16", nbytes, dev, (rows, V))
+    _check(lib.dflash2_lmhead_topk16(_ptr(h), _ptr(w), rows, D, V, _ptr(idx), _ptr(val), _ptr(st), _ptr(ws),
+                                     ws.numel(), _stream()), "dflash2_lmhead_topk16")
     return (idx, val, st) if row_status else (idx, val)
 
 

@@ -135,3 +135,25 @@ def make_target(w: Workload, seed: int) -> np.ndarray:
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     """Reinterpret bf16 bit patterns as the float32 values they denote (exact widening)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def lmhead_inputs(rows: int, hidden: int, vocab: int, seed: int, peaks: bool = True) -> dict:
+    """Inputs of the LM head with the fused top-16: draft hidden rows h ~ N(0, 1) and a
+    weight W ~ N(0, 1/hidden), both rounded to bf16, drawn in that order from
+    ``default_rng(seed)``.  With ``peaks`` every row r gets a planted peak: W row
+    peak_r (uniform, drawn after W) is set to h_r * 8 / hidden, so its logit is about 8
+    against N(0, 1) for the rest (the c1-c4 recipe of one strong candidate per slot).
+    Returns uint16 bit patterns ``h_bits`` [rows, hidden] and ``w_bits`` [vocab, hidden]
+    (and ``peak_idx``)."""
+    rng = np.random.default_rng(seed)
+    h = _normal(rng, (rows, hidden), 1.0)
+    w = np.empty((vocab, hidden), dtype=np.uint16)
+    step = 8192
+    for v0 in range(0, vocab, step):
+        w[v0:v0 + step] = f32_to_bf16_bits(_normal(rng, (min(step, vocab - v0), hidden), float(np.sqrt(1.0 / hidden))))
+    out = {"h_bits": f32_to_bf16_bits(h), "w_bits": w}
+    if peaks:
+        pidx = rng.integers(0, vocab, size=rows)
+        w[pidx] = f32_to_bf16_bits(h * np.float32(8.0 / hidden))
+        out["peak_idx"] = pidx
+    return out

@@ -89,6 +89,33 @@ dflash2_status dflash2_topk16(const uint16_t* logits, int64_t rows, int64_t voca
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * LM head with the top-16 fused in: the candidates of dflash2_topk16 taken straight
+ * from the draft hidden rows and the (shared target) LM-head weight, without writing
+ * the logits.  [FT] "Details", runtime (the target LM head gives 16 candidates per
+ * slot); [RFC] "Questions", item 4 (the draft shares the target's LM head).
+ *
+ * logit[r, v] = bf16( sum_d h[r, d] * W[v, d] ): bf16 products accumulated in fp32 on
+ * the matrix cores, then rounded to bf16 (nearest even), the precision of the draft
+ * logits dflash2_topk16 reads.  The top-16 of each row is then taken in the order of
+ * dflash2_topk16 (value desc, id asc, NaN lowest).  Values near a bf16 rounding
+ * boundary may round either way against an exact sum (fp32 accumulation order).
+ *
+ * h          bf16 bits [rows, hidden], row-major, 16-byte aligned.
+ * w          bf16 bits [vocab, hidden], row-major, 16-byte aligned (read once per
+ *            group of up to 128 rows: a larger batch streams it once per 128 rows).
+ * cand_idx   int32 [rows, 16]; cand_val float [rows, 16] (the bf16 logits widened);
+ * row_status int32 [rows] or NULL: bit 0 if a selected value is not finite.
+ * Workspace: dflash2_lmhead_topk16_workspace bytes, any contents (every call writes
+ * what it reads): one sorted 16-list per row and 256-column tile.
+ * Errors: NULL pointers, rows < 1, hidden < 256 or hidden % 256 != 0, vocab < 16 or
+ *         > 2^19, alignment, workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_lmhead_topk16_workspace(int64_t rows, int64_t vocab);
+dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64_t rows, int64_t hidden,
+                                     int64_t vocab, int32_t* cand_idx, float* cand_val, int32_t* row_status,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * Context gate H = act(W_H h + b), one `dim`-wide gate per draft position.
  * [PEGA] "What upstream shipped", item 1 (256-dim token embeddings + context gate).
  * The gate is read as a logistic sigmoid of an affine map (DFLASH2_GATE_SIGMOID);
