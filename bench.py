@@ -201,6 +201,52 @@ def per_config_throughput(dflash2, torch, dev, stream, min_bytes=600 << 20):
     return out
 
 
+def lmhead_measure(dflash2, torch, dev, stream, reps=10):
+    """The LM head with the fused top-16 at the B=15, K=7 row count (105 rows), hidden
+    5120, the Qwen vocabulary: inputs drawn on the GPU (h ~ N(0, 1), W ~ N(0, 1/5120),
+    bf16).  W is 1.556 GB, six times the Infinity Cache, so every call streams it from
+    HBM.  Also times the unfused path (torch's bf16 GEMM writing the logits, then
+    dflash2_topk16) for context."""
+    R, D, V = 105, 5120, 151936
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    h = torch.randn(R, D, device=dev, generator=gen).to(torch.bfloat16)
+    wt = torch.empty(V, D, dtype=torch.bfloat16, device=dev)
+    for v0 in range(0, V, 16384):
+        n = min(16384, V - v0)
+        wt[v0:v0 + n] = (torch.randn(n, D, device=dev, generator=gen) * (1.0 / D) ** 0.5).to(torch.bfloat16)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(reps):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (2 * reps)
+
+    fused_us = timed(lambda: dflash2.lmhead_topk16(h, wt))
+    unfused_us = timed(lambda: dflash2.topk16(h @ wt.T))
+    nbytes = V * D * 2 + R * D * 2 + R * 16 * 8
+    gbs = nbytes / (fused_us * 1e-6) / 1e9
+    return {"rows": R, "hidden": D, "vocab": V, "us_per_call": round(fused_us, 1),
+            "roofline": {"bound": "hbm", "kernel": "dflash2_lmhead_topk16 = k_lmhead_tiles + k_lmhead_merge",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                         "tflops": round(2 * R * V * D / (fused_us * 1e-6) / 1e12, 1)},
+            "unfused_torch_matmul_plus_topk16_us": round(unfused_us, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +256,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload throughput table")
     ap.add_argument("--select-only", action="store_true", help="time only the select graph (for profiling)")
+    ap.add_argument("--lmhead-only", action="store_true", help="time only the fused LM head + top-16 (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 1 GiB buffer three times (a kernel of known traffic, to scale memory counters)")
     args = ap.parse_args()
@@ -232,6 +279,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.lmhead_only:
+        print(json.dumps({"metric": METRIC, "lmhead_topk16": lmhead_measure(dflash2, torch, dev, torch.cuda.Stream())}))
+        return
     w = synth.workload(2)
     inp = synth.make_inputs(w)
     target = synth.make_target(w, seed=102)
@@ -389,6 +439,7 @@ def main():
         "components_us_per_call": components,
         "wall_s": round(wall, 3),
     }
+    result["lmhead_topk16"] = lmhead_measure(dflash2, torch, dev, stream)
     if not args.no_configs:
         result["per_config"] = per_config_throughput(dflash2, torch, dev, stream)
     if not args.no_cpu_baseline:
