@@ -79,7 +79,8 @@ __device__ __forceinline__ unsigned long long lm_rank_to_rc(int rank, int col0) 
   return make_rc(key, id, bits);
 }
 
-template <int MT>
+// RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.
+template <int MT, int RING>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
                                                               const uint16_t* __restrict__ w, int rows, int hidden,
                                                               int vocab, int row0, int ntiles,
@@ -128,49 +129,68 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[m][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // W ring: slot s holds step s of the current stage, refilled with step s of the next
-  u32x4 wr[kLmSteps][2];
+  // W ring: RING half-stages of 4 steps in registers.  Half-stage hs runs on ring slot
+  // hs % RING and refills it, kLmBurst steps at a time, with half-stage hs + RING (past
+  // the end it reloads the last one: valid memory, never used), so the two 64-byte
+  // halves of every 128-byte line of a W row are requested back to back.  Plain loads:
+  // the line stays in L2 for its second half (non-temporal loads measured 25% slower).
+  constexpr int kHalf = kLmSteps / 2;
+  const int nhalves = 2 * nstages;
+  u32x4 wr0[kHalf][2], wr1[kHalf][2], wr2[kHalf][2];
+  auto fill = [&](u32x4 (&wr)[kHalf][2], int hs) {
+    hs = hs < nhalves ? hs : nhalves - 1;
 #pragma unroll
-  for (int s = 0; s < kLmSteps; ++s)
+    for (int s = 0; s < kHalf; ++s)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) wr[s][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + 32 * s);
+      for (int nt = 0; nt < 2; ++nt)
+        wr[s][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)hs * (kLmStageDims / 2) + 32 * s);
+  };
+  fill(wr0, 0);
+  fill(wr1, 1);
+  if constexpr (RING == 3) fill(wr2, 2);
 
   u32x4 hp[MT];
   load_h(0, hp);
   store_h(hp);
   __syncthreads();
 
-  for (int st = 0; st < nstages; ++st) {
-    const int nx = st + 1 < nstages ? st + 1 : st;     // the last stage reloads itself (unused)
-    load_h(nx, hp);
+  auto half = [&](int hs, u32x4 (&wr)[kHalf][2]) {
+    const int st = hs >> 1, part = hs & 1;
+    if (part == 0) load_h(st + 1 < nstages ? st + 1 : st, hp);   // the next staged hidden slice
+    const int nw = hs + RING < nhalves ? hs + RING : nhalves - 1;
 #pragma unroll
-    for (int s = 0; s < kLmSteps; ++s) {
-      u32x4 a[MT];
+    for (int s = 0; s < kHalf; ++s) {
+      const int step = kHalf * part + s;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) a[m] = *reinterpret_cast<const u32x4*>(lds + lm_lds_off(16 * m + i16, 4 * s + g));
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(lds + lm_lds_off(16 * m + i16, 4 * step + g));
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]),
+        for (int nt = 0; nt < 2; ++nt)
+          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                                __builtin_bit_cast(bf16x8, wr[s][nt]), acc[m][nt],
                                                                0, 0, 0);
-      // refill the ring kLmBurst steps at a time, so the two 64-byte halves of every
-      // 128-byte line of a W row are requested back to back (plain loads: the line
-      // stays in L2 for its second half; non-temporal loads measured 25% slower)
+      }
       if ((s + 1) % kLmBurst == 0) {
 #pragma unroll
         for (int b = s + 1 - kLmBurst; b <= s; ++b)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
-            wr[b][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)nx * kLmStageDims + 32 * b);
+            wr[b][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)nw * (kLmStageDims / 2) + 32 * b);
       }
     }
-    __syncthreads();
-    if (st + 1 < nstages) {
-      store_h(hp);
+    if (part == 1) {
       __syncthreads();
+      if (st + 1 < nstages) {
+        store_h(hp);
+        __syncthreads();
+      }
     }
+  };
+  for (int hs = 0; hs < nhalves; hs += RING) {
+    half(hs, wr0);
+    if (hs + 1 < nhalves) half(hs + 1, wr1);
+    if constexpr (RING == 3)
+      if (hs + 2 < nhalves) half(hs + 2, wr2);
   }
 
   // ---- epilogue: per-row top-16 of the tile ---------------------------------------
@@ -244,10 +264,10 @@ __global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned
   if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
 }
 
-template <int MT>
+template <int MT, int RING>
 static void lmhead_tiles_launch(int ntiles, hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden,
                                 int vocab, int row0, unsigned long long* partials) {
-  hipLaunchKernelGGL((k_lmhead_tiles<MT>), dim3((unsigned)ntiles), dim3(kLmThreads), 0, s, h, w, rows, hidden, vocab,
+  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING>), dim3((unsigned)ntiles), dim3(kLmThreads), 0, s, h, w, rows, hidden, vocab,
                      row0, ntiles, partials);
 }
 
@@ -258,13 +278,13 @@ hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, 
   for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
     const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
     if (n <= 16)
-      lmhead_tiles_launch<1>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_tiles_launch<1, 2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
     else if (n <= 32)
-      lmhead_tiles_launch<2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_tiles_launch<2, 2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
     else if (n <= 64)
-      lmhead_tiles_launch<4>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_tiles_launch<4, 3>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
     else
-      lmhead_tiles_launch<8>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_tiles_launch<8, 3>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
   }
   hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)rows), dim3(kLmMergeThreads), 0, s, ws.partials, ntiles, cand_idx,
                      cand_val, row_status);
