@@ -44,6 +44,8 @@ int64_t fused_gate_blocks(int64_t rows, int64_t hidden, int64_t dim);
 
 struct LmheadWs {
   unsigned long long* partials;   // [rows][tiles][16] per 256-column tile top-16s, best first
+  unsigned char* tail;            // fp32 partial tiles of a split last round
+  size_t tail_bytes;
 };
 constexpr int kLmMaxRows = 128;   // rows per LM-head tile launch (eight 16-row MFMA tiles)
 int lmhead_tiles(int64_t vocab);

@@ -29,14 +29,19 @@ constexpr int kLmSteps = 8;                           // 32-wide MFMA steps per 
 constexpr int kLmStageDims = kLmSteps * 32;           // 256 hidden dims per stage
 constexpr int kLmSlots = kLmStageDims / 8;            // 16-byte slots per staged row (32)
 constexpr int kLmMergeThreads = 1024;
+constexpr int kLmMaxParts = 8;                        // hidden-dimension parts of a split tile
 constexpr int kLmBurst = 2;                           // W ring refills per burst (steps)
 static_assert(kLmSteps % kLmBurst == 0, "bursts must tile a stage");
 
 int lmhead_tiles(int64_t vocab) { return (int)((vocab + kLmCols - 1) / kLmCols); }
 
+size_t lmhead_tail_bytes();
+
 LmheadWs carve_lmhead(Carver& c, int64_t rows, int64_t vocab) {
   LmheadWs w;
   w.partials = c.take<unsigned long long>((size_t)rows * lmhead_tiles(vocab) * kNC);
+  w.tail_bytes = lmhead_tail_bytes();
+  w.tail = c.take<unsigned char>(w.tail_bytes);
   return w;
 }
 
@@ -79,20 +84,69 @@ __device__ __forceinline__ unsigned long long lm_rank_to_rc(int rank, int col0) 
   return make_rc(key, id, bits);
 }
 
+// Per-row top-16 of one tile from the accumulators (the whole work-group calls it):
+// acc[m][nt][r] is row 16 m + 4 g + r, column 32 wv + 16 nt + i16 of the tile.  Rounds
+// to bf16, sorts each row's 32 columns per wave, merges the eight wave lists of every
+// row through LDS (`lds`, MT * 8 KB, free on entry) and writes the tile's lists.
+template <int MT>
+__device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigned char* lds, int tile, int rows,
+                                              int row0, int vocab, int ntiles,
+                                              unsigned long long* __restrict__ partials) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int col0 = tile * kLmCols;
+  int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lc0 = 32 * wv + i16, lc1 = lc0 + 16;
+      int a = row16_full_sort_i32(lm_rank(acc[m][0][r], lc0, col0 + lc0 < vocab));
+      int b = row16_full_sort_i32(lm_rank(acc[m][1][r], lc1, col0 + lc1 < vocab));
+      const int x = row16_bitonic_sort_i32(max(a, dpp_i32<0x140>(b)));   // row_mirror: b ascending
+      lists[((16 * m + 4 * g + r) * kLmWaves + wv) * kNC + i16] = x;
+    }
+  }
+  __syncthreads();
+  // every wave merges the eight lists of rows wv, wv + 8, ...: lane row q takes lists
+  // 2q and 2q + 1 (the second reversed), then the rows merge pairwise
+  for (int rl = wv; rl < MT * 16; rl += kLmWaves) {
+    const int* L = lists + rl * kLmWaves * kNC;
+    int x = row16_bitonic_sort_i32(max(L[(2 * g) * kNC + i16], L[(2 * g + 1) * kNC + (kNC - 1 - i16)]));
+    x = row16_merge_rows_i32(x, 16);
+    x = row16_merge_rows_i32(x, 32);
+    const int grow = row0 + rl;
+    if (lane < kNC && grow < rows) partials[((size_t)grow * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x, col0);
+  }
+}
+
+// Work-groups [0, nfull) each own tile blockIdx.x over the whole hidden dimension and
+// end with its top-16.  The rest split the remaining tiles along the hidden dimension,
+// nparts work-groups per tile (the last round of a vocabulary that does not fill the
+// chip in whole rounds would otherwise run few work-groups): each sums its share of the
+// stages and stores the fp32 tile (tail[(tail tile, part)][wave][m][nt][lane], f32x4),
+// and k_lmhead_combine adds the parts in order and takes the top-16.
 // RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.
 template <int MT, int RING>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
                                                               const uint16_t* __restrict__ w, int rows, int hidden,
-                                                              int vocab, int row0, int ntiles,
-                                                              unsigned long long* __restrict__ partials) {
+                                                              int vocab, int row0, int ntiles, int nfull, int nparts,
+                                                              unsigned long long* __restrict__ partials,
+                                                              f32x4* __restrict__ tail) {
   // the staged hidden rows; reused by the epilogue for the waves' sorted lists
   __shared__ __align__(16) unsigned char lds[MT * 16 * kLmSlots * 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int tile = blockIdx.x;
-  const int col0 = tile * kLmCols;
   const int nstages = hidden / kLmStageDims;
+  const bool whole = (int)blockIdx.x < nfull;
+  const int u = (int)blockIdx.x - nfull;               // split work-groups: tail tile u / nparts, part u % nparts
+  const int part = whole ? 0 : u % nparts;
+  const int tile = whole ? (int)blockIdx.x : nfull + u / nparts;
+  const int s0 = whole ? 0 : (int)((long long)nstages * part / nparts);
+  const int ns = whole ? nstages : (int)((long long)nstages * (part + 1) / nparts) - s0;
+  const int col0 = tile * kLmCols;
 
   // this lane's two W rows (a column past the vocabulary reads the last row, unused)
   const uint16_t* wrow[2];
@@ -129,16 +183,17 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[m][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // W ring: RING half-stages of 4 steps in registers.  Half-stage hs runs on ring slot
-  // hs % RING and refills it, kLmBurst steps at a time, with half-stage hs + RING (past
-  // the end it reloads the last one: valid memory, never used), so the two 64-byte
-  // halves of every 128-byte line of a W row are requested back to back.  Plain loads:
-  // the line stays in L2 for its second half (non-temporal loads measured 25% slower).
+  // W ring: RING half-stages of 4 steps in registers.  Half-stage hs (of this work-
+  // group's stages s0 .. s0 + ns - 1) runs on ring slot hs % RING and refills it,
+  // kLmBurst steps at a time, with half-stage hs + RING (past the end it reloads the
+  // last one: valid memory, never used), so the two 64-byte halves of every 128-byte
+  // line of a W row are requested back to back.  Plain loads: the line stays in L2 for
+  // its second half (non-temporal loads measured 25% slower).
   constexpr int kHalf = kLmSteps / 2;
-  const int nhalves = 2 * nstages;
+  const int nhalves = 2 * ns;
   u32x4 wr0[kHalf][2], wr1[kHalf][2], wr2[kHalf][2];
   auto fill = [&](u32x4 (&wr)[kHalf][2], int hs) {
-    hs = hs < nhalves ? hs : nhalves - 1;
+    hs = 2 * s0 + (hs < nhalves ? hs : nhalves - 1);
 #pragma unroll
     for (int s = 0; s < kHalf; ++s)
 #pragma unroll
@@ -150,17 +205,17 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
   if constexpr (RING == 3) fill(wr2, 2);
 
   u32x4 hp[MT];
-  load_h(0, hp);
+  load_h(s0, hp);
   store_h(hp);
   __syncthreads();
 
   auto half = [&](int hs, u32x4 (&wr)[kHalf][2]) {
-    const int st = hs >> 1, part = hs & 1;
-    if (part == 0) load_h(st + 1 < nstages ? st + 1 : st, hp);   // the next staged hidden slice
-    const int nw = hs + RING < nhalves ? hs + RING : nhalves - 1;
+    const int st = hs >> 1, part_h = hs & 1;
+    if (part_h == 0) load_h(s0 + (st + 1 < ns ? st + 1 : st), hp);   // the next staged hidden slice
+    const int nw = 2 * s0 + (hs + RING < nhalves ? hs + RING : nhalves - 1);
 #pragma unroll
     for (int s = 0; s < kHalf; ++s) {
-      const int step = kHalf * part + s;
+      const int step = kHalf * part_h + s;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(lds + lm_lds_off(16 * m + i16, 4 * step + g));
@@ -178,9 +233,9 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
             wr[b][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)nw * (kLmStageDims / 2) + 32 * b);
       }
     }
-    if (part == 1) {
+    if (part_h == 1) {
       __syncthreads();
-      if (st + 1 < nstages) {
+      if (st + 1 < ns) {
         store_h(hp);
         __syncthreads();
       }
@@ -193,31 +248,39 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
       if (hs + 2 < nhalves) half(hs + 2, wr2);
   }
 
-  // ---- epilogue: per-row top-16 of the tile ---------------------------------------
-  // acc[m][nt][r] is row 16 m + 4 g + r, column 32 wv + 16 nt + i16 of the tile.
-  int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
+  if (whole) {
+    lm_tile_top16<MT>(acc, lds, tile, rows, row0, vocab, ntiles, partials);
+  } else {
+    f32x4* dst = tail + ((size_t)u * kLmWaves + wv) * MT * 2 * kWave + lane;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lc0 = 32 * wv + i16, lc1 = lc0 + 16;
-      int a = row16_full_sort_i32(lm_rank(acc[m][0][r], lc0, col0 + lc0 < vocab));
-      int b = row16_full_sort_i32(lm_rank(acc[m][1][r], lc1, col0 + lc1 < vocab));
-      const int x = row16_bitonic_sort_i32(max(a, dpp_i32<0x140>(b)));   // row_mirror: b ascending
-      lists[((16 * m + 4 * g + r) * kLmWaves + wv) * kNC + i16] = x;
-    }
+      for (int nt = 0; nt < 2; ++nt) dst[(m * 2 + nt) * kWave] = acc[m][nt];
   }
-  __syncthreads();
-  // every wave merges the eight lists of rows wv, wv + 8, ...: lane row q takes lists
-  // 2q and 2q + 1 (the second reversed), then the rows merge pairwise
-  for (int rl = wv; rl < MT * 16; rl += kLmWaves) {
-    const int* L = lists + rl * kLmWaves * kNC;
-    int x = row16_bitonic_sort_i32(max(L[(2 * g) * kNC + i16], L[(2 * g + 1) * kNC + (kNC - 1 - i16)]));
-    x = row16_merge_rows_i32(x, 16);
-    x = row16_merge_rows_i32(x, 32);
-    const int grow = row0 + rl;
-    if (lane < kNC && grow < rows) partials[((size_t)grow * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x, col0);
+}
+
+// The split tiles: one work-group per tile adds its nparts partial accumulators in part
+// order, then takes the tile's top-16 as the whole-tile work-groups do.
+template <int MT>
+__global__ void __launch_bounds__(kLmThreads) k_lmhead_combine(const f32x4* __restrict__ tail, int nparts, int rows,
+                                                                int vocab, int row0, int ntiles, int nfull,
+                                                                unsigned long long* __restrict__ partials) {
+  __shared__ __align__(16) unsigned char lds[MT * 16 * kLmSlots * 16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  f32x4 acc[MT][2];
+  const f32x4* src = tail + ((size_t)blockIdx.x * nparts * kLmWaves + wv) * MT * 2 * kWave + lane;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[m][nt] = src[(m * 2 + nt) * kWave];
+  for (int p = 1; p < nparts; ++p) {
+    const f32x4* sp = src + (size_t)p * kLmWaves * MT * 2 * kWave;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[m][nt] += sp[(m * 2 + nt) * kWave];
   }
+  lm_tile_top16<MT>(acc, lds, nfull + (int)blockIdx.x, rows, row0, vocab, ntiles, partials);
 }
 
 // Top-16 of a row's ntiles sorted tile lists: 64 lane rows each merge every 64th list
@@ -264,30 +327,75 @@ __global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned
   if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
 }
 
+// Work-groups resident per compute unit for k_lmhead_tiles<MT, RING> times the
+// compute units, the work-groups of one full round.
 template <int MT, int RING>
-static void lmhead_tiles_launch(int ntiles, hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden,
-                                int vocab, int row0, unsigned long long* partials) {
-  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING>), dim3((unsigned)ntiles), dim3(kLmThreads), 0, s, h, w, rows, hidden, vocab,
-                     row0, ntiles, partials);
+static int lmhead_round(int dev_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lmhead_tiles<MT, RING>, kLmThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * dev_cus;
+}
+
+template <int MT, int RING>
+static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+                         int row0, int dev_cus, const LmheadWs& ws) {
+  const int ntiles = lmhead_tiles(vocab);
+  const int nstages = hidden / kLmStageDims;
+  const int round = lmhead_round<MT, RING>(dev_cus);
+  const int tail = ntiles % round;
+  int nparts = 1;
+  // a last round under half full: split its tiles so that it fills the chip
+  if (tail > 0 && 2 * tail <= round && ntiles > round) {
+    nparts = round / tail;
+    if (nparts > nstages) nparts = nstages;
+    if (nparts > kLmMaxParts) nparts = kLmMaxParts;
+    const size_t need = (size_t)tail * nparts * kLmWaves * MT * 2 * kWave * sizeof(f32x4);
+    if (need > ws.tail_bytes) nparts = 1;
+  }
+  const int nfull = nparts > 1 ? ntiles - tail : ntiles;
+  const int grid = nfull + (nparts > 1 ? tail * nparts : 0);
+  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
+                     vocab, row0, ntiles, nfull, nparts, ws.partials, reinterpret_cast<f32x4*>(ws.tail));
+  if (nparts > 1)
+    hipLaunchKernelGGL((k_lmhead_combine<MT>), dim3((unsigned)tail), dim3(kLmThreads), 0, s,
+                       reinterpret_cast<const f32x4*>(ws.tail), nparts, rows, vocab, row0, ntiles, nfull,
+                       ws.partials);
+}
+
+size_t lmhead_tail_bytes() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  // a split round holds at most one round of work-groups, and (work-groups per compute
+  // unit) x MT <= 8 for every instance, so one round needs at most cus x 8 x 16 KB
+  return (size_t)cus * 8 * 16 * 1024;
 }
 
 hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
                                 int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
                                 hipStream_t s) {
-  const int ntiles = lmhead_tiles(vocab);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
     const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
     if (n <= 16)
-      lmhead_tiles_launch<1, 2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_group<1, 2>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else if (n <= 32)
-      lmhead_tiles_launch<2, 2>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_group<2, 2>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else if (n <= 64)
-      lmhead_tiles_launch<4, 3>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_group<4, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+    else if (n <= 112)
+      lmhead_group<7, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else
-      lmhead_tiles_launch<8, 3>(ntiles, s, h, w, rows, hidden, vocab, row0, ws.partials);
+      lmhead_group<8, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
   }
-  hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)rows), dim3(kLmMergeThreads), 0, s, ws.partials, ntiles, cand_idx,
-                     cand_val, row_status);
+  hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)rows), dim3(kLmMergeThreads), 0, s, ws.partials,
+                     lmhead_tiles(vocab), cand_idx, cand_val, row_status);
   return hipGetLastError();
 }
 

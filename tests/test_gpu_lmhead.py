@@ -94,6 +94,12 @@ def check_rows(idx_g, val_g, h_bits, w_bits, rows_sel=None, vchunk=16384):
     (130, 256, 3000, True),      # two row groups: 128 + 2
     (3, 256, 16, False),         # the smallest vocabulary: a permutation of all ids
     (5, 256, 270, False),        # a last tile with 14 columns (fewer than 16)
+    # Vocabularies past one round of work-groups (256 compute units: one 512-thread
+    # work-group each at 64+ rows, two at 16 rows or fewer) leave a last round under half
+    # full, whose tiles are split along the hidden dimension and combined:
+    (40, 2048, 70000, True),     # 274 tiles, 18 left over, split in 8 parts
+    (100, 512, 70000, False),    # seven row tiles; the 18 left over split in 2 parts
+    (5, 1024, 140000, True),     # 547 tiles, 35 left over past two per compute unit, 4 parts
 ])
 def test_lmhead_topk16_parity(d2, rows, hidden, vocab, peaks):
     inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows + hidden + vocab, peaks=peaks)
