@@ -57,16 +57,30 @@ __device__ __forceinline__ int lm_rank(float x, int lc, bool valid) {
   return valid ? (int)(((unsigned)(key - 0x8000) << 16) | (unsigned)(0xffff - lc)) : (int)0x80000000;
 }
 
-// Full descending sort of the 16 values held by each 16-lane row (Batcher's bitonic
-// sort: blocks of 2, 4, 8, then the 16-lane half-cleaners).
-__device__ __forceinline__ int row16_full_sort_i32(int x) {
-  x = bitonic_stage_i32<2, 1>(x);
-  x = bitonic_stage_i32<4, 2>(x);
-  x = bitonic_stage_i32<4, 1>(x);
-  x = bitonic_stage_i32<8, 4>(x);
-  x = bitonic_stage_i32<8, 2>(x);
-  x = bitonic_stage_i32<8, 1>(x);
-  return row16_bitonic_sort_i32(x);
+// Full descending sort of the 16 values held by each 16-lane row, for N independent
+// registers at once (Batcher's bitonic sort: blocks of 2, 4, 8, then the 16-lane
+// half-cleaners).  Each stage is applied to all N before the next, so the independent
+// DPP compare-exchanges fill each other's wait states.
+template <int N>
+__device__ __forceinline__ void row16_full_sort_i32(int (&x)[N]) {
+#define DF2_STAGE(K, J)                                              \
+  _Pragma("unroll") for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<K, J>(x[n]);
+  DF2_STAGE(2, 1) DF2_STAGE(4, 2) DF2_STAGE(4, 1) DF2_STAGE(8, 4) DF2_STAGE(8, 2) DF2_STAGE(8, 1)
+  DF2_STAGE(16, 8) DF2_STAGE(16, 4) DF2_STAGE(16, 2) DF2_STAGE(16, 1)
+#undef DF2_STAGE
+}
+
+// The bitonic half-cleaners (distances 8, 4, 2, 1) on N independent registers.
+template <int N>
+__device__ __forceinline__ void row16_bitonic_sort_i32(int (&x)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 8>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 4>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 2>(x[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 1>(x[n]);
 }
 
 // Tile list entry -> row composite of dflash2_topk16 (0 = empty).
@@ -97,27 +111,44 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
   const int g = lane >> 4, i16 = lane & 15;
   const int col0 = tile * kLmCols;
   int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
+  // (m, r) pairs two at a time: sort both halves of each pair's 32 columns, keep the
+  // top 16 of the two sorted halves (the maximum against the other half reversed is
+  // bitonic) and sort that
+  static_assert((MT * 4) % 2 == 0, "pairs are taken two at a time");
+  const int lc0 = 32 * wv + i16, lc1 = lc0 + 16;
+  const bool v0 = col0 + lc0 < vocab, v1 = col0 + lc1 < vocab;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lc0 = 32 * wv + i16, lc1 = lc0 + 16;
-      int a = row16_full_sort_i32(lm_rank(acc[m][0][r], lc0, col0 + lc0 < vocab));
-      int b = row16_full_sort_i32(lm_rank(acc[m][1][r], lc1, col0 + lc1 < vocab));
-      const int x = row16_bitonic_sort_i32(max(a, dpp_i32<0x140>(b)));   // row_mirror: b ascending
-      lists[((16 * m + 4 * g + r) * kLmWaves + wv) * kNC + i16] = x;
-    }
+  for (int k = 0; k < MT * 4; k += 2) {
+    const int m0 = k >> 2, r0 = k & 3, m1 = (k + 1) >> 2, r1 = (k + 1) & 3;
+    int x[4] = {lm_rank(acc[m0][0][r0], lc0, v0), lm_rank(acc[m0][1][r0], lc1, v1),
+                lm_rank(acc[m1][0][r1], lc0, v0), lm_rank(acc[m1][1][r1], lc1, v1)};
+    row16_full_sort_i32<4>(x);
+    int y[2] = {max(x[0], dpp_i32<0x140>(x[1])), max(x[2], dpp_i32<0x140>(x[3]))};   // row_mirror
+    row16_bitonic_sort_i32<2>(y);
+    lists[((16 * m0 + 4 * g + r0) * kLmWaves + wv) * kNC + i16] = y[0];
+    lists[((16 * m1 + 4 * g + r1) * kLmWaves + wv) * kNC + i16] = y[1];
   }
   __syncthreads();
-  // every wave merges the eight lists of rows wv, wv + 8, ...: lane row q takes lists
-  // 2q and 2q + 1 (the second reversed), then the rows merge pairwise
-  for (int rl = wv; rl < MT * 16; rl += kLmWaves) {
-    const int* L = lists + rl * kLmWaves * kNC;
-    int x = row16_bitonic_sort_i32(max(L[(2 * g) * kNC + i16], L[(2 * g + 1) * kNC + (kNC - 1 - i16)]));
-    x = row16_merge_rows_i32(x, 16);
-    x = row16_merge_rows_i32(x, 32);
-    const int grow = row0 + rl;
-    if (lane < kNC && grow < rows) partials[((size_t)grow * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x, col0);
+  // every wave merges the eight lists of rows wv, wv + 8, ..., two rows at a time:
+  // lane row q takes lists 2q and 2q + 1 (the second reversed), then the rows merge
+  // pairwise (the maximum against the mirrored partner row is bitonic)
+  static_assert((MT * 16) % (2 * kLmWaves) == 0, "two rows per wave per pass");
+  for (int rl = wv; rl < MT * 16; rl += 2 * kLmWaves) {
+    const int* L0 = lists + rl * kLmWaves * kNC;
+    const int* L1 = lists + (rl + kLmWaves) * kLmWaves * kNC;
+    int x[2] = {max(L0[(2 * g) * kNC + i16], L0[(2 * g + 1) * kNC + (kNC - 1 - i16)]),
+                max(L1[(2 * g) * kNC + i16], L1[(2 * g + 1) * kNC + (kNC - 1 - i16)])};
+    row16_bitonic_sort_i32<2>(x);
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk *= 2) {
+      x[0] = max(x[0], xor_lane_i32(dpp_i32<0x140>(x[0]), msk));
+      x[1] = max(x[1], xor_lane_i32(dpp_i32<0x140>(x[1]), msk));
+      row16_bitonic_sort_i32<2>(x);
+    }
+    if (lane < kNC && row0 + rl < rows)
+      partials[((size_t)(row0 + rl) * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x[0], col0);
+    if (lane < kNC && row0 + rl + kLmWaves < rows)
+      partials[((size_t)(row0 + rl + kLmWaves) * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x[1], col0);
   }
 }
 
@@ -126,7 +157,7 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
 // nparts work-groups per tile (the last round of a vocabulary that does not fill the
 // chip in whole rounds would otherwise run few work-groups): each sums its share of the
 // stages and stores the fp32 tile (tail[(tail tile, part)][wave][m][nt][lane], f32x4),
-// and k_lmhead_combine adds the parts in order and takes the top-16.
+// and k_lmhead_combine adds the parts in order and takes the top-16 of each 16-row tile.
 // RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.
 template <int MT, int RING>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
@@ -259,28 +290,37 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
   }
 }
 
-// The split tiles: one work-group per tile adds its nparts partial accumulators in part
-// order, then takes the tile's top-16 as the whole-tile work-groups do.
+// The split tiles: one work-group per (tile, 16-row tile) adds the nparts partial
+// accumulators of its rows in part order (two parts' loads in flight at a time), then
+// takes their top-16 as the whole-tile work-groups do.  Spreading the combine over
+// MT x as many work-groups keeps its sorting off a few compute units.
 template <int MT>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_combine(const f32x4* __restrict__ tail, int nparts, int rows,
                                                                 int vocab, int row0, int ntiles, int nfull,
                                                                 unsigned long long* __restrict__ partials) {
-  __shared__ __align__(16) unsigned char lds[MT * 16 * kLmSlots * 16];
+  __shared__ __align__(16) unsigned char lds[16 * kLmSlots * 16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  f32x4 acc[MT][2];
-  const f32x4* src = tail + ((size_t)blockIdx.x * nparts * kLmWaves + wv) * MT * 2 * kWave + lane;
+  const int tt = (int)blockIdx.x / MT, m = (int)blockIdx.x % MT;
+  constexpr size_t kPart = (size_t)kLmWaves * MT * 2 * kWave;
+  const f32x4* src = tail + ((size_t)tt * nparts * kLmWaves + wv) * MT * 2 * kWave + m * 2 * kWave + lane;
+  f32x4 acc[1][2];
+  for (int p0 = 0; p0 < nparts; p0 += 2) {
+    const bool two = p0 + 1 < nparts;
+    const f32x4* s0 = src + (size_t)p0 * kPart;
+    const f32x4* s1 = src + (size_t)(two ? p0 + 1 : p0) * kPart;   // a missing second part is not added
+    f32x4 v0[2], v1[2];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int nt = 0; nt < 2; ++nt) {
+      v0[nt] = s0[nt * kWave];
+      v1[nt] = s1[nt * kWave];
+    }
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[m][nt] = src[(m * 2 + nt) * kWave];
-  for (int p = 1; p < nparts; ++p) {
-    const f32x4* sp = src + (size_t)p * kLmWaves * MT * 2 * kWave;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[m][nt] += sp[(m * 2 + nt) * kWave];
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[0][nt] = p0 == 0 ? v0[nt] : acc[0][nt] + v0[nt];
+      if (two) acc[0][nt] += v1[nt];
+    }
   }
-  lm_tile_top16<MT>(acc, lds, nfull + (int)blockIdx.x, rows, row0, vocab, ntiles, partials);
+  lm_tile_top16<1>(acc, lds, nfull + tt, rows, row0 + 16 * m, vocab, ntiles, partials);
 }
 
 // Top-16 of a row's ntiles sorted tile lists: 64 lane rows each merge every 64th list
@@ -359,7 +399,7 @@ static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, in
   hipLaunchKernelGGL((k_lmhead_tiles<MT, RING>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
                      vocab, row0, ntiles, nfull, nparts, ws.partials, reinterpret_cast<f32x4*>(ws.tail));
   if (nparts > 1)
-    hipLaunchKernelGGL((k_lmhead_combine<MT>), dim3((unsigned)tail), dim3(kLmThreads), 0, s,
+    hipLaunchKernelGGL((k_lmhead_combine<MT>), dim3((unsigned)(tail * MT)), dim3(kLmThreads), 0, s,
                        reinterpret_cast<const f32x4*>(ws.tail), nparts, rows, vocab, row0, ntiles, nfull,
                        ws.partials);
 }
