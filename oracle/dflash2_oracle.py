@@ -545,3 +545,67 @@ def lmhead_topk16(h_bits, w_bits):
     topk16 of lmhead_logits (same order: value desc, token id asc)."""
     _, bits = lmhead_logits(h_bits, w_bits)
     return topk16(bits)
+
+
+# ----------------------------------------------------------------------------------
+# Draft attention over the per-request K/V ring (sliding window)
+# ----------------------------------------------------------------------------------
+
+
+def ring_window_keys(ctx_len: int, window: int, ring: int):
+    """Ring rows of the context keys one draft block reads, oldest first.
+
+    [FT] "Details", runtime: the draft's K/V lives in a ring of 2112 positions per
+    request (the 2048-token window plus 64 rows of room for a verify's rejected rows
+    and for prefill rows past a snapshot boundary); prefix cache: the ring is rebuilt
+    from the last 2047 context rows.  Reading: context position j sits in ring row
+    j mod ring; the block reads the last min(ctx_len, window - 1) committed positions,
+    so the window holds those plus the block's own first row, and no row of a position
+    >= ctx_len (a rejected or not yet committed row) is ever read.
+    """
+    n = min(int(ctx_len), window - 1)
+    return [(p % ring) for p in range(int(ctx_len) - n, int(ctx_len))]
+
+
+def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale=None):
+    """Non-causal draft-block attention over the window of each request's K/V ring.
+
+    [FT] "Details": the released drafts use sliding-window attention (window 2048);
+    the draft forward over [last token, mask x 7] reads the ring; a causal draft is
+    refused at startup, so the block's rows see each other.  Reading: every query row
+    of the block attends to the window's context keys (ring_window_keys) and to all
+    block keys, softmax(q . k * scale) with scale = 1/sqrt(head_dim), grouped heads
+    (query head h uses K/V head h // (Hq / Hkv)).  Rotary embedding is applied before
+    (the ring holds rotated keys).  The oracle gathers the window into a dense key list
+    and applies the definition in float64.
+
+    q [B, nq, Hq, Dh], k_blk / v_blk [B, nq, Hkv, Dh], k_ring / v_ring
+    [B, ring, Hkv, Dh] (float values; bf16 inputs are passed decoded), ctx_len [B].
+    Returns (out float64 [B, nq, Hq, Dh], pv_abs [B, nq, Hq, Dh] = sum_k p_k |v_k| with
+    normalised p, smax [B, nq, Hq] = max_k sum_d |q_d k_d| * scale).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, nq, Hq, Dh = q.shape
+    Hkv = k_blk.shape[2]
+    G = Hq // Hkv
+    ring = k_ring.shape[1]
+    scale = 1.0 / np.sqrt(Dh) if scale is None else scale
+    out = np.zeros((B, nq, Hq, Dh))
+    pv_abs = np.zeros((B, nq, Hq, Dh))
+    smax = np.zeros((B, nq, Hq))
+    for b in range(B):
+        rows = ring_window_keys(ctx_len[b], window, ring)
+        for hk in range(Hkv):
+            K = np.concatenate([np.asarray(k_ring[b, rows, hk], dtype=np.float64),
+                                np.asarray(k_blk[b, :, hk], dtype=np.float64)], axis=0)
+            V = np.concatenate([np.asarray(v_ring[b, rows, hk], dtype=np.float64),
+                                np.asarray(v_blk[b, :, hk], dtype=np.float64)], axis=0)
+            for hq in range(hk * G, (hk + 1) * G):
+                Q = q[b, :, hq]                             # [nq, Dh]
+                s = Q @ K.T * scale                         # [nq, nkeys]
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                out[b, :, hq] = p @ V
+                pv_abs[b, :, hq] = p @ np.abs(V)
+                smax[b, :, hq] = (np.abs(Q) @ np.abs(K).T * scale).max(axis=1)
+    return out, pv_abs, smax

@@ -682,3 +682,83 @@ def test_lmhead_rounds_the_exact_sum_once():
                   [-1, -(2.0**-8), -(2.0**-30)]], dtype=np.float32)
     _, bits = oracle.lmhead_logits(h, synth.f32_to_bf16_bits(W))
     assert bits[0].tolist() == [0x3F80, 0x3F82, 0x3F81, 0xBF81]
+
+
+# ---------------------------------------------------------------- ring attention -----
+
+
+def test_ring_window_rows_hand_cases():
+    # ring of 10 rows, window 5 (4 context keys): worked by hand
+    assert oracle.ring_window_keys(0, 5, 10) == []
+    assert oracle.ring_window_keys(3, 5, 10) == [0, 1, 2]
+    assert oracle.ring_window_keys(12, 5, 10) == [8, 9, 0, 1]          # positions 8..11 wrap
+    assert oracle.ring_window_keys(2047 + 100, 2048, 2112) == [(100 + i) % 2112 for i in range(2047)]
+
+
+def _ring_case(B=1, nq=2, Hq=2, Hkv=1, Dh=4, ring=10):
+    z = lambda *s: np.zeros(s)
+    return z(B, nq, Hq, Dh), z(B, nq, Hkv, Dh), z(B, nq, Hkv, Dh), z(B, ring, Hkv, Dh), z(B, ring, Hkv, Dh)
+
+
+def test_ring_attention_two_keys_closed_form():
+    # one query, one context key (position 0) and the block's own key; by hand:
+    # s = q.k / sqrt(Dh) = (2, 1) / 2 = (1, 0.5); out = (e v_ctx + e^0.5 v_blk) / (e + e^0.5)
+    q, kb, vb, kr, vr = _ring_case(nq=1, Hq=1, Dh=4)
+    q[0, 0, 0] = [1, 1, 0, 0]
+    kr[0, 0, 0] = [1, 1, 0, 0]
+    kb[0, 0, 0] = [1, 0, 0, 0]
+    vr[0, 0, 0] = [1, 0, 0, 0]
+    vb[0, 0, 0] = [0, 3, 0, 0]
+    out, _, _ = oracle.ring_attention(q, kb, vb, kr, vr, [1], window=4)
+    e1, e2 = np.exp(1.0), np.exp(0.5)
+    np.testing.assert_allclose(out[0, 0, 0], [e1 / (e1 + e2), 3 * e2 / (e1 + e2), 0, 0], rtol=1e-14)
+
+
+def test_ring_attention_equal_keys_average_the_window():
+    # all keys equal: the output is the plain mean of the values the window holds (the
+    # 3 newest context positions of 7, ring rows 4, 5, 6, and both block rows)
+    q, kb, vb, kr, vr = _ring_case(nq=2, Hq=1, Dh=4)
+    kr[:] = 1.0
+    kb[:] = 1.0
+    q[:] = 0.3
+    for row in range(10):
+        vr[0, row, 0, 0] = 100 + row
+    vb[0, :, 0, 0] = [7, 9]
+    out, _, _ = oracle.ring_attention(q, kb, vb, kr, vr, [7], window=4)
+    expect = (104 + 105 + 106 + 7 + 9) / 5
+    np.testing.assert_allclose(out[0, :, 0, 0], [expect, expect], rtol=1e-14)
+
+
+def test_ring_attention_reads_no_row_outside_the_window():
+    rng = np.random.default_rng(3)
+    q, kb, vb, kr, vr = (rng.normal(size=a.shape) for a in _ring_case(B=1, nq=3, Hq=2, Hkv=1, Dh=8, ring=12))
+    L = 15                                                    # window 6: positions 10..14 -> rows 10, 11, 0, 1, 2
+    base, _, _ = oracle.ring_attention(q, kb, vb, kr, vr, [L], window=6)
+    kr2, vr2 = kr.copy(), vr.copy()
+    for row in (3, 4, 5, 6, 7, 8, 9):                          # stale, rejected or too old
+        kr2[0, row] += 50.0
+        vr2[0, row] += 50.0
+    same, _, _ = oracle.ring_attention(q, kb, vb, kr2, vr2, [L], window=6)
+    np.testing.assert_array_equal(same, base)
+    vr2[0, 0] += 1.0                                          # a row inside the window changes it
+    diff, _, _ = oracle.ring_attention(q, kb, vb, kr, vr2, [L], window=6)
+    assert not np.allclose(diff, base)
+
+
+def test_ring_attention_grouped_heads_and_dominant_key():
+    # Hq 4 over Hkv 2: query heads 0, 1 use K/V head 0 and 2, 3 use head 1.  Each K/V
+    # head has one key the queries score far above the rest, so each output is that
+    # key's value: a wrong head map or a transposed product picks another value.
+    q, kb, vb, kr, vr = _ring_case(B=1, nq=1, Hq=4, Hkv=2, Dh=4, ring=8)
+    q[0, 0, :] = [10, 0, 0, 0]
+    kr[0, 2, 0] = [10, 0, 0, 0]                               # head 0: context position 2
+    kb[0, 0, 1] = [10, 0, 0, 0]                               # head 1: the block row
+    vr[0, :, 0] = np.arange(8)[:, None] * np.array([1, 0, 0, 0])
+    vr[0, :, 1] = 50.0
+    vb[0, 0, 0] = [-1, -1, -1, -1]
+    vb[0, 0, 1] = [0, 0, 7, 0]
+    out, _, _ = oracle.ring_attention(q, kb, vb, kr, vr, [5], window=8)
+    np.testing.assert_allclose(out[0, 0, 0], [2, 0, 0, 0], atol=1e-12)
+    np.testing.assert_allclose(out[0, 0, 1], [2, 0, 0, 0], atol=1e-12)
+    np.testing.assert_allclose(out[0, 0, 2], [0, 0, 7, 0], atol=1e-12)
+    np.testing.assert_allclose(out[0, 0, 3], [0, 0, 7, 0], atol=1e-12)
