@@ -134,6 +134,37 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
                                          ws, stream));
 }
 
+size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window) {
+  if (batch < 1 || nq < 1 || hkv < 1 || hq < hkv || hq % hkv != 0 || window < 1) return 0;
+  Carver c(nullptr);
+  carve_ring(c, batch, hkv, ring_splits((int)nq, (int)window), ring_rows_pad((int)nq, (int)hq, (int)hkv));
+  return c.off + 256;
+}
+
+dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                                      const uint16_t* k_ring, const uint16_t* v_ring, const int32_t* ctx_len,
+                                      int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t head_dim,
+                                      int64_t ring, int64_t window, float scale, float* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_blk || !v_blk || !k_ring || !v_ring || !ctx_len || !out) return DFLASH2_ERR_NULL;
+  if (batch < 1 || batch > (1 << 20) || nq < 1 || hkv < 1 || hq < hkv || hq % hkv != 0 || head_dim != 128 ||
+      nq * (hq / hkv) > kRingMaxRows || ring < 1 || ring > (1 << 24) || window < 1 || window > ring)
+    return DFLASH2_ERR_SHAPE;
+  if (isnan(scale) || isinf(scale) || scale < 0.f) return DFLASH2_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_ring) || !aligned16(v_ring) ||
+      !aligned16(out))
+    return DFLASH2_ERR_ALIGN;
+  const int nsplit = ring_splits((int)nq, (int)window);
+  const int rows_pad = ring_rows_pad((int)nq, (int)hq, (int)hkv);
+  RingWs ws;
+  dflash2_status st = carve_checked(
+      workspace, workspace_bytes, [&](Carver& c) { return carve_ring(c, batch, hkv, nsplit, rows_pad); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)head_dim);
+  return hip_status(launch_ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, (int)batch, (int)nq, (int)hq,
+                                          (int)hkv, (int)ring, (int)window, sc, nsplit, ws, out, stream));
+}
+
 size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim) {
   if (rows < 1 || hidden < 1 || dim < 1) return 0;
   Carver c(nullptr);

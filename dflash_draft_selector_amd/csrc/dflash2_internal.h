@@ -51,6 +51,15 @@ constexpr int kLmMaxRows = 128;   // rows per LM-head tile launch (eight 16-row 
 int lmhead_tiles(int64_t vocab);
 LmheadWs carve_lmhead(Carver& c, int64_t rows, int64_t vocab);
 
+struct RingWs {
+  float* ml;                      // [batch][hkv][nsplit][rows_pad][2] per-split row max and sum
+  float* o;                       // [batch][hkv][nsplit][rows_pad][128] per-split unnormalised outputs
+};
+constexpr int kRingMaxRows = 48;  // query rows (block positions x query heads per K/V head)
+int ring_rows_pad(int nq, int hq, int hkv);
+int ring_splits(int nq, int window);
+RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad);
+
 struct GateWs {
   float* partial;                 // [nsplit][rows][dim] slice sums (nsplit > 1)
   int nsplit;                     // slices of the hidden dimension
@@ -93,6 +102,11 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
 hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
                                 int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
                                 hipStream_t s);
+
+hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                                 const uint16_t* k_ring, const uint16_t* v_ring, const int32_t* ctx_len, int batch,
+                                 int nq, int hq, int hkv, int ring, int window, float scale, int nsplit, RingWs ws,
+                                 float* out, hipStream_t s);
 
 hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden,
                        int dim, int act, float* H, GateWs ws, hipStream_t s);

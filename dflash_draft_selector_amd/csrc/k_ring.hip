@@ -1,0 +1,330 @@
+// Draft-block attention over each request's K/V ring ([FT] "Details": sliding-window
+// attention with window 2048; runtime: the draft's K/V lives in a ring of 2112 rows per
+// request, the window plus room for a verify's rejected rows; the draft forward over
+// [last token, mask x 7] reads it; a causal draft is refused, so the block's rows see
+// each other).
+//
+// Keys of request b: its last min(ctx_len, window - 1) context positions (position p in
+// ring row p mod ring), then the block's own nq rows.  Every query row of the block
+// attends to all of them; query head h uses K/V head h / (Hq / Hkv).
+//
+// k_ring_partial: one 256-thread work-group per (request, K/V head, split) takes a
+// contiguous quarter (nsplit parts) of the request's keys in iterations of 128 keys
+// with an online softmax.  The rows are the nq x G query rows of the K/V head (G query
+// heads per K/V head), in MT 16-row tiles.  Per iteration: wave w computes S for keys
+// 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q fragments kept in registers, K
+// fragments loaded straight from the ring or block rows); row maxima and sums go
+// through LDS; P = exp(S - m) is split into bf16 hi + lo parts (relative error <=
+// 2^-16) and stored row-major in LDS; V is staged transposed ([dim][key]) in LDS; wave
+// w accumulates O^T for dims 32w .. 32w+31 as V^T x P^T (hi and lo).  Each work-group
+// stores its rows' (max, sum, O).  k_ring_combine merges the splits.
+#include "dflash2_internal.h"
+#include "device_common.h"
+#include "topk_dev.h"
+
+namespace df2 {
+
+constexpr int kRingThreads = 256;            // 4 waves
+constexpr int kRingDh = 128;                 // head dim
+constexpr int kRingC = 128;                  // keys per iteration
+constexpr int kRingVPitch = kRingC + 8;      // bf16 elements per staged V^T row (16-byte aligned, odd bank step)
+constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row
+
+RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad) {
+  RingWs w;
+  const size_t units = (size_t)batch * hkv * nsplit;
+  w.ml = c.take<float>(units * rows_pad * 2);
+  w.o = c.take<float>(units * rows_pad * kRingDh);
+  return w;
+}
+
+template <int MT>
+struct RingShared {
+  uint16_t vt[kRingDh][kRingVPitch];         // V^T of the iteration's keys
+  uint16_t p_hi[MT * 16][kRingPPitch];       // P rows, bf16 high part
+  uint16_t p_lo[MT * 16][kRingPPitch];       // P rows, bf16 low part
+  float red[4][MT * 16];                     // per-wave row maxima / sums
+  float alpha[MT * 16];                      // rescale of the running state
+  float mrow[MT * 16];
+};
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_rne(f); }
+
+// sum over the 16 lanes of the row, every lane gets it (the reduction order of row16_max)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xb1>(v);              // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);              // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);             // row_half_mirror
+  v += dpp_f<0x140>(v);             // row_mirror
+  return v;
+}
+
+template <int MT>
+__global__ void __launch_bounds__(kRingThreads) k_ring_partial(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
+    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
+    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nsplit, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o) {
+  __shared__ RingShared<MT> sm;
+  constexpr int kRows = MT * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
+  const int split = unit % nsplit;
+  const int bk = unit / nsplit;
+  const int kvh = bk % hkv, b = bk / hkv;
+  const int G = hq / hkv;
+  const int nrows = nq * G;
+
+  const int L = ctx_len[b] > 0 ? ctx_len[b] : 0;
+  const int nctx = L < window - 1 ? L : window - 1;
+  const int nkeys = nctx + nq;
+  const int k0 = (int)((long long)nkeys * split / nsplit);
+  const int k1 = (int)((long long)nkeys * (split + 1) / nsplit);
+
+  // Q fragments: row r = i * G + (h - kvh G) of the block (query position i, head h)
+  u32x4 qf[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = 16 * mt + i16;
+    const int rr = r < nrows ? r : 0;
+    const uint16_t* qp = q + ((size_t)(b * nq + rr / G) * hq + kvh * G + rr % G) * kRingDh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * s);
+      qf[mt][s] = r < nrows ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+  // address of key kk (any index: out-of-range keys read block row 0 and are masked)
+  auto key_off = [&](int kk) -> size_t {
+    if (kk >= 0 && kk < nctx) {
+      const int pos = L - nctx + kk;
+      return (((size_t)b * ring + pos % ring) * hkv + kvh) * kRingDh;
+    }
+    const int j = kk - nctx;
+    return ((size_t)(b * nq + (j >= 0 && j < nq ? j : 0)) * hkv + kvh) * kRingDh;
+  };
+  auto key_src = [&](int kk) { return kk >= 0 && kk < nctx; };
+
+  // running state: O^T tiles (dims 32 wv + 16 dt + 4 g + r, row 16 mt + i16)
+  f32x4 o[2][MT];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[dt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int r = tid; r < kRows; r += kRingThreads) sm.mrow[r] = -__builtin_inff();
+  float l_run[MT][4];                                       // row sums in the S layout (rows 16 mt + 4 g + r)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_run[mt][r] = 0.f;
+  __syncthreads();
+
+  for (int base = k0; base < k1; base += kRingC) {
+    // ---- S for keys base + 32 wv + 16 n + i16 ------------------------------------
+    f32x4 sacc[2][MT];
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int kk = base + 32 * wv + 16 * n + i16;
+      const uint16_t* kp = (key_src(kk) ? k_ring : k_blk) + key_off(kk) + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 32 * s);
+    }
+    // stage V^T: thread t loads key (t / 16)'s 16-byte segment t % 16 (8 rounds of 16 keys)
+#pragma unroll
+    for (int e = 0; e < kRingC * 16 / kRingThreads; ++e) {
+      const int idx = tid + kRingThreads * e;
+      const int kl = idx >> 4, seg = idx & 15;
+      const int kk = base + kl;
+      const uint16_t* vp = (key_src(kk) ? v_ring : v_blk) + key_off(kk) + 8 * seg;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(vp);
+      const bool ok = kk < k1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w = ok ? v[c] : 0u;
+        sm.vt[8 * seg + 2 * c][kl] = (uint16_t)(w & 0xffffu);
+        sm.vt[8 * seg + 2 * c + 1][kl] = (uint16_t)(w >> 16);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        sacc[n][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          sacc[n][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[mt][s]),
+                                                               __builtin_bit_cast(bf16x8, kf[n][s]), sacc[n][mt],
+                                                               0, 0, 0);
+      }
+    // scale to log2 units and mask keys past the split
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const bool valid = base + 32 * wv + 16 * n + i16 < k1;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[n][mt][r] = valid ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
+    }
+    // ---- row maxima: lanes of a 16-lane row share rows 16 mt + 4 g + r -------------
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = row16_max(fmaxf(sacc[0][mt][r], sacc[1][mt][r]));
+        if (i16 == 0) sm.red[wv][16 * mt + 4 * g + r] = x;
+      }
+    __syncthreads();
+    for (int row = tid; row < kRows; row += kRingThreads) {
+      const float it = fmaxf(fmaxf(sm.red[0][row], sm.red[1][row]), fmaxf(sm.red[2][row], sm.red[3][row]));
+      const float mo = sm.mrow[row];
+      const float mn = fmaxf(mo, it);                        // finite: every iteration has a valid key
+      sm.alpha[row] = exp2f(mo - mn);                        // 0 on the first iteration
+      sm.mrow[row] = mn;
+    }
+    __syncthreads();
+    // ---- P = exp2(S - m): row sums, and bf16 hi / lo parts into LDS -----------------
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r;
+        const float mn = sm.mrow[row];
+        float sum = 0.f;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const float p = exp2f(sacc[n][mt][r] - mn);
+          sum += p;
+          const uint32_t hi = bf16_rne_bits(p);
+          const uint32_t lo = bf16_rne_bits(p - __uint_as_float(hi << 16));
+          const int col = 32 * wv + 16 * n + i16;
+          sm.p_hi[row][col] = (uint16_t)hi;
+          sm.p_lo[row][col] = (uint16_t)lo;
+        }
+        sum = row16_sum(sum);
+        if (i16 == 0) sm.red[wv][row] = sum;
+        l_run[mt][r] *= sm.alpha[row];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r;
+        l_run[mt][r] += (sm.red[0][row] + sm.red[1][row]) + (sm.red[2][row] + sm.red[3][row]);
+      }
+    // ---- O^T += V^T x P^T (hi, then lo), after rescaling by alpha of each row ---------
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float a = sm.alpha[16 * mt + i16];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) o[dt][mt] *= a;
+    }
+#pragma unroll
+    for (int ks = 0; ks < kRingC / 32; ++ks) {
+      u32x4 vf[2];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        vf[dt] = *reinterpret_cast<const u32x4*>(&sm.vt[32 * wv + 16 * dt + i16][32 * ks + 8 * g]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 ph = *reinterpret_cast<const u32x4*>(&sm.p_hi[16 * mt + i16][32 * ks + 8 * g]);
+        const u32x4 pl = *reinterpret_cast<const u32x4*>(&sm.p_lo[16 * mt + i16][32 * ks + 8 * g]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
+                                                              __builtin_bit_cast(bf16x8, ph), o[dt][mt], 0, 0, 0);
+          o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
+                                                              __builtin_bit_cast(bf16x8, pl), o[dt][mt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();                                        // LDS is rewritten by the next iteration
+  }
+
+  // ---- the split's state: (max, sum) per row, and O (rows x 128 dims) --------------
+  float* ml = ws_ml + (size_t)unit * kRows * 2;
+  float* os = ws_o + (size_t)unit * kRows * kRingDh;
+  if (wv == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r;
+        if (i16 == 0) {
+          ml[2 * row] = k1 > k0 ? sm.mrow[row] : -__builtin_inff();
+          ml[2 * row + 1] = l_run[mt][r];
+        }
+      }
+  }
+  // O^T tile (dims 32 wv + 16 dt + 4 g + r, row 16 mt + i16) -> O[row][dims .. + 3]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      *reinterpret_cast<f32x4*>(os + (size_t)(16 * mt + i16) * kRingDh + 32 * wv + 16 * dt + 4 * g) = o[dt][mt];
+}
+
+// One work-group per (request, K/V head): out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
+template <int MT>
+__global__ void __launch_bounds__(kRingThreads) k_ring_combine(const float* __restrict__ ws_ml,
+                                                                const float* __restrict__ ws_o, int nq, int hq,
+                                                                int hkv, int nsplit, float* __restrict__ out) {
+  constexpr int kRows = MT * 16;
+  const int bk = blockIdx.x;
+  const int kvh = bk % hkv, b = bk / hkv;
+  const int G = hq / hkv;
+  const int nrows = nq * G;
+  for (int e = threadIdx.x; e < nrows * kRingDh; e += kRingThreads) {
+    const int row = e / kRingDh, d = e - row * kRingDh;
+    float M = -__builtin_inff();
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((size_t)bk * nsplit + s) * kRows * 2 + 2 * row]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t u = (size_t)bk * nsplit + s;
+      const float ms = ws_ml[u * kRows * 2 + 2 * row];
+      const float w = ms == -__builtin_inff() ? 0.f : exp2f(ms - M);
+      num += w * ws_o[(u * kRows + row) * kRingDh + d];
+      den += w * ws_ml[u * kRows * 2 + 2 * row + 1];
+    }
+    const int i = row / G, h = kvh * G + row % G;
+    out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num / den;
+  }
+}
+
+int ring_rows_pad(int nq, int hq, int hkv) {
+  const int rows = nq * (hq / hkv);
+  return rows <= 16 ? 16 : rows <= 32 ? 32 : 48;
+}
+
+int ring_splits(int nq, int window) {
+  const int keys = window - 1 + nq;
+  const int n = (keys + 511) / 512;          // about 512 keys (4 iterations) per work-group
+  return n < 1 ? 1 : n > 8 ? 8 : n;
+}
+
+template <int MT>
+static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kr,
+                        const uint16_t* vr, const int32_t* ctx, int B, int nq, int hq, int hkv, int ring, int window,
+                        float scale_log2, int nsplit, const RingWs& ws, float* out) {
+  hipLaunchKernelGGL((k_ring_partial<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(kRingThreads), 0, s, q, kb, vb, kr,
+                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit, ws.ml, ws.o);
+  hipLaunchKernelGGL((k_ring_combine<MT>), dim3((unsigned)(B * hkv)), dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq,
+                     hkv, nsplit, out);
+}
+
+hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                                 const uint16_t* k_ring, const uint16_t* v_ring, const int32_t* ctx_len, int batch,
+                                 int nq, int hq, int hkv, int ring, int window, float scale, int nsplit, RingWs ws,
+                                 float* out, hipStream_t s) {
+  const float scale_log2 = scale * 1.4426950408889634f;
+  switch (ring_rows_pad(nq, hq, hkv) / 16) {
+    case 1: ring_launch<1>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
+    case 2: ring_launch<2>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
+    default: ring_launch<3>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace df2

@@ -39,6 +39,9 @@ _SIGNATURES = {
     "dflash2_topk16": ([_c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_lmhead_topk16_workspace": ([_i64, _i64], _size),
     "dflash2_lmhead_topk16": ([_c_ptr, _c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_ring_attention_workspace": ([_i64, _i64, _i64, _i64, _i64], _size),
+    "dflash2_ring_attention": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i64, _i64, _i64,
+                                _i64, _f32, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_context_gate_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_context_gate": ([_c_ptr, _c_ptr, _int, _c_ptr, _i64, _i64, _i64, _int, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_pair_score": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr,
@@ -194,6 +197,28 @@ def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
     _check(lib.dflash2_lmhead_topk16(_ptr(h), _ptr(w), rows, D, V, _ptr(idx), _ptr(val), _ptr(st), _ptr(ws),
                                      ws.numel(), _stream()), "dflash2_lmhead_topk16")
     return (idx, val, st) if row_status else (idx, val)
+
+
+def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale: float = 0.0):
+    """Draft-block attention over each request's K/V ring: q bf16 [B, nq, Hq, Dh], k_blk /
+    v_blk bf16 [B, nq, Hkv, Dh], k_ring / v_ring bf16 [B, ring, Hkv, Dh], ctx_len int32 [B].
+    Returns float32 [B, nq, Hq, Dh]."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _contig(_need(t, n, _BF16_LIKE, q.device), n)
+    _contig(_need(ctx_len, "ctx_len", (torch.int32,), q.device), "ctx_len")
+    B, nq, hq, dh = q.shape
+    hkv, ring = k_blk.shape[2], k_ring.shape[1]
+    if k_blk.shape != (B, nq, hkv, dh) or v_blk.shape != k_blk.shape or k_ring.shape != (B, ring, hkv, dh) \
+            or v_ring.shape != k_ring.shape or ctx_len.shape != (B,):
+        raise ValueError("ring_attention: inconsistent shapes")
+    out = torch.empty((B, nq, hq, dh), dtype=torch.float32, device=q.device)
+    nbytes = lib.dflash2_ring_attention_workspace(B, nq, hq, hkv, window)
+    ws = workspace("ring_attention", nbytes, q.device, (B, nq, hq, hkv, window))
+    _check(lib.dflash2_ring_attention(_ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ring), _ptr(v_ring), _ptr(ctx_len),
+                                      B, nq, hq, hkv, dh, ring, window, scale, _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream()), "dflash2_ring_attention")
+    return out
 
 
 def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None = None, act: str = "sigmoid",

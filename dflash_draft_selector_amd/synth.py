@@ -157,3 +157,19 @@ def lmhead_inputs(rows: int, hidden: int, vocab: int, seed: int, peaks: bool = T
         w[pidx] = f32_to_bf16_bits(h * np.float32(8.0 / hidden))
         out["peak_idx"] = pidx
     return out
+
+
+def ring_inputs(B: int, nq: int, hq: int, hkv: int, ring: int, ctx_len, seed: int, dh: int = 128,
+                q_scale: float = 1.0) -> dict:
+    """Inputs of the draft-block ring attention: q (times q_scale), block K/V and ring K/V
+    ~ N(0, 1) rounded to bf16, drawn in that order from ``default_rng(seed)``; ctx_len as
+    given (an int per request).  Rows of the ring that the window does not cover hold
+    the same kind of data (a ring is reused, so stale rows are ordinary numbers)."""
+    rng = np.random.default_rng(seed)
+    out = {"q_bits": f32_to_bf16_bits(_normal(rng, (B, nq, hq, dh), q_scale)),
+           "kb_bits": f32_to_bf16_bits(_normal(rng, (B, nq, hkv, dh), 1.0)),
+           "vb_bits": f32_to_bf16_bits(_normal(rng, (B, nq, hkv, dh), 1.0)),
+           "kr_bits": f32_to_bf16_bits(_normal(rng, (B, ring, hkv, dh), 1.0)),
+           "vr_bits": f32_to_bf16_bits(_normal(rng, (B, ring, hkv, dh), 1.0)),
+           "ctx_len": np.asarray(ctx_len, dtype=np.int32)}
+    return out

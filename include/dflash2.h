@@ -116,6 +116,39 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * Draft-block attention over each request's K/V ring.  [FT] "Details": the released
+ * drafts use sliding-window attention (window 2048); runtime: the draft's K/V lives in
+ * a ring of 2112 positions per request (the window plus 64 rows of room for a verify's
+ * rejected rows and for prefill rows past a snapshot boundary), and the draft forward
+ * over [last token, mask x 7] reads it; prefix cache: the ring is rebuilt from the
+ * last 2047 context rows; a causal draft is refused at startup.
+ *
+ * Keys of request b: its last n = min(ctx_len[b], window - 1) context positions p
+ * (ring row p mod ring), then the block's nq rows.  Every query row attends to all of
+ * them (non-causal); query head h uses K/V head h / (hq / hkv);
+ * out = softmax(q k^T * scale) v, scale = 1/sqrt(head_dim) when 0 is passed.  Rows of
+ * positions >= ctx_len (rejected or unwritten) and older than the window are never read.
+ * q k^T: bf16 products accumulated in fp32 on the matrix cores; p = exp(s - max) in
+ * fp32, carried into the p v product as two bf16 parts (relative error <= 2^-16);
+ * accumulation in fp32.  Rotary embedding is applied before (the ring holds rotated
+ * keys).
+ *
+ * q bf16 [batch, nq, hq, head_dim]; k_blk, v_blk bf16 [batch, nq, hkv, head_dim];
+ * k_ring, v_ring bf16 [batch, ring, hkv, head_dim]; ctx_len int32 [batch] (values < 0
+ * read as 0); out float [batch, nq, hq, head_dim].  All 16-byte aligned, row-major.
+ * Workspace: dflash2_ring_attention_workspace bytes, any contents.
+ * Errors: NULL pointers; head_dim != 128, hq % hkv != 0, nq * hq / hkv > 48,
+ *         window < 1 or window > ring -> DFLASH2_ERR_SHAPE; scale < 0 or not finite ->
+ *         DFLASH2_ERR_VALUE; alignment; workspace.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window);
+dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                                      const uint16_t* k_ring, const uint16_t* v_ring, const int32_t* ctx_len,
+                                      int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t head_dim,
+                                      int64_t ring, int64_t window, float scale, float* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * Context gate H = act(W_H h + b), one `dim`-wide gate per draft position.
  * [PEGA] "What upstream shipped", item 1 (256-dim token embeddings + context gate).
  * The gate is read as a logistic sigmoid of an affine map (DFLASH2_GATE_SIGMOID);
