@@ -247,6 +247,45 @@ def lmhead_measure(dflash2, torch, dev, stream, reps=10):
             "unfused_torch_matmul_plus_topk16_us": round(unfused_us, 1)}
 
 
+def ring_measure(dflash2, torch, dev, stream, reps=20, nbuf=4):
+    """The draft-block attention over the K/V ring: 15 requests, [last token, mask x 7]
+    (8 rows), 32 query heads over 8 K/V heads of 128, ring 2112, window 2048, context
+    lengths past the window (so every call reads the whole window).  Inputs drawn on the
+    GPU, N(0, 1) bf16, four ring buffers rotated (126 MB of window K/V per call)."""
+    B, nq, hq, hkv, dh, ring, window = 15, 8, 32, 8, 128, 2112, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    r = lambda *s: torch.randn(*s, device=dev, generator=gen).to(torch.bfloat16)
+    q, kb, vb = r(B, nq, hq, dh), r(B, nq, hkv, dh), r(B, nq, hkv, dh)
+    krs = [r(*dflash2.ring_k_shape(B, hkv, ring, dh)) for _ in range(nbuf)]
+    vrs = [r(*dflash2.ring_v_shape(B, hkv, ring, dh)) for _ in range(nbuf)]
+    ctx = torch.randint(2048, 8192, (B,), device=dev, dtype=torch.int32, generator=gen)
+    with torch.cuda.stream(stream):
+        for i in range(nbuf):
+            dflash2.ring_attention(q, kb, vb, krs[i], vrs[i], ctx, window)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(reps):
+                dflash2.ring_attention(q, kb, vb, krs[i % nbuf], vrs[i % nbuf], ctx, window)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (2 * reps)
+    nbytes = B * hkv * (window - 1 + nq) * dh * 2 * 2 + B * nq * hq * dh * (2 + 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"batch": B, "rows": nq, "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "ring": ring, "window": window,
+            "us_per_call": round(us, 1),
+            "roofline": {"bound": "hbm", "kernel": "dflash2_ring_attention = k_ring_partial + k_ring_combine",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +295,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload throughput table")
     ap.add_argument("--select-only", action="store_true", help="time only the select graph (for profiling)")
+    ap.add_argument("--ring-only", action="store_true", help="time only the K/V ring attention (for profiling)")
     ap.add_argument("--lmhead-only", action="store_true", help="time only the fused LM head + top-16 (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 1 GiB buffer three times (a kernel of known traffic, to scale memory counters)")
@@ -279,6 +319,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.ring_only:
+        print(json.dumps({"metric": METRIC, "ring_attention": ring_measure(dflash2, torch, dev, torch.cuda.Stream())}))
+        return
     if args.lmhead_only:
         print(json.dumps({"metric": METRIC, "lmhead_topk16": lmhead_measure(dflash2, torch, dev, torch.cuda.Stream())}))
         return
@@ -440,6 +483,7 @@ def main():
         "wall_s": round(wall, 3),
     }
     result["lmhead_topk16"] = lmhead_measure(dflash2, torch, dev, stream)
+    result["ring_attention"] = ring_measure(dflash2, torch, dev, stream)
     if not args.no_configs:
         result["per_config"] = per_config_throughput(dflash2, torch, dev, stream)
     if not args.no_cpu_baseline:

@@ -9,14 +9,14 @@
 // attends to all of them; query head h uses K/V head h / (Hq / Hkv).
 //
 // k_ring_partial: one 256-thread work-group per (request, K/V head, split) takes a
-// contiguous quarter (nsplit parts) of the request's keys in iterations of 128 keys
-// with an online softmax.  The rows are the nq x G query rows of the K/V head (G query
+// contiguous 1/nsplit of the request's keys (128 or fewer at the window's size: one
+// iteration) in iterations of 128 keys with an online softmax.  The rows are the nq x G query rows of the K/V head (G query
 // heads per K/V head), in MT 16-row tiles.  Per iteration: wave w computes S for keys
 // 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q fragments kept in registers, K
 // fragments loaded straight from the ring or block rows); row maxima and sums go
 // through LDS; P = exp(S - m) is split into bf16 hi + lo parts (relative error <=
-// 2^-16) and stored row-major in LDS; V is staged transposed ([dim][key]) in LDS; wave
-// w accumulates O^T for dims 32w .. 32w+31 as V^T x P^T (hi and lo).  Each work-group
+// 2^-16) and stored row-major in LDS; V is staged row-major in LDS and read down its
+// columns; wave w accumulates O^T for dims 32w .. 32w+31 as V^T x P^T (hi and lo).  Each work-group
 // stores its rows' (max, sum, O).  k_ring_combine merges the splits.
 #include "dflash2_internal.h"
 #include "device_common.h"
@@ -27,7 +27,7 @@ namespace df2 {
 constexpr int kRingThreads = 256;            // 4 waves
 constexpr int kRingDh = 128;                 // head dim
 constexpr int kRingC = 128;                  // keys per iteration
-constexpr int kRingVPitch = kRingC + 8;      // bf16 elements per staged V^T row (16-byte aligned, odd bank step)
+constexpr int kRingVPitch = kRingDh + 8;     // bf16 elements per staged V row (16-byte aligned rows)
 constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row
 
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad) {
@@ -40,7 +40,7 @@ RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pa
 
 template <int MT>
 struct RingShared {
-  uint16_t vt[kRingDh][kRingVPitch];         // V^T of the iteration's keys
+  uint16_t v[kRingC][kRingVPitch];           // V rows of the iteration's keys
   uint16_t p_hi[MT * 16][kRingPPitch];       // P rows, bf16 high part
   uint16_t p_lo[MT * 16][kRingPPitch];       // P rows, bf16 low part
   float red[4][MT * 16];                     // per-wave row maxima / sums
@@ -131,7 +131,8 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
 #pragma unroll
       for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 32 * s);
     }
-    // stage V^T: thread t loads key (t / 16)'s 16-byte segment t % 16 (8 rounds of 16 keys)
+    // stage V rows: thread t loads key (t / 16)'s 16-byte segment t % 16 (8 rounds of
+    // 16 keys); a row's 16 segments are one contiguous 16-byte-aligned LDS run
 #pragma unroll
     for (int e = 0; e < kRingC * 16 / kRingThreads; ++e) {
       const int idx = tid + kRingThreads * e;
@@ -139,13 +140,7 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
       const int kk = base + kl;
       const uint16_t* vp = (key_src(kk) ? v_ring : v_blk) + key_off(kk) + 8 * seg;
       const u32x4 v = *reinterpret_cast<const u32x4*>(vp);
-      const bool ok = kk < k1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w = ok ? v[c] : 0u;
-        sm.vt[8 * seg + 2 * c][kl] = (uint16_t)(w & 0xffffu);
-        sm.vt[8 * seg + 2 * c + 1][kl] = (uint16_t)(w >> 16);
-      }
+      *reinterpret_cast<u32x4*>(&sm.v[kl][8 * seg]) = kk < k1 ? v : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n)
@@ -223,10 +218,18 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
     }
 #pragma unroll
     for (int ks = 0; ks < kRingC / 32; ++ks) {
+      // V^T fragment: dim 32 wv + 16 dt + i16, keys 32 ks + 8 g .. + 7 (eight 2-byte reads
+      // down a column of the row-major V rows)
       u32x4 vf[2];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        vf[dt] = *reinterpret_cast<const u32x4*>(&sm.vt[32 * wv + 16 * dt + i16][32 * ks + 8 * g]);
+      for (int dt = 0; dt < 2; ++dt) {
+        const int d = 32 * wv + 16 * dt + i16;
+        uint32_t w[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          w[c] = (uint32_t)sm.v[32 * ks + 8 * g + 2 * c][d] | ((uint32_t)sm.v[32 * ks + 8 * g + 2 * c + 1][d] << 16);
+        vf[dt] = (u32x4){w[0], w[1], w[2], w[3]};
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 ph = *reinterpret_cast<const u32x4*>(&sm.p_hi[16 * mt + i16][32 * ks + 8 * g]);
@@ -266,30 +269,57 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
       *reinterpret_cast<f32x4*>(os + (size_t)(16 * mt + i16) * kRingDh + 32 * wv + 16 * dt + 4 * g) = o[dt][mt];
 }
 
-// One work-group per (request, K/V head): out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
+// One work-group per (request, K/V head, 8 query rows): out = sum_s w_s O_s with
+// w_s = e^(m_s - M) / sum_s' e^(m_s' - M) l_s' (M the rows' maximum over the splits);
+// the weights of a row are formed once, then every output adds its splits' values with
+// all loads in flight.
+constexpr int kRingCombRows = 8;
+constexpr int kRingMaxSplits = 32;
+
 template <int MT>
 __global__ void __launch_bounds__(kRingThreads) k_ring_combine(const float* __restrict__ ws_ml,
                                                                 const float* __restrict__ ws_o, int nq, int hq,
                                                                 int hkv, int nsplit, float* __restrict__ out) {
   constexpr int kRows = MT * 16;
-  const int bk = blockIdx.x;
+  __shared__ float wsh[kRingCombRows][kRingMaxSplits];
+  const int groups = (kRows + kRingCombRows - 1) / kRingCombRows;
+  const int bk = (int)blockIdx.x / groups;
+  const int r0 = ((int)blockIdx.x % groups) * kRingCombRows;
   const int kvh = bk % hkv, b = bk / hkv;
   const int G = hq / hkv;
   const int nrows = nq * G;
-  for (int e = threadIdx.x; e < nrows * kRingDh; e += kRingThreads) {
-    const int row = e / kRingDh, d = e - row * kRingDh;
+  const size_t u0 = (size_t)bk * nsplit;
+  if (threadIdx.x < kRingCombRows) {
+    const int row = r0 + (int)threadIdx.x;
     float M = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((size_t)bk * nsplit + s) * kRows * 2 + 2 * row]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t u = (size_t)bk * nsplit + s;
-      const float ms = ws_ml[u * kRows * 2 + 2 * row];
-      const float w = ms == -__builtin_inff() ? 0.f : exp2f(ms - M);
-      num += w * ws_o[(u * kRows + row) * kRingDh + d];
-      den += w * ws_ml[u * kRows * 2 + 2 * row + 1];
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[(u0 + s) * kRows * 2 + 2 * row]);
+    float den = 0.f;
+    float w[kRingMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kRingMaxSplits; ++s) {
+      w[s] = 0.f;
+      if (s < nsplit) {
+        const float ms = ws_ml[(u0 + s) * kRows * 2 + 2 * row];
+        w[s] = ms == -__builtin_inff() ? 0.f : exp2f(ms - M);
+        den += w[s] * ws_ml[(u0 + s) * kRows * 2 + 2 * row + 1];
+      }
     }
+#pragma unroll
+    for (int s = 0; s < kRingMaxSplits; ++s) wsh[threadIdx.x][s] = w[s] / den;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kRingCombRows * kRingDh; e += kRingThreads) {
+    const int rl = e / kRingDh, d = e - rl * kRingDh;
+    const int row = r0 + rl;
+    if (row >= nrows) continue;
+    float v[kRingMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kRingMaxSplits; ++s) v[s] = s < nsplit ? ws_o[((u0 + s) * kRows + row) * kRingDh + d] : 0.f;
+    float num = 0.f;
+#pragma unroll
+    for (int s = 0; s < kRingMaxSplits; ++s) num += wsh[rl][s] * v[s];
     const int i = row / G, h = kvh * G + row % G;
-    out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num / den;
+    out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num;
   }
 }
 
@@ -300,8 +330,8 @@ int ring_rows_pad(int nq, int hq, int hkv) {
 
 int ring_splits(int nq, int window) {
   const int keys = window - 1 + nq;
-  const int n = (keys + 511) / 512;          // about 512 keys (4 iterations) per work-group
-  return n < 1 ? 1 : n > 8 ? 8 : n;
+  const int n = (keys + kRingC - 1) / kRingC;  // one 128-key iteration per work-group: no serial load round trips
+  return n < 1 ? 1 : n > kRingMaxSplits ? kRingMaxSplits : n;
 }
 
 template <int MT>
@@ -310,8 +340,9 @@ static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, co
                         float scale_log2, int nsplit, const RingWs& ws, float* out) {
   hipLaunchKernelGGL((k_ring_partial<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(kRingThreads), 0, s, q, kb, vb, kr,
                      vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit, ws.ml, ws.o);
-  hipLaunchKernelGGL((k_ring_combine<MT>), dim3((unsigned)(B * hkv)), dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq,
-                     hkv, nsplit, out);
+  const int groups = (MT * 16 + kRingCombRows - 1) / kRingCombRows;
+  hipLaunchKernelGGL((k_ring_combine<MT>), dim3((unsigned)(B * hkv * groups)), dim3(kRingThreads), 0, s, ws.ml, ws.o,
+                     nq, hq, hkv, nsplit, out);
 }
 
 hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,

@@ -199,6 +199,16 @@ def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
     return (idx, val, st) if row_status else (idx, val)
 
 
+def ring_k_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
+    """Shape of the K ring the library reads."""
+    return (B, ring, hkv, dh)
+
+
+def ring_v_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
+    """Shape of the V ring the library reads."""
+    return (B, ring, hkv, dh)
+
+
 def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale: float = 0.0):
     """Draft-block attention over each request's K/V ring: q bf16 [B, nq, Hq, Dh], k_blk /
     v_blk bf16 [B, nq, Hkv, Dh], k_ring / v_ring bf16 [B, ring, Hkv, Dh], ctx_len int32 [B].
