@@ -4,20 +4,25 @@
 // [last token, mask x 7] reads it; a causal draft is refused, so the block's rows see
 // each other).
 //
-// Keys of request b: its last min(ctx_len, window - 1) context positions (position p in
-// ring row p mod ring), then the block's own nq rows.  Every query row of the block
-// attends to all of them; query head h uses K/V head h / (Hq / Hkv).
+// Keys of request b: its last min(ctx_len, window - 1) context positions p0 .. L - 1
+// (position p in ring row p mod ring), then the block's own nq rows.  Every query row of
+// the block attends to all of them; query head h uses K/V head h / (Hq / Hkv).
 //
-// k_ring_partial: one 256-thread work-group per (request, K/V head, split) takes a
-// contiguous 1/nsplit of the request's keys (128 or fewer at the window's size: one
-// iteration) in iterations of 128 keys with an online softmax.  The rows are the nq x G query rows of the K/V head (G query
-// heads per K/V head), in MT 16-row tiles.  Per iteration: wave w computes S for keys
-// 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q fragments kept in registers, K
-// fragments loaded straight from the ring or block rows); row maxima and sums go
-// through LDS; P = exp(S - m) is split into bf16 hi + lo parts (relative error <=
-// 2^-16) and stored row-major in LDS; V is staged row-major in LDS and read down its
-// columns; wave w accumulates O^T for dims 32w .. 32w+31 as V^T x P^T (hi and lo).  Each work-group
-// stores its rows' (max, sum, O).  k_ring_combine merges the splits.
+// Ring layouts, chosen for this read (the hot one: every draft step reads the whole
+// window, a verify writes a few rows): K head-major [B][Hkv][ring][Dh]; V transposed
+// [B][Hkv][Dh][ring], so the P V product's V^T fragments (one dim, 8 consecutive
+// positions) are single 16-byte loads.  ring % 8 == 0, and positions are walked in
+// 8-aligned groups, so a group never wraps.
+//
+// k_ring_partial: one 256-thread work-group per (request, K/V head, split).  Split s <
+// nctx_splits takes the 128 positions pa + 128 s .. (pa = p0 rounded down to 8) of the
+// context, masked to [p0, L); the last split takes the block's keys.  The rows are the
+// nq x G query rows of the K/V head, in MT 16-row tiles.  Wave w computes S for keys
+// 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q and K fragments straight from memory);
+// row maxima and sums go through LDS; P = exp(S - m) is split into bf16 hi + lo parts
+// (relative error <= 2^-16) and stored row-major in LDS; wave w accumulates O^T for dims
+// 32w .. 32w+31 as V^T x P^T (hi and lo), its V^T fragments loaded at the start.  Each
+// work-group stores its rows' (max, sum, O); k_ring_combine merges the splits.
 #include "dflash2_internal.h"
 #include "device_common.h"
 #include "topk_dev.h"
@@ -26,9 +31,8 @@ namespace df2 {
 
 constexpr int kRingThreads = 256;            // 4 waves
 constexpr int kRingDh = 128;                 // head dim
-constexpr int kRingC = 128;                  // keys per iteration
-constexpr int kRingVPitch = kRingDh + 8;     // bf16 elements per staged V row (16-byte aligned rows)
-constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row
+constexpr int kRingC = 128;                  // keys per work-group
+constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row (16-byte aligned rows)
 
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad) {
   RingWs w;
@@ -40,15 +44,11 @@ RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pa
 
 template <int MT>
 struct RingShared {
-  uint16_t v[kRingC][kRingVPitch];           // V rows of the iteration's keys
   uint16_t p_hi[MT * 16][kRingPPitch];       // P rows, bf16 high part
   uint16_t p_lo[MT * 16][kRingPPitch];       // P rows, bf16 low part
-  float red[4][MT * 16];                     // per-wave row maxima / sums
-  float alpha[MT * 16];                      // rescale of the running state
-  float mrow[MT * 16];
+  float red_max[4][MT * 16];                 // per-wave row maxima
+  float red_sum[4][MT * 16];                 // per-wave row sums
 };
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return f32_to_bf16_rne(f); }
 
 // sum over the 16 lanes of the row, every lane gets it (the reduction order of row16_max)
 __device__ __forceinline__ float row16_sum(float v) {
@@ -63,12 +63,13 @@ template <int MT>
 __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
-    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nsplit, float* __restrict__ ws_ml,
+    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nctx_splits, float* __restrict__ ws_ml,
     float* __restrict__ ws_o) {
   __shared__ RingShared<MT> sm;
   constexpr int kRows = MT * 16;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
+  const int nsplit = nctx_splits + 1;
   const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
   const int split = unit % nsplit;
   const int bk = unit / nsplit;
@@ -78,11 +79,25 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
 
   const int L = ctx_len[b] > 0 ? ctx_len[b] : 0;
   const int nctx = L < window - 1 ? L : window - 1;
-  const int nkeys = nctx + nq;
-  const int k0 = (int)((long long)nkeys * split / nsplit);
-  const int k1 = (int)((long long)nkeys * (split + 1) / nsplit);
+  const int p0 = L - nctx;
+  const bool blk = split == nctx_splits;
+  const int base = blk ? 0 : (p0 & ~7) + kRingC * split;  // first key: a position, or block row 0
+  const int lo = blk ? 0 : p0;                              // keys [lo, hi) are read
+  const int hi = blk ? nq : L;
+  float* ml = ws_ml + (size_t)unit * kRows * 2;
+  float* os = ws_o + (size_t)unit * kRows * kRingDh;
+  if (base >= hi) {                                         // a context split past the window: empty
+    for (int e = tid; e < kRows; e += kRingThreads) {
+      ml[2 * e] = -__builtin_inff();
+      ml[2 * e + 1] = 0.f;
+    }
+    for (int e = tid; e < kRows * kRingDh / 4; e += kRingThreads)
+      reinterpret_cast<f32x4*>(os)[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const size_t head = (size_t)b * hkv + kvh;
 
-  // Q fragments: row r = i * G + (h - kvh G) of the block (query position i, head h)
+  // ---- loads: Q, K and V^T fragments --------------------------------------------------
   u32x4 qf[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -95,170 +110,127 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
       qf[mt][s] = r < nrows ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
-  // address of key kk (any index: out-of-range keys read block row 0 and are masked)
-  auto key_off = [&](int kk) -> size_t {
-    if (kk >= 0 && kk < nctx) {
-      const int pos = L - nctx + kk;
-      return (((size_t)b * ring + pos % ring) * hkv + kvh) * kRingDh;
+  u32x4 kf[2][4];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int key = base + 32 * wv + 16 * n + i16;
+    const uint16_t* kp = blk ? k_blk + ((size_t)(b * nq + (key < nq ? key : 0)) * hkv + kvh) * kRingDh
+                             : k_ring + (head * ring + key % ring) * kRingDh;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 8 * g + 32 * s);
+  }
+  // V^T fragment (dt, ks): dim 32 wv + 16 dt + i16, keys base + 32 ks + 8 g .. + 7, keys
+  // outside [lo, hi) zeroed (a stale row never enters, not even times zero)
+  u32x4 vf[2][kRingC / 32];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    const int d = 32 * wv + 16 * dt + i16;
+#pragma unroll
+    for (int ks = 0; ks < kRingC / 32; ++ks) {
+      const int k0 = base + 32 * ks + 8 * g;
+      uint32_t w[4];
+      if (!blk) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(v_ring + (head * kRingDh + d) * ring + k0 % ring);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool e0 = k0 + 2 * c >= lo && k0 + 2 * c < hi;
+          const bool e1 = k0 + 2 * c + 1 >= lo && k0 + 2 * c + 1 < hi;
+          w[c] = (e0 ? (v[c] & 0xffffu) : 0u) | (e1 ? (v[c] & 0xffff0000u) : 0u);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j0 = k0 + 2 * c, j1 = j0 + 1;
+          const uint32_t a = j0 < nq ? v_blk[((size_t)(b * nq + j0) * hkv + kvh) * kRingDh + d] : 0u;
+          const uint32_t bb = j1 < nq ? v_blk[((size_t)(b * nq + j1) * hkv + kvh) * kRingDh + d] : 0u;
+          w[c] = a | (bb << 16);
+        }
+      }
+      vf[dt][ks] = (u32x4){w[0], w[1], w[2], w[3]};
     }
-    const int j = kk - nctx;
-    return ((size_t)(b * nq + (j >= 0 && j < nq ? j : 0)) * hkv + kvh) * kRingDh;
-  };
-  auto key_src = [&](int kk) { return kk >= 0 && kk < nctx; };
+  }
 
-  // running state: O^T tiles (dims 32 wv + 16 dt + 4 g + r, row 16 mt + i16)
+  // ---- S = Q K^T for keys base + 32 wv + 16 n + i16, scaled to log2 units, masked -----
+  f32x4 sacc[2][MT];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int key = base + 32 * wv + 16 * n + i16;
+    const bool valid = key >= lo && key < hi;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      sacc[n][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[n][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[mt][s]),
+                                                             __builtin_bit_cast(bf16x8, kf[n][s]), sacc[n][mt], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[n][mt][r] = valid ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
+    }
+  }
+  // ---- row maxima (every row has a valid key in a non-empty split) ------------------
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = row16_max(fmaxf(sacc[0][mt][r], sacc[1][mt][r]));
+      if (i16 == 0) sm.red_max[wv][16 * mt + 4 * g + r] = x;
+    }
+  __syncthreads();
+  // ---- P = exp2(S - m): bf16 hi / lo parts into LDS, row sums -----------------------
+  float mrow[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * mt + 4 * g + r;
+      const float m = fmaxf(fmaxf(sm.red_max[0][row], sm.red_max[1][row]),
+                            fmaxf(sm.red_max[2][row], sm.red_max[3][row]));
+      mrow[mt][r] = m;
+      float sum = 0.f;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const float p = exp2f(sacc[n][mt][r] - m);
+        sum += p;
+        const uint32_t ph = f32_to_bf16_rne(p);
+        const uint32_t pl = f32_to_bf16_rne(p - __uint_as_float(ph << 16));
+        const int col = 32 * wv + 16 * n + i16;
+        sm.p_hi[row][col] = (uint16_t)ph;
+        sm.p_lo[row][col] = (uint16_t)pl;
+      }
+      sum = row16_sum(sum);
+      if (i16 == 0) sm.red_sum[wv][row] = sum;
+    }
+  __syncthreads();
+  // ---- O^T = V^T x P^T (hi, then lo) --------------------------------------------------
   f32x4 o[2][MT];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[dt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int r = tid; r < kRows; r += kRingThreads) sm.mrow[r] = -__builtin_inff();
-  float l_run[MT][4];                                       // row sums in the S layout (rows 16 mt + 4 g + r)
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) l_run[mt][r] = 0.f;
-  __syncthreads();
-
-  for (int base = k0; base < k1; base += kRingC) {
-    // ---- S for keys base + 32 wv + 16 n + i16 ------------------------------------
-    f32x4 sacc[2][MT];
-    u32x4 kf[2][4];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int kk = base + 32 * wv + 16 * n + i16;
-      const uint16_t* kp = (key_src(kk) ? k_ring : k_blk) + key_off(kk) + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 32 * s);
-    }
-    // stage V rows: thread t loads key (t / 16)'s 16-byte segment t % 16 (8 rounds of
-    // 16 keys); a row's 16 segments are one contiguous 16-byte-aligned LDS run
-#pragma unroll
-    for (int e = 0; e < kRingC * 16 / kRingThreads; ++e) {
-      const int idx = tid + kRingThreads * e;
-      const int kl = idx >> 4, seg = idx & 15;
-      const int kk = base + kl;
-      const uint16_t* vp = (key_src(kk) ? v_ring : v_blk) + key_off(kk) + 8 * seg;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(vp);
-      *reinterpret_cast<u32x4*>(&sm.v[kl][8 * seg]) = kk < k1 ? v : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        sacc[n][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          sacc[n][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[mt][s]),
-                                                               __builtin_bit_cast(bf16x8, kf[n][s]), sacc[n][mt],
-                                                               0, 0, 0);
-      }
-    // scale to log2 units and mask keys past the split
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const bool valid = base + 32 * wv + 16 * n + i16 < k1;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[n][mt][r] = valid ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
-    }
-    // ---- row maxima: lanes of a 16-lane row share rows 16 mt + 4 g + r -------------
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = row16_max(fmaxf(sacc[0][mt][r], sacc[1][mt][r]));
-        if (i16 == 0) sm.red[wv][16 * mt + 4 * g + r] = x;
-      }
-    __syncthreads();
-    for (int row = tid; row < kRows; row += kRingThreads) {
-      const float it = fmaxf(fmaxf(sm.red[0][row], sm.red[1][row]), fmaxf(sm.red[2][row], sm.red[3][row]));
-      const float mo = sm.mrow[row];
-      const float mn = fmaxf(mo, it);                        // finite: every iteration has a valid key
-      sm.alpha[row] = exp2f(mo - mn);                        // 0 on the first iteration
-      sm.mrow[row] = mn;
-    }
-    __syncthreads();
-    // ---- P = exp2(S - m): row sums, and bf16 hi / lo parts into LDS -----------------
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        const float mn = sm.mrow[row];
-        float sum = 0.f;
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const float p = exp2f(sacc[n][mt][r] - mn);
-          sum += p;
-          const uint32_t hi = bf16_rne_bits(p);
-          const uint32_t lo = bf16_rne_bits(p - __uint_as_float(hi << 16));
-          const int col = 32 * wv + 16 * n + i16;
-          sm.p_hi[row][col] = (uint16_t)hi;
-          sm.p_lo[row][col] = (uint16_t)lo;
-        }
-        sum = row16_sum(sum);
-        if (i16 == 0) sm.red[wv][row] = sum;
-        l_run[mt][r] *= sm.alpha[row];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        l_run[mt][r] += (sm.red[0][row] + sm.red[1][row]) + (sm.red[2][row] + sm.red[3][row]);
-      }
-    // ---- O^T += V^T x P^T (hi, then lo), after rescaling by alpha of each row ---------
+  for (int ks = 0; ks < kRingC / 32; ++ks)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float a = sm.alpha[16 * mt + i16];
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) o[dt][mt] *= a;
-    }
-#pragma unroll
-    for (int ks = 0; ks < kRingC / 32; ++ks) {
-      // V^T fragment: dim 32 wv + 16 dt + i16, keys 32 ks + 8 g .. + 7 (eight 2-byte reads
-      // down a column of the row-major V rows)
-      u32x4 vf[2];
+      const u32x4 ph = *reinterpret_cast<const u32x4*>(&sm.p_hi[16 * mt + i16][32 * ks + 8 * g]);
+      const u32x4 pl = *reinterpret_cast<const u32x4*>(&sm.p_lo[16 * mt + i16][32 * ks + 8 * g]);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const int d = 32 * wv + 16 * dt + i16;
-        uint32_t w[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          w[c] = (uint32_t)sm.v[32 * ks + 8 * g + 2 * c][d] | ((uint32_t)sm.v[32 * ks + 8 * g + 2 * c + 1][d] << 16);
-        vf[dt] = (u32x4){w[0], w[1], w[2], w[3]};
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 ph = *reinterpret_cast<const u32x4*>(&sm.p_hi[16 * mt + i16][32 * ks + 8 * g]);
-        const u32x4 pl = *reinterpret_cast<const u32x4*>(&sm.p_lo[16 * mt + i16][32 * ks + 8 * g]);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
-                                                              __builtin_bit_cast(bf16x8, ph), o[dt][mt], 0, 0, 0);
-          o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
-                                                              __builtin_bit_cast(bf16x8, pl), o[dt][mt], 0, 0, 0);
-        }
+        o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt][ks]),
+                                                            __builtin_bit_cast(bf16x8, ph), o[dt][mt], 0, 0, 0);
+        o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt][ks]),
+                                                            __builtin_bit_cast(bf16x8, pl), o[dt][mt], 0, 0, 0);
       }
     }
-    __syncthreads();                                        // LDS is rewritten by the next iteration
-  }
 
   // ---- the split's state: (max, sum) per row, and O (rows x 128 dims) --------------
-  float* ml = ws_ml + (size_t)unit * kRows * 2;
-  float* os = ws_o + (size_t)unit * kRows * kRingDh;
-  if (wv == 0) {
+  if (wv == 0 && i16 == 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * mt + 4 * g + r;
-        if (i16 == 0) {
-          ml[2 * row] = k1 > k0 ? sm.mrow[row] : -__builtin_inff();
-          ml[2 * row + 1] = l_run[mt][r];
-        }
+        ml[2 * row] = mrow[mt][r];
+        ml[2 * row + 1] = (sm.red_sum[0][row] + sm.red_sum[1][row]) + (sm.red_sum[2][row] + sm.red_sum[3][row]);
       }
   }
   // O^T tile (dims 32 wv + 16 dt + 4 g + r, row 16 mt + i16) -> O[row][dims .. + 3]
@@ -328,10 +300,11 @@ int ring_rows_pad(int nq, int hq, int hkv) {
   return rows <= 16 ? 16 : rows <= 32 ? 32 : 48;
 }
 
+// Context splits of 128 positions covering window - 1 positions from an 8-aligned start,
+// plus one split for the block's keys.
 int ring_splits(int nq, int window) {
-  const int keys = window - 1 + nq;
-  const int n = (keys + kRingC - 1) / kRingC;  // one 128-key iteration per work-group: no serial load round trips
-  return n < 1 ? 1 : n > kRingMaxSplits ? kRingMaxSplits : n;
+  (void)nq;
+  return (window - 1 + 7 + kRingC - 1) / kRingC + 1;
 }
 
 template <int MT>
@@ -339,7 +312,7 @@ static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, co
                         const uint16_t* vr, const int32_t* ctx, int B, int nq, int hq, int hkv, int ring, int window,
                         float scale_log2, int nsplit, const RingWs& ws, float* out) {
   hipLaunchKernelGGL((k_ring_partial<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(kRingThreads), 0, s, q, kb, vb, kr,
-                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit, ws.ml, ws.o);
+                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit - 1, ws.ml, ws.o);
   const int groups = (MT * 16 + kRingCombRows - 1) / kRingCombRows;
   hipLaunchKernelGGL((k_ring_combine<MT>), dim3((unsigned)(B * hkv * groups)), dim3(kRingThreads), 0, s, ws.ml, ws.o,
                      nq, hq, hkv, nsplit, out);

@@ -200,27 +200,27 @@ def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
 
 
 def ring_k_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
-    """Shape of the K ring the library reads."""
-    return (B, ring, hkv, dh)
+    """Shape of the K ring the library reads: head-major [B, Hkv, ring, Dh]."""
+    return (B, hkv, ring, dh)
 
 
 def ring_v_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
-    """Shape of the V ring the library reads."""
-    return (B, ring, hkv, dh)
+    """Shape of the V ring the library reads: transposed [B, Hkv, Dh, ring]."""
+    return (B, hkv, dh, ring)
 
 
 def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale: float = 0.0):
     """Draft-block attention over each request's K/V ring: q bf16 [B, nq, Hq, Dh], k_blk /
-    v_blk bf16 [B, nq, Hkv, Dh], k_ring / v_ring bf16 [B, ring, Hkv, Dh], ctx_len int32 [B].
-    Returns float32 [B, nq, Hq, Dh]."""
+    v_blk bf16 [B, nq, Hkv, Dh], k_ring bf16 [B, Hkv, ring, Dh], v_ring bf16 [B, Hkv, Dh,
+    ring] (transposed), ctx_len int32 [B].  Returns float32 [B, nq, Hq, Dh]."""
     lib = load_library()
     for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_ring, "k_ring"), (v_ring, "v_ring")):
         _contig(_need(t, n, _BF16_LIKE, q.device), n)
     _contig(_need(ctx_len, "ctx_len", (torch.int32,), q.device), "ctx_len")
     B, nq, hq, dh = q.shape
-    hkv, ring = k_blk.shape[2], k_ring.shape[1]
-    if k_blk.shape != (B, nq, hkv, dh) or v_blk.shape != k_blk.shape or k_ring.shape != (B, ring, hkv, dh) \
-            or v_ring.shape != k_ring.shape or ctx_len.shape != (B,):
+    hkv, ring = k_blk.shape[2], k_ring.shape[2]
+    if k_blk.shape != (B, nq, hkv, dh) or v_blk.shape != k_blk.shape or k_ring.shape != ring_k_shape(B, hkv, ring, dh) \
+            or v_ring.shape != ring_v_shape(B, hkv, ring, dh) or ctx_len.shape != (B,):
         raise ValueError("ring_attention: inconsistent shapes")
     out = torch.empty((B, nq, hq, dh), dtype=torch.float32, device=q.device)
     nbytes = lib.dflash2_ring_attention_workspace(B, nq, hq, hkv, window)

@@ -134,12 +134,15 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
  * keys).
  *
  * q bf16 [batch, nq, hq, head_dim]; k_blk, v_blk bf16 [batch, nq, hkv, head_dim];
- * k_ring, v_ring bf16 [batch, ring, hkv, head_dim]; ctx_len int32 [batch] (values < 0
- * read as 0); out float [batch, nq, hq, head_dim].  All 16-byte aligned, row-major.
- * Workspace: dflash2_ring_attention_workspace bytes, any contents.
- * Errors: NULL pointers; head_dim != 128, hq % hkv != 0, nq * hq / hkv > 48,
- *         window < 1 or window > ring -> DFLASH2_ERR_SHAPE; scale < 0 or not finite ->
- *         DFLASH2_ERR_VALUE; alignment; workspace.
+ * k_ring bf16 [batch, hkv, ring, head_dim] (head-major); v_ring bf16 [batch, hkv,
+ * head_dim, ring] (transposed: a position's values are one column), the layouts that
+ * let every draft step read the window with 16-byte loads (a verify writes a few rows);
+ * ctx_len int32 [batch] (values < 0 read as 0); out float [batch, nq, hq, head_dim].
+ * All row-major, 16-byte aligned.  Workspace: dflash2_ring_attention_workspace bytes,
+ * any contents.
+ * Errors: NULL pointers; head_dim != 128, hq % hkv != 0, nq * hq / hkv > 48, ring % 8
+ *         != 0, window < 1, window > ring or window > 3960 -> DFLASH2_ERR_SHAPE;
+ *         scale < 0 or not finite -> DFLASH2_ERR_VALUE; alignment; workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window);
 dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,

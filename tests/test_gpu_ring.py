@@ -29,12 +29,19 @@ def d2():
     return dflash2
 
 
-def run_and_check(d2, inp, window, what, scale=0.0):
+def gpu_args(inp):
+    """The inputs in the library's layouts: rings [B, ring, Hkv, Dh] as drawn become a
+    head-major K ring [B, Hkv, ring, Dh] and a transposed V ring [B, Hkv, Dh, ring]."""
     import torch
+    kr = np.ascontiguousarray(inp["kr_bits"].transpose(0, 2, 1, 3))
+    vr = np.ascontiguousarray(inp["vr_bits"].transpose(0, 2, 3, 1))
+    return (to_gpu_bits(inp["q_bits"]), to_gpu_bits(inp["kb_bits"]), to_gpu_bits(inp["vb_bits"]), to_gpu_bits(kr),
+            to_gpu_bits(vr), torch.from_numpy(inp["ctx_len"]).cuda())
+
+
+def run_and_check(d2, inp, window, what, scale=0.0):
     B, nq, hq, dh = inp["q_bits"].shape
-    got = cpu(d2.ring_attention(to_gpu_bits(inp["q_bits"]), to_gpu_bits(inp["kb_bits"]), to_gpu_bits(inp["vb_bits"]),
-                                to_gpu_bits(inp["kr_bits"]), to_gpu_bits(inp["vr_bits"]),
-                                torch.from_numpy(inp["ctx_len"]).cuda(), window, scale))
+    got = cpu(d2.ring_attention(*gpu_args(inp), window, scale))
     f = oracle.bf16_to_f64
     ref, pv_abs, smax = oracle.ring_attention(f(inp["q_bits"]), f(inp["kb_bits"]), f(inp["vb_bits"]),
                                               f(inp["kr_bits"]), f(inp["vr_bits"]), inp["ctx_len"], window,
@@ -51,6 +58,7 @@ def run_and_check(d2, inp, window, what, scale=0.0):
 
 @pytest.mark.parametrize("B,nq,hq,hkv,ring,window,ctx", [
     (3, 8, 8, 2, 2112, 2048, [0, 100, 5000]),          # block only; a partial window; a full window that wraps
+    (3, 8, 8, 2, 2112, 2048, [1, 2049, 4229]),         # window starts off the 8-row grid, one wraps mid-group
     (2, 8, 12, 2, 2112, 2048, [2047, 2048]),            # 48 query rows (three row tiles); window just full
     (2, 1, 4, 4, 2112, 2048, [1, 3000]),               # one query row per K/V head
     (4, 8, 8, 8, 40, 33, [31, 32, 33, 77]),             # small ring: wraps, fewer keys than iterations
@@ -68,13 +76,10 @@ def test_ring_attention_parity(d2, B, nq, hq, hkv, ring, window, ctx):
 def test_ring_attention_never_reads_rows_outside_the_window(d2):
     # NaN in every ring row the window does not cover (stale, rejected or too old): the
     # output stays finite and equal to the clean run
-    import torch
     B, nq, hq, hkv, ring, window = 2, 8, 8, 2, 2112, 2048
-    ctx = [3000, 500]
+    ctx = [3001, 501]                                     # windows starting off the 8-row grid
     inp = synth.ring_inputs(B, nq, hq, hkv, ring, ctx, seed=9)
-    args = lambda d: (to_gpu_bits(d["q_bits"]), to_gpu_bits(d["kb_bits"]), to_gpu_bits(d["vb_bits"]),
-                      to_gpu_bits(d["kr_bits"]), to_gpu_bits(d["vr_bits"]), torch.from_numpy(d["ctx_len"]).cuda())
-    clean = cpu(d2.ring_attention(*args(inp), window))
+    clean = cpu(d2.ring_attention(*gpu_args(inp), window))
     dirty = dict(inp)
     kr, vr = inp["kr_bits"].copy(), inp["vr_bits"].copy()
     for b in range(B):
@@ -84,7 +89,7 @@ def test_ring_attention_never_reads_rows_outside_the_window(d2):
                 kr[b, row] = 0x7FC0
                 vr[b, row] = 0x7FC0
     dirty["kr_bits"], dirty["vr_bits"] = kr, vr
-    got = cpu(d2.ring_attention(*args(dirty), window))
+    got = cpu(d2.ring_attention(*gpu_args(dirty), window))
     assert np.all(np.isfinite(got))
     np.testing.assert_array_equal(got, clean)
 
