@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
   const int hi = blk ? nq : L;
   float* ml = ws_ml + (size_t)unit * kRows * 2;
   float* os = ws_o + (size_t)unit * kRows * kRingDh;
-  if (base >= hi) {                                         // a context split past the window: empty
+  if (base >= hi || (!blk && nctx == 0)) {                 // a context split past the window: empty
     for (int e = tid; e < kRows; e += kRingThreads) {
       ml[2 * e] = -__builtin_inff();
       ml[2 * e + 1] = 0.f;
