@@ -59,42 +59,22 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-template <int MT>
-__global__ void __launch_bounds__(kRingThreads) k_ring_partial(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
-    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
-    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nctx_splits, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o) {
-  __shared__ RingShared<MT> sm;
+// The work of one non-empty split (BLK: the block's keys; else 128 context positions
+// from base; EDGE: some of its keys lie outside [lo, hi) and are masked).  Templated so
+// that each form's loads are straight-line code (the waits on them then count
+// outstanding loads exactly instead of draining them) and interior splits skip the
+// masking.
+template <int MT, bool BLK, bool EDGE>
+__device__ __forceinline__ void ring_split(RingShared<MT>& sm, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
+                                           const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring,
+                                           int b, int kvh, int nq, int hq, int hkv, int ring, int base, int lo, int hi,
+                                           float scale_log2, float* __restrict__ ml, float* __restrict__ os) {
   constexpr int kRows = MT * 16;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int nsplit = nctx_splits + 1;
-  const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
-  const int split = unit % nsplit;
-  const int bk = unit / nsplit;
-  const int kvh = bk % hkv, b = bk / hkv;
   const int G = hq / hkv;
   const int nrows = nq * G;
-
-  const int L = ctx_len[b] > 0 ? ctx_len[b] : 0;
-  const int nctx = L < window - 1 ? L : window - 1;
-  const int p0 = L - nctx;
-  const bool blk = split == nctx_splits;
-  const int base = blk ? 0 : (p0 & ~7) + kRingC * split;  // first key: a position, or block row 0
-  const int lo = blk ? 0 : p0;                              // keys [lo, hi) are read
-  const int hi = blk ? nq : L;
-  float* ml = ws_ml + (size_t)unit * kRows * 2;
-  float* os = ws_o + (size_t)unit * kRows * kRingDh;
-  if (base >= hi || (!blk && nctx == 0)) {                 // a context split past the window: empty
-    for (int e = tid; e < kRows; e += kRingThreads) {
-      ml[2 * e] = -__builtin_inff();
-      ml[2 * e + 1] = 0.f;
-    }
-    for (int e = tid; e < kRows * kRingDh / 4; e += kRingThreads)
-      reinterpret_cast<f32x4*>(os)[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    return;
-  }
   const size_t head = (size_t)b * hkv + kvh;
 
   // ---- loads: Q, K and V^T fragments --------------------------------------------------
@@ -114,7 +94,7 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int key = base + 32 * wv + 16 * n + i16;
-    const uint16_t* kp = blk ? k_blk + ((size_t)(b * nq + (key < nq ? key : 0)) * hkv + kvh) * kRingDh
+    const uint16_t* kp = BLK ? k_blk + ((size_t)(b * nq + (key < nq ? key : 0)) * hkv + kvh) * kRingDh
                              : k_ring + (head * ring + key % ring) * kRingDh;
 #pragma unroll
     for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 8 * g + 32 * s);
@@ -129,21 +109,25 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
     for (int ks = 0; ks < kRingC / 32; ++ks) {
       const int k0 = base + 32 * ks + 8 * g;
       uint32_t w[4];
-      if (!blk) {
+      if constexpr (!BLK) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(v_ring + (head * kRingDh + d) * ring + k0 % ring);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bool e0 = k0 + 2 * c >= lo && k0 + 2 * c < hi;
-          const bool e1 = k0 + 2 * c + 1 >= lo && k0 + 2 * c + 1 < hi;
-          w[c] = (e0 ? (v[c] & 0xffffu) : 0u) | (e1 ? (v[c] & 0xffff0000u) : 0u);
+          if constexpr (EDGE) {
+            const bool e0 = k0 + 2 * c >= lo && k0 + 2 * c < hi;
+            const bool e1 = k0 + 2 * c + 1 >= lo && k0 + 2 * c + 1 < hi;
+            w[c] = (e0 ? (v[c] & 0xffffu) : 0u) | (e1 ? (v[c] & 0xffff0000u) : 0u);
+          } else {
+            w[c] = v[c];
+          }
         }
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int j0 = k0 + 2 * c, j1 = j0 + 1;
-          const uint32_t a = j0 < nq ? v_blk[((size_t)(b * nq + j0) * hkv + kvh) * kRingDh + d] : 0u;
-          const uint32_t bb = j1 < nq ? v_blk[((size_t)(b * nq + j1) * hkv + kvh) * kRingDh + d] : 0u;
-          w[c] = a | (bb << 16);
+          const uint32_t a = v_blk[((size_t)(b * nq + (j0 < nq ? j0 : 0)) * hkv + kvh) * kRingDh + d];
+          const uint32_t bb = v_blk[((size_t)(b * nq + (j1 < nq ? j1 : 0)) * hkv + kvh) * kRingDh + d];
+          w[c] = (j0 < nq ? a : 0u) | (j1 < nq ? (bb << 16) : 0u);
         }
       }
       vf[dt][ks] = (u32x4){w[0], w[1], w[2], w[3]};
@@ -164,7 +148,8 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
         sacc[n][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[mt][s]),
                                                              __builtin_bit_cast(bf16x8, kf[n][s]), sacc[n][mt], 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[n][mt][r] = valid ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
+      for (int r = 0; r < 4; ++r)
+        sacc[n][mt][r] = (!EDGE || valid) ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
     }
   }
   // ---- row maxima (every row has a valid key in a non-empty split) ------------------
@@ -189,10 +174,11 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
       float sum = 0.f;
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const float p = exp2f(sacc[n][mt][r] - m);
+        const float p = __builtin_amdgcn_exp2f(sacc[n][mt][r] - m);   // v_exp_f32; 2^-inf = 0
         sum += p;
-        const uint32_t ph = f32_to_bf16_rne(p);
-        const uint32_t pl = f32_to_bf16_rne(p - __uint_as_float(ph << 16));
+        const __bf16 hb = static_cast<__bf16>(p);                      // v_cvt_pk_bf16_f32, nearest even
+        const uint32_t ph = __builtin_bit_cast(uint16_t, hb);
+        const uint32_t pl = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p - static_cast<float>(hb)));
         const int col = 32 * wv + 16 * n + i16;
         sm.p_hi[row][col] = (uint16_t)ph;
         sm.p_lo[row][col] = (uint16_t)pl;
@@ -241,19 +227,67 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
       *reinterpret_cast<f32x4*>(os + (size_t)(16 * mt + i16) * kRingDh + 32 * wv + 16 * dt + 4 * g) = o[dt][mt];
 }
 
-// One work-group per (request, K/V head, 8 query rows): out = sum_s w_s O_s with
+template <int MT>
+__global__ void __launch_bounds__(kRingThreads) k_ring_partial(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
+    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
+    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nctx_splits, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o) {
+  __shared__ RingShared<MT> sm;
+  constexpr int kRows = MT * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int nsplit = nctx_splits + 1;
+  const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
+  const int split = unit % nsplit;
+  const int bk = unit / nsplit;
+  const int kvh = bk % hkv, b = bk / hkv;
+  const int G = hq / hkv;
+  const int nrows = nq * G;
+
+  const int L = ctx_len[b] > 0 ? ctx_len[b] : 0;
+  const int nctx = L < window - 1 ? L : window - 1;
+  const int p0 = L - nctx;
+  const bool blk = split == nctx_splits;
+  const int base = blk ? 0 : (p0 & ~7) + kRingC * split;  // first key: a position, or block row 0
+  const int lo = blk ? 0 : p0;                              // keys [lo, hi) are read
+  const int hi = blk ? nq : L;
+  float* ml = ws_ml + (size_t)unit * kRows * 2;
+  float* os = ws_o + (size_t)unit * kRows * kRingDh;
+  if (base >= hi || (!blk && nctx == 0)) {                 // a context split past the window: empty
+    for (int e = tid; e < kRows; e += kRingThreads) {
+      ml[2 * e] = -__builtin_inff();
+      ml[2 * e + 1] = 0.f;
+    }
+    for (int e = tid; e < kRows * kRingDh / 4; e += kRingThreads)
+      reinterpret_cast<f32x4*>(os)[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (blk)
+    ring_split<MT, true, true>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
+                               scale_log2, ml, os);
+  else if (base >= lo && base + kRingC <= hi)
+    ring_split<MT, false, false>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
+                                 scale_log2, ml, os);
+  else
+    ring_split<MT, false, true>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
+                                scale_log2, ml, os);
+}
+
+// One work-group per (request, K/V head, 2 query rows): out = sum_s w_s O_s with
 // w_s = e^(m_s - M) / sum_s' e^(m_s' - M) l_s' (M the rows' maximum over the splits);
 // the weights of a row are formed once, then every output adds its splits' values with
 // all loads in flight.
-constexpr int kRingCombRows = 8;
+constexpr int kRingCombRows = 2;                // query rows per combine work-group: one output per thread
 constexpr int kRingMaxSplits = 32;
 
-template <int MT>
+template <int MT, int NSP>
 __global__ void __launch_bounds__(kRingThreads) k_ring_combine(const float* __restrict__ ws_ml,
                                                                 const float* __restrict__ ws_o, int nq, int hq,
                                                                 int hkv, int nsplit, float* __restrict__ out) {
   constexpr int kRows = MT * 16;
-  __shared__ float wsh[kRingCombRows][kRingMaxSplits];
+  __shared__ float msh[kRingCombRows][NSP], lsh[kRingCombRows][NSP];
+  __shared__ float wsh[kRingCombRows][NSP];
   const int groups = (kRows + kRingCombRows - 1) / kRingCombRows;
   const int bk = (int)blockIdx.x / groups;
   const int r0 = ((int)blockIdx.x % groups) * kRingCombRows;
@@ -261,37 +295,42 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_combine(const float* __re
   const int G = hq / hkv;
   const int nrows = nq * G;
   const size_t u0 = (size_t)bk * nsplit;
+  // every (row, split) statistic loaded at once
+  for (int e = threadIdx.x; e < kRingCombRows * nsplit; e += kRingThreads) {
+    const int rl = e / nsplit, sp = e - rl * nsplit;
+    const float* p = ws_ml + (u0 + sp) * kRows * 2 + 2 * (r0 + rl);
+    msh[rl][sp] = p[0];
+    lsh[rl][sp] = p[1];
+  }
+  __syncthreads();
   if (threadIdx.x < kRingCombRows) {
-    const int row = r0 + (int)threadIdx.x;
+    const int rl = threadIdx.x;
     float M = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[(u0 + s) * kRows * 2 + 2 * row]);
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, msh[rl][sp]);
     float den = 0.f;
-    float w[kRingMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kRingMaxSplits; ++s) {
-      w[s] = 0.f;
-      if (s < nsplit) {
-        const float ms = ws_ml[(u0 + s) * kRows * 2 + 2 * row];
-        w[s] = ms == -__builtin_inff() ? 0.f : exp2f(ms - M);
-        den += w[s] * ws_ml[(u0 + s) * kRows * 2 + 2 * row + 1];
-      }
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = msh[rl][sp] == -__builtin_inff() ? 0.f : exp2f(msh[rl][sp] - M);
+      wsh[rl][sp] = w;
+      den += w * lsh[rl][sp];
     }
-#pragma unroll
-    for (int s = 0; s < kRingMaxSplits; ++s) wsh[threadIdx.x][s] = w[s] / den;
+    for (int sp = 0; sp < nsplit; ++sp) wsh[rl][sp] /= den;
+    for (int sp = nsplit; sp < NSP; ++sp) wsh[rl][sp] = 0.f;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < kRingCombRows * kRingDh; e += kRingThreads) {
     const int rl = e / kRingDh, d = e - rl * kRingDh;
     const int row = r0 + rl;
-    if (row >= nrows) continue;
-    float v[kRingMaxSplits];
+    // every split's value in flight at once (past the last split: reread it, weight 0)
+    float v[NSP];
 #pragma unroll
-    for (int s = 0; s < kRingMaxSplits; ++s) v[s] = s < nsplit ? ws_o[((u0 + s) * kRows + row) * kRingDh + d] : 0.f;
+    for (int sp = 0; sp < NSP; ++sp) v[sp] = ws_o[((u0 + (sp < nsplit ? sp : nsplit - 1)) * kRows + row) * kRingDh + d];
     float num = 0.f;
 #pragma unroll
-    for (int s = 0; s < kRingMaxSplits; ++s) num += wsh[rl][s] * v[s];
-    const int i = row / G, h = kvh * G + row % G;
-    out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num;
+    for (int sp = 0; sp < NSP; ++sp) num += wsh[rl][sp] * v[sp];
+    if (row < nrows) {
+      const int i = row / G, h = kvh * G + row % G;
+      out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num;
+    }
   }
 }
 
@@ -314,8 +353,15 @@ static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, co
   hipLaunchKernelGGL((k_ring_partial<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(kRingThreads), 0, s, q, kb, vb, kr,
                      vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit - 1, ws.ml, ws.o);
   const int groups = (MT * 16 + kRingCombRows - 1) / kRingCombRows;
-  hipLaunchKernelGGL((k_ring_combine<MT>), dim3((unsigned)(B * hkv * groups)), dim3(kRingThreads), 0, s, ws.ml, ws.o,
-                     nq, hq, hkv, nsplit, out);
+  const dim3 grid((unsigned)(B * hkv * groups));
+  if (nsplit <= 8)
+    hipLaunchKernelGGL((k_ring_combine<MT, 8>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+  else if (nsplit <= 16)
+    hipLaunchKernelGGL((k_ring_combine<MT, 16>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+  else if (nsplit <= 24)
+    hipLaunchKernelGGL((k_ring_combine<MT, 24>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+  else
+    hipLaunchKernelGGL((k_ring_combine<MT, 32>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
 }
 
 hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
