@@ -113,7 +113,7 @@ def test_spec_accept_k64(d2, temperature):
         # request 2's drafts carry almost all of the target's mass: every position is
         # accepted and the bonus token comes from row 64
         for t in range(w.K):
-            target[2, t, tokens[2, t]] = synth.f32_to_bf16_bits(np.float32(60.0))
+            target[2, t, tokens[2, t]] = synth.f32_to_bf16_bits(np.array([60.0], dtype=np.float32))[0]
     print(f"spec_accept K=64 T={temperature}", flush=True)
     o, n, st = d2.spec_accept(to_gpu_bits(target), to_gpu(tokens), to_gpu(cand), to_gpu(q), temperature, seed=13)
     stats = check_accept(target, tokens, cand, q, temperature, 13, cpu(o), cpu(n), cpu(st))
