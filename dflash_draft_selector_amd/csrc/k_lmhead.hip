@@ -330,7 +330,7 @@ __global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned
                                                                    float* __restrict__ cand_val,
                                                                    int32_t* __restrict__ row_status) {
   constexpr int kGroups = kLmMergeThreads / kNC;      // 64 lane rows
-  constexpr int kBatch = 8;                           // lists loaded before merging
+  constexpr int kBatch = 16;                          // lists loaded before merging (one pass up to 1024 tiles)
   __shared__ unsigned long long wl[kLmMergeThreads / kWave][kNC];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
