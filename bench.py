@@ -482,6 +482,40 @@ def main():
         "components_us_per_call": components,
         "wall_s": round(wall, 3),
     }
+    # the proposer step (gated select + conv) as one library graph launch against the
+    # same calls launched one by one (same buffers, same stream, warm)
+    psel = {k: torch.empty_like(v) for k, v in sel.items()}
+    pH, py = torch.empty_like(H), torch.empty_like(y)
+
+    def proposer():
+        dflash2.select_gated(logits[0], verified, A, Bt, h, Wh, bias, "sigmoid", 0.0, 0, out=psel, H_out=pH)
+        dflash2.conv2tap(x, xp, taps, y=py)
+
+    with torch.cuda.stream(stream):
+        proposer()
+        torch.cuda.synchronize()
+        with dflash2.Graph() as pg:
+            proposer()
+        n_p = 200
+
+        def per_call(fn):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n_p):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n_p
+
+        eager_us = per_call(proposer)
+        graph_us = per_call(pg.launch)
+    pg.close()
+    result["proposer_step_graph"] = {"what": "gated select + conv2tap on one logits buffer (cache-warm), 4 kernels",
+                                     "eager_us_per_step": round(eager_us, 2),
+                                     "library_graph_us_per_step": round(graph_us, 2)}
     result["lmhead_topk16"] = lmhead_measure(dflash2, torch, dev, stream)
     result["ring_attention"] = ring_measure(dflash2, torch, dev, stream)
     if not args.no_configs:

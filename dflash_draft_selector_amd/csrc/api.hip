@@ -2,6 +2,8 @@
 // sizing, and dispatch to the kernel launchers.
 #include <math.h>
 
+#include <new>
+
 #include "dflash2.h"
 #include "dflash2_internal.h"
 #include "filter.h"
@@ -365,6 +367,50 @@ dflash2_status dflash2_spec_accept_filtered(const uint16_t* target_logits, int64
   return hip_status(launch_spec_accept_filtered(target_logits, ld, batch_stride, tokens, cand_idx, q, (int)batch,
                                                 (int)K, (int)vocab, temperature, top_k, top_p, seed, out_tokens,
                                                 n_accepted, row_status, ws.filt, stream));
+}
+
+
+struct dflash2_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+dflash2_status dflash2_graph_begin(hipStream_t stream) {
+  if (!stream) return DFLASH2_ERR_NULL;
+  return hip_status(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+}
+
+dflash2_status dflash2_graph_end(hipStream_t stream, dflash2_graph* graph) {
+  if (!stream || !graph) return DFLASH2_ERR_NULL;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture(stream, &g) != hipSuccess || !g) return DFLASH2_ERR_HIP;
+  hipGraphExec_t x = nullptr;
+  if (hipGraphInstantiate(&x, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return DFLASH2_ERR_HIP;
+  }
+  dflash2_graph h = new (std::nothrow) dflash2_graph_s{g, x};
+  if (!h) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return DFLASH2_ERR_HIP;
+  }
+  *graph = h;
+  return DFLASH2_OK;
+}
+
+dflash2_status dflash2_graph_launch(dflash2_graph graph, hipStream_t stream) {
+  if (!graph) return DFLASH2_ERR_NULL;
+  return hip_status(hipGraphLaunch(graph->exec, stream));
+}
+
+dflash2_status dflash2_graph_destroy(dflash2_graph graph) {
+  if (!graph) return DFLASH2_ERR_NULL;
+  const hipError_t a = hipGraphExecDestroy(graph->exec);
+  const hipError_t b = hipGraphDestroy(graph->graph);
+  delete graph;
+  return (a == hipSuccess && b == hipSuccess) ? DFLASH2_OK : DFLASH2_ERR_HIP;
 }
 
 }  // extern "C"

@@ -39,6 +39,10 @@ _SIGNATURES = {
     "dflash2_topk16": ([_c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_lmhead_topk16_workspace": ([_i64, _i64], _size),
     "dflash2_lmhead_topk16": ([_c_ptr, _c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_graph_begin": ([_c_ptr], _int),
+    "dflash2_graph_end": ([_c_ptr, ctypes.POINTER(ctypes.c_void_p)], _int),
+    "dflash2_graph_launch": ([_c_ptr, _c_ptr], _int),
+    "dflash2_graph_destroy": ([_c_ptr], _int),
     "dflash2_ring_attention_workspace": ([_i64, _i64, _i64, _i64, _i64], _size),
     "dflash2_ring_attention": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _f32, _c_ptr, _c_ptr, _size, _c_ptr], _int),
@@ -197,6 +201,50 @@ def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
     _check(lib.dflash2_lmhead_topk16(_ptr(h), _ptr(w), rows, D, V, _ptr(idx), _ptr(val), _ptr(st), _ptr(ws),
                                      ws.numel(), _stream()), "dflash2_lmhead_topk16")
     return (idx, val, st) if row_status else (idx, val)
+
+
+class Graph:
+    """Records the library calls made on torch's current stream inside ``with`` into one
+    HIP graph; ``launch()`` replays them with one launch on the same buffers.
+
+    Make every recorded call once before recording, so that its workspace and outputs
+    exist (pass ``out=`` / ``y=`` buffers); the current stream must not be the default
+    stream.  Inputs are refreshed in place between launches."""
+
+    def __init__(self):
+        self._lib = load_library()
+        self.handle = None
+
+    def __enter__(self):
+        s = _stream()
+        if not s:
+            raise Dflash2Error("Graph: record on a non-default stream (torch.cuda.stream(...))")
+        _check(self._lib.dflash2_graph_begin(s), "dflash2_graph_begin")
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        h = ctypes.c_void_p()
+        code = self._lib.dflash2_graph_end(_stream(), ctypes.byref(h))
+        if exc_type is None:
+            _check(code, "dflash2_graph_end")
+            self.handle = h
+        return False
+
+    def launch(self):
+        if self.handle is None:
+            raise Dflash2Error("Graph: nothing recorded")
+        _check(self._lib.dflash2_graph_launch(self.handle, _stream()), "dflash2_graph_launch")
+
+    def close(self):
+        if self.handle is not None:
+            self._lib.dflash2_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def ring_k_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:

@@ -342,6 +342,30 @@ dflash2_status dflash2_spec_accept_filtered(const uint16_t* target_logits, int64
                                             int32_t* n_accepted, int32_t* row_status, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------
+ * One launch per proposer step: HIP graphs of library calls.  [RFC] "Questions",
+ * item 5 (greedy-only CUDA-graph capture; a single active speculative generation
+ * graph) and [PEGA] "Proposal", phase 1 (the walk as a launch-floor candidate, under
+ * the same graph treatment).
+ *
+ * dflash2_graph_begin starts recording the work enqueued on `stream` (HIP stream
+ * capture, thread-local mode): the dflash2_* calls made on it until dflash2_graph_end
+ * are recorded, not run.  dflash2_graph_end instantiates them into *graph; each
+ * dflash2_graph_launch replays the whole sequence with one launch, on the buffers the
+ * calls were given (callers refresh inputs in place between launches).  The calls
+ * recorded must not need new workspace or outputs while recording (make each call once
+ * before, so its buffers exist); none of them records a memset.  The graph and its
+ * executable are host objects of the HIP runtime, owned by the caller until
+ * dflash2_graph_destroy.  `stream` must not be the legacy default stream.
+ * Errors: NULL stream or handle -> DFLASH2_ERR_NULL; a failed capture, instantiation
+ * or launch -> DFLASH2_ERR_HIP (a failed capture leaves no graph).
+ * ------------------------------------------------------------------------------- */
+typedef struct dflash2_graph_s* dflash2_graph;
+dflash2_status dflash2_graph_begin(hipStream_t stream);
+dflash2_status dflash2_graph_end(hipStream_t stream, dflash2_graph* graph);
+dflash2_status dflash2_graph_launch(dflash2_graph graph, hipStream_t stream);
+dflash2_status dflash2_graph_destroy(dflash2_graph graph);
+
 #ifdef __cplusplus
 }
 #endif
