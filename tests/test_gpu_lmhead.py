@@ -100,6 +100,7 @@ def check_rows(idx_g, val_g, h_bits, w_bits, rows_sel=None, vchunk=16384):
     (40, 2048, 70000, True),     # 274 tiles, 18 left over, split in 8 parts
     (100, 512, 70000, False),    # seven row tiles; the 18 left over split in 2 parts
     (5, 1024, 140000, True),     # 547 tiles, 35 left over past two per compute unit, 4 parts
+    (140, 512, 70000, True),     # two row groups (128 + 12), each with its split last round
 ])
 def test_lmhead_topk16_parity(d2, rows, hidden, vocab, peaks):
     inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows + hidden + vocab, peaks=peaks)
