@@ -151,7 +151,7 @@ dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, 
   if (!q || !k_blk || !v_blk || !k_ring || !v_ring || !ctx_len || !out) return DFLASH2_ERR_NULL;
   if (batch < 1 || batch > (1 << 20) || nq < 1 || hkv < 1 || hq < hkv || hq % hkv != 0 || head_dim != 128 ||
       nq * (hq / hkv) > kRingMaxRows || nq > 128 || ring < 8 || ring % 8 != 0 || ring > (1 << 24) || window < 1 ||
-      window > ring || (window + 7 + 127) / 128 + 1 > 32)
+      window > ring || ring_splits((int)nq, (int)window) > 32)
     return DFLASH2_ERR_SHAPE;
   if (isnan(scale) || isinf(scale) || scale < 0.f) return DFLASH2_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_ring) || !aligned16(v_ring) ||

@@ -12,10 +12,12 @@
 // window, a verify writes a few rows): K head-major [B][Hkv][ring][Dh]; V transposed
 // [B][Hkv][Dh][ring], so the P V product's V^T fragments (one dim, 8 consecutive
 // positions) are single 16-byte loads.  ring % 8 == 0, and positions are walked in
-// 8-aligned groups, so a group never wraps.
+// 8-aligned groups, so a group never wraps.  The context splits start on multiples of
+// kRingAlign positions: with ring % 64 == 0 (2112 = 33 x 64) a split's 128 positions
+// of one V^T row are two whole 128-byte lines instead of three partial ones.
 //
 // k_ring_partial: one 256-thread work-group per (request, K/V head, split).  Split s <
-// nctx_splits takes the 128 positions pa + 128 s .. (pa = p0 rounded down to 8) of the
+// nctx_splits takes the 128 positions pa + 128 s .. (pa = p0 rounded down to kRingAlign) of the
 // context, masked to [p0, L); the last split takes the block's keys.  The rows are the
 // nq x G query rows of the K/V head, in MT 16-row tiles.  Wave w computes S for keys
 // 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q and K fragments straight from memory);
@@ -33,6 +35,11 @@ constexpr int kRingThreads = 256;            // 4 waves
 constexpr int kRingDh = 128;                 // head dim
 constexpr int kRingC = 128;                  // keys per work-group
 constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row (16-byte aligned rows)
+#ifndef DF2_RING_ALIGN
+#define DF2_RING_ALIGN 64
+#endif
+constexpr int kRingAlign = DF2_RING_ALIGN;   // context splits start on multiples of this many positions
+static_assert(kRingAlign % 8 == 0 && kRingC % kRingAlign == 0, "split starts keep 8-aligned groups");
 
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad) {
   RingWs w;
@@ -249,7 +256,7 @@ __global__ void __launch_bounds__(kRingThreads) k_ring_partial(
   const int nctx = L < window - 1 ? L : window - 1;
   const int p0 = L - nctx;
   const bool blk = split == nctx_splits;
-  const int base = blk ? 0 : (p0 & ~7) + kRingC * split;  // first key: a position, or block row 0
+  const int base = blk ? 0 : (p0 & ~(kRingAlign - 1)) + kRingC * split;  // first key: a position, or block row 0
   const int lo = blk ? 0 : p0;                              // keys [lo, hi) are read
   const int hi = blk ? nq : L;
   float* ml = ws_ml + (size_t)unit * kRows * 2;
@@ -339,11 +346,11 @@ int ring_rows_pad(int nq, int hq, int hkv) {
   return rows <= 16 ? 16 : rows <= 32 ? 32 : 48;
 }
 
-// Context splits of 128 positions covering window - 1 positions from an 8-aligned start,
-// plus one split for the block's keys.
+// Context splits of 128 positions covering window - 1 positions from a kRingAlign-aligned
+// start, plus one split for the block's keys.
 int ring_splits(int nq, int window) {
   (void)nq;
-  return (window - 1 + 7 + kRingC - 1) / kRingC + 1;
+  return (window - 1 + kRingAlign - 1 + kRingC - 1) / kRingC + 1;
 }
 
 template <int MT>

@@ -141,7 +141,7 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
  * All row-major, 16-byte aligned.  Workspace: dflash2_ring_attention_workspace bytes,
  * any contents.
  * Errors: NULL pointers; head_dim != 128, hq % hkv != 0, nq * hq / hkv > 48, ring % 8
- *         != 0, window < 1, window > ring or window > 3960 -> DFLASH2_ERR_SHAPE;
+ *         != 0, window < 1, window > ring or window > 3906 -> DFLASH2_ERR_SHAPE;
  *         scale < 0 or not finite -> DFLASH2_ERR_VALUE; alignment; workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window);
