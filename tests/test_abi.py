@@ -146,3 +146,44 @@ def _load_missing(dflash2, tmp_path):
         dflash2.load_library(str(tmp_path / "missing.so"))
     finally:
         dflash2._lib = saved
+
+
+def test_host_validation_lmhead_ring_and_graph():
+    """The LM head, ring attention and graph entry points reject bad arguments before any
+    launch (every call below returns on the host)."""
+    d2, lib = _lib()
+    ws = ctypes.c_void_p(0x200000)
+    big = 1 << 31
+    # LM head + top-16: hidden a multiple of 256, 16 <= vocab <= 2^19, 16-byte aligned h and W
+    lm = lambda h=FAKE, w=FAKE, rows=105, hidden=5120, vocab=151936, idx=FAKE, wsb=big: lib.dflash2_lmhead_topk16(
+        h, w, rows, hidden, vocab, idx, FAKE, NULL, ws, wsb, NULL)
+    assert lm(h=NULL) == 1
+    assert lm(idx=NULL) == 1
+    for kw in ({"rows": 0}, {"hidden": 5000}, {"hidden": 128}, {"vocab": 15}, {"vocab": (1 << 19) + 1}):
+        assert lm(**kw) == 2, kw
+    assert lm(w=MIS) == 3
+    need = lib.dflash2_lmhead_topk16_workspace(105, 151936)
+    assert need >= 105 * 594 * 16 * 8
+    assert lm(wsb=need - 257) == 5
+    # ring attention: head_dim 128, GQA rows <= 48, ring % 8 == 0, window <= ring and at most
+    # 32 splits (window <= 3906), scale >= 0 and finite
+    ra = lambda q=FAKE, B=15, nq=8, hq=32, hkv=8, dh=128, ring=2112, window=2048, scale=0.0, wsb=big, ctx=FAKE: \
+        lib.dflash2_ring_attention(q, FAKE, FAKE, FAKE, FAKE, ctx, B, nq, hq, hkv, dh, ring, window, scale, FAKE, ws,
+                                   wsb, NULL)
+    assert ra(ctx=NULL) == 1
+    for kw in ({"dh": 64}, {"hq": 30}, {"hq": 56}, {"ring": 2100}, {"window": 2113}, {"window": 0}, {"B": 0},
+               {"ring": 4096, "window": 3907}):
+        assert ra(**kw) == 2, kw
+    assert ra(ring=4096, window=3906, scale=-1.0) == 6   # the largest window passes the shape checks
+    assert ra(scale=float("nan")) == 6
+    assert ra(scale=float("inf")) == 6
+    assert ra(q=MIS) == 3
+    need = lib.dflash2_ring_attention_workspace(15, 8, 32, 8, 2048)
+    assert need >= 15 * 8 * 18 * 32 * (128 + 2) * 4
+    assert ra(wsb=need - 257) == 5
+    # graphs: the default stream cannot be captured; null handles are refused
+    out = ctypes.c_void_p()
+    assert lib.dflash2_graph_begin(NULL) == 1
+    assert lib.dflash2_graph_end(NULL, ctypes.byref(out)) == 1
+    assert lib.dflash2_graph_launch(NULL, NULL) == 1
+    assert lib.dflash2_graph_destroy(NULL) == 1

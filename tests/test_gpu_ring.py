@@ -65,6 +65,8 @@ def run_and_check(d2, inp, window, what, scale=0.0):
     (2, 4, 8, 4, 64, 64, [63, 1000]),                   # window = ring
     (2, 8, 8, 2, 2112, 2048, [-5, 10]),                 # a negative length reads as 0
     (2, 4, 8, 2, 16, 1, [0, 13]),                       # window 1: the block's keys only
+    (2, 8, 8, 2, 3968, 3906, [3905, 9000]),             # the largest window: 31 context splits + the block's
+    (3, 8, 8, 2, 2056, 2048, [2100, 4111, 5000]),       # ring % 64 != 0: 64-aligned splits cross the wrap
 ])
 def test_ring_attention_parity(d2, B, nq, hq, hkv, ring, window, ctx):
     print(f"ring attention B={B} nq={nq} hq={hq} hkv={hkv} ring={ring} window={window} ctx={ctx}", flush=True)
