@@ -101,6 +101,9 @@ def check_rows(idx_g, val_g, h_bits, w_bits, rows_sel=None, vchunk=16384):
     (100, 512, 70000, False),    # seven row tiles; the 18 left over split in 2 parts
     (5, 1024, 140000, True),     # 547 tiles, 35 left over past two per compute unit, 4 parts
     (140, 512, 70000, True),     # two row groups (128 + 12), each with its split last round
+    (5, 768, 140000, True),      # three stages: the 35 left over split in 3 parts of one stage
+    (40, 1280, 70000, False),    # five stages, 18 left over: 5 parts of one stage
+    (40, 1280, 91000, True),     # 356 tiles, 100 left over: 2 parts of unequal length (2 + 3 stages)
 ])
 def test_lmhead_topk16_parity(d2, rows, hidden, vocab, peaks):
     inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows + hidden + vocab, peaks=peaks)
