@@ -57,14 +57,51 @@ __device__ __forceinline__ int lm_rank(float x, int lc, bool valid) {
   return valid ? (int)(((unsigned)(key - 0x8000) << 16) | (unsigned)(0xffff - lc)) : (int)0x80000000;
 }
 
+// Per-lane bounds of the sorting networks' compare-exchanges.  A lane's new value is
+// med3(x, partner, c): the larger of the two where c = INT_MAX, the smaller where
+// c = INT_MIN, so a compare-exchange is a DPP move and one v_med3_i32 instead of a
+// maximum, a minimum and a select.  The bounds go through an empty asm so that the
+// compiler, which knows c is one of the two extremes, does not fold the median back.
+struct LmBounds {
+  int b[10];       // stages (K, J): (2,1) (4,2) (4,1) (8,4) (8,2) (8,1) (16,8) (16,4) (16,2) (16,1)
+};
+
+template <int K, int J>
+constexpr int lm_bound_index() {
+  return K == 2 ? 0 : K == 4 ? (J == 2 ? 1 : 2) : K == 8 ? (J == 4 ? 3 : J == 2 ? 4 : 5)
+                                                : (J == 8 ? 6 : J == 4 ? 7 : J == 2 ? 8 : 9);
+}
+
+__device__ __forceinline__ int lm_bound(int K, int J) {
+  // the orientation of bitonic_stage_i32: blocks of K lanes largest first where lane bit
+  // K is clear (and for K = 16); the lower lane of a pair at distance J keeps the larger
+  const int i = threadIdx.x & 15;
+  const bool desc = K >= 16 || (i & K) == 0;
+  int c = (((i & J) == 0) == desc) ? 0x7fffffff : (int)0x80000000;
+  asm("" : "+v"(c));
+  return c;
+}
+
+__device__ __forceinline__ LmBounds lm_bounds() {
+  return LmBounds{{lm_bound(2, 1), lm_bound(4, 2), lm_bound(4, 1), lm_bound(8, 4), lm_bound(8, 2), lm_bound(8, 1),
+                   lm_bound(16, 8), lm_bound(16, 4), lm_bound(16, 2), lm_bound(16, 1)}};
+}
+
+template <int K, int J>
+__device__ __forceinline__ int lm_stage(int x, const LmBounds& bd) {
+  const int p = row_partner_i32<J>(x);
+  const int c = bd.b[lm_bound_index<K, J>()];
+  return max(min(x, p), min(max(x, p), c));     // med3(x, p, c)
+}
+
 // Full descending sort of the 16 values held by each 16-lane row, for N independent
 // registers at once (Batcher's bitonic sort: blocks of 2, 4, 8, then the 16-lane
 // half-cleaners).  Each stage is applied to all N before the next, so the independent
-// DPP compare-exchanges fill each other's wait states.
+// DPP moves fill each other's wait states.
 template <int N>
-__device__ __forceinline__ void row16_full_sort_i32(int (&x)[N]) {
+__device__ __forceinline__ void row16_full_sort_i32(int (&x)[N], const LmBounds& bd) {
 #define DF2_STAGE(K, J)                                              \
-  _Pragma("unroll") for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<K, J>(x[n]);
+  _Pragma("unroll") for (int n = 0; n < N; ++n) x[n] = lm_stage<K, J>(x[n], bd);
   DF2_STAGE(2, 1) DF2_STAGE(4, 2) DF2_STAGE(4, 1) DF2_STAGE(8, 4) DF2_STAGE(8, 2) DF2_STAGE(8, 1)
   DF2_STAGE(16, 8) DF2_STAGE(16, 4) DF2_STAGE(16, 2) DF2_STAGE(16, 1)
 #undef DF2_STAGE
@@ -72,15 +109,15 @@ __device__ __forceinline__ void row16_full_sort_i32(int (&x)[N]) {
 
 // The bitonic half-cleaners (distances 8, 4, 2, 1) on N independent registers.
 template <int N>
-__device__ __forceinline__ void row16_bitonic_sort_i32(int (&x)[N]) {
+__device__ __forceinline__ void row16_bitonic_sort_i32(int (&x)[N], const LmBounds& bd) {
 #pragma unroll
-  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 8>(x[n]);
+  for (int n = 0; n < N; ++n) x[n] = lm_stage<16, 8>(x[n], bd);
 #pragma unroll
-  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 4>(x[n]);
+  for (int n = 0; n < N; ++n) x[n] = lm_stage<16, 4>(x[n], bd);
 #pragma unroll
-  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 2>(x[n]);
+  for (int n = 0; n < N; ++n) x[n] = lm_stage<16, 2>(x[n], bd);
 #pragma unroll
-  for (int n = 0; n < N; ++n) x[n] = bitonic_stage_i32<16, 1>(x[n]);
+  for (int n = 0; n < N; ++n) x[n] = lm_stage<16, 1>(x[n], bd);
 }
 
 // Tile list entry -> row composite of dflash2_topk16 (0 = empty).
@@ -111,6 +148,7 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
   const int g = lane >> 4, i16 = lane & 15;
   const int col0 = tile * kLmCols;
   int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
+  const LmBounds bd = lm_bounds();
   // (m, r) pairs two at a time: sort both halves of each pair's 32 columns, keep the
   // top 16 of the two sorted halves (the maximum against the other half reversed is
   // bitonic) and sort that
@@ -122,9 +160,9 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
     const int m0 = k >> 2, r0 = k & 3, m1 = (k + 1) >> 2, r1 = (k + 1) & 3;
     int x[4] = {lm_rank(acc[m0][0][r0], lc0, v0), lm_rank(acc[m0][1][r0], lc1, v1),
                 lm_rank(acc[m1][0][r1], lc0, v0), lm_rank(acc[m1][1][r1], lc1, v1)};
-    row16_full_sort_i32<4>(x);
+    row16_full_sort_i32<4>(x, bd);
     int y[2] = {max(x[0], dpp_i32<0x140>(x[1])), max(x[2], dpp_i32<0x140>(x[3]))};   // row_mirror
-    row16_bitonic_sort_i32<2>(y);
+    row16_bitonic_sort_i32<2>(y, bd);
     lists[((16 * m0 + 4 * g + r0) * kLmWaves + wv) * kNC + i16] = y[0];
     lists[((16 * m1 + 4 * g + r1) * kLmWaves + wv) * kNC + i16] = y[1];
   }
@@ -138,12 +176,12 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
     const int* L1 = lists + (rl + kLmWaves) * kLmWaves * kNC;
     int x[2] = {max(L0[(2 * g) * kNC + i16], L0[(2 * g + 1) * kNC + (kNC - 1 - i16)]),
                 max(L1[(2 * g) * kNC + i16], L1[(2 * g + 1) * kNC + (kNC - 1 - i16)])};
-    row16_bitonic_sort_i32<2>(x);
+    row16_bitonic_sort_i32<2>(x, bd);
 #pragma unroll
     for (int msk = 16; msk <= 32; msk *= 2) {
       x[0] = max(x[0], xor_lane_i32(dpp_i32<0x140>(x[0]), msk));
       x[1] = max(x[1], xor_lane_i32(dpp_i32<0x140>(x[1]), msk));
-      row16_bitonic_sort_i32<2>(x);
+      row16_bitonic_sort_i32<2>(x, bd);
     }
     if (lane < kNC && row0 + rl < rows)
       partials[((size_t)(row0 + rl) * ntiles + tile) * kNC + lane] = lm_rank_to_rc(x[0], col0);
