@@ -183,7 +183,7 @@ def test_filtered_shared_target_and_k64(d2):
     # the bonus comes from row 64
     full = np.broadcast_to(tb, (B, K + 1, V)).copy()
     for t in range(K):
-        full[2, t, tokens[2, t]] = synth.f32_to_bf16_bits(np.float32(60.0))
+        full[2, t, tokens[2, t]] = synth.f32_to_bf16_bits(np.float32(60.0))[0]
     o, n, st = _verify(d2, full, tokens, cand, qq, 0.9, 20, 0.95, 9)
     check_accept(full, tokens, cand, qq, 0.9, 9, o, n, st, top_k=20, top_p=0.95)
     assert n[2] == K
