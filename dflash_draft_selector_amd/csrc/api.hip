@@ -49,7 +49,14 @@ dflash2_status check_bk(int64_t batch, int64_t K) {
   return DFLASH2_OK;
 }
 
-dflash2_status check_temp(float t) { return (t >= 0.f && !isnan(t) && !isinf(t)) ? DFLASH2_OK : DFLASH2_ERR_VALUE; }
+// A temperature is 0 (greedy) or a finite value of at least FLT_MIN (2^-126): the
+// kernels scale scores by 1/T (and by log2(e)/T), which overflows to +inf for the
+// subnormal temperatures below it.
+dflash2_status check_temp(float t) {
+  if (isnan(t) || isinf(t) || t < 0.f) return DFLASH2_ERR_VALUE;
+  if (t > 0.f && t < 1.17549435e-38f) return DFLASH2_ERR_VALUE;
+  return DFLASH2_OK;
+}
 
 struct FilteredWs {
   AcceptWs acc;      // the greedy path (temperature 0)

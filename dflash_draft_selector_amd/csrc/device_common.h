@@ -127,8 +127,12 @@ __device__ __forceinline__ int row16_pick(float s, float inv_t, float u, float* 
   if (hit) {
     pick = __builtin_ctz(hit);
   } else {
+    // rounding left u * total at or above the last prefix: the last slot with weight;
+    // with no positive weight at all (a scale the host checks rule out), the lowest
+    // slot holding the row maximum, so the slot is always in [0, 16)
     const unsigned int pos = (unsigned int)((__ballot(w > 0.f) >> shift) & 0xffffull);
-    pick = 31 - __builtin_clz(pos);
+    const unsigned int top = (unsigned int)((__ballot(fin && sv == m) >> shift) & 0xffffull);
+    pick = pos ? 31 - __builtin_clz(pos) : __builtin_ctz(top);
   }
   *q = w * (1.f / total);
   return pick;

@@ -55,7 +55,9 @@ typedef enum dflash2_status {
   DFLASH2_ERR_ALIGN = 3,      /* a pointer or row stride breaks the 16-byte alignment rule */
   DFLASH2_ERR_DTYPE = 4,      /* an unknown dtype or activation enum */
   DFLASH2_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the query returned */
-  DFLASH2_ERR_VALUE = 6,      /* temperature negative or NaN */
+  DFLASH2_ERR_VALUE = 6,      /* a value out of range: a temperature that is negative, NaN,
+                                 infinite or positive below FLT_MIN = 2^-126 (whose reciprocal
+                                 overflows); a bad top_p or scale where a call takes one */
   DFLASH2_ERR_HIP = 7         /* a HIP launch failed */
 } dflash2_status;
 

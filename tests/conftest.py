@@ -26,3 +26,27 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Reports how many walk steps and verify requests the parity checks compared with
+    the oracle, and how many of their decisions the oracle itself placed within the
+    1e-5 band of a tie or a boundary (near ties and band differences)."""
+    try:
+        import parity_util
+    except Exception:  # pragma: no cover
+        return
+    c = parity_util.COUNTS
+    if not (c["walk_steps"] or c["verify_requests"]):
+        return
+    terminalreporter.write_line(
+        "parity decisions: walk steps {walk_steps} (near ties {walk_near_ties}, in band {walk_band}); "
+        "verify requests {verify_requests} (in band {verify_band})".format(**c))
+    import json
+    out_dir = os.path.join(ROOT, "gpurun_out")
+    try:
+        os.makedirs(out_dir, exist_ok=True)
+        with open(os.path.join(out_dir, "parity_counts.json"), "w") as f:
+            json.dump(c, f)
+    except OSError:  # pragma: no cover
+        pass

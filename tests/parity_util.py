@@ -45,6 +45,11 @@ def assert_close_scaled(got, ref, scale, rel=REL, what=""):
                              f"got {got[i]!r} ref {ref[i]!r} scale {np.asarray(scale)[i]!r}")
 
 
+# Decision counts of every check in this process; the test session prints them and
+# writes them to gpurun_out/parity_counts.json (tests/conftest.py).
+COUNTS = {"walk_steps": 0, "walk_near_ties": 0, "walk_band": 0, "verify_requests": 0, "verify_band": 0}
+
+
 def check_walk(S_ref, cand_idx, tokens, slots, q, temperature, seed):
     """Teacher-forced check of a walk: every step is re-decided by the oracle on the
     predecessor slot the library chose.  Returns counts {steps, near_ties, band}."""
@@ -82,28 +87,51 @@ def check_walk(S_ref, cand_idx, tokens, slots, q, temperature, seed):
                     assert near, ("sampled step differs outside the boundary band", b, t, j, jr)
                     stats["band"] += 1
                 assert np.abs(q[b, t] - qref).max() <= REL, (b, t)
+    COUNTS["walk_steps"] += stats["steps"]
+    COUNTS["walk_near_ties"] += stats["near_ties"]
+    COUNTS["walk_band"] += stats["band"]
     return stats
 
 
+def _draw_near(weights, u, picks):
+    """Whether u * Z lies within BAND * Z of the inverse-CDF boundary below or above any
+    of the picked tokens (Z = total weight, boundaries in token-id order)."""
+    P = np.concatenate([[0.0], np.cumsum(weights)])
+    Z = P[-1]
+    return any(0 <= k < P.size and abs(u * Z - P[k]) <= BAND * Z for v in picks for k in (v, v + 1))
+
+
 def check_accept(target_bits, tokens, cand_idx, q, temperature, seed, out, n_acc, status, top_k=0, top_p=1.0):
-    """Compare a verify with the oracle; differences are allowed only where the oracle's
-    own accept test, inverse-CDF draw or top-p cut lies within BAND of a boundary."""
+    """Compare a verify with the oracle.  A request may differ only at its first
+    divergent position t, and only where the oracle's decision at t lies within BAND of
+    a boundary: the accept test at t (the library took the other branch), the inverse-CDF
+    draw at t (both rejected, or both reached the bonus, and drew different tokens), or
+    the top-p cut of target row t (the filtered p of that row moved).  Greedy verifies
+    (integer argmax over bf16 keys) must match exactly."""
     ref_out, ref_n, ref_st, traces = oracle.spec_accept(target_bits, tokens, cand_idx, q, temperature, seed,
                                                         return_trace=True, top_k=top_k, top_p=top_p)
     stats = {"requests": int(tokens.shape[0]), "band": 0}
     np.testing.assert_array_equal(status, ref_st)
+    K = tokens.shape[1]
     for b in range(tokens.shape[0]):
         if np.array_equal(out[b], ref_out[b]) and n_acc[b] == ref_n[b]:
             continue
+        assert temperature != 0.0, ("greedy verify differs", b, out[b].tolist(), ref_out[b].tolist())
+        diff = np.flatnonzero(out[b] != ref_out[b])
+        assert diff.size, ("same tokens, different accepted counts", b, int(n_acc[b]), int(ref_n[b]))
+        t = int(diff[0])
         tr = traces[b]
-        near = False
-        for (t, u, qx, px, acc) in tr["accepts"]:
-            if abs(u * qx - px) <= BAND * max(px, u * qx):
+        margins = tr.get("topp_margin", [])
+        near = bool(margins) and t < len(margins) and margins[t] <= BAND
+        accepts = {a[0]: a for a in tr["accepts"]}
+        took_draft = t < K and out[b, t] == tokens[b, t]
+        if not near and t in accepts:
+            _, u, qx, px, acc = accepts[t]
+            # the oracle accepted and the library did not, or the reverse
+            if acc != took_draft and abs(u * qx - px) <= BAND * max(px, u * qx):
                 near = True
-        if any(m <= BAND for m in tr.get("topp_margin", [])):
-            near = True
-        if tr["resample"] is not None and not near:
-            t, kind, u = tr["resample"]
+        if not near and tr["resample"] is not None and tr["resample"][0] == t and not took_draft:
+            _, kind, u = tr["resample"]
             bits = np.asarray(target_bits[b, t])
             p = (oracle.filtered_target_probs(bits, temperature, top_k, top_p) if top_k > 0 or top_p < 1.0
                  else oracle.target_probs(bits, temperature))
@@ -113,11 +141,10 @@ def check_accept(target_bits, tokens, cand_idx, q, temperature, seed, out, n_acc
                 w = np.maximum(0.0, p - qfull)
             else:
                 w = p
-            P = np.concatenate([[0.0], np.cumsum(w)])
-            Z = P[-1]
-            for k in (ref_out[b, t], ref_out[b, t] + 1, out[b, t], out[b, t] + 1):
-                if 0 <= k < P.size and abs(u * Z - P[k]) <= BAND * Z:
-                    near = True
-        assert near, ("verify differs outside the decision band", b, out[b].tolist(), ref_out[b].tolist())
+            near = _draw_near(w, u, (int(ref_out[b, t]), int(out[b, t])))
+        assert near, ("verify differs outside the decision band at its first divergent position", b, t,
+                      out[b].tolist(), ref_out[b].tolist())
         stats["band"] += 1
+    COUNTS["verify_requests"] += stats["requests"]
+    COUNTS["verify_band"] += stats["band"]
     return stats

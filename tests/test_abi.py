@@ -187,3 +187,21 @@ def test_host_validation_lmhead_ring_and_graph():
     assert lib.dflash2_graph_end(NULL, ctypes.byref(out)) == 1
     assert lib.dflash2_graph_launch(NULL, NULL) == 1
     assert lib.dflash2_graph_destroy(NULL) == 1
+
+
+def test_temperature_range_on_host():
+    """A temperature is 0 or finite and at least FLT_MIN = 2^-126: below it 1/T overflows
+    in fp32.  Subnormal temperatures are refused before any launch; FLT_MIN itself passes
+    the check (the select then stops at its too-small workspace, status 5)."""
+    d2, lib = _lib()
+    ws = ctypes.c_void_p(0x200000)
+    flt_min = 2.0 ** -126
+    sel = lambda T: lib.dflash2_select(FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 7, T, 0, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, NULL, ws, 16, NULL)
+    for T in (1e-39, 2.0 ** -127, 2.0 ** -149, -1e-39, float("inf"), float("-inf"), float("nan")):
+        assert lib.dflash2_walk(FAKE, FAKE, 1, 7, T, 0, FAKE, FAKE, FAKE, NULL) == 6, T
+        assert sel(T) == 6, T
+        assert lib.dflash2_spec_accept(FAKE, 4096, 8 * 4096, FAKE, FAKE, FAKE, 1, 7, 4096, T, 0, FAKE, FAKE, NULL, ws,
+                                       16, NULL) == 6, T
+    for T in (0.0, flt_min, 1e-30, 1.0, 3.0e38):
+        assert sel(T) == 5, T
