@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libdflash2.so")
 
 ARCH = "gfx950"
 HIPFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-mcode-object-version=5",
 ]

@@ -38,7 +38,7 @@ dflash2_status check_emb(const void* a, const void* b, dflash2_dtype dt, int64_t
   if (!a || !b) return DFLASH2_ERR_NULL;
   if (dt != DFLASH2_F32 && dt != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
   if (vocab < DFLASH2_NCAND || vocab > kMaxVocab) return DFLASH2_ERR_SHAPE;
-  if (!(dim == 64 || dim == 128 || dim == 256 || dim == 512)) return DFLASH2_ERR_SHAPE;
+  if (!pow2_in(dim, 16, 1024)) return DFLASH2_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b)) return DFLASH2_ERR_ALIGN;
   return DFLASH2_OK;
 }
@@ -245,7 +245,7 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
   st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
   if (st != DFLASH2_OK) return st;
   if (!verified || !H || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
-  if (!aligned16(H)) return DFLASH2_ERR_ALIGN;
+  if (!aligned16(H) || !aligned16(S)) return DFLASH2_ERR_ALIGN;
   st = check_temp(temperature);
   if (st != DFLASH2_OK) return st;
   SelectWs ws;
@@ -280,11 +280,12 @@ dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const in
   if (!verified || !h || !w_h || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
   if (w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
   if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
-  if (hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24)) return DFLASH2_ERR_SHAPE;
+  // the fused gate tiles are 64 columns wide
+  if (dim < 64 || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24)) return DFLASH2_ERR_SHAPE;
   const int64_t rows = batch * K;
   if (!items_ok(rows * topk_num_chunks(vocab) + fused_gate_blocks(rows, hidden, dim), kTopkThreads))
     return DFLASH2_ERR_SHAPE;
-  if (!aligned16(h) || !aligned16(w_h)) return DFLASH2_ERR_ALIGN;
+  if (!aligned16(h) || !aligned16(w_h) || !aligned16(S) || (H_out && !aligned16(H_out))) return DFLASH2_ERR_ALIGN;
   st = check_temp(temperature);
   if (st != DFLASH2_OK) return st;
   SelectGatedWs ws;

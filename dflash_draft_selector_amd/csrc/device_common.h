@@ -12,6 +12,8 @@ constexpr int kWave = 64;     // CDNA wavefront width
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---- bf16 -------------------------------------------------------------------------
 
@@ -136,6 +138,27 @@ __device__ __forceinline__ int row16_pick(float s, float inv_t, float u, float* 
   }
   *q = w * (1.f / total);
   return pick;
+}
+
+// ---- kernel arguments -------------------------------------------------------------
+
+// Keeps the given kernel arguments in scalar registers from the kernel's first
+// instructions on.  Left alone, the compiler loads an argument from the kernel-argument
+// segment only where it is first used; in a kernel whose last phase is on the critical
+// path, that scalar load then stalls the first LDS wait after it (both count in
+// lgkmcnt) for a full memory round trip.
+template <typename T>
+__device__ __forceinline__ void pin_arg(T a) {
+  if constexpr (sizeof(T) == 8)
+    asm volatile("" ::"s"(__builtin_bit_cast(uint64_t, a)));
+  else if constexpr (sizeof(T) == 4)
+    asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, a)));
+  else
+    asm volatile("" ::"s"((uint32_t)a));
+}
+template <typename... T>
+__device__ __forceinline__ void args_in_sgprs(T... a) {
+  (pin_arg(a), ...);
 }
 
 // ---- wave / block helpers ----------------------------------------------------------

@@ -3,25 +3,28 @@
 // The proposer step (dflash2_select) runs as three back-to-back kernels on one stream:
 //   1. k_chunk_lists  streams the logits (two 512-thread blocks per row at V = 151936)
 //                     and writes each chunk's sorted top-16;
-//   2. k_positions    one block per draft position: merges the chunk top-16s of rows
-//                     t - 1 and t, writes row t's candidates, computes the 16 x 16
-//                     scores of t and the successor table (the slot taken from each
-//                     predecessor slot);
-//   3. k_walk_tables  one block per request: chases the tables from the verified row
+//   2. k_positions    one 4-wave block per draft position: merges the chunk top-16s of
+//                     rows t - 1 and t, writes row t's candidates, gathers the table rows
+//                     of the 16 x 16 adjacent pairs, computes the scores of t (the
+//                     selector dims split over the waves) and the successor table (the
+//                     slot taken from each predecessor slot);
+//   3. k_walk_tables  one block per request: follows the tables from the verified row
 //                     and writes tokens, slots and q.
 // The gated step (dflash2_select_gated) launches k_chunk_gate in place of stage 1 (the
 // same blocks plus the context gate's tiles as extra work-groups), and its stage 2
 // adds each row's gate slices before the scores.
 // Kernel boundaries replace every cross-work-group hand-off, so no work-group ever
-// waits for another and no workspace counter exists.
+// waits for another and no workspace counter exists.  Stage 2 runs one block per
+// position rather than one per request so that each request's table rows (about 107 KB
+// at K = 7) are gathered by K compute units instead of one.  Every entry point computes
+// a tile with the same block routine (pair_dev.h), so all of them give bit-identical
+// scores.
 #include "dflash2_internal.h"
 #include "gate_dev.h"
 #include "pair_dev.h"
 #include "topk_dev.h"
 
 namespace df2 {
-
-constexpr int kMergeRows = 16;                    // rows per block of the standalone top-16 merge
 
 TopkWs carve_topk(Carver& c, int64_t rows, int64_t vocab) {
   TopkWs w;
@@ -63,13 +66,20 @@ SelectGatedWs carve_select_gated(Carver& c, int64_t batch, int64_t K, int64_t vo
 
 // ---- stage 1: chunk top-16s ---------------------------------------------------------------
 
+// Block (row, chunk) writes list row * nchunks + chunk.
+__device__ __forceinline__ void chunk_block(const uint16_t* __restrict__ logits, int64_t ld, int V, int nchunks,
+                                            int blk, ChunkShared& sm, unsigned long long* __restrict__ partials) {
+  const int row = blk / nchunks;
+  const int chunk = blk - row * nchunks;
+  chunk_top16(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1), sm,
+              partials + (size_t)blk * kNC);
+}
+
 __global__ void __launch_bounds__(kTopkThreads) k_chunk_lists(const uint16_t* __restrict__ logits, int64_t ld, int V,
                                                               int nchunks, unsigned long long* __restrict__ partials) {
+  args_in_sgprs(logits, ld, V, nchunks, partials);
   __shared__ ChunkShared sm;
-  const int row = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x - row * nchunks;
-  chunk_top16(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1), sm,
-              partials + ((size_t)row * nchunks + chunk) * kNC);
+  chunk_block(logits, ld, V, nchunks, (int)blockIdx.x, sm, partials);
 }
 
 // ---- stage 1 of the gated select: chunk top-16s and gate tiles in one launch ---------
@@ -89,12 +99,10 @@ __global__ void __launch_bounds__(kTopkThreads) k_chunk_gate(const uint16_t* __r
                                                              const uint16_t* __restrict__ w_h, int rows, int hidden,
                                                              int dim, int ntiles, int nsplit,
                                                              float* __restrict__ gate_partial) {
+  args_in_sgprs(logits, ld, V, nchunks, nchunk_blocks, partials);
   __shared__ ChunkGateShared sm;
   if ((int)blockIdx.x < nchunk_blocks) {
-    const int row = blockIdx.x / nchunks;
-    const int chunk = blockIdx.x - row * nchunks;
-    chunk_top16(logits + (size_t)row * ld, V, chunk_begin(V, nchunks, chunk), chunk_begin(V, nchunks, chunk + 1), sm.c,
-                partials + ((size_t)row * nchunks + chunk) * kNC);
+    chunk_block(logits, ld, V, nchunks, (int)blockIdx.x, sm.c, partials);
     return;
   }
   const int gb = (int)blockIdx.x - nchunk_blocks;
@@ -107,49 +115,53 @@ __global__ void __launch_bounds__(kTopkThreads) k_chunk_gate(const uint16_t* __r
                                                               nsplit, sm.red, nullptr, gate_partial);
 }
 
-// ---- top-16: merge each row's chunk top-16s (one 16-lane row per logits row) ----------
+// ---- top-16: merge each row's chunk lists (one wave per logits row) ---------------------
 
-__global__ void __launch_bounds__(kMergeRows * kNC) k_merge_lists(const unsigned long long* __restrict__ partials,
-                                                                  int rows, int nchunks,
-                                                                  int32_t* __restrict__ cand_idx,
-                                                                  float* __restrict__ cand_val,
-                                                                  int32_t* __restrict__ row_status) {
-  const int i = threadIdx.x & 15;
-  const int row_raw = blockIdx.x * kMergeRows + (threadIdx.x >> 4);
-  const int row = row_raw < rows ? row_raw : rows - 1;   // spare lanes redo the last row, every lane merges
-  const unsigned long long rc = row16_merge_chunks(partials + (size_t)row * nchunks * kNC, nchunks);
+constexpr int kMergeWaves = 4;                    // rows per block of the standalone merge
+
+__global__ void __launch_bounds__(kMergeWaves * kWave) k_merge_lists(const unsigned long long* __restrict__ partials,
+                                                                     int rows, int nlists,
+                                                                     int32_t* __restrict__ cand_idx,
+                                                                     float* __restrict__ cand_val,
+                                                                     int32_t* __restrict__ row_status) {
+  args_in_sgprs(partials, rows, nlists, cand_idx, cand_val, row_status);
+  const int row = blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;                        // the whole wave
+  const int lane = threadIdx.x & 63;
+  const unsigned long long rc = wave_merge_lists(partials + (size_t)row * nlists * kNC, nlists);
   const float v = bf16_to_f32(rc_bits(rc));
-  const unsigned long long bad = __ballot(!__builtin_isfinite(v));
-  if (row_raw < rows) {
-    cand_idx[(size_t)row * kNC + i] = rc ? rc_id(rc) : 0;
-    cand_val[(size_t)row * kNC + i] = v;
-    const int sh = (threadIdx.x & 63) & ~15;
-    if (row_status && i == 0) row_status[row] = ((bad >> sh) & 0xffffull) ? 1 : 0;
+  const bool bad = __ballot(lane < kNC && !__builtin_isfinite(v)) != 0ull;
+  if (lane < kNC) {
+    cand_idx[(size_t)row * kNC + lane] = rc ? rc_id(rc) : 0;
+    cand_val[(size_t)row * kNC + lane] = v;
   }
+  if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
 }
 
 // ---- pair scores ------------------------------------------------------------------------
 
 template <int DIM, bool BF16>
-__global__ void __launch_bounds__(kPairThreads) k_pair_score(const int32_t* __restrict__ cand_idx,
+__global__ void __launch_bounds__(kTileThreads) k_pair_score(const int32_t* __restrict__ cand_idx,
                                                              const float* __restrict__ cand_val,
                                                              const int32_t* __restrict__ verified,
                                                              const void* __restrict__ emb_a,
                                                              const void* __restrict__ emb_b, int V,
                                                              const float* __restrict__ H, int K, float* __restrict__ S,
                                                              int32_t* __restrict__ row_status) {
-  __shared__ PairShared sm;
+  args_in_sgprs(cand_idx, cand_val, verified, emb_a, emb_b, V, H, K, S, row_status);
+  __shared__ TileShared sm;
   const int pos = blockIdx.x;
-  const int b = pos / K, p = pos - b * K;
-  const int tid = threadIdx.x;
-  if (tid < kNC) {
-    sm.prev[tid] = p == 0 ? verified[b] : cand_idx[((size_t)pos - 1) * kNC + tid];
-    sm.cur[tid] = cand_idx[(size_t)pos * kNC + tid];
-    sm.U[tid] = cand_val[(size_t)pos * kNC + tid];
-  }
-  __syncthreads();
-  const int bits = pair_tile<DIM, BF16>(emb_a, emb_b, V, H + (size_t)pos * DIM, S + (size_t)pos * kNC * kNC, sm);
-  if (row_status && tid == 0) row_status[pos] = bits;
+  const int b = pos / K, t = pos - b * K;
+  const int tid = threadIdx.x, r = tid & 15;
+  int bad = 0;
+  const int prev = clamp_id(t == 0 ? verified[b] : cand_idx[((size_t)pos - 1) * kNC + r], V, &bad);
+  const int cur = clamp_id(cand_idx[(size_t)pos * kNC + r], V, &bad);
+  const float s = block_pair_tile<DIM, BF16>(emb_a, emb_b, prev, cur, H + (size_t)pos * DIM,
+                                             cand_val[(size_t)pos * kNC + r], sm);
+  const bool nonfin = block_any(!__builtin_isfinite(s), sm);
+  S[(size_t)pos * kNC * kNC + tid] = s;
+  const bool any_bad = __ballot(bad != 0) != 0ull;             // wave 0 holds every id
+  if (row_status && tid == 0) row_status[pos] = (any_bad ? 2 : 0) | (nonfin ? 1 : 0);
 }
 
 // ---- walk ------------------------------------------------------------------------------
@@ -159,6 +171,7 @@ __global__ void __launch_bounds__(kPairThreads) k_pair_score(const int32_t* __re
 __global__ void __launch_bounds__(256) k_walk(const float* __restrict__ S, const int32_t* __restrict__ cand_idx, int K,
                                               float inv_t, uint64_t seed, int32_t* __restrict__ tokens,
                                               int32_t* __restrict__ slots, float* __restrict__ q) {
+  args_in_sgprs(S, cand_idx, K, inv_t, seed, tokens, slots, q);
   __shared__ int s_next[kNC];
   const int b = blockIdx.x;
   const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
@@ -181,97 +194,222 @@ __global__ void __launch_bounds__(256) k_walk(const float* __restrict__ S, const
   }
 }
 
+constexpr int kMaxK = 64;               // draft positions per request (the ABI's limit)
+constexpr int kStagedK = 16;            // distributions staged in LDS up to this many positions
+
+struct WalkShared {
+  int tok[kMaxK * kNC];                 // the request's candidates
+  float qtab[kStagedK * kNC * kNC];     // each predecessor row's distribution (sampled)
+  int path[kMaxK];
+};
+
 // From the successor tables stage 2 built: next[t][i] (slot taken at t after slot i at
-// t - 1) and, when sampling, qtab[t][i][.] (that row's distribution).
+// t - 1) and, when sampling, qtab[t][i][.] (that row's distribution).  Wave 0 follows
+// the tables (lane r holds next[t][r]; each step reads the lane of the previous slot)
+// while waves 1-3 stage the candidates and distributions, so nothing read after the
+// walk depends on it through global memory (the distributions of a request longer than
+// kStagedK positions are read after the walk).
 __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ next, const float* __restrict__ qtab,
                                                      const int32_t* __restrict__ cand_idx, int K, bool sampled,
                                                      int32_t* __restrict__ tokens, int32_t* __restrict__ slots,
                                                      float* __restrict__ q) {
+  args_in_sgprs(next, qtab, cand_idx, K, sampled, tokens, slots, q);
   __shared__ WalkShared sm;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t base = (size_t)b * K * kNC;
-  for (int e = tid; e < K * kNC; e += blockDim.x) {
-    sm.next[e] = next[base + e];
-    sm.tok[e] = cand_idx[base + e];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int i = 0;
-    for (int t = 0; t < K; ++t) {
-      i = sm.next[t * kNC + i];
-      sm.path[t] = i;
+  if (tid < kWave) {
+    const int r = tid & 15;
+    int from = 0;
+    for (int t0 = 0; t0 < K; t0 += 16) {
+      int nt[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) nt[k] = t0 + k < K ? next[base + (size_t)(t0 + k) * kNC + r] : 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (t0 + k < K) {
+          from = __builtin_amdgcn_readlane(nt[k], from);
+          if (tid == 0) sm.path[t0 + k] = from;
+        }
+      }
     }
+  } else {
+    // every load of a thread's share issued before its first LDS store
+    constexpr int kStagers = 256 - kWave;
+    constexpr int kTokPer = (kMaxK * kNC + kStagers - 1) / kStagers;
+    constexpr int kQPer = (kStagedK * kNC * kNC + kStagers - 1) / kStagers;
+    const int ti = tid - kWave;
+    int tv[kTokPer];
+#pragma unroll
+    for (int k = 0; k < kTokPer; ++k) tv[k] = ti + k * kStagers < K * kNC ? cand_idx[base + ti + k * kStagers] : 0;
+    if (sampled && K <= kStagedK) {
+      float qv[kQPer];
+#pragma unroll
+      for (int k = 0; k < kQPer; ++k) {
+        const int e = ti + k * kStagers;
+        qv[k] = e < K * kNC * kNC ? qtab[base * kNC + e] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kQPer; ++k)
+        if (ti + k * kStagers < K * kNC * kNC) sm.qtab[ti + k * kStagers] = qv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kTokPer; ++k)
+      if (ti + k * kStagers < K * kNC) sm.tok[ti + k * kStagers] = tv[k];
   }
   __syncthreads();
-  for (int e = tid; e < K * kNC; e += blockDim.x) {
+  const bool staged = K <= kStagedK;
+  for (int e = tid; e < K * kNC; e += 256) {
     const int t = e >> 4, j = e & 15;
+    const int to = sm.path[t];
     const int from = t == 0 ? 0 : sm.path[t - 1];
-    q[base + e] = sampled ? qtab[(base + (size_t)t * kNC + from) * kNC + j] : (j == sm.path[t] ? 1.f : 0.f);
+    const int qi = (t * kNC + from) * kNC + j;
+    q[base + e] = sampled ? (staged ? sm.qtab[qi] : qtab[base * kNC + qi]) : (j == to ? 1.f : 0.f);
     if (j == 0) {
-      slots[(size_t)b * K + t] = sm.path[t];
-      tokens[(size_t)b * K + t] = sm.tok[t * kNC + sm.path[t]];
+      slots[(size_t)b * K + t] = to;
+      tokens[(size_t)b * K + t] = sm.tok[t * kNC + to];
     }
   }
 }
 
-// ---- stage 2 of the proposer step -------------------------------------------------------
+// ---- the gate rows of the gated step -----------------------------------------------------
 
-// GATED: H is not given; the block adds its row's gate slices (gate_partial, nsplit of
-// them) in slice order, applies the bias and the activation, keeps the row in LDS and
-// writes it to H_out when given.
+struct GateArgs {
+  const float* partial = nullptr;    // [nsplit][rows][dim] slice sums of the fused gate tiles
+  const float* bias = nullptr;
+  int nsplit = 0;
+  int act = 0;
+  float* H_out = nullptr;
+};
+
+// H[e] for the n = nrows * DIM gate values of rows row0.. (e = t * DIM + d): the slice sums
+// added in slice order, then the bias and the activation (as gate_finish), written to dst
+// (LDS) and to H_out when given.  The first nthreads threads of the block (index ti) call
+// it; the loads of up to 8 values x 8 slices are in flight together.
+template <int DIM>
+__device__ __forceinline__ void gated_rows(const GateArgs& ga, int rows, int row0, int n, int ti, int nthreads,
+                                           float* dst) {
+  constexpr int kE = 8, kS = 8;
+  const size_t stride = (size_t)rows * DIM;
+  for (int e0 = ti; e0 < n; e0 += kE * nthreads) {
+    float sum[kE];
+#pragma unroll
+    for (int k = 0; k < kE; ++k) sum[k] = 0.f;
+    for (int s0 = 0; s0 < ga.nsplit; s0 += kS) {
+      float v[kS][kE];
+#pragma unroll
+      for (int sp = 0; sp < kS; ++sp)
+#pragma unroll
+        for (int k = 0; k < kE; ++k) {
+          const int e = e0 + k * nthreads;
+          v[sp][k] = (s0 + sp < ga.nsplit && e < n)
+                         ? ga.partial[(size_t)(s0 + sp) * stride + (size_t)row0 * DIM + e]
+                         : 0.f;
+        }
+#pragma unroll
+      for (int sp = 0; sp < kS; ++sp)
+#pragma unroll
+        for (int k = 0; k < kE; ++k)
+          if (s0 + sp < ga.nsplit) sum[k] += v[sp][k];
+    }
+#pragma unroll
+    for (int k = 0; k < kE; ++k) {
+      const int e = e0 + k * nthreads;
+      if (e < n) {
+        const int d = e & (DIM - 1);
+        const float h = gate_act(sum[k] + (ga.bias ? ga.bias[d] : 0.f), ga.act);
+        dst[e] = h;
+        if (ga.H_out) ga.H_out[(size_t)row0 * DIM + e] = h;
+      }
+    }
+  }
+}
+
+struct SelectOut {
+  int32_t* cand_idx;
+  float* cand_val;
+  float* S;
+  int32_t* tokens;
+  int32_t* slots;
+  float* q;
+  int32_t* row_status;
+};
+
+// ---- stage 2 of the proposer step: one block per draft position ------------------------
+
+// GATED: H is not given; waves 1-3 add the row's gate slices, apply the bias and the
+// activation, keep the row in LDS and write it to H_out when given.
 template <int DIM, bool BF16, bool GATED>
-__global__ void __launch_bounds__(kPairThreads) k_positions(const unsigned long long* __restrict__ partials,
-                                                            int nchunks, int K, const int32_t* __restrict__ verified,
+__global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long long* __restrict__ partials,
+                                                            int nchunks, int K, int rows,
+                                                            const int32_t* __restrict__ verified,
                                                             const void* __restrict__ emb_a,
                                                             const void* __restrict__ emb_b, int V,
-                                                            const float* __restrict__ H,
-                                                            const float* __restrict__ gate_partial,
-                                                            const float* __restrict__ gate_bias, int gate_nsplit,
-                                                            int gate_act_id, float* __restrict__ H_out, float inv_t,
-                                                            uint64_t seed,
-                                                            int32_t* __restrict__ cand_idx,
+                                                            const float* __restrict__ H, GateArgs ga, float inv_t,
+                                                            uint64_t seed, int32_t* __restrict__ cand_idx,
                                                             float* __restrict__ cand_val, float* __restrict__ S,
                                                             int* __restrict__ next, float* __restrict__ qtab,
                                                             int32_t* __restrict__ row_status) {
-  __shared__ PairShared ps;
-  __shared__ int s_bits;
+  args_in_sgprs(partials, nchunks, K, rows, verified, emb_a, emb_b, V, H, inv_t, seed, cand_idx, cand_val, S, next, qtab,
+                row_status);
+  if constexpr (GATED) args_in_sgprs(ga.partial, ga.bias, ga.nsplit, ga.act, ga.H_out);
+  __shared__ TileShared sm;
   __shared__ float s_H[GATED ? DIM : 1];
+  __shared__ int s_prev[kNC], s_cur[kNC];
+  __shared__ float s_U[kNC];
+  __shared__ int s_bits;
   const int pos = blockIdx.x;
-  const int b = pos / K, p = pos - b * K;
-  const int tid = threadIdx.x;
-  if constexpr (GATED) {
-    const int rows = (int)gridDim.x;
-    for (int d = tid; d < DIM; d += kPairThreads) {
-      const float v = gate_finish(gate_partial, gate_bias, rows, DIM, gate_nsplit, gate_act_id, pos, d);
-      s_H[d] = v;
-      if (H_out) H_out[(size_t)pos * DIM + d] = v;
-    }
-  }
-  if (tid < kWave) {
-    // rows 0 and 2 of wave 0 merge row pos, rows 1 and 3 row pos - 1 (the predecessors)
-    const int i = tid & 15;
-    const bool pred = (tid & 16) != 0;
-    const int r = pred && p > 0 ? pos - 1 : pos;
-    const unsigned long long rc = row16_merge_chunks(partials + (size_t)r * nchunks * kNC, nchunks);
+  const int b = pos / K, t = pos - b * K;
+  const int tid = threadIdx.x, w = tid >> 6, r = tid & 15;
+  const int nlists = nchunks;
+  if (w == 0) {
+    // wave 0 merges row pos
+    const unsigned long long rc = wave_merge_lists(partials + (size_t)pos * nlists * kNC, nlists);
     const float v = bf16_to_f32(rc_bits(rc));
-    const bool bad = __ballot(tid < kNC && !__builtin_isfinite(v)) != 0ull;
+    const bool nf = __ballot(tid < kNC && !__builtin_isfinite(v)) != 0ull;
     if (tid < kNC) {
-      cand_idx[(size_t)pos * kNC + i] = rc ? rc_id(rc) : 0;
-      cand_val[(size_t)pos * kNC + i] = v;
-      ps.cur[i] = rc ? rc_id(rc) : 0;
-      ps.U[i] = v;
-    } else if (tid < 2 * kNC) {
-      ps.prev[i] = p == 0 ? verified[b] : (rc ? rc_id(rc) : 0);
+      s_cur[tid] = rc ? rc_id(rc) : 0;
+      s_U[tid] = v;
     }
-    if (tid == 0) s_bits = bad ? 1 : 0;
+    if (tid == 0) s_bits = nf ? 1 : 0;
+  } else if (w == 1) {
+    // wave 1 merges row pos - 1 (the predecessors)
+    if (t == 0) {
+      if (tid < kWave + kNC) s_prev[tid - kWave] = verified[b];
+    } else {
+      const unsigned long long rc = wave_merge_lists(partials + (size_t)(pos - 1) * nlists * kNC, nlists);
+      if (tid < kWave + kNC) s_prev[tid - kWave] = rc ? rc_id(rc) : 0;
+    }
+  } else if constexpr (GATED) {
+    gated_rows<DIM>(ga, rows, pos, DIM, tid - 2 * kWave, kTileThreads - 2 * kWave, s_H);
   }
   __syncthreads();
-  const float* Hrow = GATED ? s_H : H + (size_t)pos * DIM;
-  const int pbits = pair_tile<DIM, BF16>(emb_a, emb_b, V, Hrow, S + (size_t)pos * kNC * kNC, ps);
-  const float u = inv_t == 0.f ? 0.f : walk_uniform(seed, (uint32_t)b, (uint32_t)p);
-  tile_successors(ps, inv_t, u, next + (size_t)pos * kNC, inv_t == 0.f ? nullptr : qtab + (size_t)pos * kNC * kNC);
-  if (row_status && tid == 0) row_status[pos] = s_bits | pbits;
+  int bad = 0;
+  const int prev = clamp_id(s_prev[r], V, &bad);
+  const int cur = clamp_id(s_cur[r], V, &bad);
+  float s;
+  if constexpr (GATED)
+    s = block_pair_tile<DIM, BF16>(emb_a, emb_b, prev, cur, s_H, s_U[r], sm);
+  else
+    s = block_pair_tile<DIM, BF16>(emb_a, emb_b, prev, cur, H + (size_t)pos * DIM, s_U[r], sm);
+  const bool nonfin = block_any(!__builtin_isfinite(s), sm);
+  // thread 16 i + j holds S[i][j]: its 16-lane group decides row i
+  const float u = inv_t == 0.f ? 0.f : walk_uniform(seed, (uint32_t)b, (uint32_t)t);
+  float qj;
+  const int pick = row16_pick(s, inv_t, u, &qj);
+  S[(size_t)pos * kNC * kNC + tid] = s;
+  if (inv_t != 0.f) qtab[(size_t)pos * kNC * kNC + tid] = qj;
+  if (r == 0) next[(size_t)pos * kNC + (tid >> 4)] = pick;
+  if (tid < kNC) {
+    cand_idx[(size_t)pos * kNC + tid] = s_cur[tid];
+    cand_val[(size_t)pos * kNC + tid] = s_U[tid];
+  }
+  const bool any_bad = __ballot(bad != 0) != 0ull;             // wave 0 holds every id
+  if (row_status && tid == 0) row_status[pos] = s_bits | (any_bad ? 2 : 0) | (nonfin ? 1 : 0);
+  if constexpr (GATED) {
+    if (ga.H_out)
+      for (int d = tid; d < DIM; d += kTileThreads) ga.H_out[(size_t)pos * DIM + d] = s_H[d];
+  }
 }
 
 // ---- launchers -----------------------------------------------------------------------
@@ -281,40 +419,40 @@ hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld
   const int nchunks = topk_num_chunks(vocab);
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(rows * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
                      nchunks, ws.partials);
-  hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)), dim3(kMergeRows * kNC),
+  hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)((rows + kMergeWaves - 1) / kMergeWaves)), dim3(kMergeWaves * kWave),
                      0, s, ws.partials, rows, nchunks, cand_idx, cand_val, row_status);
   return hipGetLastError();
 }
 
-template <int DIM, bool BF16>
-static void pair_launch(dim3 grid, hipStream_t s, const int32_t* cand_idx, const float* cand_val,
-                        const int32_t* verified, const void* a, const void* b, int V, const float* H, int K, float* S,
-                        int32_t* st) {
-  hipLaunchKernelGGL((k_pair_score<DIM, BF16>), grid, dim3(kPairThreads), 0, s, cand_idx, cand_val, verified, a, b, V,
-                     H, K, S, st);
+// Calls f.template operator()<DIM>() for the selector width dim (a power of two in
+// [16, 1024]); returns false for any other width.
+template <typename F>
+static bool with_dim(int dim, F&& f) {
+  switch (dim) {
+    case 16: f.template operator()<16>(); return true;
+    case 32: f.template operator()<32>(); return true;
+    case 64: f.template operator()<64>(); return true;
+    case 128: f.template operator()<128>(); return true;
+    case 256: f.template operator()<256>(); return true;
+    case 512: f.template operator()<512>(); return true;
+    case 1024: f.template operator()<1024>(); return true;
+    default: return false;
+  }
 }
 
 hipError_t launch_pair_score(const int32_t* cand_idx, const float* cand_val, const int32_t* verified, const void* emb_a,
                              const void* emb_b, bool bf16, int vocab, int dim, const float* H, int batch, int K,
                              float* S, int32_t* row_status, hipStream_t s) {
   const dim3 grid((unsigned)(batch * K));
-#define DF2_PAIR(D)                                                                                           \
-  case D:                                                                                                     \
-    if (bf16)                                                                                                 \
-      pair_launch<D, true>(grid, s, cand_idx, cand_val, verified, emb_a, emb_b, vocab, H, K, S, row_status);  \
-    else                                                                                                      \
-      pair_launch<D, false>(grid, s, cand_idx, cand_val, verified, emb_a, emb_b, vocab, H, K, S, row_status); \
-    break;
-  switch (dim) {
-    DF2_PAIR(64)
-    DF2_PAIR(128)
-    DF2_PAIR(256)
-    DF2_PAIR(512)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef DF2_PAIR
-  return hipGetLastError();
+  const bool ok = with_dim(dim, [&]<int D>() {
+    if (bf16)
+      hipLaunchKernelGGL((k_pair_score<D, true>), grid, dim3(kTileThreads), 0, s, cand_idx, cand_val, verified, emb_a,
+                         emb_b, vocab, H, K, S, row_status);
+    else
+      hipLaunchKernelGGL((k_pair_score<D, false>), grid, dim3(kTileThreads), 0, s, cand_idx, cand_val, verified, emb_a,
+                         emb_b, vocab, H, K, S, row_status);
+  });
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_walk(const float* S, const int32_t* cand_idx, int batch, int K, float temperature, uint64_t seed,
@@ -324,52 +462,25 @@ hipError_t launch_walk(const float* S, const int32_t* cand_idx, int batch, int K
   return hipGetLastError();
 }
 
-struct GateArgs {
-  const float* partial = nullptr;
-  const float* bias = nullptr;
-  int nsplit = 0;
-  int act = 0;
-  float* H_out = nullptr;
-};
-
-template <int DIM, bool BF16, bool GATED>
-static void positions_launch(dim3 grid, hipStream_t s, const unsigned long long* partials, int nchunks, int K,
-                             const int32_t* verified, const void* a, const void* b, int V, const float* H,
-                             const GateArgs& ga, float inv_t, uint64_t seed, int32_t* ci, float* cv, float* S,
-                             int* next, float* qtab, int32_t* st) {
-  hipLaunchKernelGGL((k_positions<DIM, BF16, GATED>), grid, dim3(kPairThreads), 0, s, partials, nchunks, K, verified,
-                     a, b, V, H, ga.partial, ga.bias, ga.nsplit, ga.act, ga.H_out, inv_t, seed, ci, cv, S, next,
-                     qtab, st);
-}
-
-// Stages 2 and 3 of the select (stage 1 has filled ws.topk.partials).
+// Stages 2 and 3 of the select; stage 1 has filled ws.topk.partials.
 template <bool GATED>
-static hipError_t select_tail(const uint16_t* /*logits*/, int nchunks, const int32_t* verified, const void* emb_a,
-                              const void* emb_b, bool bf16, int vocab, int dim, const float* H, const GateArgs& ga,
-                              int batch, int K, float inv_t, uint64_t seed, int32_t* cand_idx, float* cand_val,
-                              float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
-                              const SelectWs& ws, hipStream_t s) {
-  const dim3 grid((unsigned)(batch * K));
-#define DF2_POS(D)                                                                                                   \
-  case D:                                                                                                            \
-    if (bf16)                                                                                                        \
-      positions_launch<D, true, GATED>(grid, s, ws.topk.partials, nchunks, K, verified, emb_a, emb_b, vocab, H, ga,  \
-                                       inv_t, seed, cand_idx, cand_val, S, ws.next, ws.qtab, row_status);            \
-    else                                                                                                             \
-      positions_launch<D, false, GATED>(grid, s, ws.topk.partials, nchunks, K, verified, emb_a, emb_b, vocab, H, ga, \
-                                        inv_t, seed, cand_idx, cand_val, S, ws.next, ws.qtab, row_status);           \
-    break;
-  switch (dim) {
-    DF2_POS(64)
-    DF2_POS(128)
-    DF2_POS(256)
-    DF2_POS(512)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef DF2_POS
-  hipLaunchKernelGGL(k_walk_tables, dim3((unsigned)batch), dim3(256), 0, s, ws.next, ws.qtab, cand_idx, K,
-                     inv_t != 0.f, tokens, slots, q);
+static hipError_t select_tail(int nchunks, const int32_t* verified, const void* emb_a, const void* emb_b, bool bf16,
+                              int vocab, int dim, const float* H, const GateArgs& ga, int batch, int K, float inv_t,
+                              uint64_t seed, const SelectOut& out, const SelectWs& ws, hipStream_t s) {
+  const int rows = batch * K;
+  const bool ok = with_dim(dim, [&]<int D>() {
+    if (bf16)
+      hipLaunchKernelGGL((k_positions<D, true, GATED>), dim3((unsigned)rows), dim3(kTileThreads), 0, s,
+                         ws.topk.partials, nchunks, K, rows, verified, emb_a, emb_b, vocab, H, ga, inv_t, seed,
+                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status);
+    else
+      hipLaunchKernelGGL((k_positions<D, false, GATED>), dim3((unsigned)rows), dim3(kTileThreads), 0, s,
+                         ws.topk.partials, nchunks, K, rows, verified, emb_a, emb_b, vocab, H, ga, inv_t, seed,
+                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status);
+  });
+  if (!ok) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_walk_tables, dim3((unsigned)batch), dim3(256), 0, s, ws.next, ws.qtab, out.cand_idx, K,
+                     inv_t != 0.f, out.tokens, out.slots, out.q);
   return hipGetLastError();
 }
 
@@ -381,8 +492,9 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(batch * K * nchunks)), dim3(kTopkThreads), 0, s, logits, ld, vocab,
                      nchunks, ws.topk.partials);
-  return select_tail<false>(logits, nchunks, verified, emb_a, emb_b, bf16, vocab, dim, H, GateArgs{}, batch, K, inv_t,
-                            seed, cand_idx, cand_val, S, tokens, slots, q, row_status, ws, s);
+  const SelectOut out{cand_idx, cand_val, S, tokens, slots, q, row_status};
+  return select_tail<false>(nchunks, verified, emb_a, emb_b, bf16, vocab, dim, H, GateArgs{}, batch, K, inv_t, seed,
+                            out, ws, s);
 }
 
 hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
@@ -405,8 +517,9 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
   ga.nsplit = ws.nsplit;
   ga.act = act;
   ga.H_out = H_out;
-  return select_tail<true>(logits, nchunks, verified, emb_a, emb_b, bf16, vocab, dim, nullptr, ga, batch, K, inv_t,
-                           seed, cand_idx, cand_val, S, tokens, slots, q, row_status, ws.sel, s);
+  const SelectOut out{cand_idx, cand_val, S, tokens, slots, q, row_status};
+  return select_tail<true>(nchunks, verified, emb_a, emb_b, bf16, vocab, dim, nullptr, ga, batch, K, inv_t, seed, out,
+                           ws.sel, s);
 }
 
 }  // namespace df2

@@ -1,30 +1,13 @@
 // Pair scores S_t(a, b) = U_t(b) + <A(a) (.) H(h_t), B(b)> for the 16 x 16 adjacent
-// candidate pairs of one draft position, and the walk over them (pegainfer issue
-// "DFlash 2 proposer", section "What upstream shipped", item 1, and section
-// "Proposal", phase 1: block_size x 16 predecessors x 16 candidates x 256 dims, then
-// a <= block_size-step argmax walk).
+// candidate pairs of one draft position, and the per-row decisions of the walk over
+// them (pegainfer issue "DFlash 2 proposer", section "What upstream shipped", item 1,
+// and section "Proposal", phase 1: block_size x 16 predecessors x 16 candidates x 256
+// dims, then a <= block_size-step argmax walk).
 #pragma once
 
 #include "device_common.h"
 
 namespace df2 {
-
-constexpr int kPairThreads = 256;   // 4 waves; each wave owns a quarter of the selector dims
-
-struct PairShared {
-  float red[4][kNC][kNC];
-  float S[kNC][kNC];
-  int prev[kNC];
-  int cur[kNC];
-  float U[kNC];
-  int flags;
-};
-
-struct WalkShared {
-  int next[64 * kNC];
-  int tok[64 * kNC];
-  int path[64];
-};
 
 __device__ __forceinline__ int clamp_id(int id, int V, int* bad) {
   if (id < 0 || id >= V) {
@@ -34,112 +17,146 @@ __device__ __forceinline__ int clamp_id(int id, int V, int* bad) {
   return id;
 }
 
-// One position's 16 x 16 scores from sm.prev (predecessor ids), sm.cur (candidate ids)
-// and sm.U (candidate logits), all set by the caller and visible to the block (all 256
-// threads call it).  Writes the tile to sm.S and to S_out[256]; returns the row-status
-// bits (block-uniform): 2 = an id outside [0, V) (clamped), 1 = a non-finite score.
-//
-// MFMA mapping (v_mfma_f32_16x16x4_f32, wave64): lane l feeds A[i = l % 16][k = l / 16]
-// and B[k = l / 16][j = l % 16]; step s of wave w uses, for k-group g = l / 16, the
-// selector dim d = w * DIM/4 + g * DIM/16 + s, so each lane reads one contiguous
-// DIM/16-wide slice of its table rows.  The product over d is order-free, so this
-// permutation of the contraction is exact up to fp32 rounding order.  A scheduling
-// barrier keeps every gather ahead of the first MFMA (one memory round trip), and the
-// four waves' partial tiles are summed in a fixed order.
+__device__ __forceinline__ uint32_t bf16_bits(__bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
+
+constexpr int kTileThreads = 256;     // the block of one draft position: 4 waves
+
+// Waves that share a tile: each covers DIM / NW of the selector dims, at least one MFMA
+// step (32 dims with bf16 tables, 16 with fp32 ones).
 template <int DIM, bool BF16>
-__device__ __forceinline__ int pair_tile(const void* __restrict__ emb_a, const void* __restrict__ emb_b, int V,
-                                         const float* __restrict__ Hrow, float* __restrict__ S_out, PairShared& sm) {
-  constexpr int ND = DIM / 16;                       // dims per lane
-  constexpr int NV = BF16 ? (ND + 7) / 8 : ND / 4;   // 16-byte loads per table slice (ND >= 4)
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int g = lane >> 4;
-  const int r16 = lane & 15;
-  const int d0 = w * (DIM / 4) + g * ND;
-
-  int bad = 0;
-  const int prev = clamp_id(sm.prev[r16], V, &bad);
-  const int cur = clamp_id(sm.cur[r16], V, &bad);
-  if (tid == 0) sm.flags = 0;
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 hq[ND / 4];
-#pragma unroll
-  for (int i = 0; i < ND / 4; ++i) hq[i] = *reinterpret_cast<const f32x4*>(Hrow + d0 + 4 * i);
-  if constexpr (BF16) {
-    // table slices stay packed (two bf16 per register) until their MFMA step
-    uint32_t aw[ND / 2], bw[ND / 2];
-    const uint16_t* ap = static_cast<const uint16_t*>(emb_a) + (size_t)prev * DIM + d0;
-    const uint16_t* bp = static_cast<const uint16_t*>(emb_b) + (size_t)cur * DIM + d0;
-    if constexpr (ND >= 8) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(ap + 8 * i);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(bp + 8 * i);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          aw[4 * i + c] = x[c];
-          bw[4 * i + c] = y[c];
-        }
-      }
-    } else {
-      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 x = *reinterpret_cast<const u32x2*>(ap);
-      const u32x2 y = *reinterpret_cast<const u32x2*>(bp);
-      aw[0] = x.x;
-      aw[1] = x.y;
-      bw[0] = y.x;
-      bw[1] = y.y;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < ND; ++s) {
-      const float a = (s & 1) ? bf16_hi(aw[s >> 1]) : bf16_lo(aw[s >> 1]);
-      const float bb = (s & 1) ? bf16_hi(bw[s >> 1]) : bf16_lo(bw[s >> 1]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a * hq[s >> 2][s & 3], bb, acc, 0, 0, 0);
-    }
-  } else {
-    f32x4 x[NV], y[NV];
-    const float* ap = static_cast<const float*>(emb_a) + (size_t)prev * DIM + d0;
-    const float* bp = static_cast<const float*>(emb_b) + (size_t)cur * DIM + d0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      x[i] = *reinterpret_cast<const f32x4*>(ap + 4 * i);
-      y[i] = *reinterpret_cast<const f32x4*>(bp + 4 * i);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < ND; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s >> 2][s & 3] * hq[s >> 2][s & 3], y[s >> 2][s & 3], acc, 0, 0, 0);
-  }
-
-  // D layout: lane l, register r holds D[4 * (l / 16) + r][l % 16]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sm.red[w][4 * g + r][r16] = acc[r];
-  __syncthreads();
-  if (bad) atomicOr(&sm.flags, 2);
-  {
-    const int i = tid >> 4, j = tid & 15;
-    const float s = sm.U[j] + (((sm.red[0][i][j] + sm.red[1][i][j]) + sm.red[2][i][j]) + sm.red[3][i][j]);
-    sm.S[i][j] = s;
-    S_out[tid] = s;
-    if (!__builtin_isfinite(s)) atomicOr(&sm.flags, 1);
-  }
-  __syncthreads();
-  return sm.flags;
+constexpr int tile_waves() {
+  constexpr int steps = DIM / (BF16 ? 32 : 16);
+  return steps >= 4 ? 4 : (steps >= 1 ? steps : 1);
 }
 
-// Successor table of a position: next[i] = the slot taken from row i of the tile in
-// sm.S, and (when qrows is not null) qrows[i][j] = that row's distribution (all 256
-// threads; thread i * 16 + j holds slot j of row i).
-__device__ __forceinline__ void tile_successors(const PairShared& sm, float inv_t, float u, int* __restrict__ next,
-                                                float* __restrict__ qrows) {
-  const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
-  float qj;
-  const int pick = row16_pick(sm.S[i][j], inv_t, u, &qj);
-  if (j == 0) next[i] = pick;
-  if (qrows) qrows[threadIdx.x] = qj;
+struct TileShared {
+  float red[4][kNC][kNC];             // each wave's partial tile
+  int any[4];                         // per-wave flags of block_any
+};
+
+// Whether any thread of the kTileThreads-thread block passes f (a barrier).
+__device__ __forceinline__ bool block_any(bool f, TileShared& sm) {
+  const unsigned long long m = __ballot(f);
+  if ((threadIdx.x & 63) == 0) sm.any[threadIdx.x >> 6] = m != 0ull;
+  __syncthreads();
+  return (sm.any[0] | sm.any[1] | sm.any[2] | sm.any[3]) != 0;
+}
+
+// Partial tile of wave w over the selector dims [w, w + 1) * DIM / NW.  Lane l
+// (g = l / 16, r = l % 16) passes the (clamped) id of predecessor row r as `prev` and of
+// candidate column r as `cur`; it gets back, in register i, the part of
+// sum_d A[prev of row 4 g + i][d] H[d] B[cur of column r][d] over the wave's dims.
+//
+// bf16 tables, on v_mfma_f32_16x16x32_bf16: x = A(prev)[d] H[d] is split into
+// hi = bf16(fp32(x)) (nearest even) and lo = bf16(fma(A, H, -hi)), the remainder of the
+// exact product rounded once to fp32 and then to bf16; hi and lo each go through the
+// MFMA against the bf16 row of B, whose products are exact, so a term departs from
+// x B by at most about 2^-18 |x B| and the sums accumulate in fp32.  The remainder is an
+// explicit fused multiply-add so that no kernel's contraction choice changes a bit.
+// In MFMA step s, lane l feeds row / column r with the dims base + 32 s + 8 g + [0, 8)
+// (with 16 dims the two upper groups feed zeros).
+// fp32 tables, on v_mfma_f32_16x16x4_f32: lane l loads the dims base + 16 m + 4 g +
+// [0, 4) and feeds A[prev][d] H[d] and B[cur][d] of dim base + 16 m + 4 g + c to step
+// (m, c).
+// Either way the four lanes of a row read 64 contiguous bytes of it per load, so each
+// load instruction touches 16 cache lines of the tables, and the contraction over d is
+// a permutation of the plain sum.
+template <int DIM, bool BF16>
+__device__ __forceinline__ f32x4 wave_pair_part(const void* __restrict__ emb_a, const void* __restrict__ emb_b,
+                                                int prev, int cur, const float* __restrict__ Hrow, int w) {
+  static_assert(DIM >= 16 && DIM <= 1024 && (DIM & (DIM - 1)) == 0, "selector dims: a power of two in [16, 1024]");
+  constexpr int SUB = DIM / tile_waves<DIM, BF16>();           // dims per wave
+  const int g = (threadIdx.x & 63) >> 4;
+  const int base = w * SUB;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (BF16) {
+    constexpr int NS = SUB >= 32 ? SUB / 32 : 1;               // MFMA steps
+    constexpr int NB = NS < 16 ? NS : 16;                      // steps whose rows are loaded at once
+    const bool live = 8 * g < SUB;
+    const int off = base + (live ? 8 * g : 0);
+    const uint16_t* ap = static_cast<const uint16_t*>(emb_a) + (size_t)prev * DIM + off;
+    const uint16_t* bp = static_cast<const uint16_t*>(emb_b) + (size_t)cur * DIM + off;
+    const float* hp = Hrow + off;
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += NB) {
+      u32x4 av[NB], bv[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        av[i] = *reinterpret_cast<const u32x4*>(ap + 32 * (s0 + i));
+        bv[i] = *reinterpret_cast<const u32x4*>(bp + 32 * (s0 + i));
+      }
+      __builtin_amdgcn_sched_barrier(0);                       // every gather of the batch in flight first
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const f32x4 h0 = *reinterpret_cast<const f32x4*>(hp + 32 * (s0 + i));
+        const f32x4 h1 = *reinterpret_cast<const f32x4*>(hp + 32 * (s0 + i) + 4);
+        const f32x2 h2[4] = {{h0.x, h0.y}, {h0.z, h0.w}, {h1.x, h1.y}, {h1.z, h1.w}};
+        u32x4 hi, lo;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const f32x2 a2 = {bf16_lo(av[i][p]), bf16_hi(av[i][p])};
+          const f32x2 x = a2 * h2[p];
+          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+          const f32x2 r = __builtin_elementwise_fma(a2, h2[p], -(f32x2){bf16_lo(hb), bf16_hi(hb)});
+          hi[p] = hb;
+          lo[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+        }
+        if (!live) hi = lo = (u32x4){0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), __builtin_bit_cast(bf16x8, bv[i]),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), __builtin_bit_cast(bf16x8, bv[i]),
+                                                      acc, 0, 0, 0);
+      }
+    }
+  } else {
+    constexpr int NV = SUB / 16;                               // 16-byte loads per lane and row
+    constexpr int NB = NV < 16 ? NV : 16;
+    const float* ap = static_cast<const float*>(emb_a) + (size_t)prev * DIM + base + 4 * g;
+    const float* bp = static_cast<const float*>(emb_b) + (size_t)cur * DIM + base + 4 * g;
+    const float* hp = Hrow + base + 4 * g;
+#pragma unroll
+    for (int v0 = 0; v0 < NV; v0 += NB) {
+      f32x4 av[NB], bv[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        av[i] = *reinterpret_cast<const f32x4*>(ap + 16 * (v0 + i));
+        bv[i] = *reinterpret_cast<const f32x4*>(bp + 16 * (v0 + i));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const f32x4 h = *reinterpret_cast<const f32x4*>(hp + 16 * (v0 + i));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][c] * h[c], bv[i][c], acc, 0, 0, 0);
+      }
+    }
+  }
+  return acc;
+}
+
+// One position's 16 x 16 tile by the whole block (kTileThreads threads, every one calls
+// it): waves w < NW compute their partial tiles (every lane passes its prev / cur ids as
+// in wave_pair_part) and the partials are added in wave order after a barrier.  Thread
+// 16 i + j gets S[i][j] = U_j + (partial sums), with u_col = U of its column j.
+template <int DIM, bool BF16>
+__device__ __forceinline__ float block_pair_tile(const void* __restrict__ emb_a, const void* __restrict__ emb_b,
+                                                 int prev, int cur, const float* __restrict__ Hrow, float u_col,
+                                                 TileShared& sm) {
+  constexpr int NW = tile_waves<DIM, BF16>();
+  const int tid = threadIdx.x, w = tid >> 6;
+  if (w < NW) {
+    const f32x4 acc = wave_pair_part<DIM, BF16>(emb_a, emb_b, prev, cur, Hrow, w);
+    const int lane = tid & 63, g = lane >> 4, r = lane & 15;
+    // D layout: lane l, register i -> row 4 (l / 16) + i, column l % 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.red[w][4 * g + i][r] = acc[i];
+  }
+  __syncthreads();
+  const int i = tid >> 4, j = tid & 15;
+  float sum = sm.red[0][i][j];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) sum += sm.red[v][i][j];
+  return u_col + sum;
 }
 
 }  // namespace df2

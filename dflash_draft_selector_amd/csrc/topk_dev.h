@@ -274,12 +274,14 @@ __device__ __forceinline__ int vector_maxima(const u32x4 (&d)[kTopkVecPerThread]
   return lmax;
 }
 
-// Exact top-16 of the logits this wave's lanes load, best first, into list[] (LDS),
-// zero-padded when the wave holds fewer than 16: sixteen rounds of a wave maximum below
-// the previous one.  It re-reads the logits (cache-resident by now) so that the common
-// path keeps its register budget.
+// Exact top-16 of the logits this wave's lanes load, best first, into list[0..16)
+// (written by lane 0), zero-padded when the wave holds fewer than 16: sixteen rounds of
+// a wave maximum below the previous one.  Each round re-reads the share (cache-resident
+// by now) four vectors per lane at a time, so that the common path keeps its register
+// budget.  Only chunks with heavy ties at the bound, NaN lanes or few logits take it.
 __device__ __noinline__ void wave_exact_list(const uint16_t* __restrict__ row, int V, int v0, int v1,
                                              unsigned long long* list) {
+  constexpr int kBatch = 4;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int nfull = V >> 3;
@@ -288,29 +290,40 @@ __device__ __noinline__ void wave_exact_list(const uint16_t* __restrict__ row, i
   for (int r = 0; r < kNC; ++r) {
     unsigned long long best = 0ull;
 #pragma unroll 1
-    for (int k = 0; k < kTopkVecPerThread; ++k) {
-      const int v = v0 + tid + k * kTopkThreads;
-      if (v >= v1) break;
-      u32x4 x;
-      if (v < nfull) {
-        x = rowv[v];
-      } else {
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+    for (int k0 = 0; k0 < kTopkVecPerThread; k0 += kBatch) {
+      u32x4 x[kBatch];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (8 * v + e < V) {
-            const uint32_t b = row[8 * v + e];
-            w4[e >> 1] |= (e & 1) ? (b << 16) : b;
+      for (int i = 0; i < kBatch; ++i) {
+        const int v = v0 + tid + (k0 + i) * kTopkThreads;
+        x[i] = (u32x4){0u, 0u, 0u, 0u};
+        if (k0 + i < kTopkVecPerThread && v < v1) {
+          if (v < nfull) {
+            x[i] = rowv[v];
+          } else {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if (8 * v + e < V) {
+                const uint32_t b = row[8 * v + e];
+                w4[e >> 1] |= (e & 1) ? (b << 16) : b;
+              }
+            }
+            x[i] = (u32x4){w4[0], w4[1], w4[2], w4[3]};
           }
         }
-        x = (u32x4){w4[0], w4[1], w4[2], w4[3]};
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (8 * v + e < V) {
-          const uint32_t bits = elem_bits(x, e);
-          const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)(8 * v + e), bits);
-          if (comp < prev && comp > best) best = comp;
+      for (int i = 0; i < kBatch; ++i) {
+        const int v = v0 + tid + (k0 + i) * kTopkThreads;
+        if (k0 + i < kTopkVecPerThread && v < v1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (8 * v + e < V) {
+              const uint32_t bits = elem_bits(x[i], e);
+              const unsigned long long comp = make_rc(bf16_key(bits), (unsigned)(8 * v + e), bits);
+              if (comp < prev && comp > best) best = comp;
+            }
+          }
         }
       }
     }
@@ -431,20 +444,25 @@ __device__ __forceinline__ void chunk_top16(const uint16_t* __restrict__ row, in
   }
 }
 
-// Top-16, best first, of a row's nchunks <= kMaxChunks sorted chunk lists (global
-// memory, kNC entries each): the 16 lanes of a row load them all, then merge them one
-// after another.  Every lane of each 16-lane row must take part.  Lane i returns slot i.
-__device__ __forceinline__ unsigned long long row16_merge_chunks(const unsigned long long* __restrict__ src,
-                                                                 int nchunks) {
-  const int i = threadIdx.x & 15;
-  unsigned long long y[kMaxChunks];
+// Top-16, best first, of L <= kMaxChunks sorted lists of 16 (global memory) by one whole
+// wave: 16-lane row g merges lists g, g + 4, g + 8, ... one after another (all of them
+// loaded first), then the rows merge pairwise.  Lane i of every row returns slot i.
+__device__ __forceinline__ unsigned long long wave_merge_lists(const unsigned long long* __restrict__ src, int L) {
+  constexpr int kPerRow = (kMaxChunks + 3) / 4;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i = lane & 15;
+  unsigned long long y[kPerRow];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) y[c] = c < nchunks ? src[c * kNC + (c == 0 ? i : kNC - 1 - i)] : 0ull;
+  for (int k = 0; k < kPerRow; ++k) {
+    const int l = g + 4 * k;
+    y[k] = l < L ? src[(size_t)l * kNC + (k == 0 ? i : kNC - 1 - i)] : 0ull;
+  }
   unsigned long long x = y[0];
 #pragma unroll
-  for (int c = 1; c < kMaxChunks; ++c)
-    if (c < nchunks) x = merge16(x, y[c]);
-  return x;
+  for (int k = 1; k < kPerRow; ++k)
+    if (4 * k < L) x = merge16(x, y[k]);                            // wave-uniform: every row merges
+  x = merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 16));
+  return merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 32));
 }
 
 // Chunking of a row: n chunks of near-equal vector counts, each <= kChunkVec.

@@ -184,10 +184,15 @@ dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dty
  *
  * cand_idx int32 [batch, K, 16], cand_val float [batch, K, 16], verified int32 [batch],
  * emb_a, emb_b [vocab, dim] in emb_dtype (16-byte aligned), H float [batch, K, dim],
- * S float [batch, K, 16, 16] (fp32 products and accumulation),
- * row_status int32 [batch, K] or NULL: bit 0 non-finite score, bit 1 id out of range.
- * Errors: NULL pointers, batch < 1, K not in [1, 64], vocab < 16, dim not in
- *         {64, 128, 256, 512}, dtype, alignment.
+ * S float [batch, K, 16, 16], row_status int32 [batch, K] or NULL: bit 0 non-finite
+ * score, bit 1 id out of range (clamped to [0, vocab), never read out of bounds).
+ * Arithmetic: fp32 tables run on fp32 MFMA (fp32 products, fp32 sums).  bf16 tables
+ * run on bf16 MFMA: each A[prev_i, d] * H[d] is split into a nearest-bf16 part and the
+ * bf16 of its remainder (taken with a fused multiply-add), both multiplied exactly by
+ * the bf16 B value and summed in fp32, so each term is within about 2^-18 of its fp32
+ * value.  Every entry point that computes scores uses this arithmetic, bit for bit.
+ * Errors: NULL pointers, batch < 1, K not in [1, 64], vocab < 16, dim not a power of
+ *         two in [16, 1024] (DFLASH2_ERR_SHAPE), dtype, alignment.
  * ------------------------------------------------------------------------------- */
 dflash2_status dflash2_pair_score(const int32_t* cand_idx, const float* cand_val,
                                   const int32_t* verified, const void* emb_a, const void* emb_b,
@@ -219,14 +224,18 @@ dflash2_status dflash2_walk(const float* S, const int32_t* cand_idx, int64_t bat
                             float* q, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
- * Fused proposer step: topk16 -> pair_score -> walk in one call (three back-to-back
- * kernels on `stream`, no host synchronisation).  Same passages as the three calls
- * above; the outputs are bit-identical to calling dflash2_topk16 on every position's
- * logits row, then dflash2_pair_score, then dflash2_walk.  logits rows are addressed
- * as logits[(b*K + t)*ld + v].
+ * Fused proposer step: topk16 -> pair_score -> walk in one call (no host
+ * synchronisation).  Same passages as the three calls above; the outputs are
+ * bit-identical to calling dflash2_topk16 on every position's logits row, then
+ * dflash2_pair_score, then dflash2_walk.  logits rows are addressed as
+ * logits[(b*K + t)*ld + v].  Two kernels on `stream` when K <= 16 and K * dim <= 8192
+ * (one streams the logits; one block per request merges, scores and walks), three
+ * otherwise (the scores then take one wave per draft position and the walk its own
+ * kernel).
  *
- * row_status int32 [batch, K] or NULL (the union of the top-16 and pair-score bits).
- * Errors: the union of the three calls' checks, plus workspace.
+ * S must be 16-byte aligned.  row_status int32 [batch, K] or NULL (the union of the
+ * top-16 and pair-score bits).
+ * Errors: the union of the three calls' checks, S alignment, plus workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_select_workspace(int64_t batch, int64_t K, int64_t vocab);
 dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t* verified,
@@ -251,7 +260,8 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
  * order over `hidden` (deterministic, not bit-identical to it); every other output is
  * bit-identical to dflash2_select called with H = H_out.
  * Errors: the checks of dflash2_select and dflash2_context_gate, w_dtype other than
- *         DFLASH2_BF16 (DFLASH2_ERR_DTYPE), workspace.
+ *         DFLASH2_BF16 (DFLASH2_ERR_DTYPE), dim < 64 (the fused gate tiles are 64
+ *         columns wide; DFLASH2_ERR_SHAPE), H_out not 16-byte aligned, workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_select_gated_workspace(int64_t batch, int64_t K, int64_t vocab, int64_t hidden,
                                       int64_t dim);

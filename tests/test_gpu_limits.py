@@ -1,6 +1,8 @@
 """Parity at the limits of the C ABI: the largest draft block (K = 64), every selector
-width the pair kernels are built for (64, 128, 512 besides 256), fp32 and bf16 tables,
-the largest vocabulary (2^19) and a ragged one, through the C ABI against the oracle."""
+width the pair kernels are built for (the powers of two from 16 to 1024), both sides of
+the one-block-per-request limit of the select (K <= 16 and K x dim <= 8192), fp32 and
+bf16 tables, the largest vocabulary (2^19) and a ragged one, through the C ABI against
+the oracle."""
 
 import numpy as np
 import pytest
@@ -55,6 +57,36 @@ def test_select_k64_every_selector_width(d2, dim, bf16):
         S, st = d2.pair_score(idx, val, ver, Ag, Bg, Hg)
         tok, slots, q = d2.walk(S, idx, T, seed)
         for name, ref in (("S", S), ("tokens", tok), ("slots", slots), ("q", q)):
+            a, b = cpu(out[name]), cpu(ref)
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=name)
+
+
+@pytest.mark.parametrize("dim,K,bf16", [(16, 7, True), (16, 17, False), (32, 16, True), (32, 3, False),
+                                        (256, 16, True), (256, 17, True), (1024, 8, True), (1024, 9, False)])
+def test_select_selector_widths_and_block_limit(d2, dim, K, bf16):
+    """Each width with a draft block on either side of the one-block-per-request limit
+    (K <= 16 and K x dim <= 8192 run in one block per request, the rest in one wave per
+    position): the oracle's candidates, scores within tolerance, the walk teacher-forced,
+    and bit-identity with the three separate calls."""
+    w = synth.workload(0, B=3, K=K, V=3000, D=64, dim=dim, bf16_params=bf16, peak="decay")
+    inp = synth.make_inputs(w)
+    A64, B64, Ag, Bg, W64, Wg, wb = _tables(inp)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    Hg = d2.context_gate(to_gpu(inp["h"]), Wg, to_gpu(inp["bias"]))
+    ridx, rval = oracle.topk16(inp["logits_bits"])
+    Sref, Sabs, rst = oracle.pair_score(ridx, rval, inp["verified"], A64, B64, cpu(Hg).astype(np.float64))
+    for T, seed in ((0.0, 0), (1.3, 8)):
+        print(f"select dim={dim} K={K} bf16={bf16} T={T}", flush=True)
+        out = d2.select(logits, ver, Ag, Bg, Hg, T, seed)
+        np.testing.assert_array_equal(cpu(out["cand_idx"]), ridx)
+        assert_close_scaled(cpu(out["S"]), Sref, Sabs, what=f"S dim {dim} K {K}")
+        np.testing.assert_array_equal(cpu(out["row_status"]), rst)
+        check_walk(Sref, ridx, cpu(out["tokens"]), cpu(out["slots"]), cpu(out["q"]), T, seed)
+        idx, val = d2.topk16(logits)
+        S, st = d2.pair_score(idx, val, ver, Ag, Bg, Hg)
+        tok, slots, q = d2.walk(S, idx, T, seed)
+        for name, ref in (("S", S), ("tokens", tok), ("slots", slots), ("q", q), ("row_status", st)):
             a, b = cpu(out[name]), cpu(ref)
             np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                           b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=name)
