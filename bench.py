@@ -1,15 +1,20 @@
 """Throughput of the DFlash 2 proposer hot path on one MI355X.
 
-One step = the whole path over one batch: the gated select (context gate, top-16, pair
-score and walk in one C call: the gate's tiles run inside the launch that streams the
-logits, then two more kernels) -> two-tap conv -> greedy verify, on the batched
-greedy workload (B=15, K=7, V=151936, hidden 5120, selector dim 256).  Inputs are synthetic
-and already resident in HBM; logits and target logits rotate through >= 16 buffers
-(> 2x the 256 MB Infinity Cache) so the streams come from HBM.  The step sequence is
-captured once in a HIP graph (one graph = one pass over every rotating buffer) and
-replayed, so host launch overhead is not timed.
+The metric's step is one dflash2_select call over one batch: top-16 over every draft
+position's logits, the pair scores of adjacent candidates and the greedy walk, on the
+batched greedy workload (B=15, K=7, V=151936, selector dim 256; the gate vectors H are
+an input, computed beforehand by dflash2_context_gate).  Inputs are synthetic and
+already resident in HBM; the logits rotate through >= 16 buffers (> 2x the 256 MB
+Infinity Cache) so the stream comes from HBM.
 
-Prints one JSON line.  `value` = draft positions per second of the whole step.
+Timing protocol: the --steps calls (buffer i % nbuf for call i) are captured in one
+HIP graph and the --warmup calls in another; the warm-up graph runs once, then the
+timed graph is replayed 7 times, each replay bracketed by HIP events on the capture
+stream and a device synchronisation on both sides.  Per-step time = the median replay
+time / steps (the spread is reported).  The whole path (gated select, two-tap conv,
+greedy verify) is timed the same way as the named extra `whole_step`.
+
+Prints one JSON line.  `value` = draft positions per second of the select.
 """
 
 from __future__ import annotations
@@ -90,8 +95,20 @@ def cpu_baseline(inp, w, budget_s=12.0):
     dt = time.perf_counter() - t0
     return {"value": positions / dt, "unit": "draft positions/s", "cores": 1, "kind": "oracle",
             "sample": f"{reqs} whole requests ({positions} positions) of the B=15,K=7,V=151936 workload, "
-                      f"float64 numpy, one thread, {dt:.1f} s; host {platform.processor() or platform.machine()} "
-                      f"with {len(os.sched_getaffinity(0))} cores visible"}
+                      f"float64 numpy, one thread, {dt:.1f} s; host CPU {cpu_model()}, "
+                      f"{len(os.sched_getaffinity(0))} cores visible"}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (the machine type when absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def per_config_throughput(dflash2, torch, dev, stream, min_bytes=600 << 20):
@@ -176,14 +193,18 @@ def per_config_throughput(dflash2, torch, dev, stream, min_bytes=600 << 20):
             reps = max(2, 64 // n)
             with torch.cuda.stream(stream):
                 g.replay()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    g.replay()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (reps * n)
-            res[name + "_us"] = round(us, 2)
+            times = []
+            for _ in range(5):
+                torch.cuda.synchronize()
+                with torch.cuda.stream(stream):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        g.replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / (reps * n))
+            res[name + "_us"] = round(sorted(times)[2], 2)
         tb = 4 if not w.bf16_params else 2
         sel_bytes = algorithmic_select_bytes(B, K, V, dim, table_bytes=tb)
         res["select_positions_per_s"] = round(B * K / (res["select_us"] * 1e-6), 1)
@@ -364,31 +385,43 @@ def main():
             step(i)
     torch.cuda.synchronize()
 
-    def capture(fn):
+    def capture(fn, n):
+        """One graph of n calls fn(0..n-1) on the capture stream."""
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            for i in range(nbuf):
+            for i in range(n):
                 fn(i)
         return graph
 
-    def time_graph(fn, reps, warm):
-        """Microseconds per call of fn, over `reps` replays of a graph of nbuf calls."""
-        graph = capture(fn)
-        with torch.cuda.stream(stream):
-            for _ in range(warm):
-                graph.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                graph.replay()
-            e1.record(stream)
+    def timed_steps(fn, steps, warmup, repeats=7):
+        """Warm-up graph of `warmup` calls run once, then the graph of `steps` calls
+        replayed `repeats` times, each replay bracketed by HIP events on the capture
+        stream with a device synchronisation on both sides.  Returns the per-call
+        microseconds of every replay, sorted."""
+        timed = capture(fn, steps)
+        warm = capture(fn, warmup) if warmup > 0 else None
+        if warm is not None:
+            with torch.cuda.stream(stream):
+                warm.replay()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * nbuf)
+        out = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                timed.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return sorted(out)
 
-    reps_sel = max(1, args.steps // nbuf)
-    select_us = time_graph(lambda i: dflash2.select(logits[i], verified, A, Bt, H, 0.0, 0, out=sel), reps_sel,
-                           max(1, args.warmup // nbuf))
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+    t_wall = time.perf_counter()
+    sel_times = timed_steps(lambda i: dflash2.select(logits[i % nbuf], verified, A, Bt, H, 0.0, 0, out=sel), steps,
+                            warmup)
+    wall = time.perf_counter() - t_wall
+    select_us = sel_times[len(sel_times) // 2]
 
     sel_bytes = algorithmic_select_bytes(w.B, w.K, w.V, w.dim)
     achieved = sel_bytes / (select_us * 1e-6) / 1e9
@@ -399,8 +432,13 @@ def main():
                 "bytes_per_launch": sel_bytes, "avg_launch_us": round(select_us, 3)}
 
     if args.select_only:
-        print(json.dumps({"metric": METRIC, "select_us": select_us, "roofline": roofline}))
+        print(json.dumps({"metric": METRIC, "select_us": select_us, "select_us_repeats": sel_times,
+                          "roofline": roofline}))
         return
+
+    # the whole path: gated select (gate inside) -> conv2tap -> greedy verify
+    step_times = timed_steps(lambda i: step(i % nbuf), steps, warmup)
+    step_us = step_times[len(step_times) // 2]
 
     # every entry point on the same workload, each as its own graph of nbuf calls
     sel_t = {k: torch.empty_like(v) for k, v in sel.items()}
@@ -433,30 +471,14 @@ def main():
         if name.startswith("spec_accept_sampled") or name.startswith("spec_accept_filtered"):
             dflash2.select(logits[0], verified, A, Bt, H, 1.0, 7, out=sel_t)
             torch.cuda.synchronize()
-        components[name] = round(time_graph(fn, 3, 1), 2)
+        times = timed_steps(lambda i, fn=fn: fn(i % nbuf), 2 * nbuf, nbuf, repeats=5)
+        components[name] = round(times[len(times) // 2], 2)
 
-    step_graph = capture(step)
-    reps = max(1, args.steps // nbuf)
-    steps = reps * nbuf
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup // nbuf)):
-            step_graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(reps):
-            step_graph.replay()
-        s1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = s0.elapsed_time(s1) / steps
     positions = w.B * w.K
-    value = positions / (ms_per_step * 1e-3)
+    value = positions / (select_us * 1e-6)
 
-    # sanity: the graph's last select matches an eager call on the same buffer
-    ref = dflash2.select(logits[nbuf - 1], verified, A, Bt, H, 0.0, 0)
+    # sanity: the timed graph's last select matches an eager call on the same buffer
+    ref = dflash2.select(logits[(steps - 1) % nbuf], verified, A, Bt, H, 0.0, 0)
     torch.cuda.synchronize()
     assert torch.equal(ref["tokens"], sel["tokens"]) and torch.equal(ref["cand_idx"], sel["cand_idx"])
 
@@ -466,19 +488,23 @@ def main():
         "unit": "draft positions/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "warmup": warmup,
+        "ms_per_step": round(select_us * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "c2: batched greedy B=15 K=7 V=151936, hidden 5120, selector dim 256, bf16 logits "
-                               "and tables; step = gated select (gate + top-16 + pair score + walk) + conv2tap + greedy verify",
+        "config": {"workload": "c2: batched greedy selector B=15 K=7 V=151936, selector dim 256, bf16 logits and "
+                               "tables; step = dflash2_select (top-16 + pair score + greedy walk; gate vectors given)",
                    "global_batch": w.B, "draft_positions_per_step": positions, "rotating_buffers": nbuf},
-        "select_only": {"positions_per_s": round(positions / (select_us * 1e-6), 1), "avg_launch_us": round(select_us, 3),
-                        "hbm_frac": roofline["frac"]},
+        "timing": {"repeats": len(sel_times), "select_us_median": round(select_us, 3),
+                   "select_us_min": round(sel_times[0], 3), "select_us_max": round(sel_times[-1], 3)},
         "roofline": roofline,
+        "whole_step": {"what": "gated select (context gate + top-16 + pair score + walk) + conv2tap + greedy verify",
+                       "us_per_step": round(step_us, 3), "us_min": round(step_times[0], 3),
+                       "us_max": round(step_times[-1], 3),
+                       "positions_per_s": round(positions / (step_us * 1e-6), 1)},
         "components_us_per_call": components,
         "wall_s": round(wall, 3),
     }
