@@ -2,6 +2,7 @@
 // sizing, and dispatch to the kernel launchers.
 #include <math.h>
 
+#include <mutex>
 #include <new>
 
 #include "dflash2.h"
@@ -10,6 +11,13 @@
 #include "topk_dev.h"
 
 using namespace df2;
+
+// Scratch of dflash2_select_noalloc: one array per GPU, in the library's own device
+// memory (resident from the code object's load on that GPU to the end of the process),
+// shared by every call on that GPU.  Host code uses the address hipGetSymbolAddress
+// gives for the current device, never the array's name.
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -55,6 +63,41 @@ dflash2_status check_bk(int64_t batch, int64_t K) {
 dflash2_status check_temp(float t) {
   if (isnan(t) || isinf(t) || t < 0.f) return DFLASH2_ERR_VALUE;
   if (t > 0.f && t < 1.17549435e-38f) return DFLASH2_ERR_VALUE;
+  return DFLASH2_OK;
+}
+
+// The argument checks of dflash2_select (and of its variant without workspace).
+dflash2_status check_select(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                            const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab, int64_t dim, const float* H,
+                            int64_t batch, int64_t K, float temperature, const int32_t* cand_idx,
+                            const float* cand_val, const float* S, const int32_t* tokens, const int32_t* slots,
+                            const float* q) {
+  dflash2_status st = check_bk(batch, K);
+  if (st != DFLASH2_OK) return st;
+  st = check_logits(logits, batch * K, vocab, ld);
+  if (st != DFLASH2_OK) return st;
+  st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
+  if (st != DFLASH2_OK) return st;
+  if (!verified || !H || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
+  if (!aligned16(H) || !aligned16(S)) return DFLASH2_ERR_ALIGN;
+  return check_temp(temperature);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// This GPU's scratch address, looked up on the first call on each device.
+dflash2_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DFLASH2_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFLASH2_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
   return DFLASH2_OK;
 }
 
@@ -238,19 +281,32 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
                               int64_t batch, int64_t K, float temperature, uint64_t seed, int32_t* cand_idx,
                               float* cand_val, float* S, int32_t* tokens, int32_t* slots, float* q,
                               int32_t* row_status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  dflash2_status st = check_bk(batch, K);
-  if (st != DFLASH2_OK) return st;
-  st = check_logits(logits, batch * K, vocab, ld);
-  if (st != DFLASH2_OK) return st;
-  st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
-  if (st != DFLASH2_OK) return st;
-  if (!verified || !H || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
-  if (!aligned16(H) || !aligned16(S)) return DFLASH2_ERR_ALIGN;
-  st = check_temp(temperature);
+  dflash2_status st = check_select(logits, ld, verified, emb_a, emb_b, emb_dtype, vocab, dim, H, batch, K, temperature,
+                                   cand_idx, cand_val, S, tokens, slots, q);
   if (st != DFLASH2_OK) return st;
   SelectWs ws;
   st = carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_select(c, batch, K, vocab); }, &ws);
   if (st != DFLASH2_OK) return st;
+  return hip_status(launch_select(logits, ld, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab, (int)dim,
+                                  H, (int)batch, (int)K, temperature, seed, cand_idx, cand_val, S, tokens, slots, q,
+                                  row_status, ws, stream));
+}
+
+dflash2_status dflash2_select_noalloc(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
+                                      const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab, int64_t dim,
+                                      const float* H, int64_t batch, int64_t K, float temperature, uint64_t seed,
+                                      int32_t* cand_idx, float* cand_val, float* S, int32_t* tokens, int32_t* slots,
+                                      float* q, int32_t* row_status, hipStream_t stream) {
+  dflash2_status st = check_select(logits, ld, verified, emb_a, emb_b, emb_dtype, vocab, dim, H, batch, K, temperature,
+                                   cand_idx, cand_val, S, tokens, slots, q);
+  if (st != DFLASH2_OK) return st;
+  const size_t need = dflash2_select_workspace(batch, K, vocab);
+  if (need == 0 || need > kNoallocScratchBytes) return DFLASH2_ERR_WORKSPACE;
+  void* ws_base = nullptr;
+  st = noalloc_scratch(&ws_base);
+  if (st != DFLASH2_OK) return st;
+  Carver c(ws_base);
+  const SelectWs ws = carve_select(c, batch, K, vocab);
   return hip_status(launch_select(logits, ld, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab, (int)dim,
                                   H, (int)batch, (int)K, temperature, seed, cand_idx, cand_val, S, tokens, slots, q,
                                   row_status, ws, stream));

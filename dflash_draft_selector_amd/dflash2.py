@@ -54,6 +54,8 @@ _SIGNATURES = {
     "dflash2_select_workspace": ([_i64, _i64, _i64], _size),
     "dflash2_select": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _f32, _u64,
                         _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_select_noalloc": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _f32,
+                                _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr], _int),
     "dflash2_select_gated_workspace": ([_i64, _i64, _i64, _i64, _i64], _size),
     "dflash2_select_gated": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _c_ptr, _int, _c_ptr,
                               _i64, _int, _i64, _i64, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -382,6 +384,40 @@ def select(logits, verified, emb_a, emb_b, H, temperature: float = 0.0, seed: in
                               _ptr(out["cand_val"]), _ptr(out["S"]), _ptr(out["tokens"]), _ptr(out["slots"]),
                               _ptr(out["q"]), _ptr(out["row_status"]), _ptr(ws), ws.numel(), _stream()),
            "dflash2_select")
+    return out
+
+
+def select_noalloc(logits, verified, emb_a, emb_b, H, temperature: float = 0.0, seed: int = 0,
+                   out: dict | None = None):
+    """select() through dflash2_select_noalloc: the library's own per-GPU scratch instead
+    of a workspace (no device allocation by the library; with `out` given, none at all).
+    Calls that overlap on one GPU race on that scratch."""
+    lib = load_library()
+    dev = logits.device
+    _need(logits, "logits", _BF16_LIKE)
+    rows, V, ld = _rows_view(logits, "logits")
+    B, K = logits.shape[0], logits.shape[1]
+    _contig(_need(verified, "verified", (torch.int32,), dev), "verified")
+    _contig(_need(emb_a, "emb_a", (torch.float32,) + _BF16_LIKE, dev), "emb_a")
+    _contig(_need(emb_b, "emb_b", (torch.float32,) + _BF16_LIKE, dev), "emb_b")
+    _contig(_need(H, "H", (torch.float32,), dev), "H")
+    dim = emb_a.shape[1]
+    if out is None:
+        out = {
+            "cand_idx": torch.empty((B, K, NCAND), dtype=torch.int32, device=dev),
+            "cand_val": torch.empty((B, K, NCAND), dtype=torch.float32, device=dev),
+            "S": torch.empty((B, K, NCAND, NCAND), dtype=torch.float32, device=dev),
+            "tokens": torch.empty((B, K), dtype=torch.int32, device=dev),
+            "slots": torch.empty((B, K), dtype=torch.int32, device=dev),
+            "q": torch.empty((B, K, NCAND), dtype=torch.float32, device=dev),
+            "row_status": torch.empty((B, K), dtype=torch.int32, device=dev),
+        }
+    _check(lib.dflash2_select_noalloc(_ptr(logits), ld, _ptr(verified), _ptr(emb_a), _ptr(emb_b),
+                                      _emb_dtype(emb_a, emb_b), V, dim, _ptr(H), B, K, float(temperature),
+                                      int(seed) & (2 ** 64 - 1), _ptr(out["cand_idx"]), _ptr(out["cand_val"]),
+                                      _ptr(out["S"]), _ptr(out["tokens"]), _ptr(out["slots"]), _ptr(out["q"]),
+                                      _ptr(out["row_status"]), _stream()),
+           "dflash2_select_noalloc")
     return out
 
 

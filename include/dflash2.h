@@ -247,6 +247,29 @@ dflash2_status dflash2_select(const uint16_t* logits, int64_t ld, const int32_t*
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * dflash2_select without a workspace argument, for callers that cannot allocate device
+ * memory (code recorded under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments (minus workspace and workspace_bytes), same outputs, bit
+ * for bit, and the same kernels as dflash2_select.
+ *
+ * Its scratch is a 4 MiB array in the library's own device memory, one per GPU, held
+ * from the library's load on that GPU until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams, other host
+ * threads) race: the caller serialises them.  The array needs no initialisation (every
+ * call writes the scratch it reads).
+ * Errors: those of dflash2_select; a request whose dflash2_select_workspace exceeds
+ *         4 MiB (above about 2000 draft positions, batch x K, at the largest vocabulary)
+ *         -> DFLASH2_ERR_WORKSPACE; the scratch address not obtainable -> DFLASH2_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+dflash2_status dflash2_select_noalloc(const uint16_t* logits, int64_t ld, const int32_t* verified,
+                                      const void* emb_a, const void* emb_b, dflash2_dtype emb_dtype,
+                                      int64_t vocab, int64_t dim, const float* H, int64_t batch,
+                                      int64_t K, float temperature, uint64_t seed, int32_t* cand_idx,
+                                      float* cand_val, float* S, int32_t* tokens, int32_t* slots,
+                                      float* q, int32_t* row_status, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * Gated proposer step: context gate -> topk16 -> pair_score -> walk in one call.
  * The passages of dflash2_context_gate and dflash2_select.  The gate's bf16 matrix
  * product runs inside the launch that streams the logits (on compute units the stream

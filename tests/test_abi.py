@@ -205,3 +205,17 @@ def test_temperature_range_on_host():
                                        16, NULL) == 6, T
     for T in (0.0, flt_min, 1e-30, 1.0, 3.0e38):
         assert sel(T) == 5, T
+
+
+def test_select_noalloc_refuses_requests_beyond_its_scratch():
+    """The select without workspace checks its request against the 4 MiB scratch on the
+    host: a request whose workspace would exceed it returns DFLASH2_ERR_WORKSPACE before
+    any HIP call; the other argument checks are those of dflash2_select."""
+    d2, lib = _lib()
+    sel = lambda B, K, V=151936, T=0.0, S=FAKE: lib.dflash2_select_noalloc(
+        FAKE, V, FAKE, FAKE, FAKE, 1, V, 256, FAKE, B, K, T, 0, FAKE, FAKE, S, FAKE, FAKE, FAKE, NULL, NULL)
+    assert lib.dflash2_select_workspace(64, 64, 1 << 19) > 4 << 20
+    assert sel(64, 64, 1 << 19) == 5
+    assert sel(1, 0) == 2
+    assert sel(15, 7, T=-1.0) == 6
+    assert sel(15, 7, S=MIS) == 3
