@@ -1,7 +1,8 @@
 """Parity of libdflash2 (HIP, gfx950) with the CPU oracle, through the C ABI.
 
-Sizes: the tiny workload c0 and the full single-GPU workloads c1, c2, c4 in full, c3
-on sampled rows; ragged vocabularies and degenerate rows for the edge cases.
+Sizes: the tiny workload c0 and the full single-GPU workloads c1, c2, c4 in full; c3 with
+the candidates and gate of all 960 rows and the scores and walk of 16 requests; ragged
+vocabularies and degenerate rows for the edge cases.
 """
 
 import numpy as np
@@ -299,8 +300,8 @@ def test_select_gated_ragged(d2):
 
 
 def test_select_gated_many_rows(d2):
-    """The gated select at c3's 960 rows: H_out within tolerance on
-    sampled rows, and every output bit-identical to dflash2_select on that H."""
+    """The gated select at c3's 960 rows: H_out within tolerance on every row, and every
+    output bit-identical to dflash2_select on that H."""
     import torch
     w = synth.workload(3)
     inp = inputs(3)
@@ -311,9 +312,8 @@ def test_select_gated_many_rows(d2):
     Hout = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=logits.device)
     out = d2.select_gated(logits, ver, Ag, Bg, to_gpu(inp["h"]), Wg, to_gpu(inp["bias"]), "sigmoid", 0.0, 0,
                           H_out=Hout)
-    rows = np.r_[0:40, 400:440, 920:960]
-    Href, _, pre_abs = oracle.context_gate(inp["h"].reshape(-1, w.D)[rows], W64, inp["bias"], True)
-    assert_close_scaled(cpu(Hout).reshape(-1, w.dim)[rows], Href, 0.25 * pre_abs, what="gated H c3")
+    Href, _, pre_abs = oracle.context_gate(inp["h"].reshape(-1, w.D), W64, inp["bias"], True)
+    assert_close_scaled(cpu(Hout).reshape(-1, w.dim), Href, 0.25 * pre_abs, what="gated H c3")
     ref = d2.select(logits, ver, Ag, Bg, Hout, 0.0, 0)
     for k in ref:
         a, b = cpu(out[k]), cpu(ref[k])
@@ -321,22 +321,26 @@ def test_select_gated_many_rows(d2):
                                       b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
 
 
-def test_select_c3_sampled_rows(d2):
+def test_select_c3_all_rows(d2):
+    """c3 (B 64, K 15, V 151936): the top-16 of all 960 rows bit-exact against the
+    oracle's full sort; the scores and the walk (teacher-forced) of 16 requests spread
+    over the batch; every request's tokens are its slots' candidates."""
     w = synth.workload(3)
     inp = inputs(3)
-    print("select c3 (sampled requests)", flush=True)
+    print("select c3 (all 960 rows)", flush=True)
     Hg, out = _run_select(d2, inp, w, 0.0, 0)
-    reqs = [0, 17, 63]
-    sub = inp["logits_bits"][reqs]
-    ridx, rval = oracle.topk16(sub)
-    np.testing.assert_array_equal(cpu(out["cand_idx"])[reqs], ridx)
+    ridx, rval = oracle.topk16(inp["logits_bits"])
+    np.testing.assert_array_equal(cpu(out["cand_idx"]), ridx)
+    np.testing.assert_array_equal(cpu(out["cand_val"]).astype(np.float64), rval)
+    reqs = list(range(0, w.B, 4))
     W64, _, _ = gate_w(inp)
     H, _, _ = oracle.context_gate(inp["h"][reqs].reshape(-1, w.D), W64, inp["bias"], True)
     A64, B64, _, _ = tables(inp)
-    Sref, Sabs, _ = oracle.pair_score(ridx, rval, inp["verified"][reqs], A64, B64, H.reshape(len(reqs), w.K, -1))
+    Sref, Sabs, rst = oracle.pair_score(ridx[reqs], rval[reqs], inp["verified"][reqs], A64, B64,
+                                        H.reshape(len(reqs), w.K, -1))
     assert_close_scaled(cpu(out["S"])[reqs], Sref, Sabs, what="c3 S")
-    check_walk(Sref, ridx, cpu(out["tokens"])[reqs], cpu(out["slots"])[reqs], cpu(out["q"])[reqs], 0.0, 0)
-    # every request: the walk is consistent with the library's own candidates
+    np.testing.assert_array_equal(cpu(out["row_status"])[reqs], rst)
+    check_walk(Sref, ridx[reqs], cpu(out["tokens"])[reqs], cpu(out["slots"])[reqs], cpu(out["q"])[reqs], 0.0, 0)
     tok, cand, slots = cpu(out["tokens"]), cpu(out["cand_idx"]), cpu(out["slots"])
     np.testing.assert_array_equal(tok, np.take_along_axis(cand, slots[..., None], axis=2)[..., 0])
 
