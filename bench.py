@@ -222,6 +222,75 @@ def per_config_throughput(dflash2, torch, dev, stream, min_bytes=600 << 20):
     return out
 
 
+def gate_measure(dflash2, torch, dev, stream, calls=32):
+    """The standalone context gate (dflash2_context_gate) on the gate shapes of the
+    workloads: 105 rows (B 15 x K 7) and 960 rows (B 64 x K 15) of hidden 5120 into 256
+    gate dims, with a bf16 weight (bf16 MFMA) and fp32 h, bf16 h, and an fp32 weight
+    (fp32 MFMA); and the gated select against the plain select at both sizes, whose
+    difference is what the fused gate adds to the step.  Each case is a graph of `calls`
+    calls with the same inputs (the weight is re-read every step in serving, so it is
+    cache-warm here too), median of 5 replays."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    D, dim, V = 5120, 256, 151936
+    out = {}
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(calls):
+                fn()
+        with torch.cuda.stream(stream):
+            g.replay()
+        times = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / calls)
+        return sorted(times)[2]
+
+    for B, K in ((15, 7), (64, 15)):
+        rows = B * K
+        h = torch.randn((B, K, D), generator=gen, device=dev)
+        hb = h.to(torch.bfloat16)
+        W = torch.randn((dim, D), generator=gen, device=dev) * (1.0 / D) ** 0.5
+        Wb = W.to(torch.bfloat16)
+        bias = torch.zeros(dim, device=dev)
+        H = torch.empty((B, K, dim), dtype=torch.float32, device=dev)
+        flops = 2.0 * rows * dim * D
+        for name, hh, WW in (("bf16_w_fp32_h", h, Wb), ("bf16_w_bf16_h", hb, Wb), ("fp32_w_fp32_h", h, W)):
+            us = timed(lambda: dflash2.context_gate(hh, WW, bias, out=H))
+            nbytes = rows * D * hh.element_size() + dim * D * WW.element_size() + rows * dim * 4
+            peak = 2500.0 if WW.dtype == torch.bfloat16 else 157.3
+            out[f"rows{rows}_{name}"] = {
+                "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / peak, 4),
+                "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                # the MFMA share of peak the kernel could reach if it streamed its bytes at the HBM peak
+                "mfma_ceiling_at_hbm_peak": round(min(1.0, (flops / (peak * 1e12)) / (nbytes / (HBM_PEAK_GBS * 1e9))), 4)}
+        logits = (torch.randn((B, K, V), generator=gen, device=dev) * 3.0).to(torch.bfloat16)
+        A = (torch.randn((V, dim), generator=gen, device=dev) / 16.0).to(torch.bfloat16)
+        Bt = (torch.randn((V, dim), generator=gen, device=dev) / 16.0).to(torch.bfloat16)
+        verified = torch.randint(0, V, (B,), generator=gen, device=dev, dtype=torch.int32)
+        sel = dflash2.select(logits, verified, A, Bt, H, 0.0, 0)
+        us_sel = timed(lambda: dflash2.select(logits, verified, A, Bt, H, 0.0, 0, out=sel))
+        us_gated = timed(lambda: dflash2.select_gated(logits, verified, A, Bt, h, Wb, bias, "sigmoid", 0.0, 0, out=sel,
+                                                      H_out=H))
+        out[f"rows{rows}_select_us"] = round(us_sel, 2)
+        out[f"rows{rows}_select_gated_us"] = round(us_gated, 2)
+        del h, hb, W, Wb, logits, A, Bt
+        torch.cuda.empty_cache()
+    return out
+
+
 def lmhead_measure(dflash2, torch, dev, stream, reps=10):
     """The LM head with the fused top-16 at the B=15, K=7 row count (105 rows), hidden
     5120, the Qwen vocabulary: inputs drawn on the GPU (h ~ N(0, 1), W ~ N(0, 1/5120),
@@ -318,6 +387,7 @@ def main():
     ap.add_argument("--select-only", action="store_true", help="time only the select graph (for profiling)")
     ap.add_argument("--ring-only", action="store_true", help="time only the K/V ring attention (for profiling)")
     ap.add_argument("--lmhead-only", action="store_true", help="time only the fused LM head + top-16 (for profiling)")
+    ap.add_argument("--gate-only", action="store_true", help="time only the context gate and the gated select")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 1 GiB buffer three times (a kernel of known traffic, to scale memory counters)")
     args = ap.parse_args()
@@ -342,6 +412,9 @@ def main():
         del src, dst
     if args.ring_only:
         print(json.dumps({"metric": METRIC, "ring_attention": ring_measure(dflash2, torch, dev, torch.cuda.Stream())}))
+        return
+    if args.gate_only:
+        print(json.dumps({"metric": METRIC, "context_gate": gate_measure(dflash2, torch, dev, torch.cuda.Stream())}))
         return
     if args.lmhead_only:
         print(json.dumps({"metric": METRIC, "lmhead_topk16": lmhead_measure(dflash2, torch, dev, torch.cuda.Stream())}))

@@ -225,10 +225,11 @@ size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim)
   return c.off + 256;
 }
 
-dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dtype w_dtype, const float* bias,
-                                    int64_t rows, int64_t hidden, int64_t dim, dflash2_gate_act act, float* H,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+dflash2_status dflash2_context_gate(const void* h, dflash2_dtype h_dtype, const void* w_h, dflash2_dtype w_dtype,
+                                    const float* bias, int64_t rows, int64_t hidden, int64_t dim, dflash2_gate_act act,
+                                    float* H, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!h || !w_h || !H) return DFLASH2_ERR_NULL;
+  if (h_dtype != DFLASH2_F32 && h_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
   if (w_dtype != DFLASH2_F32 && w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
   if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
   if (rows < 1 || rows > ((int64_t)1 << 30) || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24) ||
@@ -241,8 +242,8 @@ dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dty
   dflash2_status st =
       carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_gate(c, rows, hidden, dim); }, &ws);
   if (st != DFLASH2_OK) return st;
-  return hip_status(launch_gate(h, w_h, w_dtype == DFLASH2_BF16, bias, (int)rows, (int)hidden, (int)dim, (int)act, H,
-                                ws, stream));
+  return hip_status(launch_gate(h, h_dtype == DFLASH2_BF16, w_h, w_dtype == DFLASH2_BF16, bias, (int)rows,
+                                (int)hidden, (int)dim, (int)act, H, ws, stream));
 }
 
 dflash2_status dflash2_pair_score(const int32_t* cand_idx, const float* cand_val, const int32_t* verified,
@@ -321,8 +322,8 @@ size_t dflash2_select_gated_workspace(int64_t batch, int64_t K, int64_t vocab, i
 
 dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
                                     const void* emb_b, dflash2_dtype emb_dtype, int64_t vocab, int64_t dim,
-                                    const float* h, const void* w_h, dflash2_dtype w_dtype, const float* bias,
-                                    int64_t hidden, dflash2_gate_act act, int64_t batch, int64_t K,
+                                    const void* h, dflash2_dtype h_dtype, const void* w_h, dflash2_dtype w_dtype,
+                                    const float* bias, int64_t hidden, dflash2_gate_act act, int64_t batch, int64_t K,
                                     float temperature, uint64_t seed, float* H_out, int32_t* cand_idx,
                                     float* cand_val, float* S, int32_t* tokens, int32_t* slots, float* q,
                                     int32_t* row_status, void* workspace, size_t workspace_bytes,
@@ -334,7 +335,7 @@ dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const in
   st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
   if (st != DFLASH2_OK) return st;
   if (!verified || !h || !w_h || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
-  if (w_dtype != DFLASH2_BF16) return DFLASH2_ERR_DTYPE;
+  if (w_dtype != DFLASH2_BF16 || (h_dtype != DFLASH2_F32 && h_dtype != DFLASH2_BF16)) return DFLASH2_ERR_DTYPE;
   if (act != DFLASH2_GATE_SIGMOID && act != DFLASH2_GATE_IDENTITY) return DFLASH2_ERR_DTYPE;
   // the fused gate tiles are 64 columns wide
   if (dim < 64 || hidden < 8 || hidden % 8 != 0 || hidden > ((int64_t)1 << 24)) return DFLASH2_ERR_SHAPE;
@@ -349,9 +350,9 @@ dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const in
                      [&](Carver& c) { return carve_select_gated(c, batch, K, vocab, hidden, dim); }, &ws);
   if (st != DFLASH2_OK) return st;
   return hip_status(launch_select_gated(logits, ld, verified, emb_a, emb_b, emb_dtype == DFLASH2_BF16, (int)vocab,
-                                        (int)dim, h, static_cast<const uint16_t*>(w_h), bias, (int)hidden, (int)act,
-                                        (int)batch, (int)K, temperature, seed, H_out, cand_idx, cand_val, S, tokens,
-                                        slots, q, row_status, ws, stream));
+                                        (int)dim, h, h_dtype == DFLASH2_BF16, static_cast<const uint16_t*>(w_h), bias,
+                                        (int)hidden, (int)act, (int)batch, (int)K, temperature, seed, H_out, cand_idx,
+                                        cand_val, S, tokens, slots, q, row_status, ws, stream));
 }
 
 dflash2_status dflash2_conv2tap(const float* x, const float* x_prev, const float* taps, int64_t sites, int64_t batch,

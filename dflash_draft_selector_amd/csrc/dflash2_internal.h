@@ -93,7 +93,7 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
                          hipStream_t s);
 
 hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
-                               const void* emb_b, bool bf16, int vocab, int dim, const float* h,
+                               const void* emb_b, bool bf16, int vocab, int dim, const void* h, bool h_bf16,
                                const uint16_t* w_h, const float* bias, int hidden, int act, int batch, int K,
                                float temperature, uint64_t seed, float* H_out, int32_t* cand_idx, float* cand_val,
                                float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
@@ -108,8 +108,8 @@ hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const
                                  int nq, int hq, int hkv, int ring, int window, float scale, int nsplit, RingWs ws,
                                  float* out, hipStream_t s);
 
-hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden,
-                       int dim, int act, float* H, GateWs ws, hipStream_t s);
+hipError_t launch_gate(const void* h, bool h_bf16, const void* w_h, bool w_bf16, const float* bias, int rows,
+                       int hidden, int dim, int act, float* H, GateWs ws, hipStream_t s);
 
 hipError_t launch_conv2tap(const float* x, const float* x_prev, const float* taps, int64_t sites, int64_t batch,
                            int K, int64_t hidden, int64_t group, float* y, hipStream_t s);

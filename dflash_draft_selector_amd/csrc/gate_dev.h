@@ -1,8 +1,9 @@
 // Context gate tiles H = act(W_H h + b) (pegainfer issue "DFlash 2 proposer", section
 // "What upstream shipped", item 1: 256-dim token embeddings + context gate).
 //
-// bf16 weight: h is rounded to bf16 (nearest even) as it is loaded and the product
-// runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  A work-group owns a 16-row
+// h comes as fp32 or as bf16 (HB).  bf16 weight: fp32 h is rounded to bf16 (nearest
+// even) as it is loaded, bf16 h goes in as it is, and the product runs on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  A work-group owns a 16-row
 // x (16 NB)-column output tile over one slice of the hidden dimension; its NW waves take
 // interleaved 32-wide steps of the slice and their partial tiles are summed in LDS in
 // wave order.  With several slices the tile is stored as a partial sum and the slices
@@ -30,8 +31,8 @@ __host__ __device__ __forceinline__ void gate_slice(int hidden, int split, int n
 // Tile (mt, nt) of slice `split`; red = LDS [NW][16][16 NB].  With nsplit == 1 and H
 // given it writes H (bias and activation applied), else partial[split][row][col].  The
 // first NW * 64 threads of the block call it.
-template <int NB, int NW, int ROUND>
-__device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uint16_t* __restrict__ w,
+template <int NB, int NW, int ROUND, bool HB>
+__device__ __forceinline__ void gate_tile(const void* __restrict__ h, const uint16_t* __restrict__ w,
                                           const float* __restrict__ bias, int rows, int hidden, int dim, int act,
                                           int mt, int nt, int split, int nsplit, float* red, float* __restrict__ H,
                                           float* __restrict__ partial) {
@@ -44,7 +45,9 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
 
   const int arow = mt * 16 + r16;
   const bool arow_ok = arow < rows;
-  const float* hrow = h + (size_t)(arow_ok ? arow : 0) * hidden;
+  const size_t hoff = (size_t)(arow_ok ? arow : 0) * hidden;
+  const float* hrow = static_cast<const float*>(h) + hoff;
+  const uint16_t* hrow16 = static_cast<const uint16_t*>(h) + hoff;
   const uint16_t* wcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) wcol[j] = w + (size_t)(nt * kCols + j * 16 + r16) * hidden;
@@ -55,6 +58,7 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
 
   for (int base = s0 + wv; base < s1; base += NW * ROUND) {
     f32x4 x0[ROUND], x1[ROUND];
+    u32x4 xb[ROUND];
     u32x4 bw[ROUND][NB];
 #pragma unroll
     for (int i = 0; i < ROUND; ++i) {
@@ -62,9 +66,14 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
       const int k = st * 32 + g * 8;
       const bool kok = st < s1 && k < hidden;
       x0[i] = x1[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      xb[i] = (u32x4){0u, 0u, 0u, 0u};
       if (kok && arow_ok) {
-        x0[i] = *reinterpret_cast<const f32x4*>(hrow + k);
-        x1[i] = *reinterpret_cast<const f32x4*>(hrow + k + 4);
+        if constexpr (HB) {
+          xb[i] = *reinterpret_cast<const u32x4*>(hrow16 + k);
+        } else {
+          x0[i] = *reinterpret_cast<const f32x4*>(hrow + k);
+          x1[i] = *reinterpret_cast<const f32x4*>(hrow + k + 4);
+        }
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -74,11 +83,13 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
     }
 #pragma unroll
     for (int i = 0; i < ROUND; ++i) {
-      u32x4 a;
-      a.x = pack_bf16x2(x0[i].x, x0[i].y);
-      a.y = pack_bf16x2(x0[i].z, x0[i].w);
-      a.z = pack_bf16x2(x1[i].x, x1[i].y);
-      a.w = pack_bf16x2(x1[i].z, x1[i].w);
+      u32x4 a = xb[i];
+      if constexpr (!HB) {
+        a.x = pack_bf16x2(x0[i].x, x0[i].y);
+        a.y = pack_bf16x2(x0[i].z, x0[i].w);
+        a.z = pack_bf16x2(x1[i].x, x1[i].y);
+        a.w = pack_bf16x2(x1[i].z, x1[i].w);
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -111,9 +122,10 @@ __device__ __forceinline__ void gate_tile(const float* __restrict__ h, const uin
 // In step st lane l loads h[row][16 st + 4 g .. + 3] and W[col][16 st + 4 g .. + 3]
 // (g = l / 16, row / col = l % 16 of the tile) and feeds component j of both to MFMA j,
 // so the four MFMAs of a step contract over all 16 of its hidden indices (a permutation
-// of the sum, exact up to fp32 rounding order).
-template <int NB, int NW, int ROUND>
-__device__ __forceinline__ void gate_tile_f32(const float* __restrict__ h, const float* __restrict__ w,
+// of the sum, exact up to fp32 rounding order).  bf16 h (HB) is widened to fp32, which
+// is exact.
+template <int NB, int NW, int ROUND, bool HB>
+__device__ __forceinline__ void gate_tile_f32(const void* __restrict__ h, const float* __restrict__ w,
                                               const float* __restrict__ bias, int rows, int hidden, int dim,
                                               int act, int mt, int nt, int split, int nsplit, float* red,
                                               float* __restrict__ H, float* __restrict__ partial) {
@@ -126,7 +138,9 @@ __device__ __forceinline__ void gate_tile_f32(const float* __restrict__ h, const
 
   const int arow = mt * 16 + r16;
   const bool arow_ok = arow < rows;
-  const float* hrow = h + (size_t)(arow_ok ? arow : 0) * hidden;
+  const size_t hoff = (size_t)(arow_ok ? arow : 0) * hidden;
+  const float* hrow = static_cast<const float*>(h) + hoff;
+  const uint16_t* hrow16 = static_cast<const uint16_t*>(h) + hoff;
   const float* wcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) wcol[j] = w + (size_t)(nt * kCols + j * 16 + r16) * hidden;
@@ -144,7 +158,14 @@ __device__ __forceinline__ void gate_tile_f32(const float* __restrict__ h, const
       const int k = st * 16 + g * 4;
       const bool kok = st < s1 && k < hidden;
       x[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (kok && arow_ok) x[i] = *reinterpret_cast<const f32x4*>(hrow + k);
+      if (kok && arow_ok) {
+        if constexpr (HB) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(hrow16 + k);
+          x[i] = (f32x4){bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        } else {
+          x[i] = *reinterpret_cast<const f32x4*>(hrow + k);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         y[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};

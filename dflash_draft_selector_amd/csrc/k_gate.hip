@@ -38,9 +38,9 @@ GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim) {
   return w;
 }
 
-// NB = 16-column blocks of the tile (tile width 16 * NB = min(dim, 64)).
-template <int NB>
-__global__ void __launch_bounds__(kGateThreads) k_gate_bf16(const float* __restrict__ h, const uint16_t* __restrict__ w,
+// NB = 16-column blocks of the tile (tile width 16 * NB = min(dim, 64)); HB = h in bf16.
+template <int NB, bool HB>
+__global__ void __launch_bounds__(kGateThreads) k_gate_bf16(const void* __restrict__ h, const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int rows, int hidden,
                                                             int dim, int act, int ntiles, int nsplit,
                                                             float* __restrict__ H, float* __restrict__ partial) {
@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(kGateThreads) k_gate_bf16(const float* __restr
   const int rem = blockIdx.x - mt * per;
   const int nt = rem / nsplit;
   const int split = rem - nt * nsplit;
-  gate_tile<NB, kGateWaves, kGateRound>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H, partial);
+  gate_tile<NB, kGateWaves, kGateRound, HB>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H, partial);
 }
 
 // Sum of the slices in slice order, then bias and activation: one thread per output.
@@ -63,8 +63,8 @@ __global__ void __launch_bounds__(256) k_gate_finish(const float* __restrict__ p
   H[e] = gate_finish(partial, bias, (int)(n_out / dim), dim, nsplit, act, row, n);
 }
 
-template <int NB>
-__global__ void __launch_bounds__(kGateThreads) k_gate_f32(const float* __restrict__ h, const float* __restrict__ w,
+template <int NB, bool HB>
+__global__ void __launch_bounds__(kGateThreads) k_gate_f32(const void* __restrict__ h, const float* __restrict__ w,
                                                            const float* __restrict__ bias, int rows, int hidden, int dim,
                                                            int act, int ntiles, int nsplit, float* __restrict__ H,
                                                            float* __restrict__ partial) {
@@ -74,26 +74,32 @@ __global__ void __launch_bounds__(kGateThreads) k_gate_f32(const float* __restri
   const int rem = blockIdx.x - mt * per;
   const int nt = rem / nsplit;
   const int split = rem - nt * nsplit;
-  gate_tile_f32<NB, kGateWaves, kGateRound>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H,
+  gate_tile_f32<NB, kGateWaves, kGateRound, HB>(h, w, bias, rows, hidden, dim, act, mt, nt, split, nsplit, red, H,
                                             partial);
 }
 
-hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float* bias, int rows, int hidden, int dim,
-                       int act, float* H, GateWs ws, hipStream_t s) {
+hipError_t launch_gate(const void* h, bool h_bf16, const void* w_h, bool w_bf16, const float* bias, int rows,
+                       int hidden, int dim, int act, float* H, GateWs ws, hipStream_t s) {
   const int ct = gate_coltile(dim);
   const int ntiles = dim / ct;
   const int mtiles = (rows + 15) / 16;
   const int nsplit = ws.nsplit;
   const dim3 grid((unsigned)((long long)mtiles * ntiles * nsplit));
   const dim3 blk(kGateThreads);
-#define DF2_GATE(NB)                                                                                               \
-  case NB:                                                                                                         \
-    if (w_bf16)                                                                                                    \
-      hipLaunchKernelGGL(k_gate_bf16<NB>, grid, blk, 0, s, h, static_cast<const uint16_t*>(w_h), bias, rows, hidden, \
-                         dim, act, ntiles, nsplit, H, ws.partial);                                                 \
-    else                                                                                                           \
-      hipLaunchKernelGGL(k_gate_f32<NB>, grid, blk, 0, s, h, static_cast<const float*>(w_h), bias, rows, hidden,    \
-                         dim, act, ntiles, nsplit, H, ws.partial);                                                 \
+#define DF2_GATE_HB(NB, HB)                                                                                        \
+  if (w_bf16)                                                                                                      \
+    hipLaunchKernelGGL((k_gate_bf16<NB, HB>), grid, blk, 0, s, h, static_cast<const uint16_t*>(w_h), bias, rows,   \
+                       hidden, dim, act, ntiles, nsplit, H, ws.partial);                                           \
+  else                                                                                                             \
+    hipLaunchKernelGGL((k_gate_f32<NB, HB>), grid, blk, 0, s, h, static_cast<const float*>(w_h), bias, rows,       \
+                       hidden, dim, act, ntiles, nsplit, H, ws.partial);
+#define DF2_GATE(NB)           \
+  case NB:                     \
+    if (h_bf16) {              \
+      DF2_GATE_HB(NB, true)    \
+    } else {                   \
+      DF2_GATE_HB(NB, false)   \
+    }                          \
     break;
   switch (ct / 16) {
     DF2_GATE(1)
@@ -103,6 +109,7 @@ hipError_t launch_gate(const float* h, const void* w_h, bool w_bf16, const float
       return hipErrorInvalidValue;
   }
 #undef DF2_GATE
+#undef DF2_GATE_HB
   if (nsplit > 1) {
     const long long n = (long long)rows * dim;
     hipLaunchKernelGGL(k_gate_finish, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws.partial, bias, n, dim,

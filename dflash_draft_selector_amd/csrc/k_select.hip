@@ -92,10 +92,11 @@ union ChunkGateShared {
   float red[kTopkWaves * 16 * kFusedGateCols];
 };
 
+template <bool HB>
 __global__ void __launch_bounds__(kTopkThreads) k_chunk_gate(const uint16_t* __restrict__ logits, int64_t ld, int V,
                                                              int nchunks, int nchunk_blocks,
                                                              unsigned long long* __restrict__ partials,
-                                                             const float* __restrict__ h,
+                                                             const void* __restrict__ h,
                                                              const uint16_t* __restrict__ w_h, int rows, int hidden,
                                                              int dim, int ntiles, int nsplit,
                                                              float* __restrict__ gate_partial) {
@@ -111,7 +112,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_chunk_gate(const uint16_t* __r
   const int rem = gb - mt * per;
   const int nt = rem / nsplit;
   const int split = rem - nt * nsplit;
-  gate_tile<kFusedGateCols / 16, kTopkWaves, kFusedGateSteps>(h, w_h, nullptr, rows, hidden, dim, 0, mt, nt, split,
+  gate_tile<kFusedGateCols / 16, kTopkWaves, kFusedGateSteps, HB>(h, w_h, nullptr, rows, hidden, dim, 0, mt, nt, split,
                                                               nsplit, sm.red, nullptr, gate_partial);
 }
 
@@ -498,7 +499,7 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
 }
 
 hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified, const void* emb_a,
-                               const void* emb_b, bool bf16, int vocab, int dim, const float* h,
+                               const void* emb_b, bool bf16, int vocab, int dim, const void* h, bool h_bf16,
                                const uint16_t* w_h, const float* bias, int hidden, int act, int batch, int K,
                                float temperature, uint64_t seed, float* H_out, int32_t* cand_idx, float* cand_val,
                                float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
@@ -509,8 +510,9 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
   const int nchunk_blocks = rows * nchunks;
   const int ntiles = dim / kFusedGateCols;
   const long long blocks = (long long)nchunk_blocks + fused_gate_blocks(rows, hidden, dim);
-  hipLaunchKernelGGL(k_chunk_gate, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, ld, vocab, nchunks,
-                     nchunk_blocks, ws.sel.topk.partials, h, w_h, rows, hidden, dim, ntiles, ws.nsplit, ws.partial);
+  hipLaunchKernelGGL(h_bf16 ? k_chunk_gate<true> : k_chunk_gate<false>, dim3((unsigned)blocks), dim3(kTopkThreads), 0,
+                     s, logits, ld, vocab, nchunks, nchunk_blocks, ws.sel.topk.partials, h, w_h, rows, hidden, dim,
+                     ntiles, ws.nsplit, ws.partial);
   GateArgs ga;
   ga.partial = ws.partial;
   ga.bias = bias;

@@ -47,7 +47,8 @@ _SIGNATURES = {
     "dflash2_ring_attention": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _f32, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_context_gate_workspace": ([_i64, _i64, _i64], _size),
-    "dflash2_context_gate": ([_c_ptr, _c_ptr, _int, _c_ptr, _i64, _i64, _i64, _int, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_context_gate": ([_c_ptr, _int, _c_ptr, _int, _c_ptr, _i64, _i64, _i64, _int, _c_ptr, _c_ptr, _size, _c_ptr],
+                             _int),
     "dflash2_pair_score": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _c_ptr,
                             _c_ptr, _c_ptr], _int),
     "dflash2_walk": ([_c_ptr, _c_ptr, _i64, _i64, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr], _int),
@@ -57,8 +58,8 @@ _SIGNATURES = {
     "dflash2_select_noalloc": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _i64, _i64, _f32,
                                 _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr], _int),
     "dflash2_select_gated_workspace": ([_i64, _i64, _i64, _i64, _i64], _size),
-    "dflash2_select_gated": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _c_ptr, _int, _c_ptr,
-                              _i64, _int, _i64, _i64, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+    "dflash2_select_gated": ([_c_ptr, _i64, _c_ptr, _c_ptr, _c_ptr, _int, _i64, _i64, _c_ptr, _int, _c_ptr, _int,
+                              _c_ptr, _i64, _int, _i64, _i64, _f32, _u64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                               _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_conv2tap": ([_c_ptr, _c_ptr, _c_ptr, _i64, _i64, _i64, _i64, _i64, _c_ptr, _c_ptr], _int),
     "dflash2_spec_accept_workspace": ([_i64, _i64, _i64], _size),
@@ -283,11 +284,12 @@ def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048,
 
 def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None = None, act: str = "sigmoid",
                  out: torch.Tensor | None = None):
-    """H = act(W_H h + b) for h [..., hidden] (fp32) and W_H [dim, hidden] (fp32 or bf16).
+    """H = act(W_H h + b) for h [..., hidden] (fp32 or bf16) and W_H [dim, hidden] (fp32 or
+    bf16).
 
     `out` may supply a contiguous fp32 tensor of shape [..., dim] to write H into."""
     lib = load_library()
-    _contig(_need(h, "h", (torch.float32,)), "h")
+    _contig(_need(h, "h", (torch.float32,) + _BF16_LIKE), "h")
     _contig(_need(w_h, "w_h", (torch.float32,) + _BF16_LIKE, h.device), "w_h")
     if bias is not None:
         _contig(_need(bias, "bias", (torch.float32,), h.device), "bias")
@@ -305,7 +307,8 @@ def context_gate(h: torch.Tensor, w_h: torch.Tensor, bias: torch.Tensor | None =
     a = {"sigmoid": GATE_SIGMOID, "identity": GATE_IDENTITY}[act]
     nbytes = lib.dflash2_context_gate_workspace(rows, hidden, dim)
     ws = workspace("gate", nbytes, h.device, (rows, hidden, dim))
-    _check(lib.dflash2_context_gate(_ptr(h), _ptr(w_h), wdt, _ptr(bias), rows, hidden, dim, a, _ptr(H), _ptr(ws),
+    hdt = F32 if h.dtype == torch.float32 else BF16
+    _check(lib.dflash2_context_gate(_ptr(h), hdt, _ptr(w_h), wdt, _ptr(bias), rows, hidden, dim, a, _ptr(H), _ptr(ws),
                                     ws.numel(), _stream()), "dflash2_context_gate")
     return H
 
@@ -423,7 +426,7 @@ def select_noalloc(logits, verified, emb_a, emb_b, H, temperature: float = 0.0, 
 
 def select_gated(logits, verified, emb_a, emb_b, h, w_h, bias=None, act: str = "sigmoid", temperature: float = 0.0,
                  seed: int = 0, out: dict | None = None, H_out: torch.Tensor | None = None):
-    """Context gate + select in one call: h [B, K, hidden] fp32, w_h [dim, hidden] bf16.
+    """Context gate + select in one call: h [B, K, hidden] fp32 or bf16, w_h [dim, hidden] bf16.
 
     Returns the dict of select(); H_out (fp32 [B, K, dim]) receives the gate values the
     scores used when given.
@@ -436,7 +439,7 @@ def select_gated(logits, verified, emb_a, emb_b, h, w_h, bias=None, act: str = "
     _contig(_need(verified, "verified", (torch.int32,), dev), "verified")
     _contig(_need(emb_a, "emb_a", (torch.float32,) + _BF16_LIKE, dev), "emb_a")
     _contig(_need(emb_b, "emb_b", (torch.float32,) + _BF16_LIKE, dev), "emb_b")
-    _contig(_need(h, "h", (torch.float32,), dev), "h")
+    _contig(_need(h, "h", (torch.float32,) + _BF16_LIKE, dev), "h")
     _contig(_need(w_h, "w_h", _BF16_LIKE, dev), "w_h")
     if bias is not None:
         _contig(_need(bias, "bias", (torch.float32,), dev), "bias")
@@ -462,8 +465,8 @@ def select_gated(logits, verified, emb_a, emb_b, h, w_h, bias=None, act: str = "
     nbytes = lib.dflash2_select_gated_workspace(B, K, V, hidden, dim)
     ws = workspace("select_gated", nbytes, dev, (B, K, V, hidden, dim))
     _check(lib.dflash2_select_gated(_ptr(logits), ld, _ptr(verified), _ptr(emb_a), _ptr(emb_b),
-                                    _emb_dtype(emb_a, emb_b), V, dim, _ptr(h), _ptr(w_h), BF16, _ptr(bias), hidden, a,
-                                    B, K, float(temperature), int(seed) & (2 ** 64 - 1), _ptr(H_out),
+                                    _emb_dtype(emb_a, emb_b), V, dim, _ptr(h), F32 if h.dtype == torch.float32 else BF16,
+                                    _ptr(w_h), BF16, _ptr(bias), hidden, a, B, K, float(temperature), int(seed) & (2 ** 64 - 1), _ptr(H_out),
                                     _ptr(out["cand_idx"]), _ptr(out["cand_val"]), _ptr(out["S"]), _ptr(out["tokens"]),
                                     _ptr(out["slots"]), _ptr(out["q"]), _ptr(out["row_status"]), _ptr(ws), ws.numel(),
                                     _stream()), "dflash2_select_gated")

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DFLASH2_ABI_VERSION 1
+#define DFLASH2_ABI_VERSION 2
 #define DFLASH2_NCAND 16       /* candidates per draft position */
 #define DFLASH2_MAX_K 64       /* draft positions per request */
 #define DFLASH2_MAX_TOPK 32    /* largest top_k of the filtered verify */
@@ -159,20 +159,22 @@ dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, 
  * The gate is read as a logistic sigmoid of an affine map (DFLASH2_GATE_SIGMOID);
  * DFLASH2_GATE_IDENTITY returns the affine map.
  *
- * h        float [rows, hidden].
- * w_h      [dim, hidden] in w_dtype.  With DFLASH2_BF16 each h value is first rounded
- *          to bf16 (nearest, ties to even) and the product runs on bf16 MFMA with
- *          fp32 accumulation; with DFLASH2_F32 it runs on fp32 MFMA.
+ * h        [rows, hidden] in h_dtype (DFLASH2_F32 or DFLASH2_BF16).
+ * w_h      [dim, hidden] in w_dtype.  With DFLASH2_BF16 each fp32 h value is first
+ *          rounded to bf16 (nearest, ties to even; bf16 h is used as it is) and the
+ *          product runs on bf16 MFMA with fp32 accumulation; with DFLASH2_F32 it runs
+ *          on fp32 MFMA (bf16 h widened exactly to fp32).
  * bias     float [dim] or NULL (= 0).
  * H        float [rows, dim].
  * Errors: NULL pointers, rows < 1, hidden < 8 or hidden % 8 != 0, dim not a power of
- *         two in [16, 1024], bad dtype or act, alignment of h / w_h, workspace.
+ *         two in [16, 1024], bad h_dtype, w_dtype or act, h / w_h not 16-byte
+ *         aligned, workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_context_gate_workspace(int64_t rows, int64_t hidden, int64_t dim);
-dflash2_status dflash2_context_gate(const float* h, const void* w_h, dflash2_dtype w_dtype,
-                                    const float* bias, int64_t rows, int64_t hidden, int64_t dim,
-                                    dflash2_gate_act act, float* H, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream);
+dflash2_status dflash2_context_gate(const void* h, dflash2_dtype h_dtype, const void* w_h,
+                                    dflash2_dtype w_dtype, const float* bias, int64_t rows,
+                                    int64_t hidden, int64_t dim, dflash2_gate_act act, float* H,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * Pair scores S_t(a, b) = U_t(b) + <A(a) (.) H(h_t), B(b)> for every adjacent pair.
@@ -276,23 +278,25 @@ dflash2_status dflash2_select_noalloc(const uint16_t* logits, int64_t ld, const 
  * leaves idle or shares), and each draft position adds its own row's gate slices, so
  * H never makes a separate round trip.
  *
- * h float [batch, K, hidden]; w_h [dim, hidden] in w_dtype, which must be
- * DFLASH2_BF16 (h rounded to bf16 as in dflash2_context_gate); bias float [dim] or
+ * h [batch, K, hidden] in h_dtype (DFLASH2_F32 or DFLASH2_BF16); w_h [dim, hidden] in
+ * w_dtype, which must be DFLASH2_BF16 (fp32 h rounded to bf16 as in
+ * dflash2_context_gate); bias float [dim] or
  * NULL; act as in dflash2_context_gate.  H_out float [batch, K, dim] or NULL: the gate
  * values the scores used.  They equal dflash2_context_gate's up to the fp32 summation
  * order over `hidden` (deterministic, not bit-identical to it); every other output is
  * bit-identical to dflash2_select called with H = H_out.
  * Errors: the checks of dflash2_select and dflash2_context_gate, w_dtype other than
- *         DFLASH2_BF16 (DFLASH2_ERR_DTYPE), dim < 64 (the fused gate tiles are 64
- *         columns wide; DFLASH2_ERR_SHAPE), H_out not 16-byte aligned, workspace.
+ *         DFLASH2_BF16 or a bad h_dtype (DFLASH2_ERR_DTYPE), dim < 64 (the fused gate
+ *         tiles are 64 columns wide; DFLASH2_ERR_SHAPE), H_out not 16-byte aligned,
+ *         workspace.
  * ------------------------------------------------------------------------------- */
 size_t dflash2_select_gated_workspace(int64_t batch, int64_t K, int64_t vocab, int64_t hidden,
                                       int64_t dim);
 dflash2_status dflash2_select_gated(const uint16_t* logits, int64_t ld, const int32_t* verified,
                                     const void* emb_a, const void* emb_b, dflash2_dtype emb_dtype,
-                                    int64_t vocab, int64_t dim, const float* h, const void* w_h,
-                                    dflash2_dtype w_dtype, const float* bias, int64_t hidden,
-                                    dflash2_gate_act act, int64_t batch, int64_t K,
+                                    int64_t vocab, int64_t dim, const void* h, dflash2_dtype h_dtype,
+                                    const void* w_h, dflash2_dtype w_dtype, const float* bias,
+                                    int64_t hidden, dflash2_gate_act act, int64_t batch, int64_t K,
                                     float temperature, uint64_t seed, float* H_out,
                                     int32_t* cand_idx, float* cand_val, float* S, int32_t* tokens,
                                     int32_t* slots, float* q, int32_t* row_status, void* workspace,

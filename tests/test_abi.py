@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
     missing = [n for n in _declared() if n not in exported]
     assert not missing, missing
     assert set(d2.EXPORTED) == set(_declared())
-    assert lib.dflash2_abi_version() == 1
+    assert lib.dflash2_abi_version() == 2
 
 
 def test_header_compiles_as_c():
@@ -77,11 +77,14 @@ def test_host_validation_before_any_launch():
     assert lib.dflash2_topk16(FAKE, 4, 4096, 4096, FAKE, FAKE, NULL, ws, need - 257, NULL) == 5
     assert lib.dflash2_topk16(FAKE, 4, 4096, 4096, FAKE, FAKE, NULL, NULL, big, NULL) == 5
     # context gate
-    assert lib.dflash2_context_gate(FAKE, FAKE, 7, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 4
-    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 512, 256, 9, FAKE, ws, big, NULL) == 4
-    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 500, 256, 0, FAKE, ws, big, NULL) == 2
-    assert lib.dflash2_context_gate(FAKE, FAKE, 1, NULL, 4, 512, 250, 0, FAKE, ws, big, NULL) == 2
-    assert lib.dflash2_context_gate(FAKE, MIS, 1, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 3
+    assert lib.dflash2_context_gate(FAKE, 0, FAKE, 7, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 4
+    assert lib.dflash2_context_gate(FAKE, 2, FAKE, 1, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 4
+    assert lib.dflash2_context_gate(FAKE, 1, FAKE, 1, NULL, 4, 512, 256, 9, FAKE, ws, big, NULL) == 4
+    assert lib.dflash2_context_gate(FAKE, 0, FAKE, 1, NULL, 4, 500, 256, 0, FAKE, ws, big, NULL) == 2
+    assert lib.dflash2_context_gate(FAKE, 1, FAKE, 1, NULL, 4, 512, 250, 0, FAKE, ws, big, NULL) == 2
+    assert lib.dflash2_context_gate(FAKE, 0, MIS, 1, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 3
+    assert lib.dflash2_context_gate(MIS, 1, FAKE, 0, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 3
+    assert lib.dflash2_context_gate(NULL, 1, FAKE, 0, NULL, 4, 512, 256, 0, FAKE, ws, big, NULL) == 1
     # pair score
     assert lib.dflash2_pair_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 96, FAKE, 1, 7, FAKE, NULL, NULL) == 2
     assert lib.dflash2_pair_score(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 65, FAKE, NULL, NULL) == 2
@@ -97,12 +100,14 @@ def test_host_validation_before_any_launch():
     assert lib.dflash2_select(FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, FAKE, 1, 0, 0.0, 0, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, NULL, ws, big, NULL) == 2
     # gated select: the select checks, then the gate's
-    sg = lambda w_dtype=1, hidden=512, act=0, h=FAKE, wsb=big, K=7: lib.dflash2_select_gated(
-        FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, h, FAKE, w_dtype, NULL, hidden, act, 1, K, 0.0, 0, NULL, FAKE, FAKE,
-        FAKE, FAKE, FAKE, FAKE, NULL, ws, wsb, NULL)
+    sg = lambda w_dtype=1, hidden=512, act=0, h=FAKE, wsb=big, K=7, h_dtype=0: lib.dflash2_select_gated(
+        FAKE, 4096, FAKE, FAKE, FAKE, 1, 4096, 256, h, h_dtype, FAKE, w_dtype, NULL, hidden, act, 1, K, 0.0, 0, NULL,
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, ws, wsb, NULL)
     assert sg(K=0) == 2
     assert sg(h=NULL) == 1
     assert sg(w_dtype=0) == 4
+    assert sg(h_dtype=3) == 4
+    assert sg(h_dtype=1, h=MIS) == 3
     assert sg(act=5) == 4
     assert sg(hidden=500) == 2
     assert sg(h=MIS) == 3

@@ -138,6 +138,25 @@ def test_context_gate_ragged(d2):
         assert_close_scaled(H, Href, 0.25 * pre_abs, what="gate f32 ragged")
 
 
+def test_context_gate_bf16_h(d2):
+    """h in bf16: within tolerance of the oracle, and bit-identical to the gate of the
+    fp32 h that holds the same values (both weight dtypes)."""
+    rng = np.random.default_rng(12)
+    for rows, hidden, dim in ((1, 8, 16), (105, 5120, 256), (33, 1000, 128), (257, 1032, 64), (5, 4096, 1024)):
+        hb = synth.f32_to_bf16_bits(rng.standard_normal((rows, hidden)).astype(np.float32))
+        h64 = oracle.bf16_to_f64(hb)
+        w = (rng.standard_normal((dim, hidden)) / np.sqrt(hidden)).astype(np.float32)
+        wb = synth.f32_to_bf16_bits(w)
+        b = rng.standard_normal(dim).astype(np.float32)
+        print(f"gate bf16 h {rows}x{hidden}x{dim}", flush=True)
+        for Wg, W64, is_bf16 in ((to_gpu_bits(wb), oracle.bf16_to_f64(wb), True), (to_gpu(w), w, False)):
+            H = cpu(d2.context_gate(to_gpu_bits(hb), Wg, to_gpu(b)))
+            Href, _, pre_abs = oracle.context_gate(h64, W64, b, is_bf16)
+            assert_close_scaled(H, Href, 0.25 * pre_abs, what=f"gate bf16 h (bf16 W: {is_bf16})")
+            H32 = cpu(d2.context_gate(to_gpu(h64.astype(np.float32)), Wg, to_gpu(b)))
+            np.testing.assert_array_equal(H.view(np.uint32), H32.view(np.uint32))
+
+
 # ------------------------------------------------------------------ pair score ------
 
 
@@ -297,6 +316,34 @@ def test_select_gated_ragged(d2):
             a, b = cpu(out[k]), cpu(ref[k])
             np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                           b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+
+
+def test_select_gated_bf16_h(d2):
+    """The gated select at B 15, K 7 with h in bf16: every output, H_out included,
+    bit-identical to the gated select on the fp32 h holding the same values; H_out
+    within tolerance of the oracle's gate."""
+    import torch
+    w = synth.workload(2)
+    inp = inputs(2)
+    print("gated select bf16 h c2", flush=True)
+    A64, B64, Ag, Bg = tables(inp)
+    W64, Wg, _ = gate_w(inp)
+    hb = synth.f32_to_bf16_bits(inp["h"])
+    h64 = oracle.bf16_to_f64(hb)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    for T in (0.0, 1.0):
+        Hb = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=logits.device)
+        Hf = torch.empty_like(Hb)
+        ob = d2.select_gated(logits, ver, Ag, Bg, to_gpu_bits(hb), Wg, to_gpu(inp["bias"]), "sigmoid", T, 3, H_out=Hb)
+        of = d2.select_gated(logits, ver, Ag, Bg, to_gpu(h64.astype(np.float32)), Wg, to_gpu(inp["bias"]), "sigmoid",
+                             T, 3, H_out=Hf)
+        assert torch.equal(Hb, Hf)
+        for k in ob:
+            a, b = cpu(ob[k]), cpu(of[k])
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+        Href, _, pre_abs = oracle.context_gate(h64.reshape(-1, w.D), W64, inp["bias"], True)
+        assert_close_scaled(cpu(Hb).reshape(-1, w.dim), Href, 0.25 * pre_abs, what="gated H bf16 h")
 
 
 def test_select_gated_many_rows(d2):
