@@ -187,9 +187,11 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
 }
 
 size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window) {
-  if (batch < 1 || nq < 1 || hkv < 1 || hq < hkv || hq % hkv != 0 || window < 1) return 0;
+  if (batch < 1 || batch > (1 << 20) || nq < 1 || nq > 128 || hkv < 1 || hq < hkv || hq % hkv != 0 || window < 1 ||
+      window > (1 << 24))
+    return 0;
   Carver c(nullptr);
-  carve_ring(c, batch, hkv, ring_splits((int)nq, (int)window), ring_rows_pad((int)nq, (int)hq, (int)hkv));
+  carve_ring(c, batch, hkv, ring_splits(batch, hkv, (int)nq, (int)window), ring_rows_pad((int)nq, (int)hq, (int)hkv));
   return c.off + 256;
 }
 
@@ -200,14 +202,14 @@ dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, 
                                       size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k_blk || !v_blk || !k_ring || !v_ring || !ctx_len || !out) return DFLASH2_ERR_NULL;
   if (batch < 1 || batch > (1 << 20) || nq < 1 || hkv < 1 || hq < hkv || hq % hkv != 0 || head_dim != 128 ||
-      nq * (hq / hkv) > kRingMaxRows || nq > 128 || ring < 8 || ring % 8 != 0 || ring > (1 << 24) || window < 1 ||
-      window > ring || ring_splits((int)nq, (int)window) > 32)
+      nq * (hq / hkv) > kRingMaxRows || nq > 128 || ring < 32 || ring % 32 != 0 || ring > (1 << 24) || window < 1 ||
+      window > ring)
     return DFLASH2_ERR_SHAPE;
   if (isnan(scale) || isinf(scale) || scale < 0.f) return DFLASH2_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_ring) || !aligned16(v_ring) ||
       !aligned16(out))
     return DFLASH2_ERR_ALIGN;
-  const int nsplit = ring_splits((int)nq, (int)window);
+  const int nsplit = ring_splits(batch, hkv, (int)nq, (int)window);
   const int rows_pad = ring_rows_pad((int)nq, (int)hq, (int)hkv);
   RingWs ws;
   dflash2_status st = carve_checked(

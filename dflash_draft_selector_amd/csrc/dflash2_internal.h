@@ -52,12 +52,12 @@ int lmhead_tiles(int64_t vocab);
 LmheadWs carve_lmhead(Carver& c, int64_t rows, int64_t vocab);
 
 struct RingWs {
-  float* ml;                      // [batch][hkv][nsplit][rows_pad][2] per-split row max and sum
+  float* ml;                      // [batch][hkv][nsplit][rows_pad][2] per-split row max (log2 units) and sum
   float* o;                       // [batch][hkv][nsplit][rows_pad][128] per-split unnormalised outputs
 };
 constexpr int kRingMaxRows = 48;  // query rows (block positions x query heads per K/V head)
 int ring_rows_pad(int nq, int hq, int hkv);
-int ring_splits(int nq, int window);
+int ring_splits(int64_t batch, int64_t hkv, int nq, int window);
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad);
 
 struct GateWs {

@@ -9,37 +9,43 @@
 // the block attends to all of them; query head h uses K/V head h / (Hq / Hkv).
 //
 // Ring layouts, chosen for this read (the hot one: every draft step reads the whole
-// window, a verify writes a few rows): K head-major [B][Hkv][ring][Dh]; V transposed
-// [B][Hkv][Dh][ring], so the P V product's V^T fragments (one dim, 8 consecutive
-// positions) are single 16-byte loads.  ring % 8 == 0, and positions are walked in
-// 8-aligned groups, so a group never wraps.  The context splits start on multiples of
-// kRingAlign positions: with ring % 64 == 0 (2112 = 33 x 64) a split's 128 positions
-// of one V^T row are two whole 128-byte lines instead of three partial ones.
+// window, a verify writes a few rows): K head-major [B][Hkv][ring][Dh]; V in tiles of 32
+// positions, transposed within the tile: [B][Hkv][ring / 32][Dh][32].  ring % 32 == 0.
+// The keys of a (request, K/V head) are cut into steps of 32: context step j covers
+// positions pa + 32 j .. (pa = p0 rounded down to 32), masked to [p0, L), and is one
+// whole tile of each ring: 8 KB of K rows and 8 KB of V^T, both contiguous; the block's
+// keys follow as ceil(nq / 32) more steps.
 //
-// k_ring_partial: one 256-thread work-group per (request, K/V head, split).  Split s <
-// nctx_splits takes the 128 positions pa + 128 s .. (pa = p0 rounded down to kRingAlign) of the
-// context, masked to [p0, L); the last split takes the block's keys.  The rows are the
-// nq x G query rows of the K/V head, in MT 16-row tiles.  Wave w computes S for keys
-// 32w .. 32w+31 on v_mfma_f32_16x16x32_bf16 (Q and K fragments straight from memory);
-// row maxima and sums go through LDS; P = exp(S - m) is split into bf16 hi + lo parts
-// (relative error <= 2^-16) and stored row-major in LDS; wave w accumulates O^T for dims
-// 32w .. 32w+31 as V^T x P^T (hi and lo), its V^T fragments loaded at the start.  Each
-// work-group stores its rows' (max, sum, O); k_ring_combine merges the splits.
+// k_ring_split: one work-group of W waves (8; 4 for 48 query rows) per (request, K/V
+// head, split); split s takes an equal share of the steps and wave w every W-th of those.
+// A wave folds its steps on its own, with no LDS traffic but the Q^T slices and no
+// barrier: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A operand, in an order
+// chosen so that each lane ends up holding the scores of 8 consecutive keys of one query
+// row: exactly the lane layout of the B operand of the next product), an online softmax
+// per query row (maximum across the row's four lanes with two permlane swaps),
+// P = 2^(S - m) split into bf16 high and low parts, and O^T += V^T P^T on the same MFMA
+// with V^T straight from the tile.  Two fragment sets per wave: the next step's loads
+// are in flight while a step is folded.  At the end the waves' (max, sum, O) are merged
+// through LDS and the work-group stores its rows' state, or the normalised output when
+// there is one split; k_ring_combine merges the splits.
 #include "dflash2_internal.h"
 #include "device_common.h"
-#include "topk_dev.h"
 
 namespace df2 {
 
-constexpr int kRingThreads = 256;            // 4 waves
-constexpr int kRingDh = 128;                 // head dim
-constexpr int kRingC = 128;                  // keys per work-group
-constexpr int kRingPPitch = kRingC + 8;      // bf16 elements per staged P row (16-byte aligned rows)
-#ifndef DF2_RING_ALIGN
-#define DF2_RING_ALIGN 64
+#ifndef DF2_RING_WAVES
+#define DF2_RING_WAVES 8
 #endif
-constexpr int kRingAlign = DF2_RING_ALIGN;   // context splits start on multiples of this many positions
-static_assert(kRingAlign % 8 == 0 && kRingC % kRingAlign == 0, "split starts keep 8-aligned groups");
+#ifndef DF2_RING_TARGET
+#define DF2_RING_TARGET 256
+#endif
+constexpr int kRingWavesMax = DF2_RING_WAVES;  // waves of a split work-group (4 for 48 query rows)
+constexpr int kCombThreads = 256;
+constexpr int kRingDh = 128;                 // head dim
+constexpr int kRingStep = 32;                // keys per wave step
+constexpr int kRingTargetGroups = DF2_RING_TARGET;   // work-groups aimed for: one per compute unit
+constexpr int kRingMaxSplits = 32;
+constexpr int kRingRedPitch = 64 + 4;        // floats per staged half row of O (dims 64 at a time)
 
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad) {
   RingWs w;
@@ -49,296 +55,444 @@ RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pa
   return w;
 }
 
+// waves of the split work-group for MT row tiles: the 48-row tiles need more registers
+// than two waves per SIMD allow
 template <int MT>
+constexpr int ring_waves() { return MT < 3 ? kRingWavesMax : 4; }
+
+template <int MT, int W = ring_waves<MT>()>
 struct RingShared {
-  uint16_t p_hi[MT * 16][kRingPPitch];       // P rows, bf16 high part
-  uint16_t p_lo[MT * 16][kRingPPitch];       // P rows, bf16 low part
-  float red_max[4][MT * 16];                 // per-wave row maxima
-  float red_sum[4][MT * 16];                 // per-wave row sums
+  u32x4 q[MT][4][64];                        // Q^T B-operand slices in lane order (read each step)
+  float m[W][MT * 16];                       // per-wave row maxima (log2 units)
+  float l[W][MT * 16];                       // per-wave row sums
+  float lt[MT * 16];                         // the work-group's row sums
+  float red[W][MT * 16][kRingRedPitch];      // per-wave O, half the dims at a time
 };
 
-// sum over the 16 lanes of the row, every lane gets it (the reduction order of row16_max)
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xb1>(v);              // quad_perm [1,0,3,2]
-  v += dpp_f<0x4e>(v);              // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);             // row_half_mirror
-  v += dpp_f<0x140>(v);             // row_mirror
-  return v;
+// max / sum over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48);
+// every lane gets the same value
+__device__ __forceinline__ float quad_row_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_row_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// The work of one non-empty split (BLK: the block's keys; else 128 context positions
-// from base; EDGE: some of its keys lie outside [lo, hi) and are masked).  Templated so
-// that each form's loads are straight-line code (the waits on them then count
-// outstanding loads exactly instead of draining them) and interior splits skip the
-// masking.
-template <int MT, bool BLK, bool EDGE>
-__device__ __forceinline__ void ring_split(RingShared<MT>& sm, const uint16_t* __restrict__ q,
-                                           const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
-                                           const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring,
-                                           int b, int kvh, int nq, int hq, int hkv, int ring, int base, int lo, int hi,
-                                           float scale_log2, float* __restrict__ ml, float* __restrict__ os) {
-  constexpr int kRows = MT * 16;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, i16 = lane & 15;
-  const int G = hq / hkv;
-  const int nrows = nq * G;
-  const size_t head = (size_t)b * hkv + kvh;
+// Operands of one 32-key step as the MFMAs take them.  S^T tile t (16 keys x 16 rows):
+// A-operand row m is key 8 (m / 4) + 4 t + m % 4, so the result's lane (row, g) holds in
+// register r the score of key 8 g + 4 t + r; over t = 0, 1 that is keys 8 g .. 8 g + 7,
+// the B-operand slice of P^T for the O^T product.  k[t][s]: dims 32 s + 8 g .. + 7 of the
+// lane's key; v[dt]: V^T dim 16 dt + i16 over keys 8 g .. 8 g + 7.
+struct RingFrag {
+  u32x4 k[2][4];
+  u32x4 v[kRingDh / 16];
+};
 
-  // ---- loads: Q, K and V^T fragments --------------------------------------------------
-  u32x4 qf[MT][4];
+// Buffer resource over `bytes` bytes from p (raw, offsets in bytes; reads past the end
+// return zero).  Every per-lane offset below is a 32-bit byte offset into one head's
+// part of a ring or of the block, so a lane needs one VGPR per address instead of two.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void* p, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes), 0x00020000);
+}
+
+// The resources of one (request, K/V head): its K ring rows [ring][Dh], its V tiles
+// [ring / 32][Dh][32], and its rows of the block's K and V ([nq] rows, hkv * Dh elements
+// apart).
+struct RingRes {
+  __amdgpu_buffer_rsrc_t kr, vr, kb, vb;
+};
+
+#ifndef DF2_RING_AUX
+#define DF2_RING_AUX 0
+#endif
+constexpr int kRingAux = DF2_RING_AUX;       // cache policy of the ring reads
+
+// This lane's byte offsets within a step's tiles: K rows koff + 4 t (k[t]), V^T dim
+// i16 at positions 8 g .. 8 g + 7 (v); the tile and the 16-dim group come in as scalar or
+// immediate offsets.
+struct RingLane {
+  uint32_t k[2];
+  uint32_t v;
+};
+
+__device__ __forceinline__ RingLane ring_lane() {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int koff = 8 * (i16 >> 2) + (i16 & 3);
+  RingLane l;
+  l.k[0] = (uint32_t)koff * (kRingDh * 2) + 16 * g;
+  l.k[1] = (uint32_t)(koff + 4) * (kRingDh * 2) + 16 * g;
+  l.v = (uint32_t)i16 * (kRingStep * 2) + 16 * g;
+  return l;
+}
+
+// Context step whose tile starts at ring row rb (a multiple of 32): both tiles are
+// kRingStep * Dh * 2 = 8 KB from byte rb * Dh * 2.
+__device__ __forceinline__ void ring_load_step(RingFrag& f, const RingRes& rr, const RingLane& ln, int rb) {
+  const uint32_t tile = (uint32_t)rb * (kRingDh * 2);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.k[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rr.kr, ln.k[t] + 64 * s, tile, kRingAux);
+#pragma unroll
+  for (int dt = 0; dt < kRingDh / 16; ++dt)
+    f.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rr.vr, ln.v + dt * 16 * kRingStep * 2, tile, kRingAux);
+}
+
+// The block's keys kb0 .. kb0 + 31; keys past nq read row 0 and are masked when folded.
+__device__ __forceinline__ void ring_load_blk(RingFrag& f, const RingRes& rr, int nq, int hkv, int kb0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i16 = lane & 15;
+  const int koff = 8 * (i16 >> 2) + (i16 & 3);
+  const uint32_t rowb = (uint32_t)hkv * (kRingDh * 2);       // bytes between the block's rows
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = kb0 + koff + 4 * t;
+    const uint32_t o = (uint32_t)(key < nq ? key : 0) * rowb + 16 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.k[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rr.kb, o + 64 * s, 0, 0);
+  }
+  uint32_t w[kRingDh / 16][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j0 = kb0 + 8 * g + 2 * c, j1 = j0 + 1;
+    const uint32_t o0 = (uint32_t)(j0 < nq ? j0 : 0) * rowb + 2 * i16;
+    const uint32_t o1 = (uint32_t)(j1 < nq ? j1 : 0) * rowb + 2 * i16;
+#pragma unroll
+    for (int dt = 0; dt < kRingDh / 16; ++dt) {
+      const uint32_t a = __builtin_amdgcn_raw_buffer_load_b16(rr.vb, o0 + 32 * dt, 0, 0);
+      const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(rr.vb, o1 + 32 * dt, 0, 0);
+      w[dt][c] = a | (bb << 16);
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < kRingDh / 16; ++dt) f.v[dt] = (u32x4){w[dt][0], w[dt][1], w[dt][2], w[dt][3]};
+}
+
+// A wave's running softmax state for its rows: the maximum m (log2 units; the same in
+// the four lanes of a row), this lane's share of the row sum, and O^T (lane (row, g)
+// holds dims 16 dt + 4 g .. + 3).
+template <int MT>
+struct RingState {
+  float m[MT];
+  float l[MT];
+  f32x4 o[kRingDh / 16][MT];
+};
+
+// One step (keys base + 0 .. 31, valid where lo <= key < hi) is folded into the state:
+// ring_scores takes S^T = K Q^T (keys outside [lo, hi) get -inf), ring_accum the online
+// softmax and O^T += V^T P^T (keys outside get zero V^T words: a stale row never enters,
+// not even times zero).  The masks are computed on every step, without a branch.
+template <int MT>
+__device__ __forceinline__ void ring_scores(const RingShared<MT>& sm, const u32x4 (&k)[2][4], int base, int lo, int hi,
+                                            float scale_log2, float (&x)[MT][8]) {
+  const int lane = threadIdx.x & 63;
+  const int kl = base + 8 * (lane >> 4);       // this lane's keys: kl + 0 .. 7
+  // Q^T slices come from LDS each step: the address goes through an empty asm, so the
+  // reads cannot be hoisted out of the step loop into registers
+  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+  lds_u32x4* qs = (lds_u32x4*)&sm.q[0][0][lane];
+  asm volatile("" : "+v"(qs));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = 16 * mt + i16;
-    const int rr = r < nrows ? r : 0;
-    const uint16_t* qp = q + ((size_t)(b * nq + rr / G) * hq + kvh * G + rr % G) * kRingDh + 8 * g;
+    f32x4 sacc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-      qf[mt][s] = r < nrows ? v : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 qv = qs[(mt * 4 + s) * 64];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[t][s]),
+                                                         __builtin_bit_cast(bf16x8, qv), sacc[t], 0, 0, 0);
     }
-  }
-  u32x4 kf[2][4];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int key = base + 32 * wv + 16 * n + i16;
-    const uint16_t* kp = BLK ? k_blk + ((size_t)(b * nq + (key < nq ? key : 0)) * hkv + kvh) * kRingDh
-                             : k_ring + (head * ring + key % ring) * kRingDh;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kf[n][s] = *reinterpret_cast<const u32x4*>(kp + 8 * g + 32 * s);
-  }
-  // V^T fragment (dt, ks): dim 32 wv + 16 dt + i16, keys base + 32 ks + 8 g .. + 7, keys
-  // outside [lo, hi) zeroed (a stale row never enters, not even times zero)
-  u32x4 vf[2][kRingC / 32];
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt) {
-    const int d = 32 * wv + 16 * dt + i16;
-#pragma unroll
-    for (int ks = 0; ks < kRingC / 32; ++ks) {
-      const int k0 = base + 32 * ks + 8 * g;
-      uint32_t w[4];
-      if constexpr (!BLK) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(v_ring + (head * kRingDh + d) * ring + k0 % ring);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if constexpr (EDGE) {
-            const bool e0 = k0 + 2 * c >= lo && k0 + 2 * c < hi;
-            const bool e1 = k0 + 2 * c + 1 >= lo && k0 + 2 * c + 1 < hi;
-            w[c] = (e0 ? (v[c] & 0xffffu) : 0u) | (e1 ? (v[c] & 0xffff0000u) : 0u);
-          } else {
-            w[c] = v[c];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j0 = k0 + 2 * c, j1 = j0 + 1;
-          const uint32_t a = v_blk[((size_t)(b * nq + (j0 < nq ? j0 : 0)) * hkv + kvh) * kRingDh + d];
-          const uint32_t bb = v_blk[((size_t)(b * nq + (j1 < nq ? j1 : 0)) * hkv + kvh) * kRingDh + d];
-          w[c] = (j0 < nq ? a : 0u) | (j1 < nq ? (bb << 16) : 0u);
-        }
-      }
-      vf[dt][ks] = (u32x4){w[0], w[1], w[2], w[3]};
-    }
-  }
-
-  // ---- S = Q K^T for keys base + 32 wv + 16 n + i16, scaled to log2 units, masked -----
-  f32x4 sacc[2][MT];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int key = base + 32 * wv + 16 * n + i16;
-    const bool valid = key >= lo && key < hi;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[n][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc[n][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[mt][s]),
-                                                             __builtin_bit_cast(bf16x8, kf[n][s]), sacc[n][mt], 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sacc[n][mt][r] = (!EDGE || valid) ? sacc[n][mt][r] * scale_log2 : -__builtin_inff();
-    }
-  }
-  // ---- row maxima (every row has a valid key in a non-empty split) ------------------
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = row16_max(fmaxf(sacc[0][mt][r], sacc[1][mt][r]));
-      if (i16 == 0) sm.red_max[wv][16 * mt + 4 * g + r] = x;
-    }
-  __syncthreads();
-  // ---- P = exp2(S - m): bf16 hi / lo parts into LDS, row sums -----------------------
-  float mrow[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * mt + 4 * g + r;
-      const float m = fmaxf(fmaxf(sm.red_max[0][row], sm.red_max[1][row]),
-                            fmaxf(sm.red_max[2][row], sm.red_max[3][row]));
-      mrow[mt][r] = m;
-      float sum = 0.f;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const float p = __builtin_amdgcn_exp2f(sacc[n][mt][r] - m);   // v_exp_f32; 2^-inf = 0
-        sum += p;
-        const __bf16 hb = static_cast<__bf16>(p);                      // v_cvt_pk_bf16_f32, nearest even
-        const uint32_t ph = __builtin_bit_cast(uint16_t, hb);
-        const uint32_t pl = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p - static_cast<float>(hb)));
-        const int col = 32 * wv + 16 * n + i16;
-        sm.p_hi[row][col] = (uint16_t)ph;
-        sm.p_lo[row][col] = (uint16_t)pl;
-      }
-      sum = row16_sum(sum);
-      if (i16 == 0) sm.red_sum[wv][row] = sum;
-    }
-  __syncthreads();
-  // ---- O^T = V^T x P^T (hi, then lo) --------------------------------------------------
-  f32x4 o[2][MT];
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[dt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < kRingC / 32; ++ks)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 ph = *reinterpret_cast<const u32x4*>(&sm.p_hi[16 * mt + i16][32 * ks + 8 * g]);
-      const u32x4 pl = *reinterpret_cast<const u32x4*>(&sm.p_lo[16 * mt + i16][32 * ks + 8 * g]);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt][ks]),
-                                                            __builtin_bit_cast(bf16x8, ph), o[dt][mt], 0, 0, 0);
-        o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt][ks]),
-                                                            __builtin_bit_cast(bf16x8, pl), o[dt][mt], 0, 0, 0);
-      }
-    }
-
-  // ---- the split's state: (max, sum) per row, and O (rows x 128 dims) --------------
-  if (wv == 0 && i16 == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        ml[2 * row] = mrow[mt][r];
-        ml[2 * row + 1] = (sm.red_sum[0][row] + sm.red_sum[1][row]) + (sm.red_sum[2][row] + sm.red_sum[3][row]);
+        const int jj = 4 * t + r;
+        const float v = sacc[t][r] * scale_log2;
+        x[mt][jj] = (unsigned)(kl + jj - lo) < (unsigned)(hi - lo) ? v : -__builtin_inff();
       }
   }
-  // O^T tile (dims 32 wv + 16 dt + 4 g + r, row 16 mt + i16) -> O[row][dims .. + 3]
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-      *reinterpret_cast<f32x4*>(os + (size_t)(16 * mt + i16) * kRingDh + 32 * wv + 16 * dt + 4 * g) = o[dt][mt];
 }
 
 template <int MT>
-__global__ void __launch_bounds__(kRingThreads) k_ring_partial(
+__device__ __forceinline__ void ring_accum(u32x4 (&v)[kRingDh / 16], const float (&x)[MT][8], int base, int lo, int hi,
+                                           RingState<MT>& st) {
+  const int lane = threadIdx.x & 63;
+  const int kl = base + 8 * (lane >> 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bool v0 = (unsigned)(kl + 2 * c - lo) < (unsigned)(hi - lo);
+    const bool v1 = (unsigned)(kl + 2 * c + 1 - lo) < (unsigned)(hi - lo);
+    const uint32_t keep = (v0 ? 0xffffu : 0u) | (v1 ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int dt = 0; dt < kRingDh / 16; ++dt) v[dt][c] &= keep;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) mloc = fmaxf(mloc, x[mt][jj]);
+    const float mn = fmaxf(st.m[mt], quad_row_max(mloc));   // finite: every step holds a valid key
+    const float alpha = st.m[mt] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - mn);
+    st.m[mt] = mn;
+    float sum = 0.f;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float p0 = __builtin_amdgcn_exp2f(x[mt][2 * c] - mn);   // v_exp_f32; 2^-inf = 0
+      const float p1 = __builtin_amdgcn_exp2f(x[mt][2 * c + 1] - mn);
+      sum += p0;
+      sum += p1;
+      const bf16x2 h = __builtin_convertvector((f32x2){p0, p1}, bf16x2);   // nearest even
+      const f32x2 hf = __builtin_convertvector(h, f32x2);
+      const bf16x2 lw = __builtin_convertvector((f32x2){p0 - hf[0], p1 - hf[1]}, bf16x2);
+      ph[c] = __builtin_bit_cast(uint32_t, h);
+      pl[c] = __builtin_bit_cast(uint32_t, lw);
+    }
+    st.l[mt] = st.l[mt] * alpha + sum;
+#pragma unroll
+    for (int dt = 0; dt < kRingDh / 16; ++dt) st.o[dt][mt] *= alpha;
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, (u32x4){ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, (u32x4){pl[0], pl[1], pl[2], pl[3]});
+#pragma unroll
+    for (int dt = 0; dt < kRingDh / 16; ++dt) {
+      st.o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[dt]), bh, st.o[dt][mt], 0, 0,
+                                                             0);
+      st.o[dt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[dt]), bl, st.o[dt][mt], 0, 0,
+                                                             0);
+    }
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void ring_fold(const RingShared<MT>& sm, RingFrag& f, int base, int lo, int hi,
+                                          float scale_log2, RingState<MT>& st) {
+  float x[MT][8];
+  ring_scores<MT>(sm, f.k, base, lo, hi, scale_log2, x);
+  ring_accum<MT>(f.v, x, base, lo, hi, st);
+}
+
+// Steps of a request: context steps covering [pa, L) (none when the window is empty),
+// then the block's.
+struct RingSteps {
+  int L, p0, pa, nsc, total;
+};
+
+__device__ __forceinline__ RingSteps ring_steps(int ctx, int window, int nq) {
+  RingSteps r;
+  r.L = ctx > 0 ? ctx : 0;
+  const int nctx = r.L < window - 1 ? r.L : window - 1;
+  r.p0 = r.L - nctx;
+  r.pa = r.p0 & ~(kRingStep - 1);
+  r.nsc = nctx > 0 ? (r.L - r.pa + kRingStep - 1) / kRingStep : 0;
+  r.total = r.nsc + (nq + kRingStep - 1) / kRingStep;
+  return r;
+}
+
+template <int MT>
+__global__ void __launch_bounds__(64 * ring_waves<MT>(), (MT < 3 ? 8 : 4) / ring_waves<MT>()) k_ring_split(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
-    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nctx_splits, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o) {
+    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nsplit, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o, float* __restrict__ out) {
   __shared__ RingShared<MT> sm;
   constexpr int kRows = MT * 16;
+  constexpr int kRingWaves = ring_waves<MT>();
+  constexpr int kRingThreads = 64 * kRingWaves;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int nsplit = nctx_splits + 1;
   const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
   const int split = unit % nsplit;
   const int bk = unit / nsplit;
   const int kvh = bk % hkv, b = bk / hkv;
   const int G = hq / hkv;
   const int nrows = nq * G;
+  const size_t head = (size_t)b * hkv + kvh;
 
-  const int L = ctx_len[b] > 0 ? ctx_len[b] : 0;
-  const int nctx = L < window - 1 ? L : window - 1;
-  const int p0 = L - nctx;
-  const bool blk = split == nctx_splits;
-  const int base = blk ? 0 : (p0 & ~(kRingAlign - 1)) + kRingC * split;  // first key: a position, or block row 0
-  const int lo = blk ? 0 : p0;                              // keys [lo, hi) are read
-  const int hi = blk ? nq : L;
-  float* ml = ws_ml + (size_t)unit * kRows * 2;
-  float* os = ws_o + (size_t)unit * kRows * kRingDh;
-  if (base >= hi || (!blk && nctx == 0)) {                 // a context split past the window: empty
-    for (int e = tid; e < kRows; e += kRingThreads) {
-      ml[2 * e] = -__builtin_inff();
-      ml[2 * e + 1] = 0.f;
-    }
-    for (int e = tid; e < kRows * kRingDh / 4; e += kRingThreads)
-      reinterpret_cast<f32x4*>(os)[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    return;
+  const RingSteps rs = ring_steps(ctx_len[b], window, nq);
+  const int c0 = (int)((long long)split * rs.total / nsplit);
+  const int c1 = (int)((long long)(split + 1) * rs.total / nsplit);
+
+  // the wave's steps (wave-uniform: the loop and its branches stay scalar); the first
+  // step's loads are issued before Q is staged, so that the two latencies overlap
+  RingRes rr;
+  rr.kr = ring_rsrc(k_ring + head * ring * kRingDh, (uint64_t)ring * kRingDh * 2);
+  rr.vr = ring_rsrc(v_ring + head * kRingDh * ring, (uint64_t)ring * kRingDh * 2);
+  const size_t blk0 = ((size_t)b * nq * hkv + kvh) * kRingDh;
+  const uint64_t blk_bytes = ((uint64_t)(nq - 1) * hkv + 1) * kRingDh * 2;
+  rr.kb = ring_rsrc(k_blk + blk0, blk_bytes);
+  rr.vb = ring_rsrc(v_blk + blk0, blk_bytes);
+  RingFrag f;
+  int j = c0 + __builtin_amdgcn_readfirstlane(wv);
+  const int jend = c1 < rs.nsc ? c1 : rs.nsc;   // the wave's context steps: j, j + W, .. < jend
+  const RingLane ln = ring_lane();
+  const int jlast = j + kRingWaves * ((jend - 1 - j) / kRingWaves);
+  const int rstep = kRingStep * kRingWaves;     // ring rows between the wave's steps
+  int rb = (rs.pa + kRingStep * j) % ring;
+  const int rlast = (rs.pa + kRingStep * jlast) % ring;
+  if (j < jend) ring_load_step(f, rr, ln, rb);
+
+  // Q^T as the B operand, staged in LDS: entry [mt][s][lane] is row 16 mt + lane % 16,
+  // dims 32 s + 8 (lane / 16) .. + 7 (zero for padding rows)
+  for (int e = tid; e < MT * 4 * 64; e += kRingThreads) {
+    const int mt = e >> 8, s4 = (e >> 6) & 3, l = e & 63;
+    const int r = 16 * mt + (l & 15);
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (r < nrows)
+      v = *reinterpret_cast<const u32x4*>(q + ((size_t)(b * nq + r / G) * hq + kvh * G + r % G) * kRingDh + 32 * s4 +
+                                          8 * (l >> 4));
+    sm.q[mt][s4][l] = v;
   }
-  if (blk)
-    ring_split<MT, true, true>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
-                               scale_log2, ml, os);
-  else if (base >= lo && base + kRingC <= hi)
-    ring_split<MT, false, false>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
-                                 scale_log2, ml, os);
-  else
-    ring_split<MT, false, true>(sm, q, k_blk, v_blk, k_ring, v_ring, b, kvh, nq, hq, hkv, ring, base, lo, hi,
-                                scale_log2, ml, os);
+  __syncthreads();
+  RingState<MT> st;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    st.m[mt] = -__builtin_inff();
+    st.l[mt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < kRingDh / 16; ++dt) st.o[dt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (j < jend) {
+    // two fragment sets, the next step's loads issued before this one is folded (past the
+    // wave's last step its last one is loaded again, from cache)
+    RingFrag fb;
+    for (;;) {
+      {
+        int rn = rb + rstep;
+        rn = rn >= ring ? rn % ring : rn;
+        ring_load_step(fb, rr, ln, j + kRingWaves < jend ? rn : rlast);
+        const int base = rs.pa + kRingStep * j;
+        ring_fold<MT>(sm, f, base, rs.p0, rs.L, scale_log2, st);
+        j += kRingWaves;
+        rb = rn;
+        if (j >= jend) break;
+      }
+      {
+        int rn = rb + rstep;
+        rn = rn >= ring ? rn % ring : rn;
+        ring_load_step(f, rr, ln, j + kRingWaves < jend ? rn : rlast);
+        const int base = rs.pa + kRingStep * j;
+        ring_fold<MT>(sm, fb, base, rs.p0, rs.L, scale_log2, st);
+        j += kRingWaves;
+        rb = rn;
+        if (j >= jend) break;
+      }
+    }
+  }
+  for (; j < c1; j += kRingWaves) {             // steps of the block's keys
+    const int kb0 = kRingStep * (j - rs.nsc);
+    ring_load_blk(f, rr, nq, hkv, kb0);
+    ring_fold<MT>(sm, f, kb0, 0, nq, scale_log2, st);
+  }
+
+  // ---- merge the waves: row maxima and sums, then O half the dims at a time -----------
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float lw = quad_row_sum(st.l[mt]);
+    if (g == 0) {
+      sm.m[wv][16 * mt + i16] = st.m[mt];
+      sm.l[wv][16 * mt + i16] = lw;
+    }
+  }
+  __syncthreads();
+  float aself[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = 16 * mt + i16;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kRingWaves; ++w) M = fmaxf(M, sm.m[w][row]);
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRingWaves; ++w)
+      lt += (sm.m[w][row] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sm.m[w][row] - M)) * sm.l[w][row];
+    aself[mt] = st.m[mt] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - M);
+    if (wv == 0 && g == 0) {
+      sm.lt[row] = lt;
+      if (nsplit > 1) {
+        ws_ml[((size_t)unit * kRows + row) * 2] = M;
+        ws_ml[((size_t)unit * kRows + row) * 2 + 1] = lt;
+      }
+    }
+  }
+  float* os = ws_o + (size_t)unit * kRows * kRingDh;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+        *reinterpret_cast<f32x4*>(&sm.red[wv][16 * mt + i16][16 * d4 + 4 * g]) = st.o[4 * half + d4][mt] * aself[mt];
+    __syncthreads();
+    for (int e = tid; e < kRows * 16; e += kRingThreads) {
+      const int row = e >> 4, c4 = e & 15;
+      f32x4 v = *reinterpret_cast<const f32x4*>(&sm.red[0][row][4 * c4]);
+#pragma unroll
+      for (int w = 1; w < kRingWaves; ++w) v += *reinterpret_cast<const f32x4*>(&sm.red[w][row][4 * c4]);
+      const int d = 64 * half + 4 * c4;
+      if (nsplit > 1) {
+        *reinterpret_cast<f32x4*>(os + (size_t)row * kRingDh + d) = v;
+      } else if (row < nrows) {
+        const float inv = 1.f / sm.lt[row];
+        const int i = row / G, h = kvh * G + row % G;
+        *reinterpret_cast<f32x4*>(out + ((size_t)(b * nq + i) * hq + h) * kRingDh + d) = v * inv;
+      }
+    }
+    __syncthreads();
+  }
 }
 
-// One work-group per (request, K/V head, 2 query rows): out = sum_s w_s O_s with
-// w_s = e^(m_s - M) / sum_s' e^(m_s' - M) l_s' (M the rows' maximum over the splits);
-// the weights of a row are formed once, then every output adds its splits' values with
-// all loads in flight.
-constexpr int kRingCombRows = 2;                // query rows per combine work-group: one output per thread
-constexpr int kRingMaxSplits = 32;
-
+// One wave per (request, K/V head, query row): out = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = 2^(m_s - M) (M the row's maximum over the splits).  Every split's (max, sum) and
+// the lane's two dims of every split's O are loaded at once; the splits are added in
+// order.
 template <int MT, int NSP>
-__global__ void __launch_bounds__(kRingThreads) k_ring_combine(const float* __restrict__ ws_ml,
+__global__ void __launch_bounds__(kCombThreads) k_ring_combine(const float* __restrict__ ws_ml,
                                                                 const float* __restrict__ ws_o, int nq, int hq,
-                                                                int hkv, int nsplit, float* __restrict__ out) {
+                                                                int hkv, int nsplit, int nunits,
+                                                                float* __restrict__ out) {
   constexpr int kRows = MT * 16;
-  __shared__ float msh[kRingCombRows][NSP], lsh[kRingCombRows][NSP];
-  __shared__ float wsh[kRingCombRows][NSP];
-  const int groups = (kRows + kRingCombRows - 1) / kRingCombRows;
-  const int bk = (int)blockIdx.x / groups;
-  const int r0 = ((int)blockIdx.x % groups) * kRingCombRows;
-  const int kvh = bk % hkv, b = bk / hkv;
+  const int lane = threadIdx.x & 63;
+  const int wid = (int)blockIdx.x * (kCombThreads / 64) + (int)(threadIdx.x >> 6);
+  if (wid >= nunits) return;                       // whole waves
   const int G = hq / hkv;
   const int nrows = nq * G;
+  const int bk = wid / nrows, row = wid - bk * nrows;
   const size_t u0 = (size_t)bk * nsplit;
-  // every (row, split) statistic loaded at once
-  for (int e = threadIdx.x; e < kRingCombRows * nsplit; e += kRingThreads) {
-    const int rl = e / nsplit, sp = e - rl * nsplit;
-    const float* p = ws_ml + (u0 + sp) * kRows * 2 + 2 * (r0 + rl);
-    msh[rl][sp] = p[0];
-    lsh[rl][sp] = p[1];
+  float m = -__builtin_inff(), l = 0.f;
+  if (lane < nsplit) {
+    m = ws_ml[((u0 + lane) * kRows + row) * 2];
+    l = ws_ml[((u0 + lane) * kRows + row) * 2 + 1];
   }
-  __syncthreads();
-  if (threadIdx.x < kRingCombRows) {
-    const int rl = threadIdx.x;
-    float M = -__builtin_inff();
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, msh[rl][sp]);
-    float den = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float w = msh[rl][sp] == -__builtin_inff() ? 0.f : exp2f(msh[rl][sp] - M);
-      wsh[rl][sp] = w;
-      den += w * lsh[rl][sp];
-    }
-    for (int sp = 0; sp < nsplit; ++sp) wsh[rl][sp] /= den;
-    for (int sp = nsplit; sp < NSP; ++sp) wsh[rl][sp] = 0.f;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kRingCombRows * kRingDh; e += kRingThreads) {
-    const int rl = e / kRingDh, d = e - rl * kRingDh;
-    const int row = r0 + rl;
-    // every split's value in flight at once (past the last split: reread it, weight 0)
-    float v[NSP];
+  f32x2 o[NSP];
 #pragma unroll
-    for (int sp = 0; sp < NSP; ++sp) v[sp] = ws_o[((u0 + (sp < nsplit ? sp : nsplit - 1)) * kRows + row) * kRingDh + d];
-    float num = 0.f;
+  for (int sp = 0; sp < NSP; ++sp)
+    o[sp] = *reinterpret_cast<const f32x2*>(ws_o + ((u0 + (sp < nsplit ? sp : 0)) * kRows + row) * kRingDh + 2 * lane);
+  float M = m;
 #pragma unroll
-    for (int sp = 0; sp < NSP; ++sp) num += wsh[rl][sp] * v[sp];
-    if (row < nrows) {
-      const int i = row / G, h = kvh * G + row % G;
-      out[((size_t)(b * nq + i) * hq + h) * kRingDh + d] = num;
-    }
+  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+  const float w = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M);
+  float den = w * l;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) den += __shfl_xor(den, x);
+  f32x2 num = (f32x2){0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < NSP; ++sp) {
+    const float ws = __shfl(w, sp);                // zero past the last split
+    num += ws * o[sp];
   }
+  const int i = row / G, h = (bk % hkv) * G + row % G;
+  const int b = bk / hkv;
+  *reinterpret_cast<f32x2*>(out + ((size_t)(b * nq + i) * hq + h) * kRingDh + 2 * lane) = num * (1.f / den);
 }
 
 int ring_rows_pad(int nq, int hq, int hkv) {
@@ -346,35 +500,47 @@ int ring_rows_pad(int nq, int hq, int hkv) {
   return rows <= 16 ? 16 : rows <= 32 ? 32 : 48;
 }
 
-// Context splits of 128 positions covering window - 1 positions from a kRingAlign-aligned
-// start, plus one split for the block's keys.
-int ring_splits(int nq, int window) {
-  (void)nq;
-  return (window - 1 + kRingAlign - 1 + kRingC - 1) / kRingC + 1;
+// The most steps a request can have: window - 1 context positions from a 32-aligned
+// start, then the block's.
+static int ring_max_steps(int nq, int window) {
+  return (window - 1 + 2 * (kRingStep - 1)) / kRingStep + (nq + kRingStep - 1) / kRingStep;
+}
+
+// Splits per (request, K/V head): enough work-groups for two per compute unit, at least
+// one step per wave of the longest request, at most kRingMaxSplits.
+int ring_splits(int64_t batch, int64_t hkv, int nq, int window) {
+  const int64_t pairs = batch * hkv;
+  int64_t n = kRingTargetGroups / pairs;
+  const int most = (ring_max_steps(nq, window) + kRingWavesMax - 1) / kRingWavesMax;
+  if (n > most) n = most;
+  if (n > kRingMaxSplits) n = kRingMaxSplits;
+  return n < 1 ? 1 : (int)n;
 }
 
 template <int MT>
 static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kr,
                         const uint16_t* vr, const int32_t* ctx, int B, int nq, int hq, int hkv, int ring, int window,
                         float scale_log2, int nsplit, const RingWs& ws, float* out) {
-  hipLaunchKernelGGL((k_ring_partial<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(kRingThreads), 0, s, q, kb, vb, kr,
-                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit - 1, ws.ml, ws.o);
-  const int groups = (MT * 16 + kRingCombRows - 1) / kRingCombRows;
-  const dim3 grid((unsigned)(B * hkv * groups));
-  if (nsplit <= 8)
-    hipLaunchKernelGGL((k_ring_combine<MT, 8>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+  hipLaunchKernelGGL((k_ring_split<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(64 * ring_waves<MT>()), 0, s, q, kb, vb, kr,
+                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit, ws.ml, ws.o, out);
+  if (nsplit == 1) return;
+  const int nunits = B * hkv * nq * (hq / hkv);
+  const dim3 grid((unsigned)((nunits + kCombThreads / 64 - 1) / (kCombThreads / 64)));
+  if (nsplit <= 4)
+    hipLaunchKernelGGL((k_ring_combine<MT, 4>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
+  else if (nsplit <= 8)
+    hipLaunchKernelGGL((k_ring_combine<MT, 8>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
   else if (nsplit <= 16)
-    hipLaunchKernelGGL((k_ring_combine<MT, 16>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
-  else if (nsplit <= 24)
-    hipLaunchKernelGGL((k_ring_combine<MT, 24>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+    hipLaunchKernelGGL((k_ring_combine<MT, 16>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
   else
-    hipLaunchKernelGGL((k_ring_combine<MT, 32>), grid, dim3(kRingThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, out);
+    hipLaunchKernelGGL((k_ring_combine<MT, 32>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
 }
 
 hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
                                  const uint16_t* k_ring, const uint16_t* v_ring, const int32_t* ctx_len, int batch,
                                  int nq, int hq, int hkv, int ring, int window, float scale, int nsplit, RingWs ws,
                                  float* out, hipStream_t s) {
+  if (nsplit < 1 || nsplit > kRingMaxSplits) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   switch (ring_rows_pad(nq, hq, hkv) / 16) {
     case 1: ring_launch<1>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;

@@ -256,20 +256,36 @@ def ring_k_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
 
 
 def ring_v_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
-    """Shape of the V ring the library reads: transposed [B, Hkv, Dh, ring]."""
-    return (B, hkv, dh, ring)
+    """Shape of the V ring the library reads: tiles of 32 positions, transposed within the
+    tile, [B, Hkv, ring / 32, Dh, 32] (position p, dim d at [p // 32, d, p % 32])."""
+    if ring % 32:
+        raise ValueError("ring_v_shape: ring must be a multiple of 32")
+    return (B, hkv, ring // 32, dh, 32)
+
+
+def ring_v_tiles(v_rows):
+    """A V ring held as rows [B, ring, Hkv, Dh] in the library's tiled layout
+    [B, Hkv, ring / 32, Dh, 32] (a copy; torch tensor or numpy array)."""
+    B, ring, hkv, dh = v_rows.shape
+    t = v_rows.reshape(B, ring // 32, 32, hkv, dh)
+    if isinstance(t, torch.Tensor):
+        return t.permute(0, 3, 1, 4, 2).contiguous()
+    import numpy as np
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2))
 
 
 def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale: float = 0.0):
     """Draft-block attention over each request's K/V ring: q bf16 [B, nq, Hq, Dh], k_blk /
-    v_blk bf16 [B, nq, Hkv, Dh], k_ring bf16 [B, Hkv, ring, Dh], v_ring bf16 [B, Hkv, Dh,
-    ring] (transposed), ctx_len int32 [B].  Returns float32 [B, nq, Hq, Dh]."""
+    v_blk bf16 [B, nq, Hkv, Dh], k_ring bf16 [B, Hkv, ring, Dh], v_ring bf16 [B, Hkv, ring / 32,
+    Dh, 32] (ring_v_shape / ring_v_tiles), ctx_len int32 [B].  Returns float32 [B, nq, Hq, Dh]."""
     lib = load_library()
     for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_ring, "k_ring"), (v_ring, "v_ring")):
         _contig(_need(t, n, _BF16_LIKE, q.device), n)
     _contig(_need(ctx_len, "ctx_len", (torch.int32,), q.device), "ctx_len")
     B, nq, hq, dh = q.shape
     hkv, ring = k_blk.shape[2], k_ring.shape[2]
+    if ring % 32:
+        raise ValueError("ring_attention: the ring must be a multiple of 32 positions")
     if k_blk.shape != (B, nq, hkv, dh) or v_blk.shape != k_blk.shape or k_ring.shape != ring_k_shape(B, hkv, ring, dh) \
             or v_ring.shape != ring_v_shape(B, hkv, ring, dh) or ctx_len.shape != (B,):
         raise ValueError("ring_attention: inconsistent shapes")

@@ -170,21 +170,22 @@ def test_host_validation_lmhead_ring_and_graph():
     need = lib.dflash2_lmhead_topk16_workspace(105, 151936)
     assert need >= 105 * 594 * 16 * 8
     assert lm(wsb=need - 257) == 5
-    # ring attention: head_dim 128, GQA rows <= 48, ring % 8 == 0, window <= ring and at most
-    # 32 splits (window <= 3906), scale >= 0 and finite
+    # ring attention: head_dim 128, GQA rows <= 48, ring a multiple of 32, window <= ring,
+    # scale >= 0 and finite
     ra = lambda q=FAKE, B=15, nq=8, hq=32, hkv=8, dh=128, ring=2112, window=2048, scale=0.0, wsb=big, ctx=FAKE: \
         lib.dflash2_ring_attention(q, FAKE, FAKE, FAKE, FAKE, ctx, B, nq, hq, hkv, dh, ring, window, scale, FAKE, ws,
                                    wsb, NULL)
     assert ra(ctx=NULL) == 1
-    for kw in ({"dh": 64}, {"hq": 30}, {"hq": 56}, {"ring": 2100}, {"window": 2113}, {"window": 0}, {"B": 0},
-               {"ring": 4096, "window": 3907}):
+    for kw in ({"dh": 64}, {"hq": 30}, {"hq": 56}, {"ring": 2100}, {"ring": 2056}, {"ring": 16, "window": 1},
+               {"window": 2113}, {"window": 0}, {"B": 0}, {"ring": 4096, "window": 4097}):
         assert ra(**kw) == 2, kw
-    assert ra(ring=4096, window=3906, scale=-1.0) == 6   # the largest window passes the shape checks
+    assert ra(ring=1 << 20, window=1 << 20, scale=-1.0) == 6   # any window up to the ring passes the shape checks
     assert ra(scale=float("nan")) == 6
     assert ra(scale=float("inf")) == 6
     assert ra(q=MIS) == 3
     need = lib.dflash2_ring_attention_workspace(15, 8, 32, 8, 2048)
-    assert need >= 15 * 8 * 18 * 32 * (128 + 2) * 4
+    assert need >= 15 * 8 * 2 * 32 * (128 + 2) * 4        # two splits per (request, K/V head)
+    assert lib.dflash2_ring_attention_workspace(15, 8, 32, 8, 1 << 20) <= 15 * 8 * 32 * 32 * (128 + 2) * 4 + 4096
     assert ra(wsb=need - 257) == 5
     # graphs: the default stream cannot be captured; null handles are refused
     out = ctypes.c_void_p()

@@ -6,7 +6,7 @@ cores (32 per step, head_dim/32 steps), so a score is off by at most
 (head_dim/32 + 33) 2^-24 max_k sum_d |q_d k_d| * scale (the scale in fp32 included);
 a score error e moves the normalised output by at most 2e in units of
 sum_k p_k |v_k|; p enters the p v product as two bf16 parts (2^-16); the p v sums run in
-fp32 over the window's keys and the splits.  Checked per element:
+fp32 over the window's keys, chunk by chunk, and the splits.  Checked per element:
 |out - ref| <= (2 (Dh/32 + 33) 2^-24 smax + 2^-15 + (nkeys/32 + 64) 2^-24) sum_k p_k |v_k|.
 """
 
@@ -31,10 +31,12 @@ def d2():
 
 def gpu_args(inp):
     """The inputs in the library's layouts: rings [B, ring, Hkv, Dh] as drawn become a
-    head-major K ring [B, Hkv, ring, Dh] and a transposed V ring [B, Hkv, Dh, ring]."""
+    head-major K ring [B, Hkv, ring, Dh] and a V ring in tiles of 32 positions,
+    transposed within the tile [B, Hkv, ring / 32, Dh, 32]."""
     import torch
+    B, ring, hkv, dh = inp["vr_bits"].shape
     kr = np.ascontiguousarray(inp["kr_bits"].transpose(0, 2, 1, 3))
-    vr = np.ascontiguousarray(inp["vr_bits"].transpose(0, 2, 3, 1))
+    vr = np.ascontiguousarray(inp["vr_bits"].reshape(B, ring // 32, 32, hkv, dh).transpose(0, 3, 1, 4, 2))
     return (to_gpu_bits(inp["q_bits"]), to_gpu_bits(inp["kb_bits"]), to_gpu_bits(inp["vb_bits"]), to_gpu_bits(kr),
             to_gpu_bits(vr), torch.from_numpy(inp["ctx_len"]).cuda())
 
@@ -61,12 +63,14 @@ def run_and_check(d2, inp, window, what, scale=0.0):
     (3, 8, 8, 2, 2112, 2048, [1, 2049, 4229]),         # window starts off the 8-row grid, one wraps mid-group
     (2, 8, 12, 2, 2112, 2048, [2047, 2048]),            # 48 query rows (three row tiles); window just full
     (2, 1, 4, 4, 2112, 2048, [1, 3000]),               # one query row per K/V head
-    (4, 8, 8, 8, 40, 33, [31, 32, 33, 77]),             # small ring: wraps, fewer keys than iterations
+    (4, 8, 8, 8, 64, 33, [31, 32, 33, 77]),             # small ring: wraps, fewer steps than waves
     (2, 4, 8, 4, 64, 64, [63, 1000]),                   # window = ring
     (2, 8, 8, 2, 2112, 2048, [-5, 10]),                 # a negative length reads as 0
-    (2, 4, 8, 2, 16, 1, [0, 13]),                       # window 1: the block's keys only
-    (2, 8, 8, 2, 3968, 3906, [3905, 9000]),             # the largest window: 31 context splits + the block's
-    (3, 8, 8, 2, 2056, 2048, [2100, 4111, 5000]),       # ring % 64 != 0: 64-aligned splits cross the wrap
+    (2, 4, 8, 2, 32, 1, [0, 13]),                       # window 1: the block's keys only
+    (2, 8, 8, 2, 3968, 3906, [3905, 9000]),             # 123 context steps over 16 splits
+    (2, 8, 8, 2, 20480, 20480, [20479, 30000]),         # 641 steps: 32 splits, several steps per wave
+    (2, 8, 8, 2, 768, 700, [300, 650]),                 # 22 context steps: uneven shares per wave
+    (3, 8, 8, 2, 2080, 2048, [2100, 4111, 5000]),       # ring of 65 tiles: the window wraps mid-ring
 ])
 def test_ring_attention_parity(d2, B, nq, hq, hkv, ring, window, ctx):
     print(f"ring attention B={B} nq={nq} hq={hq} hkv={hkv} ring={ring} window={window} ctx={ctx}", flush=True)
