@@ -191,7 +191,7 @@ size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, i
       window > (1 << 24))
     return 0;
   Carver c(nullptr);
-  carve_ring(c, batch, hkv, ring_splits(batch, hkv, (int)nq, (int)window), ring_rows_pad((int)nq, (int)hq, (int)hkv));
+  carve_ring(c, batch, hkv, ring_splits(batch, hkv, (int)nq, (int)hq, (int)window), ring_rows_pad((int)nq, (int)hq, (int)hkv));
   return c.off + 256;
 }
 
@@ -209,7 +209,7 @@ dflash2_status dflash2_ring_attention(const uint16_t* q, const uint16_t* k_blk, 
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_ring) || !aligned16(v_ring) ||
       !aligned16(out))
     return DFLASH2_ERR_ALIGN;
-  const int nsplit = ring_splits(batch, hkv, (int)nq, (int)window);
+  const int nsplit = ring_splits(batch, hkv, (int)nq, (int)hq, (int)window);
   const int rows_pad = ring_rows_pad((int)nq, (int)hq, (int)hkv);
   RingWs ws;
   dflash2_status st = carve_checked(

@@ -57,7 +57,7 @@ struct RingWs {
 };
 constexpr int kRingMaxRows = 48;  // query rows (block positions x query heads per K/V head)
 int ring_rows_pad(int nq, int hq, int hkv);
-int ring_splits(int64_t batch, int64_t hkv, int nq, int window);
+int ring_splits(int64_t batch, int64_t hkv, int nq, int hq, int window);
 RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pad);
 
 struct GateWs {

@@ -16,18 +16,21 @@
 // whole tile of each ring: 8 KB of K rows and 8 KB of V^T, both contiguous; the block's
 // keys follow as ceil(nq / 32) more steps.
 //
-// k_ring_split: one work-group of W waves (8; 4 for 48 query rows) per (request, K/V
-// head, split); split s takes an equal share of the steps and wave w every W-th of those.
-// A wave folds its steps on its own, with no LDS traffic but the Q^T slices and no
-// barrier: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A operand, in an order
-// chosen so that each lane ends up holding the scores of 8 consecutive keys of one query
-// row: exactly the lane layout of the B operand of the next product), an online softmax
-// per query row (maximum across the row's four lanes with two permlane swaps),
-// P = 2^(S - m) split into bf16 high and low parts, and O^T += V^T P^T on the same MFMA
-// with V^T straight from the tile.  Two fragment sets per wave: the next step's loads
-// are in flight while a step is folded.  At the end the waves' (max, sum, O) are merged
-// through LDS and the work-group stores its rows' state, or the normalised output when
-// there is one split; k_ring_combine merges the splits.
+// k_ring_split: one work-group of 8 waves per (request, K/V head, 16 query rows, key
+// split).  The row tiles of a (request, K/V head) run side by side on one XCD and read
+// the same tiles, so HBM delivers each tile once and L2 the rest; key splits are added
+// only when the row tiles alone leave compute units idle.  A split takes an equal share
+// of the steps and wave w every 8th of those.  A wave folds its steps on its own, with
+// no LDS traffic but the Q^T slices and no barrier: S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (K rows as the A operand, in an order chosen so that each lane
+// ends up holding the scores of 8 consecutive keys of one query row: exactly the lane
+// layout of the B operand of the next product), an online softmax per query row
+// (maximum across the row's four lanes with two permlane swaps), P = 2^(S - m) split
+// into bf16 high and low parts, and O^T += V^T P^T on the same MFMA with V^T straight
+// from the tile.  Two fragment sets per wave: the next step's loads are in flight while
+// a step is folded.  At the end the waves' (max, sum, O) are merged through LDS and the
+// work-group writes the normalised output, or its rows' state when there are several
+// splits, which k_ring_combine then merges.
 #include "dflash2_internal.h"
 #include "device_common.h"
 
@@ -39,7 +42,8 @@ namespace df2 {
 #ifndef DF2_RING_TARGET
 #define DF2_RING_TARGET 256
 #endif
-constexpr int kRingWavesMax = DF2_RING_WAVES;  // waves of a split work-group (4 for 48 query rows)
+constexpr int kRingWaves = DF2_RING_WAVES;   // waves of a split work-group
+constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kCombThreads = 256;
 constexpr int kRingDh = 128;                 // head dim
 constexpr int kRingStep = 32;                // keys per wave step
@@ -55,12 +59,7 @@ RingWs carve_ring(Carver& c, int64_t batch, int64_t hkv, int nsplit, int rows_pa
   return w;
 }
 
-// waves of the split work-group for MT row tiles: the 48-row tiles need more registers
-// than two waves per SIMD allow
-template <int MT>
-constexpr int ring_waves() { return MT < 3 ? kRingWavesMax : 4; }
-
-template <int MT, int W = ring_waves<MT>()>
+template <int MT, int W = kRingWaves>
 struct RingShared {
   u32x4 q[MT][4][64];                        // Q^T B-operand slices in lane order (read each step)
   float m[W][MT * 16];                       // per-wave row maxima (log2 units)
@@ -298,20 +297,26 @@ __device__ __forceinline__ RingSteps ring_steps(int ctx, int window, int nq) {
 }
 
 template <int MT>
-__global__ void __launch_bounds__(64 * ring_waves<MT>(), (MT < 3 ? 8 : 4) / ring_waves<MT>()) k_ring_split(
+__global__ void __launch_bounds__(kRingThreads, 8 / kRingWaves) k_ring_split(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_blk, const uint16_t* __restrict__ v_blk,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, const int32_t* __restrict__ ctx_len,
-    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nsplit, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o, float* __restrict__ out) {
+    int nq, int hq, int hkv, int ring, int window, float scale_log2, int nsplit, int ntile, int nunits,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, float* __restrict__ out) {
   __shared__ RingShared<MT> sm;
   constexpr int kRows = MT * 16;
-  constexpr int kRingWaves = ring_waves<MT>();
-  constexpr int kRingThreads = 64 * kRingWaves;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int unit = blockIdx.x;                              // (b * hkv + kvh) * nsplit + split
-  const int split = unit % nsplit;
-  const int bk = unit / nsplit;
+  // work-group id -> (request, K/V head, split) unit u and row tile rt; the ntile row
+  // tiles of a unit get ids 8 apart, so they run on one XCD and share its L2 copy of the
+  // unit's K/V tiles (the ring is read from HBM once)
+  const int id = blockIdx.x;
+  const int u = ((id >> 3) / ntile) * 8 + (id & 7);
+  const int rt = (id >> 3) % ntile;
+  if (u >= nunits) return;                                  // padding work-groups
+  const int split = u % nsplit;
+  const int bk = u / nsplit;
+  const int unit = (bk * ntile + rt) * nsplit + split;      // this work-group's partial-sum slot
+  const int row0 = kRows * rt;                              // its first query row
   const int kvh = bk % hkv, b = bk / hkv;
   const int G = hq / hkv;
   const int nrows = nq * G;
@@ -344,7 +349,7 @@ __global__ void __launch_bounds__(64 * ring_waves<MT>(), (MT < 3 ? 8 : 4) / ring
   // dims 32 s + 8 (lane / 16) .. + 7 (zero for padding rows)
   for (int e = tid; e < MT * 4 * 64; e += kRingThreads) {
     const int mt = e >> 8, s4 = (e >> 6) & 3, l = e & 63;
-    const int r = 16 * mt + (l & 15);
+    const int r = row0 + 16 * mt + (l & 15);
     u32x4 v = (u32x4){0u, 0u, 0u, 0u};
     if (r < nrows)
       v = *reinterpret_cast<const u32x4*>(q + ((size_t)(b * nq + r / G) * hq + kvh * G + r % G) * kRingDh + 32 * s4 +
@@ -441,9 +446,9 @@ __global__ void __launch_bounds__(64 * ring_waves<MT>(), (MT < 3 ? 8 : 4) / ring
       const int d = 64 * half + 4 * c4;
       if (nsplit > 1) {
         *reinterpret_cast<f32x4*>(os + (size_t)row * kRingDh + d) = v;
-      } else if (row < nrows) {
+      } else if (row0 + row < nrows) {
         const float inv = 1.f / sm.lt[row];
-        const int i = row / G, h = kvh * G + row % G;
+        const int i = (row0 + row) / G, h = kvh * G + (row0 + row) % G;
         *reinterpret_cast<f32x4*>(out + ((size_t)(b * nq + i) * hq + h) * kRingDh + d) = v * inv;
       }
     }
@@ -458,7 +463,7 @@ __global__ void __launch_bounds__(64 * ring_waves<MT>(), (MT < 3 ? 8 : 4) / ring
 template <int MT, int NSP>
 __global__ void __launch_bounds__(kCombThreads) k_ring_combine(const float* __restrict__ ws_ml,
                                                                 const float* __restrict__ ws_o, int nq, int hq,
-                                                                int hkv, int nsplit, int nunits,
+                                                                int hkv, int nsplit, int ntile, int nunits,
                                                                 float* __restrict__ out) {
   constexpr int kRows = MT * 16;
   const int lane = threadIdx.x & 63;
@@ -467,16 +472,17 @@ __global__ void __launch_bounds__(kCombThreads) k_ring_combine(const float* __re
   const int G = hq / hkv;
   const int nrows = nq * G;
   const int bk = wid / nrows, row = wid - bk * nrows;
-  const size_t u0 = (size_t)bk * nsplit;
+  const int rt = row / kRows, rl = row - rt * kRows;      // row tile and row within it
+  const size_t u0 = ((size_t)bk * ntile + rt) * nsplit;
   float m = -__builtin_inff(), l = 0.f;
   if (lane < nsplit) {
-    m = ws_ml[((u0 + lane) * kRows + row) * 2];
-    l = ws_ml[((u0 + lane) * kRows + row) * 2 + 1];
+    m = ws_ml[((u0 + lane) * kRows + rl) * 2];
+    l = ws_ml[((u0 + lane) * kRows + rl) * 2 + 1];
   }
   f32x2 o[NSP];
 #pragma unroll
   for (int sp = 0; sp < NSP; ++sp)
-    o[sp] = *reinterpret_cast<const f32x2*>(ws_o + ((u0 + (sp < nsplit ? sp : 0)) * kRows + row) * kRingDh + 2 * lane);
+    o[sp] = *reinterpret_cast<const f32x2*>(ws_o + ((u0 + (sp < nsplit ? sp : 0)) * kRows + rl) * kRingDh + 2 * lane);
   float M = m;
 #pragma unroll
   for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
@@ -506,34 +512,18 @@ static int ring_max_steps(int nq, int window) {
   return (window - 1 + 2 * (kRingStep - 1)) / kRingStep + (nq + kRingStep - 1) / kRingStep;
 }
 
-// Splits per (request, K/V head): enough work-groups for two per compute unit, at least
-// one step per wave of the longest request, at most kRingMaxSplits.
-int ring_splits(int64_t batch, int64_t hkv, int nq, int window) {
-  const int64_t pairs = batch * hkv;
-  int64_t n = kRingTargetGroups / pairs;
-  const int most = (ring_max_steps(nq, window) + kRingWavesMax - 1) / kRingWavesMax;
+// Row tiles of 16 query rows per (request, K/V head); each is its own work-group.
+static int ring_tiles(int nq, int hq, int hkv) { return ring_rows_pad(nq, hq, hkv) / 16; }
+
+// Key splits per (request, K/V head): enough work-groups (row tiles x splits) for one per
+// compute unit, at least one step per wave of the longest request, at most kRingMaxSplits.
+int ring_splits(int64_t batch, int64_t hkv, int nq, int hq, int window) {
+  const int64_t groups = batch * hkv * ring_tiles(nq, hq, (int)hkv);
+  int64_t n = kRingTargetGroups / groups;
+  const int most = (ring_max_steps(nq, window) + kRingWaves - 1) / kRingWaves;
   if (n > most) n = most;
   if (n > kRingMaxSplits) n = kRingMaxSplits;
   return n < 1 ? 1 : (int)n;
-}
-
-template <int MT>
-static void ring_launch(hipStream_t s, const uint16_t* q, const uint16_t* kb, const uint16_t* vb, const uint16_t* kr,
-                        const uint16_t* vr, const int32_t* ctx, int B, int nq, int hq, int hkv, int ring, int window,
-                        float scale_log2, int nsplit, const RingWs& ws, float* out) {
-  hipLaunchKernelGGL((k_ring_split<MT>), dim3((unsigned)(B * hkv * nsplit)), dim3(64 * ring_waves<MT>()), 0, s, q, kb, vb, kr,
-                     vr, ctx, nq, hq, hkv, ring, window, scale_log2, nsplit, ws.ml, ws.o, out);
-  if (nsplit == 1) return;
-  const int nunits = B * hkv * nq * (hq / hkv);
-  const dim3 grid((unsigned)((nunits + kCombThreads / 64 - 1) / (kCombThreads / 64)));
-  if (nsplit <= 4)
-    hipLaunchKernelGGL((k_ring_combine<MT, 4>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
-  else if (nsplit <= 8)
-    hipLaunchKernelGGL((k_ring_combine<MT, 8>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
-  else if (nsplit <= 16)
-    hipLaunchKernelGGL((k_ring_combine<MT, 16>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
-  else
-    hipLaunchKernelGGL((k_ring_combine<MT, 32>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, nunits, out);
 }
 
 hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
@@ -542,10 +532,22 @@ hipError_t launch_ring_attention(const uint16_t* q, const uint16_t* k_blk, const
                                  float* out, hipStream_t s) {
   if (nsplit < 1 || nsplit > kRingMaxSplits) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
-  switch (ring_rows_pad(nq, hq, hkv) / 16) {
-    case 1: ring_launch<1>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
-    case 2: ring_launch<2>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
-    default: ring_launch<3>(s, q, k_blk, v_blk, k_ring, v_ring, ctx_len, batch, nq, hq, hkv, ring, window, scale_log2, nsplit, ws, out); break;
+  const int ntile = ring_tiles(nq, hq, hkv);
+  const int nunits = batch * hkv * nsplit;                 // (request, K/V head, split)
+  const unsigned groups = (unsigned)((nunits + 7) / 8 * 8 * ntile);
+  hipLaunchKernelGGL((k_ring_split<1>), dim3(groups), dim3(kRingThreads), 0, s, q, k_blk, v_blk, k_ring, v_ring,
+                     ctx_len, nq, hq, hkv, ring, window, scale_log2, nsplit, ntile, nunits, ws.ml, ws.o, out);
+  if (nsplit > 1) {
+    const int nrows_all = batch * hkv * nq * (hq / hkv);
+    const dim3 grid((unsigned)((nrows_all + kCombThreads / 64 - 1) / (kCombThreads / 64)));
+    if (nsplit <= 4)
+      hipLaunchKernelGGL((k_ring_combine<1, 4>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, ntile, nrows_all, out);
+    else if (nsplit <= 8)
+      hipLaunchKernelGGL((k_ring_combine<1, 8>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, ntile, nrows_all, out);
+    else if (nsplit <= 16)
+      hipLaunchKernelGGL((k_ring_combine<1, 16>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, ntile, nrows_all, out);
+    else
+      hipLaunchKernelGGL((k_ring_combine<1, 32>), grid, dim3(kCombThreads), 0, s, ws.ml, ws.o, nq, hq, hkv, nsplit, ntile, nrows_all, out);
   }
   return hipGetLastError();
 }

@@ -184,7 +184,7 @@ def test_host_validation_lmhead_ring_and_graph():
     assert ra(scale=float("inf")) == 6
     assert ra(q=MIS) == 3
     need = lib.dflash2_ring_attention_workspace(15, 8, 32, 8, 2048)
-    assert need >= 15 * 8 * 2 * 32 * (128 + 2) * 4        # two splits per (request, K/V head)
+    assert need >= 15 * 8 * 32 * (128 + 2) * 4            # (max, sum, O) of every query row
     assert lib.dflash2_ring_attention_workspace(15, 8, 32, 8, 1 << 20) <= 15 * 8 * 32 * 32 * (128 + 2) * 4 + 4096
     assert ra(wsb=need - 257) == 5
     # graphs: the default stream cannot be captured; null handles are refused
