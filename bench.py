@@ -371,7 +371,7 @@ def ring_measure(dflash2, torch, dev, stream, reps=20, nbuf=4):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"batch": B, "rows": nq, "q_heads": hq, "kv_heads": hkv, "head_dim": dh, "ring": ring, "window": window,
             "us_per_call": round(us, 1),
-            "roofline": {"bound": "hbm", "kernel": "dflash2_ring_attention = k_ring_partial + k_ring_combine",
+            "roofline": {"bound": "hbm", "kernel": "dflash2_ring_attention = k_ring_split (+ k_ring_combine when keys are split)",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}}
 
