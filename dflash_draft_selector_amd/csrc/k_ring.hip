@@ -9,12 +9,16 @@
 // the block attends to all of them; query head h uses K/V head h / (Hq / Hkv).
 //
 // Ring layouts, chosen for this read (the hot one: every draft step reads the whole
-// window, a verify writes a few rows): K head-major [B][Hkv][ring][Dh]; V in tiles of 32
-// positions, transposed within the tile: [B][Hkv][ring / 32][Dh][32].  ring % 32 == 0.
+// window, a verify writes a few rows), both in tiles of 32 positions per (request, K/V
+// head), ring % 32 == 0:
+//   K [B][Hkv][ring / 32][2][4][4][16][8]: tile position p, dim d at [(p / 4) % 2]
+//     [d / 32][(d % 32) / 8][4 (p / 8) + p % 4][d % 8], the order in which the MFMA
+//     A-operand slices of a step are read, so each slice is one contiguous 1 KB;
+//   V [B][Hkv][ring / 32][Dh][32]: transposed within the tile.
 // The keys of a (request, K/V head) are cut into steps of 32: context step j covers
 // positions pa + 32 j .. (pa = p0 rounded down to 32), masked to [p0, L), and is one
-// whole tile of each ring: 8 KB of K rows and 8 KB of V^T, both contiguous; the block's
-// keys follow as ceil(nq / 32) more steps.
+// whole tile of each ring (8 KB each); the block's keys follow as ceil(nq / 32) more
+// steps.
 //
 // k_ring_split: one work-group of 8 waves per (request, K/V head, 16 query rows, key
 // split).  The row tiles of a (request, K/V head) run side by side on one XCD and read
@@ -101,9 +105,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void* p, uint6
                                            (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes), 0x00020000);
 }
 
-// The resources of one (request, K/V head): its K ring rows [ring][Dh], its V tiles
-// [ring / 32][Dh][32], and its rows of the block's K and V ([nq] rows, hkv * Dh elements
-// apart).
+// The resources of one (request, K/V head): its K and V tiles (ring * Dh elements each),
+// and its rows of the block's K and V ([nq] rows, hkv * Dh elements apart).
 struct RingRes {
   __amdgpu_buffer_rsrc_t kr, vr, kb, vb;
 };
@@ -113,33 +116,33 @@ struct RingRes {
 #endif
 constexpr int kRingAux = DF2_RING_AUX;       // cache policy of the ring reads
 
-// This lane's byte offsets within a step's tiles: K rows koff + 4 t (k[t]), V^T dim
-// i16 at positions 8 g .. 8 g + 7 (v); the tile and the 16-dim group come in as scalar or
-// immediate offsets.
+// This lane's byte offsets within a step's tiles: its 16 bytes of every K slice (k), and
+// V^T dim i16 at positions 8 g .. 8 g + 7 (v); the tile and the slice or 16-dim group
+// come in as scalar or immediate offsets.
 struct RingLane {
-  uint32_t k[2];
+  uint32_t k;
   uint32_t v;
 };
 
 __device__ __forceinline__ RingLane ring_lane() {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, i16 = lane & 15;
-  const int koff = 8 * (i16 >> 2) + (i16 & 3);
   RingLane l;
-  l.k[0] = (uint32_t)koff * (kRingDh * 2) + 16 * g;
-  l.k[1] = (uint32_t)(koff + 4) * (kRingDh * 2) + 16 * g;
+  l.k = (uint32_t)lane * 16;
   l.v = (uint32_t)i16 * (kRingStep * 2) + 16 * g;
   return l;
 }
 
 // Context step whose tile starts at ring row rb (a multiple of 32): both tiles are
-// kRingStep * Dh * 2 = 8 KB from byte rb * Dh * 2.
+// kRingStep * Dh * 2 = 8 KB from byte rb * Dh * 2; K slice (t, s) is the tile's 1 KB
+// number 4 t + s.
 __device__ __forceinline__ void ring_load_step(RingFrag& f, const RingRes& rr, const RingLane& ln, int rb) {
   const uint32_t tile = (uint32_t)rb * (kRingDh * 2);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) f.k[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rr.kr, ln.k[t] + 64 * s, tile, kRingAux);
+    for (int s = 0; s < 4; ++s)
+      f.k[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rr.kr, ln.k + (4 * t + s) * 1024, tile, kRingAux);
 #pragma unroll
   for (int dt = 0; dt < kRingDh / 16; ++dt)
     f.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rr.vr, ln.v + dt * 16 * kRingStep * 2, tile, kRingAux);

@@ -251,8 +251,26 @@ class Graph:
 
 
 def ring_k_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
-    """Shape of the K ring the library reads: head-major [B, Hkv, ring, Dh]."""
-    return (B, hkv, ring, dh)
+    """Shape of the K ring the library reads: tiles of 32 positions [B, Hkv, ring / 32,
+    32 * Dh], each tile in the order the matrix cores read it (ring_k_tiles)."""
+    if ring % 32:
+        raise ValueError("ring_k_shape: ring must be a multiple of 32")
+    return (B, hkv, ring // 32, 32 * dh)
+
+
+def ring_k_tiles(k_rows):
+    """A K ring held as rows [B, ring, Hkv, Dh] (Dh = 128) in the library's tiled layout:
+    position p, dim d of tile p // 32 (pp = p % 32) at [(pp // 4) % 2][d // 32]
+    [(d % 32) // 8][4 (pp // 8) + pp % 4][d % 8] within the tile's 32 * Dh elements (a
+    copy; torch tensor or numpy array)."""
+    B, ring, hkv, dh = k_rows.shape
+    # source axes: b, tile, pp // 8, (pp // 4) % 2, pp % 4, head, d // 32, (d % 32) // 8, d % 8
+    t = k_rows.reshape(B, ring // 32, 4, 2, 4, hkv, dh // 32, 4, 8)
+    order = (0, 5, 1, 3, 6, 7, 2, 4, 8)
+    if isinstance(t, torch.Tensor):
+        return t.permute(*order).contiguous().reshape(B, hkv, ring // 32, 32 * dh)
+    import numpy as np
+    return np.ascontiguousarray(t.transpose(*order)).reshape(B, hkv, ring // 32, 32 * dh)
 
 
 def ring_v_shape(B: int, hkv: int, ring: int, dh: int) -> tuple:
@@ -276,16 +294,15 @@ def ring_v_tiles(v_rows):
 
 def ring_attention(q, k_blk, v_blk, k_ring, v_ring, ctx_len, window: int = 2048, scale: float = 0.0):
     """Draft-block attention over each request's K/V ring: q bf16 [B, nq, Hq, Dh], k_blk /
-    v_blk bf16 [B, nq, Hkv, Dh], k_ring bf16 [B, Hkv, ring, Dh], v_ring bf16 [B, Hkv, ring / 32,
-    Dh, 32] (ring_v_shape / ring_v_tiles), ctx_len int32 [B].  Returns float32 [B, nq, Hq, Dh]."""
+    v_blk bf16 [B, nq, Hkv, Dh], k_ring bf16 [B, Hkv, ring / 32, 32 * Dh] (ring_k_shape /
+    ring_k_tiles), v_ring bf16 [B, Hkv, ring / 32, Dh, 32] (ring_v_shape / ring_v_tiles),
+    ctx_len int32 [B].  Returns float32 [B, nq, Hq, Dh]."""
     lib = load_library()
     for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_ring, "k_ring"), (v_ring, "v_ring")):
         _contig(_need(t, n, _BF16_LIKE, q.device), n)
     _contig(_need(ctx_len, "ctx_len", (torch.int32,), q.device), "ctx_len")
     B, nq, hq, dh = q.shape
-    hkv, ring = k_blk.shape[2], k_ring.shape[2]
-    if ring % 32:
-        raise ValueError("ring_attention: the ring must be a multiple of 32 positions")
+    hkv, ring = k_blk.shape[2], 32 * k_ring.shape[2]
     if k_blk.shape != (B, nq, hkv, dh) or v_blk.shape != k_blk.shape or k_ring.shape != ring_k_shape(B, hkv, ring, dh) \
             or v_ring.shape != ring_v_shape(B, hkv, ring, dh) or ctx_len.shape != (B,):
         raise ValueError("ring_attention: inconsistent shapes")

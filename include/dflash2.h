@@ -136,12 +136,16 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
  * keys).
  *
  * q bf16 [batch, nq, hq, head_dim]; k_blk, v_blk bf16 [batch, nq, hkv, head_dim];
- * k_ring bf16 [batch, hkv, ring, head_dim] (head-major); v_ring bf16 [batch, hkv,
- * ring / 32, head_dim, 32] (tiles of 32 positions, transposed within the tile: position
- * p, dim d at [p / 32][d][p % 32]), the layouts that let every draft step read the
- * window as contiguous 8 KB tiles of K and V (a verify writes a few rows); ctx_len int32
- * [batch] (values < 0 read as 0); out float [batch, nq, hq, head_dim].  All row-major,
- * 16-byte aligned.  Workspace: dflash2_ring_attention_workspace bytes, any contents.
+ * Both rings are kept in tiles of 32 positions per (request, K/V head), the layouts that
+ * let every draft step read the window as contiguous 8 KB tiles (a verify writes a few
+ * rows); position p, dim d of tile p / 32 (pp = p % 32):
+ *   k_ring bf16 [batch, hkv, ring / 32, 2, 4, 4, 16, 8] at
+ *     [(pp / 4) % 2][d / 32][(d % 32) / 8][4 (pp / 8) + pp % 4][d % 8]
+ *     (the order in which the matrix cores read a tile);
+ *   v_ring bf16 [batch, hkv, ring / 32, head_dim, 32] at [d][pp] (transposed).
+ * ctx_len int32 [batch] (values < 0 read as 0); out float [batch, nq, hq, head_dim].
+ * Other arrays row-major; all 16-byte aligned.  Workspace:
+ * dflash2_ring_attention_workspace bytes, any contents.
  * Errors: NULL pointers; head_dim != 128, hq % hkv != 0, nq * hq / hkv > 48, ring < 32
  *         or ring % 32 != 0, window < 1 or window > ring -> DFLASH2_ERR_SHAPE;
  *         scale < 0 or not finite -> DFLASH2_ERR_VALUE; alignment; workspace.

@@ -30,13 +30,12 @@ def d2():
 
 
 def gpu_args(inp):
-    """The inputs in the library's layouts: rings [B, ring, Hkv, Dh] as drawn become a
-    head-major K ring [B, Hkv, ring, Dh] and a V ring in tiles of 32 positions,
-    transposed within the tile [B, Hkv, ring / 32, Dh, 32]."""
+    """The inputs in the library's layouts: rings [B, ring, Hkv, Dh] as drawn become the
+    tiled K and V rings (tests/test_ring_layout.py pins both re-layouts)."""
     import torch
-    B, ring, hkv, dh = inp["vr_bits"].shape
-    kr = np.ascontiguousarray(inp["kr_bits"].transpose(0, 2, 1, 3))
-    vr = np.ascontiguousarray(inp["vr_bits"].reshape(B, ring // 32, 32, hkv, dh).transpose(0, 3, 1, 4, 2))
+    from dflash_draft_selector_amd import dflash2
+    kr = dflash2.ring_k_tiles(inp["kr_bits"])
+    vr = dflash2.ring_v_tiles(inp["vr_bits"])
     return (to_gpu_bits(inp["q_bits"]), to_gpu_bits(inp["kb_bits"]), to_gpu_bits(inp["vb_bits"]), to_gpu_bits(kr),
             to_gpu_bits(vr), torch.from_numpy(inp["ctx_len"]).cuda())
 
