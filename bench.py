@@ -515,6 +515,11 @@ def main():
 
     # every entry point on the same workload, each as its own graph of nbuf calls
     sel_t = {k: torch.empty_like(v) for k, v in sel.items()}
+
+    def three_calls(lg):
+        ci, cv = dflash2.topk16(lg)
+        return dflash2.walk(dflash2.pair_score(ci, cv, verified, A, Bt, H)[0], ci, 0.0, 0)
+
     Hs = torch.empty_like(H)
     y2 = torch.empty_like(y)
     comp_fns = {
@@ -523,6 +528,10 @@ def main():
         "select_sampled_T1": lambda i: dflash2.select(logits[i], verified, A, Bt, H, 1.0, 7, out=sel_t),
         "select_gated_greedy": lambda i: dflash2.select_gated(logits[i], verified, A, Bt, h, Wh, bias, "sigmoid", 0.0, 0,
                                                               out=sel_t, H_out=Hs),
+        # the same path as three separate calls (topk16 -> pair_score -> walk; bit-identical
+        # to the select), and the select on one buffer only (cache-warm: a cache number)
+        "select_three_calls_greedy": lambda i: three_calls(logits[i]),
+        "select_greedy_cache_warm_1buf": lambda i: dflash2.select(logits[0], verified, A, Bt, H, 0.0, 0, out=sel_t),
         "conv2tap": lambda i: dflash2.conv2tap(x, xp, taps, y=y2),
         "spec_accept_greedy": lambda i: dflash2.spec_accept(targets[i], sel["tokens"], sel["cand_idx"], sel["q"], 0.0, 0),
         "spec_accept_sampled_T1": lambda i: dflash2.spec_accept(targets[i], sel_t["tokens"], sel_t["cand_idx"],
@@ -549,6 +558,25 @@ def main():
 
     positions = w.B * w.K
     value = positions / (select_us * 1e-6)
+
+    # a measured read stream on the same GPU, the reference the select's bandwidth is
+    # also quoted against: torch's sum over 1 GiB read as int64 (one kernel per call,
+    # eager; the fastest of torch's reductions here: bf16 and fp32 max-reductions read
+    # at 2.0 and 3.6 TB/s)
+    big = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    for _ in range(2):
+        torch.sum(big)
+    torch.cuda.synchronize()
+    rs = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(big)
+        e1.record()
+        torch.cuda.synchronize()
+        rs.append(big.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del big
+    read_stream_gbs = sorted(rs)[len(rs) // 2]
 
     # sanity: the timed graph's last select matches an eager call on the same buffer
     ref = dflash2.select(logits[(steps - 1) % nbuf], verified, A, Bt, H, 0.0, 0)
@@ -579,6 +607,8 @@ def main():
                        "us_max": round(step_times[-1], 3),
                        "positions_per_s": round(positions / (step_us * 1e-6), 1)},
         "components_us_per_call": components,
+        "read_stream": {"what": "torch.sum over 1 GiB read as int64, eager, median of 5", "gbs": round(read_stream_gbs, 1),
+                        "select_frac_of_read_stream": round(achieved / read_stream_gbs, 4)},
         "wall_s": round(wall, 3),
     }
     # the proposer step (gated select + conv) as one library graph launch against the
