@@ -182,8 +182,40 @@ dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64
   dflash2_status st =
       carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_lmhead(c, rows, vocab); }, &ws);
   if (st != DFLASH2_OK) return st;
-  return hip_status(launch_lmhead_topk16(h, w, (int)rows, (int)hidden, (int)vocab, cand_idx, cand_val, row_status,
-                                         ws, stream));
+  return hip_status(launch_lmhead_topk16(h, w, false, (int)rows, (int)hidden, (int)vocab, cand_idx, cand_val,
+                                         row_status, ws, stream));
+}
+
+size_t dflash2_lmhead_packed_bytes(int64_t vocab, int64_t hidden) {
+  if (vocab < DFLASH2_NCAND || vocab > kMaxVocab || hidden < 256 || hidden % 256 != 0 || hidden > ((int64_t)1 << 20))
+    return 0;
+  return lmhead_packed_elems(vocab, hidden) * sizeof(uint16_t);
+}
+
+dflash2_status dflash2_lmhead_pack(const uint16_t* w, int64_t vocab, int64_t hidden, uint16_t* w_packed,
+                                   hipStream_t stream) {
+  if (!w || !w_packed) return DFLASH2_ERR_NULL;
+  if (vocab < DFLASH2_NCAND || vocab > kMaxVocab || hidden < 256 || hidden % 256 != 0 || hidden > ((int64_t)1 << 20))
+    return DFLASH2_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(w_packed)) return DFLASH2_ERR_ALIGN;
+  return hip_status(launch_lmhead_pack(w, (int)vocab, (int)hidden, w_packed, stream));
+}
+
+dflash2_status dflash2_lmhead_topk16_packed(const uint16_t* h, const uint16_t* w_packed, int64_t rows,
+                                            int64_t hidden, int64_t vocab, int32_t* cand_idx, float* cand_val,
+                                            int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  if (!h || !w_packed || !cand_idx || !cand_val) return DFLASH2_ERR_NULL;
+  if (rows < 1 || rows > kMaxItems / 1024 || hidden < 256 || hidden % 256 != 0 || hidden > ((int64_t)1 << 20) ||
+      vocab < DFLASH2_NCAND || vocab > kMaxVocab)
+    return DFLASH2_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_packed)) return DFLASH2_ERR_ALIGN;
+  LmheadWs ws;
+  dflash2_status st =
+      carve_checked(workspace, workspace_bytes, [&](Carver& c) { return carve_lmhead(c, rows, vocab); }, &ws);
+  if (st != DFLASH2_OK) return st;
+  return hip_status(launch_lmhead_topk16(h, w_packed, true, (int)rows, (int)hidden, (int)vocab, cand_idx, cand_val,
+                                         row_status, ws, stream));
 }
 
 size_t dflash2_ring_attention_workspace(int64_t batch, int64_t nq, int64_t hq, int64_t hkv, int64_t window) {

@@ -99,7 +99,9 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
                                float* S, int32_t* tokens, int32_t* slots, float* q, int32_t* row_status,
                                SelectGatedWs ws, hipStream_t s);
 
-hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+size_t lmhead_packed_elems(int64_t vocab, int64_t hidden);
+hipError_t launch_lmhead_pack(const uint16_t* w, int vocab, int hidden, uint16_t* w_packed, hipStream_t s);
+hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, bool packed, int rows, int hidden, int vocab,
                                 int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
                                 hipStream_t s);
 

@@ -196,8 +196,10 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
 // chip in whole rounds would otherwise run few work-groups): each sums its share of the
 // stages and stores the fp32 tile (tail[(tail tile, part)][wave][m][nt][lane], f32x4),
 // and k_lmhead_combine adds the parts in order and takes the top-16 of each 16-row tile.
-// RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.
-template <int MT, int RING>
+// RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.  PACKED: W in the
+// packed layout of lm_packed_offset (each load instruction one contiguous 1 KB), else
+// row-major [vocab][hidden] (each instruction 64 bytes of 16 rows).
+template <int MT, int RING, bool PACKED>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
                                                               const uint16_t* __restrict__ w, int rows, int hidden,
                                                               int vocab, int row0, int ntiles, int nfull, int nparts,
@@ -217,13 +219,22 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
   const int ns = whole ? nstages : (int)((long long)nstages * (part + 1) / nparts) - s0;
   const int col0 = tile * kLmCols;
 
-  // this lane's two W rows (a column past the vocabulary reads the last row, unused)
+  // this lane's two W rows (a column past the vocabulary reads the last row, unused), or
+  // its 16 bytes of every packed 1 KB slice of the tile
   const uint16_t* wrow[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int col = col0 + 32 * wv + 16 * nt + i16;
     wrow[nt] = w + (size_t)(col < vocab ? col : vocab - 1) * hidden + 8 * g;
   }
+  const uint16_t* wpk = w + (size_t)tile * kLmCols * hidden + wv * 512 + lane * 8;
+  // W fragment (half-stage hs, step s of it, column tile nt)
+  auto wfrag = [&](int hs, int s, int nt) -> u32x4 {
+    if constexpr (PACKED)
+      return *reinterpret_cast<const u32x4*>(wpk + ((size_t)(hs * (kLmSteps / 2) + s) * 2 + nt) * (kLmWaves * 512));
+    else
+      return *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)hs * (kLmStageDims / 2) + 32 * s);
+  };
 
   // staging of one 256-dim stage of the hidden rows: thread slot e covers row
   // (tid + 512 e) / 32, 16-byte slot (tid + 512 e) % 32; rows past the group are zero
@@ -267,7 +278,7 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
     for (int s = 0; s < kHalf; ++s)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        wr[s][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)hs * (kLmStageDims / 2) + 32 * s);
+        wr[s][nt] = wfrag(hs, s, nt);
   };
   fill(wr0, 0);
   fill(wr1, 1);
@@ -299,7 +310,7 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
         for (int b = s + 1 - kLmBurst; b <= s; ++b)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
-            wr[b][nt] = *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)nw * (kLmStageDims / 2) + 32 * b);
+            wr[b][nt] = wfrag(nw, b, nt);
       }
     }
     if (part_h == 1) {
@@ -407,21 +418,22 @@ __global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned
 
 // Work-groups resident per compute unit for k_lmhead_tiles<MT, RING> times the
 // compute units, the work-groups of one full round.
-template <int MT, int RING>
+template <int MT, int RING, bool PACKED>
 static int lmhead_round(int dev_cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lmhead_tiles<MT, RING>, kLmThreads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lmhead_tiles<MT, RING, PACKED>, kLmThreads, 0) !=
+          hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   return per_cu * dev_cus;
 }
 
-template <int MT, int RING>
+template <int MT, int RING, bool PACKED>
 static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
                          int row0, int dev_cus, const LmheadWs& ws) {
   const int ntiles = lmhead_tiles(vocab);
   const int nstages = hidden / kLmStageDims;
-  const int round = lmhead_round<MT, RING>(dev_cus);
+  const int round = lmhead_round<MT, RING, PACKED>(dev_cus);
   const int tail = ntiles % round;
   int nparts = 1;
   // a last round under half full: split its tiles so that it fills the chip
@@ -434,7 +446,7 @@ static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, in
   }
   const int nfull = nparts > 1 ? ntiles - tail : ntiles;
   const int grid = nfull + (nparts > 1 ? tail * nparts : 0);
-  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
+  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING, PACKED>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
                      vocab, row0, ntiles, nfull, nparts, ws.partials, reinterpret_cast<f32x4*>(ws.tail));
   if (nparts > 1)
     hipLaunchKernelGGL((k_lmhead_combine<MT>), dim3((unsigned)(tail * MT)), dim3(kLmThreads), 0, s,
@@ -452,28 +464,71 @@ size_t lmhead_tail_bytes() {
   return (size_t)cus * 8 * 16 * 1024;
 }
 
-hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+template <bool PACKED>
+static void lmhead_groups(hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
+                          int cus, const LmheadWs& ws) {
+  for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
+    const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
+    if (n <= 16)
+      lmhead_group<1, 2, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+    else if (n <= 32)
+      lmhead_group<2, 2, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+    else if (n <= 64)
+      lmhead_group<4, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+    else if (n <= 112)
+      lmhead_group<7, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+    else
+      lmhead_group<8, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+  }
+}
+
+hipError_t launch_lmhead_topk16(const uint16_t* h, const uint16_t* w, bool packed, int rows, int hidden, int vocab,
                                 int32_t* cand_idx, float* cand_val, int32_t* row_status, LmheadWs ws,
                                 hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
-    const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
-    if (n <= 16)
-      lmhead_group<1, 2>(s, h, w, rows, hidden, vocab, row0, cus, ws);
-    else if (n <= 32)
-      lmhead_group<2, 2>(s, h, w, rows, hidden, vocab, row0, cus, ws);
-    else if (n <= 64)
-      lmhead_group<4, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
-    else if (n <= 112)
-      lmhead_group<7, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
-    else
-      lmhead_group<8, 3>(s, h, w, rows, hidden, vocab, row0, cus, ws);
-  }
+  if (packed)
+    lmhead_groups<true>(s, h, w, rows, hidden, vocab, cus, ws);
+  else
+    lmhead_groups<false>(s, h, w, rows, hidden, vocab, cus, ws);
   hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)rows), dim3(kLmMergeThreads), 0, s, ws.partials,
                      lmhead_tiles(vocab), cand_idx, cand_val, row_status);
+  return hipGetLastError();
+}
+
+// ---- the packed weight ---------------------------------------------------------------
+// Tile T of 256 vocabulary columns, 32-dim step k of the hidden dimension: 16 KB laid out
+// [column tile nt (2)][wave (8)][dim group g (4)][column i (16)][8 dims], column
+// 256 T + 32 wave + 16 nt + i, dims 32 k + 8 g .. + 7: each 1 KB is one MFMA B-operand
+// slice of one wave, lane 16 g + i reading its 16 bytes.  Columns past the vocabulary
+// are zero.
+size_t lmhead_packed_elems(int64_t vocab, int64_t hidden) { return (size_t)lmhead_tiles(vocab) * kLmCols * hidden; }
+
+// One thread per 16-byte piece of the packed weight.
+__global__ void __launch_bounds__(256) k_lmhead_pack(const uint16_t* __restrict__ w, int vocab, int hidden,
+                                                      uint16_t* __restrict__ wp, size_t npieces) {
+  const size_t p = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= npieces) return;
+  const int lane = (int)(p & 63);
+  const size_t q = p >> 6;                           // (T * nsteps + k) * 16 + nt * 8 + wave
+  const int wave = (int)(q & 7), nt = (int)((q >> 3) & 1);
+  const size_t tk = q >> 4;
+  const int nsteps = hidden / 32;
+  const int k = (int)(tk % nsteps);
+  const int T = (int)(tk / nsteps);
+  const int col = T * kLmCols + 32 * wave + 16 * nt + (lane & 15);
+  const int d0 = 32 * k + 8 * (lane >> 4);
+  u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+  if (col < vocab) v = *reinterpret_cast<const u32x4*>(w + (size_t)col * hidden + d0);
+  *reinterpret_cast<u32x4*>(wp + p * 8) = v;
+}
+
+hipError_t launch_lmhead_pack(const uint16_t* w, int vocab, int hidden, uint16_t* wp, hipStream_t s) {
+  const size_t npieces = lmhead_packed_elems(vocab, hidden) / 8;
+  hipLaunchKernelGGL(k_lmhead_pack, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0, s, w, vocab, hidden, wp,
+                     npieces);
   return hipGetLastError();
 }
 

@@ -39,6 +39,10 @@ _SIGNATURES = {
     "dflash2_topk16": ([_c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
     "dflash2_lmhead_topk16_workspace": ([_i64, _i64], _size),
     "dflash2_lmhead_topk16": ([_c_ptr, _c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size, _c_ptr], _int),
+    "dflash2_lmhead_packed_bytes": ([_i64, _i64], _size),
+    "dflash2_lmhead_pack": ([_c_ptr, _i64, _i64, _c_ptr, _c_ptr], _int),
+    "dflash2_lmhead_topk16_packed": ([_c_ptr, _c_ptr, _i64, _i64, _i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _size,
+                                      _c_ptr], _int),
     "dflash2_graph_begin": ([_c_ptr], _int),
     "dflash2_graph_end": ([_c_ptr, ctypes.POINTER(ctypes.c_void_p)], _int),
     "dflash2_graph_launch": ([_c_ptr, _c_ptr], _int),
@@ -203,6 +207,45 @@ def lmhead_topk16(h: torch.Tensor, w: torch.Tensor, row_status: bool = False):
     ws = workspace("lmhead_topk16", nbytes, dev, (rows, V))
     _check(lib.dflash2_lmhead_topk16(_ptr(h), _ptr(w), rows, D, V, _ptr(idx), _ptr(val), _ptr(st), _ptr(ws),
                                      ws.numel(), _stream()), "dflash2_lmhead_topk16")
+    return (idx, val, st) if row_status else (idx, val)
+
+
+def lmhead_pack(w: torch.Tensor) -> torch.Tensor:
+    """The LM-head weight bf16 [V, D] in the packed layout lmhead_topk16_packed reads (a
+    new bf16 tensor of dflash2_lmhead_packed_bytes, done once per weight)."""
+    lib = load_library()
+    _contig(_need(w, "w", _BF16_LIKE), "w")
+    if w.dim() != 2:
+        raise ValueError("lmhead_pack: w must be [V, D]")
+    V, D = w.shape
+    nbytes = lib.dflash2_lmhead_packed_bytes(V, D)
+    if nbytes == 0:
+        raise ValueError("lmhead_pack: unsupported shape")
+    wp = torch.empty(nbytes // 2, dtype=w.dtype, device=w.device)
+    _check(lib.dflash2_lmhead_pack(_ptr(w), V, D, _ptr(wp), _stream()), "dflash2_lmhead_pack")
+    return wp
+
+
+def lmhead_topk16_packed(h: torch.Tensor, w_packed: torch.Tensor, vocab: int, row_status: bool = False):
+    """lmhead_topk16 on a weight packed by lmhead_pack (bit-identical results): h bf16
+    [rows, D] (or [..., D]), w_packed from lmhead_pack of a [vocab, D] weight."""
+    lib = load_library()
+    _contig(_need(h, "h", _BF16_LIKE), "h")
+    _contig(_need(w_packed, "w_packed", _BF16_LIKE, h.device), "w_packed")
+    if h.dim() < 2:
+        raise ValueError("lmhead_topk16_packed: h must be [..., D]")
+    D, V = h.shape[-1], int(vocab)
+    if w_packed.numel() * 2 != lib.dflash2_lmhead_packed_bytes(V, D):
+        raise ValueError("lmhead_topk16_packed: w_packed does not hold a packed [vocab, D] weight")
+    rows = h.numel() // D
+    dev = h.device
+    idx = torch.empty(h.shape[:-1] + (NCAND,), dtype=torch.int32, device=dev)
+    val = torch.empty(h.shape[:-1] + (NCAND,), dtype=torch.float32, device=dev)
+    st = torch.empty(h.shape[:-1], dtype=torch.int32, device=dev) if row_status else None
+    nbytes = lib.dflash2_lmhead_topk16_workspace(rows, V)
+    ws = workspace("lmhead_topk16", nbytes, dev, (rows, V))
+    _check(lib.dflash2_lmhead_topk16_packed(_ptr(h), _ptr(w_packed), rows, D, V, _ptr(idx), _ptr(val), _ptr(st),
+                                            _ptr(ws), ws.numel(), _stream()), "dflash2_lmhead_topk16_packed")
     return (idx, val, st) if row_status else (idx, val)
 
 

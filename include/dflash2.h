@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DFLASH2_ABI_VERSION 2
+#define DFLASH2_ABI_VERSION 3
 #define DFLASH2_NCAND 16       /* candidates per draft position */
 #define DFLASH2_MAX_K 64       /* draft positions per request */
 #define DFLASH2_MAX_TOPK 32    /* largest top_k of the filtered verify */
@@ -116,6 +116,33 @@ size_t dflash2_lmhead_topk16_workspace(int64_t rows, int64_t vocab);
 dflash2_status dflash2_lmhead_topk16(const uint16_t* h, const uint16_t* w, int64_t rows, int64_t hidden,
                                      int64_t vocab, int32_t* cand_idx, float* cand_val, int32_t* row_status,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * The same LM head on a weight packed once for the matrix cores.  The weight is
+ * constant (the target's LM head, [RFC] "Questions", item 4), so it can be re-laid once
+ * at load time in the order the tile kernel reads it: every load instruction then reads
+ * one contiguous 1 KB instead of 64 bytes of 16 rows.  Results are bit-identical to
+ * dflash2_lmhead_topk16 on the unpacked weight.
+ *
+ * Packed layout (bf16 bits, dflash2_lmhead_packed_bytes bytes): tiles of 256 vocabulary
+ * columns; tile T, hidden step k (32 dims) is 16 KB laid out
+ * [nt (2)][wave (8)][g (4)][i (16)][8 dims], column 256 T + 32 wave + 16 nt + i, dims
+ * 32 k + 8 g .. + 7; columns past the vocabulary are zero.  Element (v, d) sits at
+ * ((((T * hidden / 32 + d / 32) * 2 + nt) * 8 + wave) * 64 + 16 ((d % 32) / 8) + i) * 8
+ * + d % 8 with T = v / 256, wave = (v % 256) / 32, nt = (v % 32) / 16, i = v % 16.
+ *
+ * dflash2_lmhead_pack: w bf16 bits [vocab, hidden] row-major -> w_packed (16-byte
+ *   aligned, dflash2_lmhead_packed_bytes; 0 on a bad shape); enqueued on `stream`.
+ * dflash2_lmhead_topk16_packed: as dflash2_lmhead_topk16 with w_packed in place of w.
+ * Errors: as dflash2_lmhead_topk16.
+ * ------------------------------------------------------------------------------- */
+size_t dflash2_lmhead_packed_bytes(int64_t vocab, int64_t hidden);
+dflash2_status dflash2_lmhead_pack(const uint16_t* w, int64_t vocab, int64_t hidden, uint16_t* w_packed,
+                                   hipStream_t stream);
+dflash2_status dflash2_lmhead_topk16_packed(const uint16_t* h, const uint16_t* w_packed, int64_t rows,
+                                            int64_t hidden, int64_t vocab, int32_t* cand_idx, float* cand_val,
+                                            int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * Draft-block attention over each request's K/V ring.  [FT] "Details": the released

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
     missing = [n for n in _declared() if n not in exported]
     assert not missing, missing
     assert set(d2.EXPORTED) == set(_declared())
-    assert lib.dflash2_abi_version() == 2
+    assert lib.dflash2_abi_version() == 3
 
 
 def test_header_compiles_as_c():
@@ -170,6 +170,19 @@ def test_host_validation_lmhead_ring_and_graph():
     need = lib.dflash2_lmhead_topk16_workspace(105, 151936)
     assert need >= 105 * 594 * 16 * 8
     assert lm(wsb=need - 257) == 5
+    # the packed LM head: the same checks; the packed size covers whole 256-column tiles
+    lmp = lambda h=FAKE, w=FAKE, rows=105, hidden=5120, vocab=151936, idx=FAKE, wsb=big: \
+        lib.dflash2_lmhead_topk16_packed(h, w, rows, hidden, vocab, idx, FAKE, NULL, ws, wsb, NULL)
+    assert lmp(w=NULL) == 1
+    for kw in ({"rows": 0}, {"hidden": 5000}, {"vocab": 15}, {"vocab": (1 << 19) + 1}):
+        assert lmp(**kw) == 2, kw
+    assert lmp(h=MIS) == 3
+    assert lmp(wsb=need - 257) == 5
+    assert lib.dflash2_lmhead_packed_bytes(151936, 5120) == 594 * 256 * 5120 * 2
+    assert lib.dflash2_lmhead_packed_bytes(151936, 5000) == 0 and lib.dflash2_lmhead_packed_bytes(15, 5120) == 0
+    assert lib.dflash2_lmhead_pack(NULL, 151936, 5120, FAKE, NULL) == 1
+    assert lib.dflash2_lmhead_pack(FAKE, 151936, 5000, FAKE, NULL) == 2
+    assert lib.dflash2_lmhead_pack(FAKE, 151936, 5120, MIS, NULL) == 3
     # ring attention: head_dim 128, GQA rows <= 48, ring a multiple of 32, window <= ring,
     # scale >= 0 and finite
     ra = lambda q=FAKE, B=15, nq=8, hq=32, hkv=8, dh=128, ring=2112, window=2048, scale=0.0, wsb=big, ctx=FAKE: \

@@ -168,3 +168,57 @@ def test_lmhead_topk16_full_size_sampled_rows(d2):
     n_eq, n_ex, n_amb = check_rows(cpu(idx), cpu(val), inp["h_bits"], inp["w_bits"], rows_sel=sel)
     print(f"  sampled rows equal to the oracle {n_eq}/8; exact-checked {n_ex}; ambiguous cut {n_amb}", flush=True)
     assert np.mean(cpu(idx)[:, 0] == inp["peak_idx"]) > 0.9
+
+
+def pack_ref(w_bits):
+    """The packed layout of include/dflash2.h (dflash2_lmhead_pack), written out with
+    numpy: columns padded with zeros to whole 256-column tiles, then per tile and 32-dim
+    step [nt][wave][g][i][8 dims] for column 256 T + 32 wave + 16 nt + i, dims
+    32 k + 8 g .. + 7."""
+    V, D = w_bits.shape
+    T = (V + 255) // 256
+    wp = np.zeros((T * 256, D), dtype=np.uint16)
+    wp[:V] = w_bits
+    t = wp.reshape(T, 8, 2, 16, D // 32, 4, 8)            # T, wave, nt, i, k, g, e
+    return np.ascontiguousarray(t.transpose(0, 4, 2, 1, 5, 3, 6)).reshape(-1)
+
+
+@pytest.mark.parametrize("vocab,hidden", [(300, 512), (4096, 256), (16, 768)])
+def test_lmhead_pack_layout(d2, vocab, hidden):
+    w = synth.lmhead_inputs(3, hidden, vocab, seed=vocab)["w_bits"]
+    wp = d2.lmhead_pack(to_gpu_bits(w))
+    np.testing.assert_array_equal(cpu(wp).view(np.uint16), pack_ref(w))
+
+
+@pytest.mark.parametrize("rows,hidden,vocab", [
+    (7, 256, 5003),              # one row tile, ragged last column tile
+    (105, 512, 9000),            # eight row tiles
+    (130, 256, 3000),            # two row groups
+    (5, 256, 270),               # a last tile with 14 columns
+    (40, 2048, 70000),           # split last round, 8 parts
+    (40, 1280, 91000),           # split parts of unequal length
+])
+def test_lmhead_topk16_packed_is_bit_identical(d2, rows, hidden, vocab):
+    inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows * 3 + vocab)
+    print(f"lmhead packed rows={rows} hidden={hidden} vocab={vocab}", flush=True)
+    h, w = to_gpu_bits(inp["h_bits"]), to_gpu_bits(inp["w_bits"])
+    idx, val, st = d2.lmhead_topk16(h, w, row_status=True)
+    pidx, pval, pst = d2.lmhead_topk16_packed(h, d2.lmhead_pack(w), vocab, row_status=True)
+    np.testing.assert_array_equal(cpu(pidx), cpu(idx))
+    np.testing.assert_array_equal(cpu(pval), cpu(val))
+    np.testing.assert_array_equal(cpu(pst), cpu(st))
+    if rows <= 40:
+        n_eq, n_ex, n_amb = check_rows(cpu(pidx), cpu(pval), inp["h_bits"], inp["w_bits"])
+        assert n_ex >= rows // 2
+
+
+def test_lmhead_topk16_packed_full_size(d2):
+    # the benchmark's launch on the packed weight: bit-identical to the row-major weight
+    rows, hidden, vocab = 105, 5120, synth.VOCAB_QWEN
+    inp = synth.lmhead_inputs(rows, hidden, vocab, seed=2)
+    h, w = to_gpu_bits(inp["h_bits"]), to_gpu_bits(inp["w_bits"])
+    idx, val = d2.lmhead_topk16(h, w)
+    wp = d2.lmhead_pack(w)
+    pidx, pval = d2.lmhead_topk16_packed(h, wp, vocab)
+    np.testing.assert_array_equal(cpu(pidx), cpu(idx))
+    np.testing.assert_array_equal(cpu(pval), cpu(val))
