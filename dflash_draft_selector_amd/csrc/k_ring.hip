@@ -344,8 +344,11 @@ __global__ void __launch_bounds__(kRingThreads, 8 / kRingWaves) k_ring_split(
   const RingLane ln = ring_lane();
   const int jlast = j + kRingWaves * ((jend - 1 - j) / kRingWaves);
   const int rstep = kRingStep * kRingWaves;     // ring rows between the wave's steps
-  int rb = (rs.pa + kRingStep * j) % ring;
-  const int rlast = (rs.pa + kRingStep * jlast) % ring;
+  // positions relative to pa from here on (a context length near INT_MAX stays in range)
+  const int ra = rs.pa % ring;                  // ring row of position pa
+  const int lo = rs.p0 - rs.pa, hi = rs.L - rs.pa;
+  int rb = (ra + kRingStep * j) % ring;
+  const int rlast = (ra + kRingStep * jlast) % ring;
   if (j < jend) ring_load_step(f, rr, ln, rb);
 
   // Q^T as the B operand, staged in LDS: entry [mt][s][lane] is row 16 mt + lane % 16,
@@ -378,8 +381,7 @@ __global__ void __launch_bounds__(kRingThreads, 8 / kRingWaves) k_ring_split(
         int rn = rb + rstep;
         rn = rn >= ring ? rn % ring : rn;
         ring_load_step(fb, rr, ln, j + kRingWaves < jend ? rn : rlast);
-        const int base = rs.pa + kRingStep * j;
-        ring_fold<MT>(sm, f, base, rs.p0, rs.L, scale_log2, st);
+        ring_fold<MT>(sm, f, kRingStep * j, lo, hi, scale_log2, st);
         j += kRingWaves;
         rb = rn;
         if (j >= jend) break;
@@ -388,8 +390,7 @@ __global__ void __launch_bounds__(kRingThreads, 8 / kRingWaves) k_ring_split(
         int rn = rb + rstep;
         rn = rn >= ring ? rn % ring : rn;
         ring_load_step(f, rr, ln, j + kRingWaves < jend ? rn : rlast);
-        const int base = rs.pa + kRingStep * j;
-        ring_fold<MT>(sm, fb, base, rs.p0, rs.L, scale_log2, st);
+        ring_fold<MT>(sm, fb, kRingStep * j, lo, hi, scale_log2, st);
         j += kRingWaves;
         rb = rn;
         if (j >= jend) break;

@@ -70,6 +70,7 @@ def run_and_check(d2, inp, window, what, scale=0.0):
     (2, 8, 8, 2, 20480, 20480, [20479, 30000]),         # 641 steps: 32 splits, several steps per wave
     (2, 8, 8, 2, 768, 700, [300, 650]),                 # 22 context steps: uneven shares per wave
     (3, 8, 8, 2, 2080, 2048, [2100, 4111, 5000]),       # ring of 65 tiles: the window wraps mid-ring
+    (2, 8, 8, 2, 2112, 2048, [2**31 - 1, 2**31 - 77]),  # context lengths at the top of int32
 ])
 def test_ring_attention_parity(d2, B, nq, hq, hkv, ring, window, ctx):
     print(f"ring attention B={B} nq={nq} hq={hq} hkv={hkv} ring={ring} window={window} ctx={ctx}", flush=True)
