@@ -45,28 +45,36 @@ def algorithmic_select_bytes(B, K, V, dim, table_bytes=2):
 
 
 SELECT_SOURCES = ("k_select.hip", "topk_dev.h", "pair_dev.h", "gate_dev.h", "device_common.h", "dflash2_internal.h")
+RING_SOURCES = ("k_ring.hip", "dflash2_internal.h", "device_common.h")
+LMHEAD_SOURCES = ("k_lmhead.hip", "topk_dev.h", "dflash2_internal.h", "device_common.h")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "select_c2_memory_counters.md")
+RING_COUNTERS_MD = os.path.join(ROOT, "profiles", "ring_attention_b15_memory_counters.md")
+LMHEAD_COUNTERS_MD = os.path.join(ROOT, "profiles", "lmhead_topk16_c2_memory_counters.md")
 
 
-def measured_select_traffic():
-    """HBM bytes per dflash2_select launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel of known size), or None when the
-    select's kernel sources changed since the counters were taken."""
+def measured_traffic(md_path, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy kernel of known size), or None when the kernel's sources
+    changed since the counters were taken (the summary records their sha256)."""
     import hashlib
     import re
     try:
-        text = open(COUNTERS_MD).read()
+        text = open(md_path).read()
     except OSError:
         return None
     m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
-    m_h = re.search(r"^select_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    m_h = re.search(r"^(?:select_)?sources_sha256: ([0-9a-f]{64})$", text, re.M)
     if not (m_t and m_h):
         return None
     h = hashlib.sha256()
-    for f in SELECT_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "dflash_draft_selector_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(m_t.group(1)) if h.hexdigest() == m_h.group(1) else None
+
+
+def measured_select_traffic():
+    return measured_traffic(COUNTERS_MD, SELECT_SOURCES)
 
 
 def cpu_baseline(inp, w, budget_s=12.0):
@@ -337,7 +345,8 @@ def lmhead_measure(dflash2, torch, dev, stream, reps=10):
             "roofline": {"bound": "hbm",
                          "kernel": "dflash2_lmhead_topk16_packed = k_lmhead_tiles (packed W) + k_lmhead_merge",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(LMHEAD_COUNTERS_MD, LMHEAD_SOURCES), "bytes_per_launch": nbytes,
                          "tflops": round(2 * R * V * D / (packed_us * 1e-6) / 1e12, 1)},
             "unfused_torch_matmul_plus_topk16_us": round(unfused_us, 1)}
 
@@ -378,7 +387,8 @@ def ring_measure(dflash2, torch, dev, stream, reps=20, nbuf=4):
             "us_per_call": round(us, 1),
             "roofline": {"bound": "hbm", "kernel": "dflash2_ring_attention = k_ring_split (+ k_ring_combine when keys are split)",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(RING_COUNTERS_MD, RING_SOURCES), "bytes_per_launch": nbytes}}
 
 
 def main():
