@@ -40,18 +40,12 @@
 
 namespace df2 {
 
-#ifndef DF2_RING_WAVES
-#define DF2_RING_WAVES 8
-#endif
-#ifndef DF2_RING_TARGET
-#define DF2_RING_TARGET 256
-#endif
-constexpr int kRingWaves = DF2_RING_WAVES;   // waves of a split work-group
+constexpr int kRingWaves = 8;                // waves of a split work-group
 constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kCombThreads = 256;
 constexpr int kRingDh = 128;                 // head dim
 constexpr int kRingStep = 32;                // keys per wave step
-constexpr int kRingTargetGroups = DF2_RING_TARGET;   // work-groups aimed for: one per compute unit
+constexpr int kRingTargetGroups = 256;       // work-groups aimed for: one per compute unit
 constexpr int kRingMaxSplits = 32;
 constexpr int kRingRedPitch = 64 + 4;        // floats per staged half row of O (dims 64 at a time)
 
@@ -111,10 +105,7 @@ struct RingRes {
   __amdgpu_buffer_rsrc_t kr, vr, kb, vb;
 };
 
-#ifndef DF2_RING_AUX
-#define DF2_RING_AUX 0
-#endif
-constexpr int kRingAux = DF2_RING_AUX;       // cache policy of the ring reads
+constexpr int kRingAux = 0;                  // cache policy of the ring reads (non-temporal re-fetched half lines)
 
 // This lane's byte offsets within a step's tiles: its 16 bytes of every K slice (k), and
 // V^T dim i16 at positions 8 g .. 8 g + 7 (v); the tile and the slice or 16-dim group
