@@ -286,11 +286,14 @@ struct GateArgs {
 // H[e] for the n = nrows * DIM gate values of rows row0.. (e = t * DIM + d): the slice sums
 // added in slice order, then the bias and the activation (as gate_finish), written to dst
 // (LDS) and to H_out when given.  The first nthreads threads of the block (index ti) call
-// it; the loads of up to 8 values x 8 slices are in flight together.
+// it; each thread's loads of kE values x kS slices are in flight together (kE values per
+// thread cover DIM with 128 threads; 16 slices when kE <= 2, so the ten slices of a
+// 5120-wide hidden cost one memory round trip).
 template <int DIM>
 __device__ __forceinline__ void gated_rows(const GateArgs& ga, int rows, int row0, int n, int ti, int nthreads,
                                            float* dst) {
-  constexpr int kE = 8, kS = 8;
+  constexpr int kE = DIM >= 1024 ? 8 : (DIM + 127) / 128;
+  constexpr int kS = kE <= 2 ? 16 : 8;
   const size_t stride = (size_t)rows * DIM;
   for (int e0 = ti; e0 < n; e0 += kE * nthreads) {
     float sum[kE];
