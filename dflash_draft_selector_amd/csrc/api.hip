@@ -37,7 +37,8 @@ dflash2_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH2_OK : 
 dflash2_status check_logits(const uint16_t* logits, int64_t rows, int64_t vocab, int64_t ld) {
   if (!logits) return DFLASH2_ERR_NULL;
   if (rows < 1 || vocab < DFLASH2_NCAND || vocab > kMaxVocab || ld < vocab) return DFLASH2_ERR_SHAPE;
-  if (rows > kMaxItems || !items_ok(rows * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
+  // the stream grids pad the rows (or requests) to a multiple of 8, one lane per XCD
+  if (rows > kMaxItems || !items_ok((rows + 7) / 8 * 8 * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
   if (!aligned16(logits) || (ld % 8) != 0) return DFLASH2_ERR_ALIGN;
   return DFLASH2_OK;
 }
@@ -53,7 +54,7 @@ dflash2_status check_emb(const void* a, const void* b, dflash2_dtype dt, int64_t
 
 dflash2_status check_bk(int64_t batch, int64_t K) {
   if (batch < 1 || batch >= ((int64_t)1 << 31) || K < 1 || K > DFLASH2_MAX_K) return DFLASH2_ERR_SHAPE;
-  if (!items_ok(batch * K, 256)) return DFLASH2_ERR_SHAPE;
+  if (!items_ok((batch + 7) / 8 * 8 * K, 256)) return DFLASH2_ERR_SHAPE;
   return DFLASH2_OK;
 }
 
@@ -76,6 +77,7 @@ dflash2_status check_select(const uint16_t* logits, int64_t ld, const int32_t* v
   if (st != DFLASH2_OK) return st;
   st = check_logits(logits, batch * K, vocab, ld);
   if (st != DFLASH2_OK) return st;
+  if (!items_ok((batch + 7) / 8 * 8 * K * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
   st = check_emb(emb_a, emb_b, emb_dtype, vocab, dim);
   if (st != DFLASH2_OK) return st;
   if (!verified || !H || !cand_idx || !cand_val || !S || !tokens || !slots || !q) return DFLASH2_ERR_NULL;
