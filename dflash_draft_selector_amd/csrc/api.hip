@@ -421,7 +421,7 @@ dflash2_status dflash2_spec_accept(const uint16_t* target_logits, int64_t ld, in
   if (st != DFLASH2_OK) return st;
   if (batch_stride < 0 || (batch_stride > 0 && batch_stride < (K + 1) * ld)) return DFLASH2_ERR_SHAPE;
   if (batch_stride % 8 != 0) return DFLASH2_ERR_ALIGN;
-  if (!items_ok(nrows * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
+  if (!items_ok(xcd_chunk_grid(batch, K + 1, topk_num_chunks(vocab)), kTopkThreads)) return DFLASH2_ERR_SHAPE;
   if (!tokens || !cand_idx || !out_tokens || !n_accepted) return DFLASH2_ERR_NULL;
   st = check_temp(temperature);
   if (st != DFLASH2_OK) return st;
@@ -453,7 +453,7 @@ dflash2_status dflash2_spec_accept_filtered(const uint16_t* target_logits, int64
   if (st != DFLASH2_OK) return st;
   if (batch_stride < 0 || (batch_stride > 0 && batch_stride < (K + 1) * ld)) return DFLASH2_ERR_SHAPE;
   if (batch_stride % 8 != 0) return DFLASH2_ERR_ALIGN;
-  if (!items_ok(nrows * topk_num_chunks(vocab), kTopkThreads)) return DFLASH2_ERR_SHAPE;
+  if (!items_ok(xcd_chunk_grid(batch, K + 1, topk_num_chunks(vocab)), kTopkThreads)) return DFLASH2_ERR_SHAPE;
   if (!tokens || !cand_idx || !out_tokens || !n_accepted) return DFLASH2_ERR_NULL;
   st = check_temp(temperature);
   if (st != DFLASH2_OK) return st;

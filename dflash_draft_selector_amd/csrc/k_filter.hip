@@ -154,14 +154,17 @@ __device__ __noinline__ int gather_raised(const uint16_t* __restrict__ rowp, int
 __global__ void __launch_bounds__(kTopkThreads) k_filter_topk(const uint16_t* __restrict__ target, int64_t ld,
                                                               int64_t batch_stride, int K, int V, int nchunks,
                                                               int top_k, unsigned long long* __restrict__ lists,
-                                                              int* __restrict__ flags) {
+                                                              int* __restrict__ flags, int batch) {
   __shared__ unsigned long long s_cand[kTopkWaves][kFiltCap];
   __shared__ unsigned long long s_thr[kTopkWaves];
   __shared__ u32x4 s_vec[kTopkWaves][kFiltVecCap];
   __shared__ int s_vpos[kTopkWaves][kFiltVecCap];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int r = blockIdx.x / nchunks;
-  const int c = blockIdx.x - r * nchunks;
+  // per-request rows: request b's blocks on the XCD of its decide work-group
+  const int blk = batch_stride == 0 ? (int)blockIdx.x : xcd_chunk_block((int)blockIdx.x, batch, K + 1, nchunks);
+  if (blk < 0) return;                            // padding ids (the whole work-group)
+  const int r = blk / nchunks;
+  const int c = blk - r * nchunks;
   const int b = batch_stride == 0 ? 0 : r / (K + 1);
   const int t = batch_stride == 0 ? r : r - b * (K + 1);
   const uint16_t* rowp = target + (size_t)b * batch_stride + (size_t)t * ld;
@@ -534,10 +537,10 @@ hipError_t launch_spec_accept_filtered(const uint16_t* target, int64_t ld, int64
                                        int K, int vocab, float temperature, int top_k, float top_p, uint64_t seed,
                                        int32_t* out_tokens, int32_t* n_accepted, int32_t* row_status, FilterWs ws,
                                        hipStream_t s) {
-  const int nrows = batch_stride == 0 ? K + 1 : batch * (K + 1);
   const int nchunks = topk_num_chunks(vocab);
-  hipLaunchKernelGGL(k_filter_topk, dim3((unsigned)(nrows * nchunks)), dim3(kTopkThreads), 0, s, target, ld,
-                     batch_stride, K, vocab, nchunks, top_k, ws.lists, ws.flags);
+  const dim3 grid((unsigned)(batch_stride == 0 ? (long long)(K + 1) * nchunks : xcd_chunk_grid(batch, K + 1, nchunks)));
+  hipLaunchKernelGGL(k_filter_topk, grid, dim3(kTopkThreads), 0, s, target, ld, batch_stride, K, vocab, nchunks, top_k,
+                     ws.lists, ws.flags, batch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_filter_decide, dim3((unsigned)batch), dim3(kFiltThreads), 0, s, tokens, cand_idx, q,

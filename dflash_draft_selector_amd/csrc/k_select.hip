@@ -80,15 +80,11 @@ __global__ void __launch_bounds__(kTopkThreads) k_chunk_lists(const uint16_t* __
                                                               int batch, int K) {
   args_in_sgprs(logits, ld, V, nchunks, partials, batch, K);
   __shared__ ChunkShared sm;
-  // placement: the K * nchunks blocks of request b take the ids 8 * slot + b % 8, which
-  // the dispatcher deals to one XCD, as it does the request's position blocks below, so
-  // the chunk lists are read back from the L2 they were written to
-  const int per = K * nchunks;
-  const int id = (int)blockIdx.x;
-  const int x = id & 7, slot = id >> 3;
-  const int b = x + 8 * (slot / per);
-  if (b >= batch) return;                         // padding ids of the last XCD lanes
-  chunk_block(logits, ld, V, nchunks, b * per + (slot - (slot / per) * per), sm, partials);
+  // a request's chunk blocks on the XCD of its position blocks (k_positions), so the
+  // chunk lists are read back from the L2 they were written to
+  const int blk = xcd_chunk_block((int)blockIdx.x, batch, K, nchunks);
+  if (blk < 0) return;                            // padding ids (the whole work-group)
+  chunk_block(logits, ld, V, nchunks, blk, sm, partials);
 }
 
 // ---- stage 1 of the gated select: chunk top-16s and gate tiles in one launch ---------
@@ -372,10 +368,8 @@ __global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long 
   __shared__ float s_U[kNC];
   __shared__ int s_bits;
   // placement as in k_chunk_lists: the K blocks of request b on the XCD of b % 8
-  const int xid = (int)blockIdx.x;
-  const int xb = (xid & 7) + 8 * ((xid >> 3) / K);
-  if (xb >= rows / K) return;                     // padding ids (the whole block)
-  const int pos = xb * K + (xid >> 3) % K;
+  const int pos = xcd_chunk_block((int)blockIdx.x, rows / K, K, 1);
+  if (pos < 0) return;                            // padding ids (the whole block)
   const int b = pos / K, t = pos - b * K;
   const int tid = threadIdx.x, w = tid >> 6, r = tid & 15;
   const int nlists = nchunks;
@@ -434,7 +428,7 @@ __global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long 
 hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld, int32_t* cand_idx, float* cand_val,
                          int32_t* row_status, TopkWs ws, hipStream_t s) {
   const int nchunks = topk_num_chunks(vocab);
-  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(8 * ((rows + 7) / 8) * nchunks)), dim3(kTopkThreads), 0, s, logits,
+  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)xcd_chunk_grid(rows, 1, nchunks)), dim3(kTopkThreads), 0, s, logits,
                      ld, vocab, nchunks, ws.partials, rows, 1);
   hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)((rows + kMergeWaves - 1) / kMergeWaves)), dim3(kMergeWaves * kWave),
                      0, s, ws.partials, rows, nchunks, cand_idx, cand_val, row_status);
@@ -485,7 +479,7 @@ static hipError_t select_tail(int nchunks, const int32_t* verified, const void* 
                               int vocab, int dim, const float* H, const GateArgs& ga, int batch, int K, float inv_t,
                               uint64_t seed, const SelectOut& out, const SelectWs& ws, hipStream_t s) {
   const int rows = batch * K;
-  const dim3 grid((unsigned)(8 * ((batch + 7) / 8) * K));    // XCD lanes x requests per lane x K
+  const dim3 grid((unsigned)xcd_chunk_grid(batch, K, 1));      // placed as k_chunk_lists
   const bool ok = with_dim(dim, [&]<int D>() {
     if (bf16)
       hipLaunchKernelGGL((k_positions<D, true, GATED>), grid, dim3(kTileThreads), 0, s,
@@ -508,7 +502,7 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
                          int32_t* tokens, int32_t* slots, float* q, int32_t* row_status, SelectWs ws, hipStream_t s) {
   const int nchunks = topk_num_chunks(vocab);
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
-  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)(8 * ((batch + 7) / 8) * K * nchunks)), dim3(kTopkThreads), 0, s,
+  hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)xcd_chunk_grid(batch, K, nchunks)), dim3(kTopkThreads), 0, s,
                      logits, ld, vocab, nchunks, ws.topk.partials, batch, K);
   const SelectOut out{cand_idx, cand_val, S, tokens, slots, q, row_status};
   return select_tail<false>(nchunks, verified, emb_a, emb_b, bf16, vocab, dim, H, GateArgs{}, batch, K, inv_t, seed,

@@ -465,6 +465,23 @@ __device__ __forceinline__ unsigned long long wave_merge_lists(const unsigned lo
   return merge16(x, xor_lane_u64(dpp_u64<0x140>(x), 32));
 }
 
+// Placement of a stream over the rows of several requests: the rows_per * nchunks
+// chunk work-groups of request b take the work-group ids 8 * slot + b % 8, which the
+// dispatcher deals to one XCD (work-group id mod 8 picks the XCD), so that the kernel
+// after the stream, which reads request b's chunk results from work-group b (also on
+// XCD b % 8), finds them in the L2 they were written to.  Returns the chunk block
+// (row * nchunks + chunk, rows counted over all requests) of work-group id, or -1 for the
+// padding ids of the last lanes; the grid has 8 * ceil(batch / 8) * rows_per * nchunks ids.
+__device__ __forceinline__ int xcd_chunk_block(int id, int batch, int rows_per, int nchunks) {
+  const int per = rows_per * nchunks;
+  const int x = id & 7, slot = id >> 3;
+  const int b = x + 8 * (slot / per);
+  return b < batch ? b * per + (slot - (slot / per) * per) : -1;
+}
+__host__ __device__ __forceinline__ long long xcd_chunk_grid(long long batch, long long rows_per, long long nchunks) {
+  return 8 * ((batch + 7) / 8) * rows_per * nchunks;
+}
+
 // Chunking of a row: n chunks of near-equal vector counts, each <= kChunkVec.
 __host__ __device__ __forceinline__ int topk_num_chunks(long long vocab) {
   const long long nvec = (vocab + 7) / 8;
