@@ -1,8 +1,8 @@
 """Parity at the limits of the C ABI: the largest draft block (K = 64), every selector
 width the pair kernels are built for (the powers of two from 16 to 1024), both sides of
-the one-block-per-request limit of the select (K <= 16 and K x dim <= 8192), fp32 and
-bf16 tables, the largest vocabulary (2^19) and a ragged one, through the C ABI against
-the oracle."""
+the walk's staging limit (the step distributions of up to 16 positions staged in LDS),
+fp32 and bf16 tables, the largest vocabulary (2^19) and a ragged one, batches at and past
+whole lanes of 8 requests, through the C ABI against the oracle."""
 
 import numpy as np
 import pytest
@@ -65,10 +65,10 @@ def test_select_k64_every_selector_width(d2, dim, bf16):
 @pytest.mark.parametrize("dim,K,bf16", [(16, 7, True), (16, 17, False), (32, 16, True), (32, 3, False),
                                         (256, 16, True), (256, 17, True), (1024, 8, True), (1024, 9, False)])
 def test_select_selector_widths_and_block_limit(d2, dim, K, bf16):
-    """Each width with a draft block on either side of the one-block-per-request limit
-    (K <= 16 and K x dim <= 8192 run in one block per request, the rest in one wave per
-    position): the oracle's candidates, scores within tolerance, the walk teacher-forced,
-    and bit-identity with the three separate calls."""
+    """Each width with a draft block on either side of the walk's staging limit (the
+    step distributions of K <= 16 positions are staged in LDS, longer blocks read them
+    from memory): the oracle's candidates, scores within tolerance, the walk
+    teacher-forced, and bit-identity with the three separate calls."""
     w = synth.workload(0, B=3, K=K, V=3000, D=64, dim=dim, bf16_params=bf16, peak="decay")
     inp = synth.make_inputs(w)
     A64, B64, Ag, Bg, W64, Wg, wb = _tables(inp)
@@ -154,3 +154,42 @@ def test_spec_accept_k64(d2, temperature):
     else:
         assert cpu(n)[2] == 64
     print("verify stats", stats, flush=True)
+
+
+@pytest.mark.parametrize("B", [8, 9, 17])
+def test_select_and_verify_across_xcd_lanes(d2, B):
+    """Batches at and just past whole lanes of 8 requests (the streams place each
+    request's work-groups on one XCD, padding the grid to whole lanes): the select
+    against the oracle and equal to the three separate calls, and the sampled, filtered
+    and greedy verifies against the oracle."""
+    w = synth.workload(0, B=B, K=3, V=3000, D=64, dim=64, bf16_params=True, peak="decay")
+    inp = synth.make_inputs(w)
+    A64, B64, Ag, Bg, W64, Wg, wb = _tables(inp)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    Hg = d2.context_gate(to_gpu(inp["h"]), Wg, to_gpu(inp["bias"]))
+    ridx, rval = oracle.topk16(inp["logits_bits"])
+    Sref, Sabs, rst = oracle.pair_score(ridx, rval, inp["verified"], A64, B64, cpu(Hg).astype(np.float64))
+    print(f"select B={B} (lanes of 8)", flush=True)
+    out = d2.select(logits, ver, Ag, Bg, Hg, 1.0, 4)
+    np.testing.assert_array_equal(cpu(out["cand_idx"]), ridx)
+    assert_close_scaled(cpu(out["S"]), Sref, Sabs, what=f"S B {B}")
+    np.testing.assert_array_equal(cpu(out["row_status"]), rst)
+    check_walk(Sref, ridx, cpu(out["tokens"]), cpu(out["slots"]), cpu(out["q"]), 1.0, 4)
+    idx, val = d2.topk16(logits)
+    S, st = d2.pair_score(idx, val, ver, Ag, Bg, Hg)
+    tok, slots, q = d2.walk(S, idx, 1.0, 4)
+    for name, ref in (("S", S), ("tokens", tok), ("slots", slots), ("q", q)):
+        a, b = cpu(out[name]), cpu(ref)
+        np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                      b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=name)
+    rng = np.random.default_rng(40 + B)
+    target = synth.f32_to_bf16_bits(rng.standard_normal((w.B, w.K + 1, w.V), dtype=np.float32) * 3.0)
+    tokens, cand, qd = cpu(out["tokens"]), cpu(out["cand_idx"]), cpu(out["q"])
+    for T, kw in ((1.0, {}), (1.0, {"top_k": 20, "top_p": 0.95}), (0.0, {})):
+        print(f"verify B={B} T={T} {kw}", flush=True)
+        if kw:
+            o, n, vst = d2.spec_accept_filtered(to_gpu_bits(target), out["tokens"], out["cand_idx"], out["q"], T,
+                                                seed=6, **kw)
+        else:
+            o, n, vst = d2.spec_accept(to_gpu_bits(target), out["tokens"], out["cand_idx"], out["q"], T, seed=6)
+        check_accept(target, tokens, cand, qd, T, 6, cpu(o), cpu(n), cpu(vst), **kw)
