@@ -513,7 +513,7 @@ def main():
 
     sel_bytes = algorithmic_select_bytes(w.B, w.K, w.V, w.dim)
     achieved = sel_bytes / (select_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "dflash2_select = k_chunk_lists + k_positions + k_walk_tables",
+    roofline = {"bound": "hbm", "kernel": "dflash2_select = k_chunk_lists + k_positions (its last block per request walks)",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_select_traffic(),

@@ -162,6 +162,25 @@ __device__ __forceinline__ void args_in_sgprs(T... a) {
   (pin_arg(a), ...);
 }
 
+// ---- hand-offs between work-groups of one launch ---------------------------------------
+// Relaxed stores and loads at agent scope are performed where every compute unit sees
+// them (written through to the device's coherence point; no stale L1 or L2 copy is
+// read), so a value stored this way by one work-group is read by another once the
+// storing wave's memory counter has drained and the reader has learnt so through an
+// atomic.  The drain carries a memory clobber so that the compiler moves no access across
+// it.  (A release / acquire fence pair would also order plain stores, but its release
+// writes back the whole L2 of the work-group's XCD.)
+
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---- wave / block helpers ----------------------------------------------------------
 
 

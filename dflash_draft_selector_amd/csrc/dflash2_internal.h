@@ -31,7 +31,9 @@ struct SelectWs {
   TopkWs topk;
   int* next;                      // [rows][16] successor slot per predecessor slot
   float* qtab;                    // [rows][16][16] distribution of each predecessor's row
+  unsigned* tickets;              // [batch] x kWalkTicketStride: positions built per request
 };
+constexpr int kWalkTicketStride = 64;   // 256 bytes apart: concurrent atomics on one line serialise
 SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab);
 
 struct SelectGatedWs {

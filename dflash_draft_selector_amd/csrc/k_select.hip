@@ -1,24 +1,28 @@
 // Top-16, pair-score and walk kernels, and the proposer step built from them.
 //
-// The proposer step (dflash2_select) runs as three back-to-back kernels on one stream:
+// The proposer step (dflash2_select) runs as two back-to-back kernels on one stream:
 //   1. k_chunk_lists  streams the logits (two 512-thread blocks per row at V = 151936)
-//                     and writes each chunk's sorted top-16;
+//                     and writes each chunk's sorted top-16; it also zeroes one ticket
+//                     per request for stage 2;
 //   2. k_positions    one 4-wave block per draft position: merges the chunk top-16s of
 //                     rows t - 1 and t, writes row t's candidates, gathers the table rows
 //                     of the 16 x 16 adjacent pairs, computes the scores of t (the
 //                     selector dims split over the waves) and the successor table (the
-//                     slot taken from each predecessor slot);
-//   3. k_walk_tables  one block per request: follows the tables from the verified row
-//                     and writes tokens, slots and q.
+//                     slot taken from each predecessor slot); the block that completes
+//                     its request's last table (counted on the request's ticket) then
+//                     follows the tables from the verified row and writes tokens, slots
+//                     and q.
 // The gated step (dflash2_select_gated) launches k_chunk_gate in place of stage 1 (the
 // same blocks plus the context gate's tiles as extra work-groups), and its stage 2
 // adds each row's gate slices before the scores.
-// Kernel boundaries replace every cross-work-group hand-off, so no work-group ever
-// waits for another and no workspace counter exists.  Stage 2 runs one block per
-// position rather than one per request so that each request's table rows (about 107 KB
-// at K = 7) are gathered by K compute units instead of one.  Every entry point computes
-// a tile with the same block routine (pair_dev.h), so all of them give bit-identical
-// scores.
+// A kernel boundary hands the chunk lists to stage 2; inside stage 2 the tables reach the
+// walking block through agent-scope stores and loads and the ticket, so no work-group
+// ever waits for another (the walk this way costs less than a third kernel's boundary
+// and launch; the chunk lists' hand-off measured no cheaper than the boundary).  Stage 2
+// runs one block per position rather than one per request so that each request's table
+// rows (about 107 KB at K = 7) are gathered by K compute units instead of one.  Every
+// entry point computes a tile with the same block routine (pair_dev.h), so all of them
+// give bit-identical scores.
 #include "dflash2_internal.h"
 #include "gate_dev.h"
 #include "pair_dev.h"
@@ -37,6 +41,7 @@ SelectWs carve_select(Carver& c, int64_t batch, int64_t K, int64_t vocab) {
   w.topk = carve_topk(c, batch * K, vocab);
   w.next = c.take<int>((size_t)(batch * K * kNC));
   w.qtab = c.take<float>((size_t)(batch * K * kNC * kNC));
+  w.tickets = c.take<unsigned>((size_t)batch * kWalkTicketStride);
   return w;
 }
 
@@ -77,9 +82,13 @@ __device__ __forceinline__ void chunk_block(const uint16_t* __restrict__ logits,
 
 __global__ void __launch_bounds__(kTopkThreads) k_chunk_lists(const uint16_t* __restrict__ logits, int64_t ld, int V,
                                                               int nchunks, unsigned long long* __restrict__ partials,
-                                                              int batch, int K) {
-  args_in_sgprs(logits, ld, V, nchunks, partials, batch, K);
+                                                              int batch, int K, unsigned* __restrict__ tickets) {
+  args_in_sgprs(logits, ld, V, nchunks, partials, batch, K, tickets);
   __shared__ ChunkShared sm;
+  // the next kernel's per-request tickets start at zero (written here, read after the
+  // kernel boundary)
+  if (tickets && blockIdx.x == 0)
+    for (int b = (int)threadIdx.x; b < batch; b += kTopkThreads) tickets[(size_t)b * kWalkTicketStride] = 0u;
   // a request's chunk blocks on the XCD of its position blocks (k_positions), so the
   // chunk lists are read back from the L2 they were written to
   const int blk = xcd_chunk_block((int)blockIdx.x, batch, K, nchunks);
@@ -104,9 +113,12 @@ __global__ void __launch_bounds__(kTopkThreads) k_chunk_gate(const uint16_t* __r
                                                              const void* __restrict__ h,
                                                              const uint16_t* __restrict__ w_h, int rows, int hidden,
                                                              int dim, int ntiles, int nsplit,
-                                                             float* __restrict__ gate_partial) {
+                                                             float* __restrict__ gate_partial,
+                                                             unsigned* __restrict__ tickets, int batch) {
   args_in_sgprs(logits, ld, V, nchunks, nchunk_blocks, partials);
   __shared__ ChunkGateShared sm;
+  if (blockIdx.x == 0)
+    for (int b = (int)threadIdx.x; b < batch; b += kTopkThreads) tickets[(size_t)b * kWalkTicketStride] = 0u;
   if ((int)blockIdx.x < nchunk_blocks) {
     chunk_block(logits, ld, V, nchunks, (int)blockIdx.x, sm.c, partials);
     return;
@@ -209,19 +221,17 @@ struct WalkShared {
   int path[kMaxK];
 };
 
-// From the successor tables stage 2 built: next[t][i] (slot taken at t after slot i at
-// t - 1) and, when sampling, qtab[t][i][.] (that row's distribution).  Wave 0 follows
+// The walk of request b from the successor tables its position blocks built: next[t][i]
+// (slot taken at t after slot i at t - 1) and, when sampling, qtab[t][i][.] (that row's
+// distribution), stored at agent scope by the request's other blocks.  Wave 0 follows
 // the tables (lane r holds next[t][r]; each step reads the lane of the previous slot)
 // while waves 1-3 stage the candidates and distributions, so nothing read after the
 // walk depends on it through global memory (the distributions of a request longer than
-// kStagedK positions are read after the walk).
-__global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ next, const float* __restrict__ qtab,
-                                                     const int32_t* __restrict__ cand_idx, int K, bool sampled,
-                                                     int32_t* __restrict__ tokens, int32_t* __restrict__ slots,
-                                                     float* __restrict__ q) {
-  args_in_sgprs(next, qtab, cand_idx, K, sampled, tokens, slots, q);
-  __shared__ WalkShared sm;
-  const int b = blockIdx.x;
+// kStagedK positions are read after the walk).  All 256 threads of the block call it.
+__device__ __forceinline__ void walk_tables(int b, int K, bool sampled, const int* __restrict__ next,
+                                            const float* __restrict__ qtab, const int32_t* __restrict__ cand_idx,
+                                            int32_t* __restrict__ tokens, int32_t* __restrict__ slots,
+                                            float* __restrict__ q, WalkShared& sm) {
   const int tid = threadIdx.x;
   const size_t base = (size_t)b * K * kNC;
   if (tid < kWave) {
@@ -230,7 +240,7 @@ __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ nex
     for (int t0 = 0; t0 < K; t0 += 16) {
       int nt[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) nt[k] = t0 + k < K ? next[base + (size_t)(t0 + k) * kNC + r] : 0;
+      for (int k = 0; k < 16; ++k) nt[k] = t0 + k < K ? load_agent(next + base + (size_t)(t0 + k) * kNC + r) : 0;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         if (t0 + k < K) {
@@ -241,19 +251,20 @@ __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ nex
     }
   } else {
     // every load of a thread's share issued before its first LDS store
-    constexpr int kStagers = 256 - kWave;
+    constexpr int kStagers = kTileThreads - kWave;
     constexpr int kTokPer = (kMaxK * kNC + kStagers - 1) / kStagers;
     constexpr int kQPer = (kStagedK * kNC * kNC + kStagers - 1) / kStagers;
     const int ti = tid - kWave;
     int tv[kTokPer];
 #pragma unroll
-    for (int k = 0; k < kTokPer; ++k) tv[k] = ti + k * kStagers < K * kNC ? cand_idx[base + ti + k * kStagers] : 0;
+    for (int k = 0; k < kTokPer; ++k)
+      tv[k] = ti + k * kStagers < K * kNC ? load_agent(cand_idx + base + ti + k * kStagers) : 0;
     if (sampled && K <= kStagedK) {
       float qv[kQPer];
 #pragma unroll
       for (int k = 0; k < kQPer; ++k) {
         const int e = ti + k * kStagers;
-        qv[k] = e < K * kNC * kNC ? qtab[base * kNC + e] : 0.f;
+        qv[k] = e < K * kNC * kNC ? load_agent(qtab + base * kNC + e) : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < kQPer; ++k)
@@ -265,12 +276,12 @@ __global__ void __launch_bounds__(256) k_walk_tables(const int* __restrict__ nex
   }
   __syncthreads();
   const bool staged = K <= kStagedK;
-  for (int e = tid; e < K * kNC; e += 256) {
+  for (int e = tid; e < K * kNC; e += kTileThreads) {
     const int t = e >> 4, j = e & 15;
     const int to = sm.path[t];
     const int from = t == 0 ? 0 : sm.path[t - 1];
     const int qi = (t * kNC + from) * kNC + j;
-    q[base + e] = sampled ? (staged ? sm.qtab[qi] : qtab[base * kNC + qi]) : (j == to ? 1.f : 0.f);
+    q[base + e] = sampled ? (staged ? sm.qtab[qi] : load_agent(qtab + base * kNC + qi)) : (j == to ? 1.f : 0.f);
     if (j == 0) {
       slots[(size_t)b * K + t] = to;
       tokens[(size_t)b * K + t] = sm.tok[t * kNC + to];
@@ -358,12 +369,20 @@ __global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long 
                                                             uint64_t seed, int32_t* __restrict__ cand_idx,
                                                             float* __restrict__ cand_val, float* __restrict__ S,
                                                             int* __restrict__ next, float* __restrict__ qtab,
-                                                            int32_t* __restrict__ row_status) {
+                                                            int32_t* __restrict__ row_status,
+                                                            unsigned* __restrict__ tickets,
+                                                            int32_t* __restrict__ tokens, int32_t* __restrict__ slots,
+                                                            float* __restrict__ q) {
   args_in_sgprs(partials, nchunks, K, rows, verified, emb_a, emb_b, V, H, inv_t, seed, cand_idx, cand_val, S, next, qtab,
                 row_status);
   if constexpr (GATED) args_in_sgprs(ga.partial, ga.bias, ga.nsplit, ga.act, ga.H_out);
-  __shared__ TileShared sm;
+  __shared__ union {
+    TileShared tile;
+    WalkShared walk;
+  } shm;
+  TileShared& sm = shm.tile;
   __shared__ float s_H[GATED ? DIM : 1];
+  __shared__ int s_walker;
   __shared__ int s_prev[kNC], s_cur[kNC];
   __shared__ float s_U[kNC];
   __shared__ int s_bits;
@@ -409,10 +428,11 @@ __global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long 
   float qj;
   const int pick = row16_pick(s, inv_t, u, &qj);
   S[(size_t)pos * kNC * kNC + tid] = s;
-  if (inv_t != 0.f) qtab[(size_t)pos * kNC * kNC + tid] = qj;
-  if (r == 0) next[(size_t)pos * kNC + (tid >> 4)] = pick;
+  // what the request's walk reads goes out at agent scope (another block may walk)
+  if (inv_t != 0.f) store_agent(qtab + (size_t)pos * kNC * kNC + tid, qj);
+  if (r == 0) store_agent(next + (size_t)pos * kNC + (tid >> 4), pick);
   if (tid < kNC) {
-    cand_idx[(size_t)pos * kNC + tid] = s_cur[tid];
+    store_agent(cand_idx + (size_t)pos * kNC + tid, s_cur[tid]);
     cand_val[(size_t)pos * kNC + tid] = s_U[tid];
   }
   const bool any_bad = __ballot(bad != 0) != 0ull;             // wave 0 holds every id
@@ -421,6 +441,15 @@ __global__ void __launch_bounds__(kTileThreads) k_positions(const unsigned long 
     if (ga.H_out)
       for (int d = tid; d < DIM; d += kTileThreads) ga.H_out[(size_t)pos * DIM + d] = s_H[d];
   }
+  // the block that builds its request's last position walks the request: a ticket per
+  // request (zeroed by the stream kernel) counts the positions whose tables are out
+  drain_memory();
+  __syncthreads();
+  if (tid == 0)
+    s_walker = __hip_atomic_fetch_add(tickets + (size_t)b * kWalkTicketStride, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) + 1u == (unsigned)K;
+  __syncthreads();
+  if (s_walker) walk_tables(b, K, inv_t != 0.f, next, qtab, cand_idx, tokens, slots, q, shm.walk);
 }
 
 // ---- launchers -----------------------------------------------------------------------
@@ -429,7 +458,7 @@ hipError_t launch_topk16(const uint16_t* logits, int rows, int vocab, int64_t ld
                          int32_t* row_status, TopkWs ws, hipStream_t s) {
   const int nchunks = topk_num_chunks(vocab);
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)xcd_chunk_grid(rows, 1, nchunks)), dim3(kTopkThreads), 0, s, logits,
-                     ld, vocab, nchunks, ws.partials, rows, 1);
+                     ld, vocab, nchunks, ws.partials, rows, 1, (unsigned*)nullptr);
   hipLaunchKernelGGL(k_merge_lists, dim3((unsigned)((rows + kMergeWaves - 1) / kMergeWaves)), dim3(kMergeWaves * kWave),
                      0, s, ws.partials, rows, nchunks, cand_idx, cand_val, row_status);
   return hipGetLastError();
@@ -484,15 +513,15 @@ static hipError_t select_tail(int nchunks, const int32_t* verified, const void* 
     if (bf16)
       hipLaunchKernelGGL((k_positions<D, true, GATED>), grid, dim3(kTileThreads), 0, s,
                          ws.topk.partials, nchunks, K, rows, verified, emb_a, emb_b, vocab, H, ga, inv_t, seed,
-                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status);
+                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status, ws.tickets, out.tokens,
+                         out.slots, out.q);
     else
       hipLaunchKernelGGL((k_positions<D, false, GATED>), grid, dim3(kTileThreads), 0, s,
                          ws.topk.partials, nchunks, K, rows, verified, emb_a, emb_b, vocab, H, ga, inv_t, seed,
-                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status);
+                         out.cand_idx, out.cand_val, out.S, ws.next, ws.qtab, out.row_status, ws.tickets, out.tokens,
+                         out.slots, out.q);
   });
   if (!ok) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_walk_tables, dim3((unsigned)batch), dim3(256), 0, s, ws.next, ws.qtab, out.cand_idx, K,
-                     inv_t != 0.f, out.tokens, out.slots, out.q);
   return hipGetLastError();
 }
 
@@ -503,7 +532,7 @@ hipError_t launch_select(const uint16_t* logits, int64_t ld, const int32_t* veri
   const int nchunks = topk_num_chunks(vocab);
   const float inv_t = temperature == 0.f ? 0.f : 1.f / temperature;
   hipLaunchKernelGGL(k_chunk_lists, dim3((unsigned)xcd_chunk_grid(batch, K, nchunks)), dim3(kTopkThreads), 0, s,
-                     logits, ld, vocab, nchunks, ws.topk.partials, batch, K);
+                     logits, ld, vocab, nchunks, ws.topk.partials, batch, K, ws.tickets);
   const SelectOut out{cand_idx, cand_val, S, tokens, slots, q, row_status};
   return select_tail<false>(nchunks, verified, emb_a, emb_b, bf16, vocab, dim, H, GateArgs{}, batch, K, inv_t, seed,
                             out, ws, s);
@@ -523,7 +552,7 @@ hipError_t launch_select_gated(const uint16_t* logits, int64_t ld, const int32_t
   const long long blocks = (long long)nchunk_blocks + fused_gate_blocks(rows, hidden, dim);
   hipLaunchKernelGGL(h_bf16 ? k_chunk_gate<true> : k_chunk_gate<false>, dim3((unsigned)blocks), dim3(kTopkThreads), 0,
                      s, logits, ld, vocab, nchunks, nchunk_blocks, ws.sel.topk.partials, h, w_h, rows, hidden, dim,
-                     ntiles, ws.nsplit, ws.partial);
+                     ntiles, ws.nsplit, ws.partial, ws.sel.tickets, batch);
   GateArgs ga;
   ga.partial = ws.partial;
   ga.bias = bias;

@@ -261,10 +261,9 @@ dflash2_status dflash2_walk(const float* S, const int32_t* cand_idx, int64_t bat
  * synchronisation).  Same passages as the three calls above; the outputs are
  * bit-identical to calling dflash2_topk16 on every position's logits row, then
  * dflash2_pair_score, then dflash2_walk.  logits rows are addressed as
- * logits[(b*K + t)*ld + v].  Two kernels on `stream` when K <= 16 and K * dim <= 8192
- * (one streams the logits; one block per request merges, scores and walks), three
- * otherwise (the scores then take one wave per draft position and the walk its own
- * kernel).
+ * logits[(b*K + t)*ld + v].  Two kernels on `stream`: one streams the logits, then one
+ * block per draft position merges its candidates and scores its row, and the block that
+ * finishes a request's last row walks that request.
  *
  * S must be 16-byte aligned.  row_status int32 [batch, K] or NULL (the union of the
  * top-16 and pair-score bits).
