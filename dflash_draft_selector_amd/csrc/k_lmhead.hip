@@ -4,15 +4,17 @@
 // 16 candidates per slot; [RFC] "Questions", item 4: the draft shares the target's LM
 // head).
 //
-// Stage 1, k_lmhead_tiles: one 512-thread work-group per 256 vocabulary columns (and
-// per group of up to 128 rows).  Each wave owns two 16-column tiles for every 16-row
-// tile, on v_mfma_f32_16x16x32_bf16 with fp32 accumulators.  W rows go straight from
-// HBM into the MFMA B operand (each lane 16 contiguous bytes of one W row per step),
-// loaded up to eight steps ahead in a register ring; the hidden rows (read by every
+// Stage 1, k_lmhead_tiles: 512-thread work-groups, one round of them resident, each
+// running a sequence of 256-column vocabulary tiles (per group of up to 128 rows).  Each
+// wave owns two 16-column tiles for every 16-row tile, on v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulators.  W rows go straight from HBM into the MFMA B operand (each lane 16
+// contiguous bytes of one W row per step), loaded up to twelve steps ahead in a register
+// ring that runs on from one tile into the next; the hidden rows (read by every
 // work-group, so cache-resident) are staged 256 dims at a time through LDS with an XOR
 // swizzle, so the 16 rows a wave reads per instruction sit in distinct banks.  The
 // epilogue rounds the accumulators to bf16, sorts each row's 32 columns per wave with
-// DPP bitonic networks and merges the eight wave lists of every row through LDS.
+// DPP bitonic networks and merges the eight wave lists of every row through LDS, while
+// the next tile's first W loads are in flight.
 // Stage 2, k_lmhead_merge: one work-group per row merges the row's sorted tile lists.
 //
 // Selection order: value descending, token id ascending, NaN below -inf (the order of
@@ -72,19 +74,29 @@ constexpr int lm_bound_index() {
                                                 : (J == 8 ? 6 : J == 4 ? 7 : J == 2 ? 8 : 9);
 }
 
-__device__ __forceinline__ int lm_bound(int K, int J) {
+__device__ __forceinline__ int lm_bound(int i, int K, int J) {
   // the orientation of bitonic_stage_i32: blocks of K lanes largest first where lane bit
   // K is clear (and for K = 16); the lower lane of a pair at distance J keeps the larger
-  const int i = threadIdx.x & 15;
   const bool desc = K >= 16 || (i & K) == 0;
   int c = (((i & J) == 0) == desc) ? 0x7fffffff : (int)0x80000000;
   asm("" : "+v"(c));
   return c;
 }
 
-__device__ __forceinline__ LmBounds lm_bounds() {
-  return LmBounds{{lm_bound(2, 1), lm_bound(4, 2), lm_bound(4, 1), lm_bound(8, 4), lm_bound(8, 2), lm_bound(8, 1),
-                   lm_bound(16, 8), lm_bound(16, 4), lm_bound(16, 2), lm_bound(16, 1)}};
+// This lane's index in its wave, computed where it is used: the tile kernel runs its
+// epilogue inside the loop over tiles, and a lane-derived value the compiler hoisted out
+// of that loop would stay live (and spill) across the main loop.
+__device__ __forceinline__ int lm_lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+__device__ __forceinline__ LmBounds lm_bounds(int lane) {
+  const int i = lane & 15;
+  return LmBounds{{lm_bound(i, 2, 1), lm_bound(i, 4, 2), lm_bound(i, 4, 1), lm_bound(i, 8, 4), lm_bound(i, 8, 2),
+                   lm_bound(i, 8, 1), lm_bound(i, 16, 8), lm_bound(i, 16, 4), lm_bound(i, 16, 2),
+                   lm_bound(i, 16, 1)}};
 }
 
 template <int K, int J>
@@ -138,17 +150,16 @@ __device__ __forceinline__ unsigned long long lm_rank_to_rc(int rank, int col0) 
 // Per-row top-16 of one tile from the accumulators (the whole work-group calls it):
 // acc[m][nt][r] is row 16 m + 4 g + r, column 32 wv + 16 nt + i16 of the tile.  Rounds
 // to bf16, sorts each row's 32 columns per wave, merges the eight wave lists of every
-// row through LDS (`lds`, MT * 8 KB, free on entry) and writes the tile's lists.
+// row through LDS (`lists`, [MT * 16 rows][8 waves][16], MT * 8 KB, free on entry) and
+// writes the tile's lists.  wv: this wave's index in the work-group.
 template <int MT>
-__device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigned char* lds, int tile, int rows,
-                                              int row0, int vocab, int ntiles,
+__device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], int* lists, int tile, int rows, int row0,
+                                              int vocab, int ntiles, int wv,
                                               unsigned long long* __restrict__ partials) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = lm_lane_here();
   const int g = lane >> 4, i16 = lane & 15;
   const int col0 = tile * kLmCols;
-  int* lists = reinterpret_cast<int*>(lds);            // [MT * 16 rows][8 waves][16]
-  const LmBounds bd = lm_bounds();
+  const LmBounds bd = lm_bounds(lane);
   // (m, r) pairs two at a time: sort both halves of each pair's 32 columns, keep the
   // top 16 of the two sorted halves (the maximum against the other half reversed is
   // bitonic) and sort that
@@ -190,54 +201,81 @@ __device__ __forceinline__ void lm_tile_top16(const f32x4 (&acc)[MT][2], unsigne
   }
 }
 
-// Work-groups [0, nfull) each own tile blockIdx.x over the whole hidden dimension and
-// end with its top-16.  The rest split the remaining tiles along the hidden dimension,
-// nparts work-groups per tile (the last round of a vocabulary that does not fill the
-// chip in whole rounds would otherwise run few work-groups): each sums its share of the
-// stages and stores the fp32 tile (tail[(tail tile, part)][wave][m][nt][lane], f32x4),
-// and k_lmhead_combine adds the parts in order and takes the top-16 of each 16-row tile.
-// RING: W half-stages (4 MFMA steps each) kept in flight, 2 or 3.  PACKED: W in the
-// packed layout of lm_packed_offset (each load instruction one contiguous 1 KB), else
+// The work of one group of rows is a sequence of units: units [0, nfull) are whole tiles
+// (tile k over the whole hidden dimension, ending with its top-16); the rest split the
+// remaining tiles along the hidden dimension, nparts units per tile (the last round of a
+// vocabulary that does not fill the chip in whole rounds would otherwise run few
+// work-groups): each sums its share of the stages and stores the fp32 tile
+// (tail[(tail tile, part)][wave][m][nt][lane], f32x4), and k_lmhead_combine adds the
+// parts in order and takes the top-16 of each 16-row tile.
+struct LmUnit {
+  int tile, s0, ns;    // the unit's tile and its stages s0 .. s0 + ns - 1
+};
+
+__device__ __forceinline__ LmUnit lm_unit(int k, int nfull, int nparts, int nstages) {
+  if (k < nfull) return LmUnit{k, 0, nstages};
+  const int u = k - nfull, part = u % nparts;
+  const int s0 = (int)((long long)nstages * part / nparts);
+  return LmUnit{nfull + u / nparts, s0, (int)((long long)nstages * (part + 1) / nparts) - s0};
+}
+
+// Each work-group runs units blockIdx.x, blockIdx.x + gridDim.x, ... back to back (the
+// grid is one round of resident work-groups), and its W ring runs on across them: the
+// last half-stages of a unit refill the ring with the next unit's first ones, and the
+// next unit's first hidden stage is loaded with them, so those loads are in flight while
+// the unit's epilogue sorts.
+// PACKED: W in the packed layout of lm_packed_offset (each load instruction one contiguous 1 KB), else
 // row-major [vocab][hidden] (each instruction 64 bytes of 16 rows).
-template <int MT, int RING, bool PACKED>
+template <int MT, bool PACKED>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __restrict__ h,
                                                               const uint16_t* __restrict__ w, int rows, int hidden,
                                                               int vocab, int row0, int ntiles, int nfull, int nparts,
                                                               unsigned long long* __restrict__ partials,
                                                               f32x4* __restrict__ tail) {
-  // the staged hidden rows; reused by the epilogue for the waves' sorted lists
+  // the staged hidden rows, and the epilogue's sorted lists (apart, so that the next
+  // unit's first stage is staged before the epilogue)
   __shared__ __align__(16) unsigned char lds[MT * 16 * kLmSlots * 16];
+  __shared__ int lists[MT * 16 * kLmWaves * kNC];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int nstages = hidden / kLmStageDims;
-  const bool whole = (int)blockIdx.x < nfull;
-  const int u = (int)blockIdx.x - nfull;               // split work-groups: tail tile u / nparts, part u % nparts
-  const int part = whole ? 0 : u % nparts;
-  const int tile = whole ? (int)blockIdx.x : nfull + u / nparts;
-  const int s0 = whole ? 0 : (int)((long long)nstages * part / nparts);
-  const int ns = whole ? nstages : (int)((long long)nstages * (part + 1) / nparts) - s0;
-  const int col0 = tile * kLmCols;
+  const int nunits = nfull + (ntiles - nfull) * nparts;
+  const int stride = (int)gridDim.x;
+  constexpr int kHalf = kLmSteps / 2;
+  constexpr int kPk = kLmWaves * 512;                  // elements of one packed (step, column tile) slice
 
-  // this lane's two W rows (a column past the vocabulary reads the last row, unused), or
-  // its 16 bytes of every packed 1 KB slice of the tile
-  const uint16_t* wrow[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int col = col0 + 32 * wv + 16 * nt + i16;
-    wrow[nt] = w + (size_t)(col < vocab ? col : vocab - 1) * hidden + 8 * g;
-  }
-  const uint16_t* wpk = w + (size_t)tile * kLmCols * hidden + wv * 512 + lane * 8;
-  // W fragment (half-stage hs, step s of it, column tile nt)
-  auto wfrag = [&](int hs, int s, int nt) -> u32x4 {
+  // W of tile t, half-stage ha of the hidden dimension: a uniform base, plus per lane
+  // its 16 bytes of every packed 1 KB slice, or the offset of its row (column of the
+  // tile; a column past the vocabulary reads the last row, unused) and dims
+  auto wbase = [&](int t, int ha) -> const uint16_t* {
     if constexpr (PACKED)
-      return *reinterpret_cast<const u32x4*>(wpk + ((size_t)(hs * (kLmSteps / 2) + s) * 2 + nt) * (kLmWaves * 512));
+      return w + (size_t)t * kLmCols * hidden + (size_t)ha * kHalf * 2 * kPk;
     else
-      return *reinterpret_cast<const u32x4*>(wrow[nt] + (size_t)hs * (kLmStageDims / 2) + 32 * s);
+      return w + (size_t)t * kLmCols * hidden + (size_t)ha * (kLmStageDims / 2);
+  };
+  auto wlane = [&](int t, int nt) -> unsigned {
+    if constexpr (PACKED) {
+      return (unsigned)(nt * kPk + wv * 512 + lane * 8);
+    } else {
+      const int last = vocab - 1 - t * kLmCols;
+      const int lc = 32 * wv + 16 * nt + i16;
+      return (unsigned)((lc < last ? lc : last) * hidden + 8 * g);
+    }
+  };
+  // W fragment of step s of the half-stage at b, column tile nt (lane offset o)
+  auto wfrag = [&](const uint16_t* b, unsigned o, int s) -> u32x4 {
+    if constexpr (PACKED)
+      return *reinterpret_cast<const u32x4*>(b + (size_t)s * 2 * kPk + o);
+    else
+      return *reinterpret_cast<const u32x4*>(b + o + 32 * s);
   };
 
   // staging of one 256-dim stage of the hidden rows: thread slot e covers row
-  // (tid + 512 e) / 32, 16-byte slot (tid + 512 e) % 32; rows past the group are zero
+  // (tid + 512 e) / 32, 16-byte slot (tid + 512 e) % 32; rows past the group are zero,
+  // their loads skipped (reading a valid row for them instead, so that every path issues
+  // the same loads, measured 2-5% slower: every padding lane of the chip then reads the
+  // same few lines)
   auto load_h = [&](int st, u32x4 (&hp)[MT]) {
 #pragma unroll
     for (int e = 0; e < MT; ++e) {
@@ -250,12 +288,19 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
     }
   };
   auto store_h = [&](const u32x4 (&hp)[MT]) {
+    // row tid / 32 + 16 e has the swizzle of row tid / 32: one offset, plus e rows of 16
+    const int base = lm_lds_off(tid / kLmSlots, tid % kLmSlots);
 #pragma unroll
-    for (int e = 0; e < MT; ++e) {
-      const int idx = tid + kLmThreads * e;
-      *reinterpret_cast<u32x4*>(lds + lm_lds_off(idx / kLmSlots, idx % kLmSlots)) = hp[e];
-    }
+    for (int e = 0; e < MT; ++e)
+      *reinterpret_cast<u32x4*>(lds + base + e * (kLmThreads / kLmSlots) * kLmSlots * 16) = hp[e];
   };
+
+  // this work-group's units k, k + gridDim.x, ...: the current one and the next.
+  int k = (int)blockIdx.x;
+  if (k >= nunits) return;
+  LmUnit cu = lm_unit(k, nfull, nparts, nstages);
+  bool more = k + stride < nunits;
+  LmUnit nu = more ? lm_unit(k + stride, nfull, nparts, nstages) : cu;
 
   f32x4 acc[MT][2];
 #pragma unroll
@@ -263,36 +308,43 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[m][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // W ring: RING half-stages of 4 steps in registers.  Half-stage hs (of this work-
-  // group's stages s0 .. s0 + ns - 1) runs on ring slot hs % RING and refills it,
-  // kLmBurst steps at a time, with half-stage hs + RING (past the end it reloads the
-  // last one: valid memory, never used), so the two 64-byte halves of every 128-byte
-  // line of a W row are requested back to back.  Plain loads: the line stays in L2 for
-  // its second half (non-temporal loads measured 25% slower).
-  constexpr int kHalf = kLmSteps / 2;
-  const int nhalves = 2 * ns;
-  u32x4 wr0[kHalf][2], wr1[kHalf][2], wr2[kHalf][2];
-  auto fill = [&](u32x4 (&wr)[kHalf][2], int hs) {
-    hs = 2 * s0 + (hs < nhalves ? hs : nhalves - 1);
+  // W ring: the two half-stages (4 MFMA steps each) of a stage in registers, wr0 and
+  // wr1.  Each half refills its slot, kLmBurst steps at a time, with the same half of the
+  // unit's next stage or, on the unit's last stage, of the next unit's first one, so
+  // that the next unit starts with its first stage loaded; past the last unit it reloads
+  // itself (valid, cache-resident, unused).  Every path issues the same W loads, so that
+  // waiting for a hidden slice leaves the ring's loads in flight.
+  // The two 64-byte halves of every 128-byte line of a row-major W row are requested back
+  // to back.  Plain loads: the line stays in L2 for its second half (non-temporal loads
+  // measured 25% slower).
+  u32x4 wr0[kHalf][2], wr1[kHalf][2];
+  auto fill = [&](u32x4 (&wr)[kHalf][2], int part_h) {
+    const uint16_t* b = wbase(cu.tile, 2 * cu.s0 + part_h);
+    const unsigned o0 = wlane(cu.tile, 0), o1 = wlane(cu.tile, 1);
 #pragma unroll
-    for (int s = 0; s < kHalf; ++s)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        wr[s][nt] = wfrag(hs, s, nt);
+    for (int s = 0; s < kHalf; ++s) {
+      wr[s][0] = wfrag(b, o0, s);
+      wr[s][1] = wfrag(b, o1, s);
+    }
   };
   fill(wr0, 0);
   fill(wr1, 1);
-  if constexpr (RING == 3) fill(wr2, 2);
 
   u32x4 hp[MT];
-  load_h(s0, hp);
+  load_h(cu.s0, hp);
   store_h(hp);
   __syncthreads();
 
-  auto half = [&](int hs, u32x4 (&wr)[kHalf][2]) {
-    const int st = hs >> 1, part_h = hs & 1;
-    if (part_h == 0) load_h(s0 + (st + 1 < ns ? st + 1 : st), hp);   // the next staged hidden slice
-    const int nw = 2 * s0 + (hs + RING < nhalves ? hs + RING : nhalves - 1);
+  // Half part_h of a stage, on ring slot part_h.  sn: the stage loaded meanwhile, of
+  // tile tn (this unit's next stage, the next unit's first, or past the last unit this
+  // stage again, staged to no use).  The W refills stay where they are written
+  // (scheduling barriers), a half-stage ahead of their use, and the hidden slice is
+  // staged on every path, so that the compiler does not sink its loads next to their use
+  // (into the branch that would stage it), which would wait for the whole ring there.
+  auto half = [&](u32x4 (&wr)[kHalf][2], const int part_h, const int tn, const int sn) {
+    if (part_h == 0) load_h(sn, hp);                  // the next staged hidden slice
+    const uint16_t* b = wbase(tn, 2 * sn + part_h);   // what this ring slot is refilled with
+    const unsigned o0 = wlane(tn, 0), o1 = wlane(tn, 1);
 #pragma unroll
     for (int s = 0; s < kHalf; ++s) {
       const int step = kHalf * part_h + s;
@@ -307,35 +359,47 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
       }
       if ((s + 1) % kLmBurst == 0) {
 #pragma unroll
-        for (int b = s + 1 - kLmBurst; b <= s; ++b)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            wr[b][nt] = wfrag(nw, b, nt);
+        for (int q = s + 1 - kLmBurst; q <= s; ++q) {
+          wr[q][0] = wfrag(b, o0, q);
+          wr[q][1] = wfrag(b, o1, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (part_h == 1) {
       __syncthreads();
-      if (st + 1 < ns) {
-        store_h(hp);
-        __syncthreads();
-      }
+      store_h(hp);
+      __syncthreads();
     }
   };
-  for (int hs = 0; hs < nhalves; hs += RING) {
-    half(hs, wr0);
-    if (hs + 1 < nhalves) half(hs + 1, wr1);
-    if constexpr (RING == 3)
-      if (hs + 2 < nhalves) half(hs + 2, wr2);
-  }
 
-  if (whole) {
-    lm_tile_top16<MT>(acc, lds, tile, rows, row0, vocab, ntiles, partials);
-  } else {
-    f32x4* dst = tail + ((size_t)u * kLmWaves + wv) * MT * 2 * kWave + lane;
+  for (;;) {
+    for (int st = 0; st < cu.ns; ++st) {
+      const bool own = st + 1 < cu.ns;
+      const int tn = own || !more ? cu.tile : nu.tile;
+      const int sn = own ? cu.s0 + st + 1 : more ? nu.s0 : cu.s0 + st;
+      half(wr0, 0, tn, sn);
+      half(wr1, 1, tn, sn);
+    }
+    // the unit is done: its top-16, or its part
+    if (k < nfull) {
+      lm_tile_top16<MT>(acc, lists, cu.tile, rows, row0, vocab, ntiles, wv, partials);
+    } else {
+      f32x4* dst = tail + ((size_t)(k - nfull) * kLmWaves + wv) * MT * 2 * kWave + lm_lane_here();
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) dst[(m * 2 + nt) * kWave] = acc[m][nt];
+    }
+    if (!more) break;
+    k += stride;
+    cu = nu;
+    more = k + stride < nunits;
+    if (more) nu = lm_unit(k + stride, nfull, nparts, nstages);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) dst[(m * 2 + nt) * kWave] = acc[m][nt];
+      for (int nt = 0; nt < 2; ++nt) acc[m][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -347,7 +411,7 @@ template <int MT>
 __global__ void __launch_bounds__(kLmThreads) k_lmhead_combine(const f32x4* __restrict__ tail, int nparts, int rows,
                                                                 int vocab, int row0, int ntiles, int nfull,
                                                                 unsigned long long* __restrict__ partials) {
-  __shared__ __align__(16) unsigned char lds[16 * kLmSlots * 16];
+  __shared__ int lists[16 * kLmWaves * kNC];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int tt = (int)blockIdx.x / MT, m = (int)blockIdx.x % MT;
   constexpr size_t kPart = (size_t)kLmWaves * MT * 2 * kWave;
@@ -369,7 +433,7 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_combine(const f32x4* __re
       if (two) acc[0][nt] += v1[nt];
     }
   }
-  lm_tile_top16<1>(acc, lds, nfull + tt, rows, row0 + 16 * m, vocab, ntiles, partials);
+  lm_tile_top16<1>(acc, lists, nfull + tt, rows, row0 + 16 * m, vocab, ntiles, wv, partials);
 }
 
 // Top-16 of a row's ntiles sorted tile lists: 64 lane rows each merge every 64th list
@@ -416,24 +480,24 @@ __global__ void __launch_bounds__(kLmMergeThreads) k_lmhead_merge(const unsigned
   if (row_status && lane == 0) row_status[row] = bad ? 1 : 0;
 }
 
-// Work-groups resident per compute unit for k_lmhead_tiles<MT, RING> times the
-// compute units, the work-groups of one full round.
-template <int MT, int RING, bool PACKED>
-static int lmhead_round(int dev_cus) {
+// Work-groups of k_lmhead_tiles<MT, PACKED> resident per compute unit.
+template <int MT, bool PACKED>
+static int lmhead_per_cu() {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lmhead_tiles<MT, RING, PACKED>, kLmThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lmhead_tiles<MT, PACKED>, kLmThreads, 0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
-  return per_cu * dev_cus;
+  return per_cu;
 }
 
-template <int MT, int RING, bool PACKED>
+template <int MT, bool PACKED>
 static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, int rows, int hidden, int vocab,
                          int row0, int dev_cus, const LmheadWs& ws) {
   const int ntiles = lmhead_tiles(vocab);
   const int nstages = hidden / kLmStageDims;
-  const int round = lmhead_round<MT, RING, PACKED>(dev_cus);
+  const int per_cu = lmhead_per_cu<MT, PACKED>();
+  const int round = per_cu * dev_cus;                  // the work-groups of one full round
   const int tail = ntiles % round;
   int nparts = 1;
   // a last round under half full: split its tiles so that it fills the chip
@@ -445,8 +509,11 @@ static void lmhead_group(hipStream_t s, const uint16_t* h, const uint16_t* w, in
     if (need > ws.tail_bytes) nparts = 1;
   }
   const int nfull = nparts > 1 ? ntiles - tail : ntiles;
-  const int grid = nfull + (nparts > 1 ? tail * nparts : 0);
-  hipLaunchKernelGGL((k_lmhead_tiles<MT, RING, PACKED>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
+  const int nunits = nfull + (nparts > 1 ? tail * nparts : 0);
+  // one round of work-groups runs the units in turn (each every grid-th one), so that a
+  // tile's epilogue overlaps the next tile's first loads
+  const int grid = nunits < round ? nunits : round;
+  hipLaunchKernelGGL((k_lmhead_tiles<MT, PACKED>), dim3((unsigned)grid), dim3(kLmThreads), 0, s, h, w, rows, hidden,
                      vocab, row0, ntiles, nfull, nparts, ws.partials, reinterpret_cast<f32x4*>(ws.tail));
   if (nparts > 1)
     hipLaunchKernelGGL((k_lmhead_combine<MT>), dim3((unsigned)(tail * MT)), dim3(kLmThreads), 0, s,
@@ -470,15 +537,15 @@ static void lmhead_groups(hipStream_t s, const uint16_t* h, const uint16_t* w, i
   for (int row0 = 0; row0 < rows; row0 += kLmMaxRows) {
     const int n = rows - row0 < kLmMaxRows ? rows - row0 : kLmMaxRows;
     if (n <= 16)
-      lmhead_group<1, 2, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+      lmhead_group<1, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else if (n <= 32)
-      lmhead_group<2, 2, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+      lmhead_group<2, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else if (n <= 64)
-      lmhead_group<4, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+      lmhead_group<4, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else if (n <= 112)
-      lmhead_group<7, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+      lmhead_group<7, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
     else
-      lmhead_group<8, 3, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
+      lmhead_group<8, PACKED>(s, h, w, rows, hidden, vocab, row0, cus, ws);
   }
 }
 
