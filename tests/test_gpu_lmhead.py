@@ -104,6 +104,11 @@ def check_rows(idx_g, val_g, h_bits, w_bits, rows_sel=None, vchunk=16384):
     (5, 768, 140000, True),      # three stages: the 35 left over split in 3 parts of one stage
     (40, 1280, 70000, False),    # five stages, 18 left over: 5 parts of one stage
     (40, 1280, 91000, True),     # 356 tiles, 100 left over: 2 parts of unequal length (2 + 3 stages)
+    # One round of work-groups runs the tiles in turn, the W ring running on from one
+    # tile into the next; with more than half a round left over nothing is split:
+    (105, 512, 100000, True),    # 391 tiles: work-groups 0-134 run two whole tiles each
+    (105, 256, 70000, False),    # one stage per tile, so every stage hands over to the next tile
+    (7, 256, 200000, True),      # 782 tiles at two work-groups per compute unit: 270 run two
 ])
 def test_lmhead_topk16_parity(d2, rows, hidden, vocab, peaks):
     inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows + hidden + vocab, peaks=peaks)
@@ -197,6 +202,7 @@ def test_lmhead_pack_layout(d2, vocab, hidden):
     (5, 256, 270),               # a last tile with 14 columns
     (40, 2048, 70000),           # split last round, 8 parts
     (40, 1280, 91000),           # split parts of unequal length
+    (105, 256, 70000),           # tiles run in turn, one stage each
 ])
 def test_lmhead_topk16_packed_is_bit_identical(d2, rows, hidden, vocab):
     inp = synth.lmhead_inputs(rows, hidden, vocab, seed=rows * 3 + vocab)
