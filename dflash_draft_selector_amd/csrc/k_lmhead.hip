@@ -263,12 +263,15 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
       return (unsigned)((lc < last ? lc : last) * hidden + 8 * g);
     }
   };
-  // W fragment of step s of the half-stage at b, column tile nt (lane offset o)
-  auto wfrag = [&](const uint16_t* b, unsigned o, int s) -> u32x4 {
-    if constexpr (PACKED)
-      return *reinterpret_cast<const u32x4*>(b + (size_t)s * 2 * kPk + o);
-    else
-      return *reinterpret_cast<const u32x4*>(b + o + 32 * s);
+  // The half-stage at b as a buffer resource; `live` false gives one of no records,
+  // whose loads return zero without touching memory (past the last unit: the loads are
+  // still issued, so that the compiler's wait counts stay the same on every path).
+  auto wres = [&](const uint16_t* b, bool live) -> __amdgpu_buffer_rsrc_t {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b), (short)0, live ? 0x7fffffff : 0, 0x00020000);
+  };
+  // W fragment of step s of a half-stage, column tile nt (lane element offset o)
+  auto wfrag = [&](__amdgpu_buffer_rsrc_t rs, unsigned o, int s) -> u32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * (o + (PACKED ? s * 2 * kPk : 32 * s)), 0, 0);
   };
 
   // staging of one 256-dim stage of the hidden rows: thread slot e covers row
@@ -312,19 +315,19 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
   // wr1.  Each half refills its slot, kLmBurst steps at a time, with the same half of the
   // unit's next stage or, on the unit's last stage, of the next unit's first one, so
   // that the next unit starts with its first stage loaded; past the last unit it reloads
-  // itself (valid, cache-resident, unused).  Every path issues the same W loads, so that
-  // waiting for a hidden slice leaves the ring's loads in flight.
+  // nothing (loads of no records).  Every path issues the same W loads, so that waiting
+  // for a hidden slice leaves the ring's loads in flight.
   // The two 64-byte halves of every 128-byte line of a row-major W row are requested back
   // to back.  Plain loads: the line stays in L2 for its second half (non-temporal loads
   // measured 25% slower).
   u32x4 wr0[kHalf][2], wr1[kHalf][2];
   auto fill = [&](u32x4 (&wr)[kHalf][2], int part_h) {
-    const uint16_t* b = wbase(cu.tile, 2 * cu.s0 + part_h);
+    const __amdgpu_buffer_rsrc_t rs = wres(wbase(cu.tile, 2 * cu.s0 + part_h), true);
     const unsigned o0 = wlane(cu.tile, 0), o1 = wlane(cu.tile, 1);
 #pragma unroll
     for (int s = 0; s < kHalf; ++s) {
-      wr[s][0] = wfrag(b, o0, s);
-      wr[s][1] = wfrag(b, o1, s);
+      wr[s][0] = wfrag(rs, o0, s);
+      wr[s][1] = wfrag(rs, o1, s);
     }
   };
   fill(wr0, 0);
@@ -336,14 +339,15 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
   __syncthreads();
 
   // Half part_h of a stage, on ring slot part_h.  sn: the stage loaded meanwhile, of
-  // tile tn (this unit's next stage, the next unit's first, or past the last unit this
-  // stage again, staged to no use).  The W refills stay where they are written
+  // tile tn (this unit's next stage or the next unit's first); live false past the last
+  // unit (sn is then this stage: its hidden slice is staged again, to no use, and the W
+  // refills read nothing).  The W refills stay where they are written
   // (scheduling barriers), a half-stage ahead of their use, and the hidden slice is
   // staged on every path, so that the compiler does not sink its loads next to their use
   // (into the branch that would stage it), which would wait for the whole ring there.
-  auto half = [&](u32x4 (&wr)[kHalf][2], const int part_h, const int tn, const int sn) {
+  auto half = [&](u32x4 (&wr)[kHalf][2], const int part_h, const int tn, const int sn, const bool live) {
     if (part_h == 0) load_h(sn, hp);                  // the next staged hidden slice
-    const uint16_t* b = wbase(tn, 2 * sn + part_h);   // what this ring slot is refilled with
+    const __amdgpu_buffer_rsrc_t rs = wres(wbase(tn, 2 * sn + part_h), live);   // this ring slot's refill
     const unsigned o0 = wlane(tn, 0), o1 = wlane(tn, 1);
 #pragma unroll
     for (int s = 0; s < kHalf; ++s) {
@@ -360,8 +364,8 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
       if ((s + 1) % kLmBurst == 0) {
 #pragma unroll
         for (int q = s + 1 - kLmBurst; q <= s; ++q) {
-          wr[q][0] = wfrag(b, o0, q);
-          wr[q][1] = wfrag(b, o1, q);
+          wr[q][0] = wfrag(rs, o0, q);
+          wr[q][1] = wfrag(rs, o1, q);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -378,8 +382,8 @@ __global__ void __launch_bounds__(kLmThreads) k_lmhead_tiles(const uint16_t* __r
       const bool own = st + 1 < cu.ns;
       const int tn = own || !more ? cu.tile : nu.tile;
       const int sn = own ? cu.s0 + st + 1 : more ? nu.s0 : cu.s0 + st;
-      half(wr0, 0, tn, sn);
-      half(wr1, 1, tn, sn);
+      half(wr0, 0, tn, sn, own || more);
+      half(wr1, 1, tn, sn, own || more);
     }
     // the unit is done: its top-16, or its part
     if (k < nfull) {
