@@ -43,7 +43,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         "parity decisions: walk steps {walk_steps} (near ties {walk_near_ties}, in band {walk_band}); "
         "verify requests {verify_requests} (in band {verify_band})".format(**c))
     import json
-    out_dir = os.path.join(ROOT, "gpurun_out")
+    out_dir = os.path.join(ROOT, os.environ.get("DFLASH2_OUT_DIR", "gpurun_out"))
     try:
         os.makedirs(out_dir, exist_ok=True)
         with open(os.path.join(out_dir, "parity_counts.json"), "w") as f:

@@ -46,7 +46,7 @@ def assert_close_scaled(got, ref, scale, rel=REL, what=""):
 
 
 # Decision counts of every check in this process; the test session prints them and
-# writes them to gpurun_out/parity_counts.json (tests/conftest.py).
+# writes them to parity_counts.json in the run's output folder (tests/conftest.py).
 COUNTS = {"walk_steps": 0, "walk_near_ties": 0, "walk_band": 0, "verify_requests": 0, "verify_band": 0}
 
 
