@@ -8,8 +8,8 @@
 // running a sequence of 256-column vocabulary tiles (per group of up to 128 rows).  Each
 // wave owns two 16-column tiles for every 16-row tile, on v_mfma_f32_16x16x32_bf16 with
 // fp32 accumulators.  W rows go straight from HBM into the MFMA B operand (each lane 16
-// contiguous bytes of one W row per step), loaded up to twelve steps ahead in a register
-// ring that runs on from one tile into the next; the hidden rows (read by every
+// contiguous bytes of one W row per step), loaded a stage (eight steps) ahead in a
+// register ring that runs on from one tile into the next; the hidden rows (read by every
 // work-group, so cache-resident) are staged 256 dims at a time through LDS with an XOR
 // swizzle, so the 16 rows a wave reads per instruction sit in distinct banks.  The
 // epilogue rounds the accumulators to bf16, sorts each row's 32 columns per wave with
