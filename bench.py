@@ -343,7 +343,7 @@ def lmhead_measure(dflash2, torch, dev, stream, reps=10):
     return {"rows": R, "hidden": D, "vocab": V, "us_per_call": round(packed_us, 1),
             "row_major_weight_us_per_call": round(fused_us, 1),
             "roofline": {"bound": "hbm",
-                         "kernel": "dflash2_lmhead_topk16_packed = k_lmhead_tiles (packed W) + k_lmhead_merge",
+                         "kernel": "dflash2_lmhead_topk16_packed = k_lmhead_tiles (packed W; its tiles in turn) + k_lmhead_combine (split tiles) + k_lmhead_merge",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(LMHEAD_COUNTERS_MD, LMHEAD_SOURCES), "bytes_per_launch": nbytes,
