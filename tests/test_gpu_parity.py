@@ -123,8 +123,13 @@ def test_context_gate(d2, wl):
 
 def test_context_gate_ragged(d2):
     rng = np.random.default_rng(4)
+    # From 256 rows a bf16 weight takes wide tiles (64 rows x 256 columns over parts of
+    # the hidden dimension) when dim is a multiple of 256 and hidden of 128: two column
+    # tiles with one-stage parts, one part (H written by the tiles), uneven parts of two
+    # and three stages with a ragged last row group.
     for rows, hidden, dim in ((1, 8, 16), (17, 520, 64), (33, 1000, 128), (5, 4096, 1024), (300, 200, 128),
-                              (257, 1032, 256)):
+                              (257, 1032, 256), (300, 1024, 512), (300, 128, 256), (1000, 5120, 256),
+                              (640, 384, 256)):
         h = rng.standard_normal((rows, hidden)).astype(np.float32)
         w = (rng.standard_normal((dim, hidden)) / np.sqrt(hidden)).astype(np.float32)
         wb = synth.f32_to_bf16_bits(w)
@@ -142,7 +147,8 @@ def test_context_gate_bf16_h(d2):
     """h in bf16: within tolerance of the oracle, and bit-identical to the gate of the
     fp32 h that holds the same values (both weight dtypes)."""
     rng = np.random.default_rng(12)
-    for rows, hidden, dim in ((1, 8, 16), (105, 5120, 256), (33, 1000, 128), (257, 1032, 64), (5, 4096, 1024)):
+    for rows, hidden, dim in ((1, 8, 16), (105, 5120, 256), (33, 1000, 128), (257, 1032, 64), (5, 4096, 1024),
+                              (320, 1024, 256)):
         hb = synth.f32_to_bf16_bits(rng.standard_normal((rows, hidden)).astype(np.float32))
         h64 = oracle.bf16_to_f64(hb)
         w = (rng.standard_normal((dim, hidden)) / np.sqrt(hidden)).astype(np.float32)
