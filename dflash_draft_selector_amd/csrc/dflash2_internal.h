@@ -67,6 +67,8 @@ struct GateWs {
   int nsplit;                     // slices of the hidden dimension
 };
 int gate_splits(int64_t rows, int64_t hidden, int64_t dim);
+bool gate_wide(int64_t rows, int64_t hidden, int64_t dim);        // wide gate tiles (bf16 weight)
+int gate_wide_parts(int64_t rows, int64_t hidden, int64_t dim);
 GateWs carve_gate(Carver& c, int64_t rows, int64_t hidden, int64_t dim);
 constexpr int kGateBlockThreads = 512;    // threads of a standalone gate work-group
 int64_t gate_grid_blocks(int64_t rows, int64_t hidden, int64_t dim);

@@ -324,6 +324,45 @@ def test_select_gated_ragged(d2):
                                           b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
 
 
+def test_select_gated_300_rows(d2):
+    """The gated select at 20 requests of 15 positions (300 rows, not a whole number of
+    the gate's 16-row tiles' groups), hidden 1024, a bias, both activations, greedy and
+    sampled: H_out within tolerance of the oracle's gate and every other output
+    bit-identical to dflash2_select with that H; h in bf16 bit-identical to the fp32 h
+    holding the same values."""
+    import torch
+    w = synth.workload(0, B=20, K=15, V=3000, D=1024, dim=256, bf16_params=True)
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(21)
+    bias = rng.normal(0.0, 0.5, size=w.dim).astype(np.float32)
+    A64, B64, Ag, Bg = tables(inp)
+    W64, Wg, _ = gate_w(inp)
+    logits, ver = to_gpu_bits(inp["logits_bits"]), to_gpu(inp["verified"])
+    hb = synth.f32_to_bf16_bits(inp["h"].reshape(-1, w.D))
+    h64 = oracle.bf16_to_f64(hb)
+    for act, T in (("sigmoid", 0.0), ("identity", 0.8)):
+        print(f"gated select 300 rows act={act} T={T}", flush=True)
+        Hout = torch.empty((w.B, w.K, w.dim), dtype=torch.float32, device=logits.device)
+        out = d2.select_gated(logits, ver, Ag, Bg, to_gpu(h64.astype(np.float32).reshape(w.B, w.K, w.D)), Wg,
+                              to_gpu(bias), act, T, 5, H_out=Hout)
+        Href, _, pre_abs = oracle.context_gate(h64, W64, bias, True, act=act)
+        assert_close_scaled(cpu(Hout).reshape(-1, w.dim), Href, pre_abs * (0.25 if act == "sigmoid" else 1.0),
+                            what=f"gated H 300 rows {act}")
+        ref = d2.select(logits, ver, Ag, Bg, Hout, T, 5)
+        for k in ref:
+            a, b = cpu(out[k]), cpu(ref[k])
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+        Hout_b = torch.empty_like(Hout)
+        out_b = d2.select_gated(logits, ver, Ag, Bg, to_gpu_bits(hb.reshape(w.B, w.K, w.D)), Wg, to_gpu(bias), act, T,
+                                5, H_out=Hout_b)
+        np.testing.assert_array_equal(cpu(Hout_b).view(np.uint32), cpu(Hout).view(np.uint32))
+        for k in out:
+            a, b = cpu(out_b[k]), cpu(out[k])
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b, err_msg=k)
+
+
 def test_select_gated_bf16_h(d2):
     """The gated select at B 15, K 7 with h in bf16: every output, H_out included,
     bit-identical to the gated select on the fp32 h holding the same values; H_out
