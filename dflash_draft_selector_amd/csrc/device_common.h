@@ -67,8 +67,6 @@ __device__ __forceinline__ float walk_uniform(uint64_t seed, uint32_t b, uint32_
   return word_to_uniform(r.x0);
 }
 
-// ---- 16-slot row decisions shared by the pair stage and the walk ------------------
-
 // ---- 16-slot row decisions (lane-parallel) --------------------------------------------
 // A row of 16 scores lives in a group of 16 consecutive lanes (lane j of the group
 // holds slot j); the group reduces and scans it with DPP row operations.
@@ -183,7 +181,6 @@ __device__ __forceinline__ void drain_memory() { asm volatile("s_waitcnt vmcnt(0
 
 // ---- wave / block helpers ----------------------------------------------------------
 
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -198,6 +195,5 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   }
   return v;
 }
-
 
 }  // namespace df2
